@@ -1,0 +1,419 @@
+"""fp64 CPU oracle for the IP-TTCD layer forward.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import or call
+this module; only the tests, the package's ``smoke()`` check and the CPU
+baseline leg of the benchmark do.  It shares no code with the HIP library.
+
+It is a plain, slow, obviously-correct restatement of what the method
+computes, in float64 NumPy (BLAS matmul is the only library primitive).
+Sources are the pages on "Learning What to Remember: Test-Time Training via
+Context Distillation":
+
+  [README]   the GitHub README "TTCD: Test-Time Training via Context
+             Distillation" (sections "Model configuration", "Fused
+             inference kernels")
+  [NOTES]    the papernotes.org notes on the NeurIPS 2026 paper (method
+             section: overall framework, key designs 1-4)
+  [PODCAST]  the podcast transcript of the paper (cues on sliding windows,
+             Eq. 4 / Eq. 6 / Eq. 12 and Proposition 1)
+
+Readings taken where the pages leave a step open (all shared with the HIP
+path and listed in the design notes):
+  * window w holds w keys including the query's own position:
+    key j is visible to query t iff 0 <= t - j < w;
+  * the student window is a token window (not chunk aligned);
+  * the teacher path is the layer's main path (its MLP output receives the
+    fast weight);
+  * a chunk's write acts on strictly later chunks;
+  * the short conv is a full-sequence causal depthwise conv with zero left
+    padding, tap kc-1 on the current token, no bias;  <- parity unpinned
+    (orientation; the pages do not fix it)
+  * l2 normalisation is per token over d_ff with x / max(||x||, eps);
+  * beta is one scalar per (batch, chunk) and is the exact coefficient of
+    R_i K_i^T;
+  * layer glue: h = x + O W_o^T, RMSNorm(eps=1e-6, gain gamma), SwiGLU;
+    Q/K already carry any positional encoding.  <- parity unpinned (the
+    pages do not describe the glue; it is a declared standard block)
+
+Layouts (row-major, token-major): q [B,T,Hq,D], k/v [B,Tk,Hkv,D],
+x [B,T,d], w_o [d, Hq*D], w_gate/w_up [f, d], w_down0 [d, f],
+w_proj [f, f], conv taps [f, kc], beta [B, n_chunks].
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+F64 = np.float64
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=F64)
+
+
+# ==========================================================================
+# O1  dual-window causal sliding-window attention
+#     [PODCAST] cue on sliding windows: a token attends only to the most
+#     recent w tokens; [README] "Fused inference kernels": one pass yields
+#     the teacher (long window) and student (short window) outputs over the
+#     same Q/K/V; [NOTES] overall framework: w_S < w_T over one backbone.
+# ==========================================================================
+
+
+def window_attention(q, k, v, window: int, scale: Optional[float] = None,
+                     q_pos0: int = 0, rows: Optional[Sequence[int]] = None,
+                     block: int = 256):
+    """Causal sliding-window softmax attention, one window.
+
+    q [B,Tq,Hq,D], k/v [B,Tk,Hkv,D].  Query i sits at position q_pos0 + i;
+    key j at position j.  Query head h reads kv head h // (Hq/Hkv).
+    Visible set of query t: J(t) = {j : max(0, t-window+1) <= j <= t}.
+
+    Returns o [B,Tq,Hq,D] and lse [B,Hq,Tq] (natural log), both float64:
+        o[t]   = sum_{j in J} exp(s_j - m) v_j / sum_{j in J} exp(s_j - m)
+        lse[t] = m + log sum_{j in J} exp(s_j - m),   s_j = scale <q_t, k_j>
+    If ``rows`` is given, only those query indices are computed (others
+    stay zero).
+    """
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    B, Tq, Hq, D = q.shape
+    Tk, Hkv = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = np.zeros((B, Tq, Hq, D), F64)
+    lse = np.zeros((B, Hq, Tq), F64)
+    idx = np.arange(Tq) if rows is None else np.asarray(sorted(set(int(r) for r in rows)))
+    if idx.size == 0:
+        return o, lse
+    for b in range(B):
+        for s0 in range(0, idx.size, block):
+            sel = idx[s0:s0 + block]
+            t = q_pos0 + sel  # absolute positions
+            j_lo = max(0, int(t.min()) - window + 1)
+            j_hi = min(Tk - 1, int(t.max()))
+            j = np.arange(j_lo, j_hi + 1)
+            diff = t[:, None] - j[None, :]
+            mask = (diff >= 0) & (diff < window)
+            for h in range(Hq):
+                g = h // G
+                qs = q[b, sel, h, :]                      # [n, D]
+                ks = k[b, j_lo:j_hi + 1, g, :]            # [m, D]
+                vs = v[b, j_lo:j_hi + 1, g, :]
+                s = (qs @ ks.T) * scale
+                s = np.where(mask, s, -np.inf)
+                m = s.max(axis=1, keepdims=True)
+                p = np.exp(s - m)
+                l = p.sum(axis=1, keepdims=True)
+                o[b, sel, h, :] = (p @ vs) / l
+                lse[b, h, sel] = (m + np.log(l))[:, 0]
+    return o, lse
+
+
+def dual_window_attention(q, k, v, w_teacher: int, w_student: int,
+                          scale: Optional[float] = None, q_pos0: int = 0,
+                          rows: Optional[Sequence[int]] = None):
+    """Teacher (w_T) and student (w_S) outputs of one shared Q/K/V.
+
+    Returns (o_t, o_s, lse_t, lse_s).  This is the definition applied once
+    per window; the single-pass fusion the pages describe is an exact
+    rewrite of it ([README] "Fused inference kernels").
+    """
+    o_t, lse_t = window_attention(q, k, v, w_teacher, scale, q_pos0, rows)
+    o_s, lse_s = window_attention(q, k, v, w_student, scale, q_pos0, rows)
+    return o_t, o_s, lse_t, lse_s
+
+
+def window_attention_bruteforce(q, k, v, window: int, scale: Optional[float] = None,
+                                q_pos0: int = 0, band: Optional[Tuple[int, int]] = None):
+    """Pure-loop version of ``window_attention`` for tiny shapes.
+
+    ``band=(a, b)`` makes the visible keys of query t the set
+    {j : a <= t - j < b}; (0, window) is the plain window.  Used to pin the
+    vectorised oracle and the far-band identity.
+    """
+    B, Tq, Hq, D = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    Tk, Hkv = len(k[0]), len(k[0][0])
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    a, bnd = (0, window) if band is None else band
+    o = [[[[0.0] * D for _ in range(Hq)] for _ in range(Tq)] for _ in range(B)]
+    lse = [[[float("-inf")] * Tq for _ in range(Hq)] for _ in range(B)]
+    for b in range(B):
+        for i in range(Tq):
+            t = q_pos0 + i
+            for h in range(Hq):
+                g = h // G
+                keys = [jj for jj in range(Tk) if a <= t - jj < bnd]
+                if not keys:
+                    continue
+                sc = []
+                for jj in keys:
+                    acc = 0.0
+                    for e in range(D):
+                        acc += float(q[b][i][h][e]) * float(k[b][jj][g][e])
+                    sc.append(acc * scale)
+                mx = max(sc)
+                w = [math.exp(x - mx) for x in sc]
+                tot = sum(w)
+                for e in range(D):
+                    acc = 0.0
+                    for wi, jj in zip(w, keys):
+                        acc += wi * float(v[b][jj][g][e])
+                    o[b][i][h][e] = acc / tot
+                lse[b][h][i] = mx + math.log(tot)
+    return np.array(o, F64), np.array(lse, F64)
+
+
+# ==========================================================================
+# O2-O3  half-layer glue and the SwiGLU MLP activations of both paths
+#     [NOTES] key design 2: both paths' MLP activations are computed with
+#     the base weights (off-policy); the glue itself is a declared standard
+#     pre-norm block (parity unpinned by the pages).
+# ==========================================================================
+
+
+def attn_out_residual(x, o, w_o):
+    """h = x + concat_heads(o) W_o^T.   x [B,T,d], o [B,T,Hq,D], w_o [d,Hq*D]."""
+    o = _f64(o)
+    B, T, Hq, D = o.shape
+    return _f64(x) + o.reshape(B, T, Hq * D) @ _f64(w_o).T
+
+
+def rmsnorm(h, gamma=None, eps: float = 1e-6):
+    """u = h / sqrt(mean(h^2) + eps) * gamma, over the last axis."""
+    h = _f64(h)
+    u = h / np.sqrt(np.mean(h * h, axis=-1, keepdims=True) + eps)
+    if gamma is not None:
+        u = u * _f64(gamma)
+    return u
+
+
+def silu(a):
+    a = _f64(a)
+    return a / (1.0 + np.exp(-a))
+
+
+def swiglu_hidden(u, w_gate, w_up):
+    """Z = silu(u W_gate^T) * (u W_up^T): the input of W_down.  [.., f]"""
+    u = _f64(u)
+    return silu(u @ _f64(w_gate).T) * (u @ _f64(w_up).T)
+
+
+# ==========================================================================
+# O4-O8  fast-weight update of W_down (IP-TTCD)
+#     [NOTES] key design 3 (the practical update, Eq. 12 in [PODCAST]):
+#       R_i = W_down^(0) W_proj (conv_T(Z_i^T) - conv_S(Z_i^S)),
+#       K_i = l2norm(conv_S(Z_i^S)),  dW_i = beta_i R_i K_i^T;
+#     [NOTES] key design 2: off-policy activations at W_down^(0), causal
+#     prefix sum over chunks; [README] "Fused inference kernels": the conv
+#     is a chunked depthwise causal conv equal to a plain full-sequence one.
+# ==========================================================================
+
+
+def causal_depthwise_conv(z, taps):
+    """zbar[t, c] = sum_{i=0}^{kc-1} taps[c, i] * z[t - (kc-1) + i, c],
+    with z[tau < 0] = 0.  z [..., T, f], taps [f, kc]."""
+    z = _f64(z)
+    taps = _f64(taps)
+    kc = taps.shape[1]
+    T = z.shape[-2]
+    out = np.zeros_like(z)
+    for i in range(kc):
+        shift = kc - 1 - i          # how far back tap i looks
+        if shift >= T:
+            continue
+        if shift == 0:
+            out += z * taps[:, i]
+        else:
+            out[..., shift:, :] += z[..., :T - shift, :] * taps[:, i]
+    return out
+
+
+def l2_normalize(x, eps: float = 1e-12):
+    """x / max(||x||_2, eps) over the last axis (a zero row stays zero)."""
+    x = _f64(x)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return x / np.maximum(n, eps)
+
+
+def fastweight_terms(z_t, z_s, conv_t, conv_s, w_down0, w_proj, eps: float = 1e-12):
+    """Per-token write terms of one sequence.
+
+    Returns (r [T, d], k [T, f], dbar [T, f], zbar_s [T, f]):
+        dbar_t = conv_T(Z^T)_t - conv_S(Z^S)_t
+        r_t    = W_down^(0) (W_proj dbar_t)
+        k_t    = conv_S(Z^S)_t / max(||conv_S(Z^S)_t||, eps)
+    """
+    zb_t = causal_depthwise_conv(z_t, conv_t)
+    zb_s = causal_depthwise_conv(z_s, conv_s)
+    dbar = zb_t - zb_s
+    r = (dbar @ _f64(w_proj).T) @ _f64(w_down0).T
+    k = l2_normalize(zb_s, eps)
+    return r, k, dbar, zb_s
+
+
+def chunk_bounds(T: int, C: int) -> List[Tuple[int, int]]:
+    return [(i, min(i + C, T)) for i in range(0, T, C)]
+
+
+def fastweight_apply_prefix(r, k, beta, z_main, w_down0, C: int,
+                            return_states: bool = False):
+    """Running causal prefix over chunks (one sequence).
+
+        S_0 = W_down^(0),   S_{i+1} = S_i + beta_i R_i^T K_i
+        y_t = S_{floor(t/C)} z_main[t]
+
+    r [T,d], k [T,f], beta [n], z_main [T,f]  ->  y [T,d] (and S_N).
+    """
+    r, k, z = _f64(r), _f64(k), _f64(z_main)
+    T = z.shape[0]
+    S = _f64(w_down0).copy()
+    y = np.zeros((T, S.shape[0]), F64)
+    states = []
+    for i, (a, b) in enumerate(chunk_bounds(T, C)):
+        if return_states:
+            states.append(S.copy())
+        y[a:b] = z[a:b] @ S.T
+        S = S + float(beta[i]) * (r[a:b].T @ k[a:b])
+    if return_states:
+        return y, S, states
+    return y, S
+
+
+def fastweight_apply_explicit(r, k, beta, z_main, w_down0, C: int):
+    """Same result, each chunk's weight summed afresh from the explicit
+    per-chunk updates: S_i = W_down^(0) + sum_{j<i} dW_j."""
+    r, k, z = _f64(r), _f64(k), _f64(z_main)
+    T = z.shape[0]
+    bounds = chunk_bounds(T, C)
+    dWs = [float(beta[j]) * (r[a:b].T @ k[a:b]) for j, (a, b) in enumerate(bounds)]
+    y = np.zeros((T, w_down0.shape[0]), F64)
+    for i, (a, b) in enumerate(bounds):
+        S = _f64(w_down0).copy()
+        for j in range(i):
+            S = S + dWs[j]
+        y[a:b] = z[a:b] @ S.T
+    return y
+
+
+def fastweight_apply_lowrank(r, k, beta, z_main, w_down0, C: int):
+    """Same result in low-rank form, never forming a d x f update:
+        y_t = W_down^(0) z_t + sum_{j < i} beta_j R_j^T (K_j z_t)."""
+    r, k, z = _f64(r), _f64(k), _f64(z_main)
+    T = z.shape[0]
+    bounds = chunk_bounds(T, C)
+    y = z @ _f64(w_down0).T
+    for i, (a, b) in enumerate(bounds):
+        for j in range(i):
+            ja, jb = bounds[j]
+            y[a:b] += float(beta[j]) * ((z[a:b] @ k[ja:jb].T) @ r[ja:jb])
+    return y
+
+
+def fastweight_scan(z_t, z_s, z_main, conv_t, conv_s, w_down0, w_proj, beta,
+                    C: int, eps: float = 1e-12, form: str = "prefix"):
+    """Fast-weight stream + prefix + apply for a batch.
+
+    z_* [B,T,f], beta [B, n_chunks].  Returns dict with y [B,T,d],
+    state [B,d,f] (= S_N, the weight after every chunk's write), r [B,T,d],
+    k [B,T,f] (unit keys), dbar [B,T,f].
+    """
+    z_t, z_s, z_main = _f64(z_t), _f64(z_s), _f64(z_main)
+    B, T, f = z_t.shape
+    d = w_down0.shape[0]
+    y = np.zeros((B, T, d), F64)
+    st = np.zeros((B, d, f), F64)
+    rr = np.zeros((B, T, d), F64)
+    kk = np.zeros((B, T, f), F64)
+    dd = np.zeros((B, T, f), F64)
+    for b in range(B):
+        r, k, dbar, _ = fastweight_terms(z_t[b], z_s[b], conv_t, conv_s, w_down0, w_proj, eps)
+        if form == "prefix":
+            yb, S = fastweight_apply_prefix(r, k, beta[b], z_main[b], w_down0, C)
+        elif form == "explicit":
+            yb = fastweight_apply_explicit(r, k, beta[b], z_main[b], w_down0, C)
+            S = None
+        elif form == "lowrank":
+            yb = fastweight_apply_lowrank(r, k, beta[b], z_main[b], w_down0, C)
+            S = None
+        else:
+            raise ValueError(form)
+        y[b] = yb
+        if S is not None:
+            st[b] = S
+        rr[b], kk[b], dd[b] = r, k, dbar
+    return {"y": y, "state": st, "r": rr, "k": kk, "dbar": dd}
+
+
+# ==========================================================================
+# full layer (prefill) and one decode step
+# ==========================================================================
+
+
+def layer_forward(q, k, v, x, w, w_teacher: int, w_student: int, C: int,
+                  rms_eps: float = 1e-6, l2_eps: float = 1e-12,
+                  main_path: str = "teacher", scale: Optional[float] = None):
+    """IP-TTCD layer forward from Q/K/V onward (prefill).
+
+    w: dict with w_o, gamma, w_gate, w_up, w_down0, w_proj, conv_t, conv_s,
+    beta [B, n].  Returns dict with out [B,T,d] and the intermediates.
+    """
+    o_t, o_s, lse_t, lse_s = dual_window_attention(q, k, v, w_teacher, w_student, scale)
+    h_t = attn_out_residual(x, o_t, w["w_o"])
+    h_s = attn_out_residual(x, o_s, w["w_o"])
+    z_t = swiglu_hidden(rmsnorm(h_t, w.get("gamma"), rms_eps), w["w_gate"], w["w_up"])
+    z_s = swiglu_hidden(rmsnorm(h_s, w.get("gamma"), rms_eps), w["w_gate"], w["w_up"])
+    z_main, h_main = (z_t, h_t) if main_path == "teacher" else (z_s, h_s)
+    fw = fastweight_scan(z_t, z_s, z_main, w["conv_t"], w["conv_s"], w["w_down0"],
+                         w["w_proj"], w["beta"], C, l2_eps)
+    out = h_main + fw["y"]
+    return {"out": out, "o_t": o_t, "o_s": o_s, "lse_t": lse_t, "lse_s": lse_s,
+            "h_t": h_t, "h_s": h_s, "z_t": z_t, "z_s": z_s, "y": fw["y"],
+            "r": fw["r"], "k": fw["k"], "dbar": fw["dbar"], "state": fw["state"]}
+
+
+def decode_step(q, k_cache, v_cache, x, w, pos: int, w_teacher: int, w_student: int,
+                r_list, k_list, beta_list, C: int, rms_eps: float = 1e-6,
+                scale: Optional[float] = None, key_offset: int = 0):
+    """One generated token per sequence at absolute position ``pos``.
+
+    q [B,1,Hq,D]; k_cache/v_cache [B, M, Hkv, D] hold keys at positions
+    key_offset .. key_offset+M-1 (the new token's key included, at ``pos``).
+    The fast weight is taken straight from the chunk lists (low-rank form):
+        y = W_down^(0) z + sum_j beta_j R_j^T (K_j z)
+    r_list [B, n*C, d], k_list [B, n*C, f] (unit keys), beta_list [B, n].
+    """
+    B = q.shape[0]
+    # positions relative to the slice held in the cache arrays
+    qpos = pos - key_offset
+    o_t, o_s, lse_t, lse_s = dual_window_attention(q, k_cache, v_cache, w_teacher,
+                                                   w_student, scale, q_pos0=qpos)
+    h = attn_out_residual(x, o_t, w["w_o"])
+    z = swiglu_hidden(rmsnorm(h, w.get("gamma"), rms_eps), w["w_gate"], w["w_up"])
+    y = z @ _f64(w["w_down0"]).T
+    r_list, k_list = _f64(r_list), _f64(k_list)
+    n = beta_list.shape[1]
+    for b in range(B):
+        for j in range(n):
+            a, e = j * C, (j + 1) * C
+            y[b] += float(beta_list[b, j]) * ((z[b] @ k_list[b, a:e].T) @ r_list[b, a:e])
+    return {"out": h + y, "o_t": o_t, "o_s": o_s, "lse_t": lse_t, "lse_s": lse_s,
+            "h": h, "z": z, "y": y}
+
+
+def fold_lists(w_down0, r_list, k_list, beta_list, C: int):
+    """Dense weight from chunk lists: W_down^(0) + sum_j beta_j R_j^T K_j."""
+    r_list, k_list = _f64(r_list), _f64(k_list)
+    B = r_list.shape[0]
+    out = np.repeat(_f64(w_down0)[None], B, axis=0)
+    for b in range(B):
+        for j in range(beta_list.shape[1]):
+            a, e = j * C, (j + 1) * C
+            out[b] += float(beta_list[b, j]) * (r_list[b, a:e].T @ k_list[b, a:e])
+    return out
