@@ -1,0 +1,537 @@
+// C ABI of the IP-TTCD layer forward: host-side validation, workspace
+// planning and launch sequencing on one HIP stream.  No allocation, no host
+// synchronisation, no exceptions across the boundary.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/ttcd.h"
+#include "kernels.hpp"
+
+using namespace ttcd;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ttcd_status fail(ttcd_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+ttcd_status ok() {
+  g_err[0] = '\0';
+  return TTCD_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+#define REQ_PTR(p)                                                       \
+  do {                                                                   \
+    if (!(p)) return fail(TTCD_ERR_NULL_POINTER, "%s is NULL", #p);      \
+    if (!aligned16(p))                                                   \
+      return fail(TTCD_ERR_ALIGNMENT, "%s is not 16-byte aligned", #p);  \
+  } while (0)
+#define OPT_PTR(p)                                                       \
+  do {                                                                   \
+    if ((p) && !aligned16(p))                                            \
+      return fail(TTCD_ERR_ALIGNMENT, "%s is not 16-byte aligned", #p);  \
+  } while (0)
+#define OPT_PTR4(p)                                                      \
+  do {                                                                   \
+    if ((p) && !aligned4(p))                                             \
+      return fail(TTCD_ERR_ALIGNMENT, "%s is not 4-byte aligned", #p);   \
+  } while (0)
+#define HIPCHK(expr)                                                           \
+  do {                                                                         \
+    hipError_t e_ = (expr);                                                    \
+    if (e_ != hipSuccess)                                                      \
+      return fail(TTCD_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+// Bump allocator over the caller's workspace (256-byte aligned slices).
+struct Plan {
+  char* base;
+  size_t off = 0;
+  explicit Plan(void* b) : base((char*)b) {}
+  void* take(size_t bytes) {
+    off = (off + 255) & ~(size_t)255;
+    void* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  }
+};
+
+bool dt_ok(int dt) { return dt == TTCD_F32 || dt == TTCD_BF16; }
+int pad64(int n) { return (n + 63) / 64 * 64; }
+
+ttcd_status check_attn(const ttcd_attn_desc* d) {
+  if (!d) return fail(TTCD_ERR_NULL_POINTER, "desc is NULL");
+  if (!dt_ok(d->in_dtype) || !dt_ok(d->out_dtype))
+    return fail(TTCD_ERR_UNSUPPORTED, "unknown dtype");
+  if (d->batch < 1 || d->seq_q < 1 || d->seq_k < 1)
+    return fail(TTCD_ERR_BAD_SHAPE, "batch, seq_q and seq_k must be >= 1");
+  const int rows = d->kv_rows ? d->kv_rows : d->seq_k;
+  if (rows < d->seq_k) return fail(TTCD_ERR_BAD_SHAPE, "kv_rows < seq_k");
+  if (d->q_pos0 < 0 || (long)d->q_pos0 + d->seq_q > d->seq_k)
+    return fail(TTCD_ERR_BAD_SHAPE, "need 0 <= q_pos0 and q_pos0 + seq_q <= seq_k");
+  if (d->n_q_heads < 1 || d->n_kv_heads < 1 || d->n_q_heads % d->n_kv_heads)
+    return fail(TTCD_ERR_BAD_SHAPE, "n_q_heads must be a positive multiple of n_kv_heads");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(TTCD_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", d->head_dim);
+  if (d->w_student < 1 || d->w_teacher < d->w_student)
+    return fail(TTCD_ERR_BAD_SHAPE, "need 1 <= w_student <= w_teacher");
+  if ((long)rows * d->n_kv_heads * d->head_dim * d->batch > (1L << 40))
+    return fail(TTCD_ERR_BAD_SHAPE, "k/v too large");
+  if (d->seq_q == 1 && d->n_q_heads / d->n_kv_heads > 4)
+    return fail(TTCD_ERR_UNSUPPORTED, "single-query path supports up to 4 q heads per kv head");
+  return TTCD_OK;
+}
+
+float attn_scale(const ttcd_attn_desc* d) {
+  return d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)d->head_dim);
+}
+
+// ---- attention planning (shared by the stand-alone call and the layer)
+struct AttnBufs {
+  void* vt = nullptr;
+  float* part = nullptr;
+  int nsplit = 0, split_len = 0;
+};
+
+void plan_attn(const ttcd_attn_desc* d, Plan& p, AttnBufs& b) {
+  if (d->seq_q == 1) {
+    decode_attn_plan(d->w_teacher, &b.nsplit, &b.split_len);
+    b.part = (float*)p.take(decode_attn_part_bytes(d->batch, d->n_q_heads, d->head_dim, b.nsplit));
+  } else {
+    b.vt = p.take(attn_vt_bytes(d->batch, d->n_kv_heads, d->head_dim, d->seq_k, d->in_dtype));
+  }
+}
+
+hipError_t run_attn(const ttcd_attn_desc* d, const AttnBufs& wb, const void* q, const void* k,
+                    const void* v, void* o_t, void* o_s, float* lse_t, float* lse_s, int out_dt,
+                    hipStream_t s) {
+  const int rows = d->kv_rows ? d->kv_rows : d->seq_k;
+  if (d->seq_q == 1) {
+    DecodeAttnArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o_t = o_t; a.o_s = o_s; a.lse_t = lse_t; a.lse_s = lse_s;
+    a.part = wb.part;
+    a.B = d->batch; a.pos = d->q_pos0; a.kv_rows = rows; a.Hq = d->n_q_heads;
+    a.Hkv = d->n_kv_heads; a.D = d->head_dim; a.wT = d->w_teacher; a.wS = d->w_student;
+    a.scale = attn_scale(d); a.in_dt = d->in_dtype; a.out_dt = out_dt;
+    a.nsplit = wb.nsplit; a.split_len = wb.split_len;
+    return launch_decode_attn(a, s);
+  }
+  AttnArgs a{};
+  a.q = q; a.k = k; a.v = v; a.vt = wb.vt; a.vt_ld = pad64(d->seq_k);
+  a.o_t = o_t; a.o_s = o_s; a.lse_t = lse_t; a.lse_s = lse_s;
+  a.B = d->batch; a.Tq = d->seq_q; a.Tk = d->seq_k; a.kv_rows = rows; a.q_pos0 = d->q_pos0;
+  a.Hq = d->n_q_heads; a.Hkv = d->n_kv_heads; a.D = d->head_dim; a.wT = d->w_teacher;
+  a.wS = d->w_student; a.scale = attn_scale(d); a.in_dt = d->in_dtype; a.out_dt = out_dt;
+  return launch_dual_window_attn(a, s);
+}
+
+// ---- fast-weight planning
+ttcd_status check_fw(const ttcd_fw_desc* d) {
+  if (!d) return fail(TTCD_ERR_NULL_POINTER, "desc is NULL");
+  if (!dt_ok(d->in_dtype) || !dt_ok(d->out_dtype))
+    return fail(TTCD_ERR_UNSUPPORTED, "unknown dtype");
+  if (d->batch < 1 || d->seq < 1) return fail(TTCD_ERR_BAD_SHAPE, "batch and seq must be >= 1");
+  if (d->d_model < 8 || d->d_model % 8 || d->d_ff < 8 || d->d_ff % 8)
+    return fail(TTCD_ERR_BAD_SHAPE, "d_model and d_ff must be positive multiples of 8");
+  if (d->chunk < 16 || d->chunk % 16)
+    return fail(TTCD_ERR_BAD_SHAPE, "chunk must be a positive multiple of 16");
+  if (d->conv_k < 1 || d->conv_k > 8) return fail(TTCD_ERR_BAD_SHAPE, "conv_k must be in [1, 8]");
+  return TTCD_OK;
+}
+
+struct FwBufs {
+  void *dbar, *zbt, *wpt, *m, *rst, *states;
+  float* sc;
+  int Tpad, N;
+};
+
+void plan_fw(int B, int T, int d, int f, int C, int dt, Plan& p, FwBufs& w) {
+  const size_t es = dsize(dt);
+  w.Tpad = pad64(T);
+  w.N = (T + C - 1) / C;
+  w.dbar = p.take((size_t)B * w.Tpad * f * es);
+  w.zbt = p.take((size_t)B * f * w.Tpad * es);
+  w.sc = (float*)p.take((size_t)B * w.Tpad * sizeof(float));
+  w.wpt = p.take((size_t)f * f * es);
+  w.m = p.take((size_t)d * f * es);
+  w.rst = p.take((size_t)B * d * w.Tpad * es);
+  w.states = p.take((size_t)B * (w.N > 1 ? w.N - 1 : 0) * d * f * es);
+}
+
+// Runs the fast-weight stream, residual projection, prefix states and the
+// apply.  res (fp32 [B*T, d]) non-NULL: out = res + y; else out = y (out_dt).
+hipError_t run_fw(int B, int T, int d, int f, int C, int kc, float eps, int dt,
+                  const void* zt, const void* zs, const void* zmain, const void* conv_t,
+                  const void* conv_s, const void* w0, const void* wp, const float* beta,
+                  const float* res, void* out, int out_dt, float* state_out, const FwBufs& w,
+                  hipStream_t s) {
+  hipError_t e;
+  const int N = w.N;
+  // (1) conv, difference, key norms
+  StreamArgs sa{};
+  sa.zt = zt; sa.zs = zs; sa.conv_t = conv_t; sa.conv_s = conv_s; sa.beta = beta;
+  sa.dbar = w.dbar; sa.zbt = w.zbt; sa.sc = w.sc;
+  sa.B = B; sa.T = T; sa.f = f; sa.kc = kc; sa.chunk = C; sa.nchunks = N; sa.eps = eps;
+  sa.in_dt = dt;
+  if ((e = launch_fw_stream(sa, s)) != hipSuccess) return e;
+  // (2) M = W0 W_proj  (as NT: B operand = W_proj^T)
+  if ((e = launch_transpose(wp, w.wpt, f, f, f, f, 1, 0, 0, (int)dsize(dt), s)) != hipSuccess)
+    return e;
+  GemmArgs g{};
+  g.A = w0; g.lda = f; g.B = w.wpt; g.ldb = f; g.C = w.m; g.ldc = f;
+  g.M = d; g.N = f; g.K = f; g.in_dt = dt; g.out_dt = dt; g.epi = EPI_STORE; g.batch = 1;
+  if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+  // (3) Rs^T[b] = (M dbar_b^T) * sc_b   -> [d, Tpad]
+  g = GemmArgs{};
+  g.A = w.m; g.lda = f; g.B = w.dbar; g.ldb = f; g.C = w.rst; g.ldc = w.Tpad;
+  g.M = d; g.N = w.Tpad; g.K = f; g.in_dt = dt; g.out_dt = dt; g.epi = EPI_STORE;
+  g.colscale = w.sc; g.batch = B; g.sA = 0; g.sB = (long)w.Tpad * f;
+  g.sC = (long)d * w.Tpad; g.sScale = w.Tpad;
+  if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+  // (4) prefix states S_1 .. S_{N-1} (and S_N when asked for)
+  const int nstates = N - 1;
+  const int nwrites = state_out ? N : nstates;
+  if (nwrites > 0) {
+    StateArgs st{};
+    st.A = w.rst; st.lda = w.Tpad; st.B = w.zbt; st.ldb = w.Tpad; st.W0 = w0;
+    st.states = w.states; st.final_out = state_out;
+    st.d = d; st.f = f; st.T = T; st.chunk = C; st.nstates = nstates; st.nwrites = nwrites;
+    st.in_dt = dt; st.st_dt = dt; st.batch = B; st.sA = (long)d * w.Tpad;
+    st.sB = (long)f * w.Tpad; st.sStates = (long)nstates * d * f; st.sFinal = (long)d * f;
+    if ((e = launch_fw_states(st, s)) != hipSuccess) return e;
+  }
+  // (5) apply: out = [res +] Z_main S_{t/C}^T
+  g = GemmArgs{};
+  g.A = zmain; g.lda = f; g.B = w0; g.ldb = f; g.C = out; g.ldc = d;
+  g.M = T; g.N = d; g.K = f; g.in_dt = dt; g.out_dt = res ? F32 : out_dt;
+  g.epi = res ? EPI_RESIDUAL : EPI_STORE;
+  g.res = res; g.ldr = d; g.res_rows = B * T; g.res_dt = F32;
+  g.batch = B; g.sA = (long)T * f; g.sB = 0; g.sC = (long)T * d; g.sRes = (long)T * d;
+  g.chunk = C; g.Bchunks = w.states; g.sBchunk = (long)d * f;
+  g.sBchunksBatch = (long)nstates * d * f;
+  return launch_gemm(g, s);
+}
+
+ttcd_status check_layer(const ttcd_layer_desc* d, const ttcd_fw_state* dec) {
+  if (!d) return fail(TTCD_ERR_NULL_POINTER, "desc is NULL");
+  ttcd_status st = check_attn(&d->attn);
+  if (st != TTCD_OK) return st;
+  if (d->d_model < 8 || d->d_model % 8 || d->d_ff < 8 || d->d_ff % 8)
+    return fail(TTCD_ERR_BAD_SHAPE, "d_model and d_ff must be positive multiples of 8");
+  if (d->chunk < 16 || d->chunk % 16)
+    return fail(TTCD_ERR_BAD_SHAPE, "chunk must be a positive multiple of 16");
+  if (d->conv_k < 1 || d->conv_k > 8) return fail(TTCD_ERR_BAD_SHAPE, "conv_k must be in [1, 8]");
+  if (d->main_path != TTCD_MAIN_TEACHER && d->main_path != TTCD_MAIN_STUDENT)
+    return fail(TTCD_ERR_BAD_SHAPE, "unknown main_path");
+  if (dec) {
+    if (d->attn.seq_q != 1) return fail(TTCD_ERR_BAD_SHAPE, "decode needs seq_q == 1");
+    if (d->attn.q_pos0 != d->attn.seq_k - 1)
+      return fail(TTCD_ERR_BAD_SHAPE, "decode needs q_pos0 == seq_k - 1");
+    if (dec->n_chunks < 0) return fail(TTCD_ERR_BAD_SHAPE, "n_chunks < 0");
+  } else {
+    if (d->attn.seq_q != d->attn.seq_k || d->attn.q_pos0 != 0)
+      return fail(TTCD_ERR_BAD_SHAPE, "prefill needs seq_q == seq_k and q_pos0 == 0");
+  }
+  return TTCD_OK;
+}
+
+struct LayerBufs {
+  AttnBufs at;
+  void *o[2], *u, *z[2], *zdec;
+  float *h[2], *lse[2], *y;
+  float* cbuf;
+  FwBufs fw;
+};
+
+void plan_layer(const ttcd_layer_desc* d, const ttcd_fw_state* dec, Plan& p, LayerBufs& b) {
+  const ttcd_attn_desc& a = d->attn;
+  const int dt = a.in_dtype;
+  const size_t es = dsize(dt);
+  const long BT = (long)a.batch * a.seq_q;
+  const long HD = (long)a.n_q_heads * a.head_dim;
+  plan_attn(&a, p, b.at);
+  for (int i = 0; i < 2; ++i) {
+    b.o[i] = p.take(BT * HD * es);
+    b.lse[i] = (float*)p.take((size_t)a.batch * a.n_q_heads * a.seq_q * sizeof(float));
+    b.h[i] = (float*)p.take(BT * d->d_model * sizeof(float));
+    b.z[i] = p.take(BT * d->d_ff * es);
+  }
+  b.u = p.take(BT * d->d_model * es);
+  b.y = (float*)p.take(BT * d->d_model * sizeof(float));
+  if (dec) {
+    const long rows = (long)dec->n_chunks * d->chunk;
+    const long nseg = (rows + 255) / 256;
+    b.cbuf = (float*)p.take(((size_t)a.batch * rows + (size_t)a.batch * nseg * d->d_model) *
+                            sizeof(float));
+  } else {
+    plan_fw(a.batch, a.seq_q, d->d_model, d->d_ff, d->chunk, dt, p, b.fw);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ttcd_status_string(ttcd_status s) {
+  switch (s) {
+    case TTCD_OK: return "TTCD_OK";
+    case TTCD_ERR_NULL_POINTER: return "TTCD_ERR_NULL_POINTER";
+    case TTCD_ERR_BAD_SHAPE: return "TTCD_ERR_BAD_SHAPE";
+    case TTCD_ERR_UNSUPPORTED: return "TTCD_ERR_UNSUPPORTED";
+    case TTCD_ERR_WORKSPACE_TOO_SMALL: return "TTCD_ERR_WORKSPACE_TOO_SMALL";
+    case TTCD_ERR_ALIGNMENT: return "TTCD_ERR_ALIGNMENT";
+    case TTCD_ERR_HIP: return "TTCD_ERR_HIP";
+  }
+  return "TTCD_ERR_UNKNOWN";
+}
+
+const char* ttcd_last_error(void) { return g_err; }
+
+const char* ttcd_version(void) { return "0.1.0 gfx950"; }
+
+size_t ttcd_dual_window_attn_workspace_size(const ttcd_attn_desc* d) {
+  if (check_attn(d) != TTCD_OK) return 0;
+  Plan p(nullptr);
+  AttnBufs b;
+  plan_attn(d, p, b);
+  return p.off;
+}
+
+ttcd_status ttcd_dual_window_attn(const ttcd_attn_desc* d, const void* q, const void* k,
+                                  const void* v, void* o_t, void* o_s, float* lse_t,
+                                  float* lse_s, void* ws, size_t ws_bytes, void* stream) {
+  ttcd_status st = check_attn(d);
+  if (st != TTCD_OK) return st;
+  REQ_PTR(q); REQ_PTR(k); REQ_PTR(v); REQ_PTR(o_t); REQ_PTR(o_s);
+  OPT_PTR4(lse_t); OPT_PTR4(lse_s);
+  const size_t need = ttcd_dual_window_attn_workspace_size(d);
+  if (ws_bytes < need)
+    return fail(TTCD_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (need && !ws) return fail(TTCD_ERR_NULL_POINTER, "workspace is NULL");
+  OPT_PTR(ws);
+  Plan p(ws);
+  AttnBufs b;
+  plan_attn(d, p, b);
+  HIPCHK(run_attn(d, b, q, k, v, o_t, o_s, lse_t, lse_s, d->out_dtype, (hipStream_t)stream));
+  return ok();
+}
+
+size_t ttcd_fastweight_scan_workspace_size(const ttcd_fw_desc* d) {
+  if (check_fw(d) != TTCD_OK) return 0;
+  Plan p(nullptr);
+  FwBufs w;
+  plan_fw(d->batch, d->seq, d->d_model, d->d_ff, d->chunk, d->in_dtype, p, w);
+  return p.off;
+}
+
+ttcd_status ttcd_fastweight_scan(const ttcd_fw_desc* d, const void* zt, const void* zs,
+                                 const void* zmain, const void* conv_t, const void* conv_s,
+                                 const void* w_down0, const void* w_proj, const float* beta,
+                                 void* y, float* state_out, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  ttcd_status st = check_fw(d);
+  if (st != TTCD_OK) return st;
+  REQ_PTR(zt); REQ_PTR(zs); REQ_PTR(zmain); REQ_PTR(conv_t); REQ_PTR(conv_s);
+  REQ_PTR(w_down0); REQ_PTR(w_proj); REQ_PTR(y); OPT_PTR(state_out);
+  if (!beta) return fail(TTCD_ERR_NULL_POINTER, "beta is NULL");
+  OPT_PTR4(beta);
+  const size_t need = ttcd_fastweight_scan_workspace_size(d);
+  if (ws_bytes < need)
+    return fail(TTCD_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (!ws) return fail(TTCD_ERR_NULL_POINTER, "workspace is NULL");
+  OPT_PTR(ws);
+  Plan p(ws);
+  FwBufs w;
+  plan_fw(d->batch, d->seq, d->d_model, d->d_ff, d->chunk, d->in_dtype, p, w);
+  const float eps = d->l2_eps > 0.f ? d->l2_eps : 1e-12f;
+  HIPCHK(run_fw(d->batch, d->seq, d->d_model, d->d_ff, d->chunk, d->conv_k, eps, d->in_dtype, zt,
+                zs, zmain, conv_t, conv_s, w_down0, w_proj, beta, nullptr, y, d->out_dtype,
+                state_out, w, (hipStream_t)stream));
+  return ok();
+}
+
+size_t ttcd_layer_forward_workspace_size(const ttcd_layer_desc* d, const ttcd_fw_state* dec) {
+  if (check_layer(d, dec) != TTCD_OK) return 0;
+  Plan p(nullptr);
+  LayerBufs b;
+  plan_layer(d, dec, p, b);
+  return p.off;
+}
+
+ttcd_status ttcd_layer_forward(const ttcd_layer_desc* d, const ttcd_layer_weights* wt,
+                               const void* q, const void* k, const void* v, const void* x,
+                               float* out, const ttcd_fw_state* dec, const ttcd_layer_aux* aux,
+                               void* ws, size_t ws_bytes, void* stream) {
+  ttcd_status st = check_layer(d, dec);
+  if (st != TTCD_OK) return st;
+  if (!wt) return fail(TTCD_ERR_NULL_POINTER, "weights is NULL");
+  REQ_PTR(q); REQ_PTR(k); REQ_PTR(v); REQ_PTR(x); REQ_PTR(out);
+  REQ_PTR(wt->w_o); OPT_PTR(wt->rms_gamma); REQ_PTR(wt->w_gate); REQ_PTR(wt->w_up);
+  REQ_PTR(wt->w_down0);
+  if (!dec) {
+    REQ_PTR(wt->w_proj); REQ_PTR(wt->conv_t); REQ_PTR(wt->conv_s);
+    if (!wt->beta) return fail(TTCD_ERR_NULL_POINTER, "weights->beta is NULL");
+    OPT_PTR4(wt->beta);
+  } else {
+    OPT_PTR(dec->state_dense); OPT_PTR(dec->r_list); OPT_PTR(dec->k_list);
+    OPT_PTR4(dec->beta_list);
+    if (!dec->state_dense && dec->n_chunks > 0 && (!dec->r_list || !dec->k_list || !dec->beta_list))
+      return fail(TTCD_ERR_NULL_POINTER, "decode state: lists or state_dense required");
+  }
+  const ttcd_layer_aux no_aux{};
+  if (!aux) aux = &no_aux;
+  OPT_PTR(aux->o_teacher); OPT_PTR(aux->o_student); OPT_PTR4(aux->lse_teacher);
+  OPT_PTR4(aux->lse_student); OPT_PTR(aux->z_teacher); OPT_PTR(aux->z_student);
+  OPT_PTR(aux->y); OPT_PTR(aux->state_out);
+  if (dec && (aux->z_student || aux->state_out))
+    return fail(TTCD_ERR_BAD_SHAPE, "z_student / state_out are prefill-only outputs");
+  const size_t need = ttcd_layer_forward_workspace_size(d, dec);
+  if (ws_bytes < need)
+    return fail(TTCD_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (!ws) return fail(TTCD_ERR_NULL_POINTER, "workspace is NULL");
+  OPT_PTR(ws);
+
+  hipStream_t s = (hipStream_t)stream;
+  const ttcd_attn_desc& a = d->attn;
+  const int dt = a.in_dtype;
+  const int B = a.batch, T = a.seq_q;
+  const long BT = (long)B * T;
+  const int dm = d->d_model, f = d->d_ff;
+  const int HD = a.n_q_heads * a.head_dim;
+  const float rms_eps = d->rms_eps > 0.f ? d->rms_eps : 1e-6f;
+  const float l2_eps = d->l2_eps > 0.f ? d->l2_eps : 1e-12f;
+  Plan p(ws);
+  LayerBufs b;
+  plan_layer(d, dec, p, b);
+  void* o[2] = {aux->o_teacher ? aux->o_teacher : b.o[0], aux->o_student ? aux->o_student : b.o[1]};
+  float* lse[2] = {aux->lse_teacher ? aux->lse_teacher : b.lse[0],
+                   aux->lse_student ? aux->lse_student : b.lse[1]};
+  void* z[2] = {aux->z_teacher ? aux->z_teacher : b.z[0], aux->z_student ? aux->z_student : b.z[1]};
+
+  // attention, both windows, O in the layer's element type
+  HIPCHK(run_attn(&a, b.at, q, k, v, o[0], o[1], lse[0], lse[1], dt, s));
+
+  // per path: h = x + O W_o^T ; Z = SwiGLU(RMSNorm(h))
+  const int npaths = dec ? 1 : 2;
+  const int main = (d->main_path == TTCD_MAIN_STUDENT) ? 1 : 0;
+  for (int pi = 0; pi < npaths; ++pi) {
+    const int path = dec ? main : pi;
+    GemmArgs g{};
+    g.A = o[path]; g.lda = HD; g.B = wt->w_o; g.ldb = HD; g.C = b.h[path]; g.ldc = dm;
+    g.M = (int)BT; g.N = dm; g.K = HD; g.in_dt = dt; g.out_dt = F32; g.epi = EPI_RESIDUAL;
+    g.res = x; g.ldr = dm; g.res_rows = (int)BT; g.res_dt = dt; g.batch = 1;
+    HIPCHK(launch_gemm(g, s));
+    HIPCHK(launch_rmsnorm(b.h[path], wt->rms_gamma, b.u, (int)BT, dm, rms_eps, dt, dt, s));
+    g = GemmArgs{};
+    g.A = b.u; g.lda = dm; g.B = wt->w_gate; g.B2 = wt->w_up; g.ldb = dm; g.C = z[path];
+    g.ldc = f; g.M = (int)BT; g.N = f; g.K = dm; g.in_dt = dt; g.out_dt = dt;
+    g.epi = EPI_SWIGLU; g.batch = 1;
+    HIPCHK(launch_gemm(g, s));
+  }
+
+  if (!dec) {
+    float* y = aux->y;
+    if (y) {
+      HIPCHK(run_fw(B, T, dm, f, d->chunk, d->conv_k, l2_eps, dt, z[0], z[1], z[main],
+                    wt->conv_t, wt->conv_s, wt->w_down0, wt->w_proj, wt->beta, nullptr, y, F32,
+                    aux->state_out, b.fw, s));
+      HIPCHK(launch_add(b.h[main], y, out, BT * dm, s));
+    } else {
+      HIPCHK(run_fw(B, T, dm, f, d->chunk, d->conv_k, l2_eps, dt, z[0], z[1], z[main],
+                    wt->conv_t, wt->conv_s, wt->w_down0, wt->w_proj, wt->beta, b.h[main], out,
+                    F32, aux->state_out, b.fw, s));
+    }
+    return ok();
+  }
+
+  // decode: y = S z  (dense) or W0 z + sum_j beta_j R_j^T (K_j z)  (lists)
+  float* y = aux->y ? aux->y : b.y;
+  if (dec->state_dense) {
+    HIPCHK(launch_dense_apply(dec->state_dense, z[main], y, B, dm, f, dt, 0, s));
+  } else {
+    GemmArgs g{};
+    g.A = z[main]; g.lda = f; g.B = wt->w_down0; g.ldb = f; g.C = y; g.ldc = dm;
+    g.M = B; g.N = dm; g.K = f; g.in_dt = dt; g.out_dt = F32; g.epi = EPI_STORE; g.batch = 1;
+    HIPCHK(launch_gemm(g, s));
+    if (dec->n_chunks > 0) {
+      ListApplyArgs la{};
+      la.z = z[main]; la.r_list = dec->r_list; la.k_list = dec->k_list; la.beta = dec->beta_list;
+      la.cbuf = b.cbuf; la.y = y; la.B = B; la.d = dm; la.f = f; la.chunk = d->chunk;
+      la.n = dec->n_chunks; la.in_dt = dt;
+      HIPCHK(launch_list_apply(la, s));
+    }
+  }
+  HIPCHK(launch_add(b.h[main], y, out, (long)B * dm, s));
+  return ok();
+}
+
+size_t ttcd_fastweight_fold_workspace_size(const ttcd_fw_desc* d, int32_t n_chunks) {
+  if (!d || n_chunks < 0) return 0;
+  const size_t rows = (size_t)n_chunks * d->chunk;
+  const size_t es = dsize(d->in_dtype);
+  Plan p(nullptr);
+  p.take((size_t)d->batch * d->d_model * rows * es);
+  p.take((size_t)d->batch * d->d_ff * rows * es);
+  p.take((size_t)d->batch * rows * sizeof(float));
+  return p.off;
+}
+
+
+ttcd_status ttcd_fastweight_fold(const ttcd_fw_desc* d, const void* w_down0, const void* r_list,
+                                 const void* k_list, const float* beta_list, int32_t n_chunks,
+                                 float* state_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!d) return fail(TTCD_ERR_NULL_POINTER, "desc is NULL");
+  if (!dt_ok(d->in_dtype)) return fail(TTCD_ERR_UNSUPPORTED, "unknown dtype");
+  if (d->batch < 1 || d->d_model < 8 || d->d_model % 8 || d->d_ff < 8 || d->d_ff % 8)
+    return fail(TTCD_ERR_BAD_SHAPE, "batch >= 1, d_model and d_ff multiples of 8");
+  if (d->chunk < 16 || d->chunk % 16)
+    return fail(TTCD_ERR_BAD_SHAPE, "chunk must be a positive multiple of 16");
+  if (n_chunks < 0) return fail(TTCD_ERR_BAD_SHAPE, "n_chunks < 0");
+  REQ_PTR(w_down0); REQ_PTR(state_out);
+  if (n_chunks > 0) {
+    REQ_PTR(r_list); REQ_PTR(k_list);
+    if (!beta_list) return fail(TTCD_ERR_NULL_POINTER, "beta_list is NULL");
+    OPT_PTR4(beta_list);
+  }
+  const size_t need = ttcd_fastweight_fold_workspace_size(d, n_chunks);
+  if (ws_bytes < need)
+    return fail(TTCD_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (need && !ws) return fail(TTCD_ERR_NULL_POINTER, "workspace is NULL");
+  OPT_PTR(ws);
+  hipStream_t s = (hipStream_t)stream;
+  const int B = d->batch, dm = d->d_model, f = d->d_ff, C = d->chunk, dt = d->in_dtype;
+  const long rows = (long)n_chunks * C;
+  if (rows > (1L << 30)) return fail(TTCD_ERR_BAD_SHAPE, "lists too long");
+  Plan p(ws);
+  void* rst = p.take((size_t)B * dm * rows * dsize(dt));
+  void* kt = p.take((size_t)B * f * rows * dsize(dt));
+  if (n_chunks > 0) {
+    HIPCHK(launch_transpose_scale(r_list, rst, (int)rows, dm, B, beta_list, C, n_chunks, dt, s));
+    HIPCHK(launch_transpose_scale(k_list, kt, (int)rows, f, B, nullptr, 1, 0, dt, s));
+  }
+  StateArgs st{};
+  st.A = rst; st.lda = rows; st.B = kt; st.ldb = rows; st.W0 = w_down0;
+  st.states = nullptr; st.final_out = state_out;
+  st.d = dm; st.f = f; st.T = (int)rows; st.chunk = C; st.nstates = 0; st.nwrites = n_chunks;
+  st.in_dt = dt; st.st_dt = F32; st.batch = B; st.sA = (long)dm * rows; st.sB = (long)f * rows;
+  st.sStates = 0; st.sFinal = (long)dm * f;
+  if (n_chunks > 0) {
+    HIPCHK(launch_fw_states(st, s));
+  } else {
+    HIPCHK(launch_widen_repeat(w_down0, state_out, (long)dm * f, B, dt, s));
+  }
+  return ok();
+}
+
+}  // extern "C"

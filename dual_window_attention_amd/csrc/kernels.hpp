@@ -1,0 +1,152 @@
+// Internal launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ttcd {
+
+enum DType { F32 = 0, BF16 = 1 };
+
+inline size_t dsize(int dt) { return dt == BF16 ? 2 : 4; }
+
+// ---------------------------------------------------------------- attention
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* vt;           // workspace: V transposed [B][Hkv][D][vt_ld] (bf16 path)
+  int vt_ld;
+  void* o_t;
+  void* o_s;
+  float* lse_t;
+  float* lse_s;
+  int B, Tq, Tk, kv_rows, q_pos0, Hq, Hkv, D, wT, wS;
+  float scale;
+  int in_dt, out_dt;
+};
+// Returns hipSuccess or the launch error.
+hipError_t launch_dual_window_attn(const AttnArgs& a, hipStream_t s);
+size_t attn_vt_bytes(int B, int Hkv, int D, int Tk, int in_dt);
+
+// ---------------------------------------------------------------- decode attention
+struct DecodeAttnArgs {
+  const void* q;      // [B, 1, Hq, D]
+  const void* k;      // [B, kv_rows, Hkv, D]
+  const void* v;
+  void* o_t;          // [B, 1, Hq, D] out_dt
+  void* o_s;
+  float* lse_t;       // [B, Hq]
+  float* lse_s;
+  float* part;        // workspace partials
+  int B, pos, kv_rows, Hq, Hkv, D, wT, wS;
+  float scale;
+  int in_dt, out_dt;
+  int nsplit, split_len;
+};
+void decode_attn_plan(int wT, int* nsplit, int* split_len);
+size_t decode_attn_part_bytes(int B, int Hq, int D, int nsplit);
+hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- GEMM (C = A B^T)
+// A [M, K] (row stride lda), B [N, K] (row stride ldb), both K-contiguous.
+enum Epi {
+  EPI_STORE = 0,        // C = acc (* colscale[n] if given)
+  EPI_RESIDUAL = 1,     // C(f32) = acc + res[(m % res_rows) * ldr + n]
+  EPI_SWIGLU = 2,       // C = silu(A Bg^T) * (A Bu^T); B2 = Bu, N = f
+};
+struct GemmArgs {
+  const void* A; long lda;
+  const void* B; long ldb;
+  const void* B2;                 // second B (swiglu up) or NULL
+  void* C; long ldc;
+  int M, N, K;
+  int in_dt;                      // A, B dtype
+  int out_dt;                     // C dtype
+  int epi;
+  const float* colscale;          // EPI_STORE: per-column scale (or NULL)
+  const void* res; long ldr; int res_rows; int res_dt;   // EPI_RESIDUAL
+  // batching over blockIdx.z: pointer strides in elements
+  int batch; long sA, sB, sC, sRes, sScale;
+  // chunked B (fast-weight apply): rows [c*chunk, (c+1)*chunk) of each batch
+  // use B = (c == 0 ? B : Bchunks + (c-1) * sBchunk); 0 disables
+  int chunk; const void* Bchunks; long sBchunk; long sBchunksBatch;
+};
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
+
+// Fast-weight prefix states:
+//   acc = W0 (fp32); for i in [0, nstates): acc += A_i B_i^T over tokens of
+//   chunk i; states[i] = acc  (state i = weight after chunk i's write).
+// A = Rs^T [d, T] (lda = T), B = Zb^T [f, T] (ldb = T).
+struct StateArgs {
+  const void* A; long lda;
+  const void* B; long ldb;
+  const void* W0;                  // [d, f] in_dt
+  void* states;                    // [nstates, d, f] st_dt
+  float* final_out;                // optional [d, f] fp32: weight after all writes
+  int d, f, T, chunk, nstates, nwrites;
+  int in_dt, st_dt;
+  int batch; long sA, sB, sStates, sFinal;
+};
+hipError_t launch_fw_states(const StateArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- elementwise / stream
+// u = rmsnorm(h) * gamma, h fp32 [rows, d] -> u [rows, d] out_dt
+hipError_t launch_rmsnorm(const float* h, const void* gamma, void* u, int rows, int d,
+                          float eps, int in_dt, int out_dt, hipStream_t s);
+
+// fast-weight stream: conv, difference, key norms.
+//   dbar [B, T, f] = conv_t(zt) - conv_s(zs)   (in_dt)
+//   zbt  [B, f, T] = conv_s(zs) transposed      (in_dt)
+//   sc   [B, T]    = beta[b, t / chunk] / max(||conv_s(zs)[t]||, eps)
+struct StreamArgs {
+  const void* zt; const void* zs;
+  const void* conv_t; const void* conv_s;
+  const float* beta;
+  void* dbar; void* zbt; float* sc;
+  int B, T, f, kc, chunk, nchunks;
+  float eps;
+  int in_dt;
+};
+hipError_t launch_fw_stream(const StreamArgs& a, hipStream_t s);
+
+// out [cols, rows] = in [rows, cols]^T (per batch), 2- or 4-byte elements
+hipError_t launch_transpose(const void* in, void* out, int rows, int cols, long ld_in,
+                            long ld_out, int batch, long s_in, long s_out, int esize,
+                            hipStream_t s);
+// out[b] [cols, rows] = in[b] [rows, cols]^T, row r scaled by
+// scale[b * nscale + r / rows_per_scale] when scale is given
+hipError_t launch_transpose_scale(const void* in, void* out, int rows, int cols, int batch,
+                                  const float* scale, int rows_per_scale, int nscale, int dt,
+                                  hipStream_t s);
+// V [B, kv_rows, Hkv, D] -> vt [B, Hkv, D, vt_ld] (keys >= Tk zero)
+hipError_t launch_v_transpose(const void* v, void* vt, int B, int Tk, int kv_rows, int Hkv,
+                              int D, int vt_ld, int esize, hipStream_t s);
+
+// decode fast-weight apply from low-rank lists:
+//   c[b, t]  = k_list[b, t] . z[b]          (t < n*chunk)
+//   y[b]    += sum_j beta[b, j] sum_{t in j} c[b, t] r_list[b, t]
+struct ListApplyArgs {
+  const void* z;          // [B, f] in_dt
+  const void* r_list;     // [B, n*C, d]
+  const void* k_list;     // [B, n*C, f]
+  const float* beta;      // [B, n]
+  float* cbuf;            // workspace [B, n*C]
+  float* y;               // [B, d] fp32, accumulated into
+  int B, d, f, chunk, n;
+  int in_dt;
+};
+hipError_t launch_list_apply(const ListApplyArgs& a, hipStream_t s);
+// y[b] (+)= S[b] z[b], S fp32 [B, d, f]
+hipError_t launch_dense_apply(const float* S, const void* z, float* y, int B, int d, int f,
+                              int in_dt, int accumulate, hipStream_t s);
+// out[i] = a[i] + b[i] (fp32)
+hipError_t launch_add(const float* a, const float* b, float* out, long n, hipStream_t s);
+// out[b][i] = float(in[i]) for every b < batch
+hipError_t launch_widen_repeat(const void* in, float* out, long n, int batch, int in_dt,
+                               hipStream_t s);
+// convert fp32 -> dt
+hipError_t launch_convert(const float* in, void* out, long n, int out_dt, hipStream_t s);
+
+}  // namespace ttcd

@@ -258,11 +258,9 @@ def decode_inputs(cfg: LayerConfig, seed: Optional[int] = None) -> Dict[str, obj
 
     Only the teacher window of the cache is drawn (positions
     [L - w_T + 1, L], the new token sits at L); everything older is a NaN
-    sentinel on the device.  Returned K/V windows are [B, w_T, Hkv, D].
-
-    The fast-weight state is given as low-rank chunk lists of the n = L / C
-    completed chunks: R_j rows ~ N(0, 1/L), K_j rows unit-norm Gaussians,
-    beta_j ~ U(0,1).
+    sentinel on the device.  Returned K/V windows are [B, W, Hkv, D] with
+    W = min(w_T, L + 1).  The fast-weight lists are drawn per sequence by
+    ``decode_lists``.
     """
     s = cfg.seed if seed is None else seed
     B, L, Hq, Hkv, D = cfg.batch, cfg.cache_len, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
@@ -274,18 +272,41 @@ def decode_inputs(cfg: LayerConfig, seed: Optional[int] = None) -> Dict[str, obj
     out["v_win"] = normal(s, "dec_v", (B, W, Hkv, D), 1.0, dt)
     out["x"] = normal(s, "dec_x", (B, 1, cfg.d_model), 1.0, dt)
     n = L // cfg.chunk
-    out["r_list"] = normal(s, "dec_r", (B, n * cfg.chunk, cfg.d_model), 1.0 / np.sqrt(L), dt)
-    kr = _rng(s, "dec_klist").standard_normal(size=(B, n * cfg.chunk, cfg.d_ff), dtype=np.float32)
-    kr /= np.linalg.norm(kr, axis=-1, keepdims=True)
-    out["k_list"] = _store(kr, dt)
-    del kr
     out["beta_list"] = _rng(s, "dec_beta").random(size=(B, n)).astype(np.float32)
     out["n_chunks"] = n
     out["window_start"] = L + 1 - W
     return out
 
 
+def decode_lists(cfg: LayerConfig, b: int, seed: Optional[int] = None) -> Tuple[Tensor, Tensor]:
+    """Low-rank fast-weight lists of sequence ``b``: the n = L / C completed
+    chunks, R rows ~ N(0, 1/L) [n*C, d] and K rows unit-norm Gaussians
+    [n*C, f]."""
+    s = cfg.seed if seed is None else seed
+    L = cfg.cache_len
+    n = L // cfg.chunk
+    r = normal(s, f"dec_r_{b}", (n * cfg.chunk, cfg.d_model), 1.0 / np.sqrt(L), cfg.dtype)
+    kr = _rng(s, f"dec_klist_{b}").standard_normal(size=(n * cfg.chunk, cfg.d_ff), dtype=np.float32)
+    kr /= np.linalg.norm(kr, axis=-1, keepdims=True)
+    return r, _store(kr, cfg.dtype)
+
+
 def config_summary(cfg: LayerConfig) -> Dict[str, object]:
     keys = ["name", "dtype", "batch", "seq", "n_q_heads", "n_kv_heads", "head_dim",
             "w_teacher", "w_student", "d_model", "d_ff", "chunk", "conv_k"]
     return {k: getattr(cfg, k) for k in keys}
+
+
+def to_torch(t: Tensor, device="cuda"):
+    """Copy a host tensor to ``device`` in its storage type (bit exact)."""
+    import torch
+
+    if t.dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(t.data).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(t.data)).to(device)
+
+
+def f32_to_torch(x: np.ndarray, device="cuda"):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)

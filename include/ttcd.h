@@ -1,0 +1,260 @@
+/*
+ * ttcd.h -- C ABI of the IP-TTCD layer forward for AMD Instinct MI355X (gfx950).
+ *
+ * IP-TTCD ("Learning What to Remember: Test-Time Training via Context
+ * Distillation") runs one shared Q/K/V through causal sliding-window
+ * attention twice -- a long teacher window w_T and a short student window
+ * w_S -- and writes the teacher/student gap of the SwiGLU MLP activations
+ * into the MLP down-projection as a chunk-wise fast weight.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor is caller-owned DEVICE memory, row-major, contiguous,
+ *     16-byte aligned.  The library allocates nothing, never synchronises
+ *     the host and enqueues all work on `stream` (a hipStream_t; NULL is
+ *     the default stream).
+ *   - All arguments are validated on the host before anything is
+ *     enqueued.  On error nothing is enqueued, outputs are untouched and
+ *     ttcd_last_error() holds a message (thread-local).
+ *   - Element types: TTCD_BF16 (bfloat16) or TTCD_F32.  Intermediate
+ *     accumulation is fp32 in every kernel.
+ *   - Outputs must not alias inputs.  Results are bitwise deterministic
+ *     run to run (no atomics in any reduction).
+ *   - Scratch memory is a caller-provided `workspace` of at least the
+ *     size returned by the matching *_workspace_size() call.
+ *   - Weights use the pages' column-vector convention (W_down is d x f and
+ *     maps an f-vector z to W_down z); as row-major arrays that is the
+ *     [out_features, in_features] layout.
+ */
+#ifndef TTCD_H
+#define TTCD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TTCD_OK = 0,
+  TTCD_ERR_NULL_POINTER = 1,       /* a required pointer is NULL          */
+  TTCD_ERR_BAD_SHAPE = 2,          /* sizes inconsistent or out of range  */
+  TTCD_ERR_UNSUPPORTED = 3,        /* valid but not implemented (dtype, head_dim) */
+  TTCD_ERR_WORKSPACE_TOO_SMALL = 4,
+  TTCD_ERR_ALIGNMENT = 5,          /* a pointer is not 16-byte aligned    */
+  TTCD_ERR_HIP = 6                 /* a HIP launch or runtime call failed */
+} ttcd_status;
+
+typedef enum { TTCD_F32 = 0, TTCD_BF16 = 1 } ttcd_dtype;
+
+/* Which path's MLP output receives the fast weight and forms the layer
+ * output.  The pages do not say; the teacher (the model's own long-window
+ * attention) is the default. */
+typedef enum { TTCD_MAIN_TEACHER = 0, TTCD_MAIN_STUDENT = 1 } ttcd_main_path;
+
+/* ------------------------------------------------------------------------
+ * Dual-window causal sliding-window attention.
+ *
+ * Defined by the paper's two views of one backbone (papernotes.org notes,
+ * "overall framework"; podcast transcript, sliding-window cue): a query at
+ * position t attends to the keys j with 0 <= t - j < w, for the teacher
+ * window w_T and the student window w_S <= w_T, over the SAME q/k/v.  Both
+ * outputs come out of one pass over K/V (README "Fused inference
+ * kernels").  Softmax scale `scale` (<= 0 means 1/sqrt(head_dim)).
+ *
+ *   q        [batch, seq_q, n_q_heads, head_dim]          in_dtype
+ *   k, v     [batch, kv_rows, n_kv_heads, head_dim]        in_dtype
+ *            key row j sits at absolute position j; query row i sits at
+ *            position q_pos0 + i.  kv_rows (0 = seq_k) is the per-sequence
+ *            row capacity of k/v (a decode cache may be larger than seq_k).
+ *   o_teacher, o_student [batch, seq_q, n_q_heads, head_dim] out_dtype
+ *   lse_teacher, lse_student [batch, n_q_heads, seq_q] fp32, natural-log
+ *            log-sum-exp of each row's scaled scores; either may be NULL.
+ * Query head h reads kv head h / (n_q_heads / n_kv_heads) (GQA).
+ * Requires q_pos0 + seq_q <= seq_k <= kv_rows, 1 <= w_student <= w_teacher,
+ * head_dim in {64, 128}.  Keys older than the teacher window of every query
+ * are never read, so they may hold anything (NaN included).
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t batch;
+  int32_t seq_q;
+  int32_t seq_k;
+  int32_t kv_rows;      /* 0 -> seq_k */
+  int32_t q_pos0;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t w_teacher;
+  int32_t w_student;
+  float scale;          /* <= 0 -> 1/sqrt(head_dim) */
+  ttcd_dtype in_dtype;
+  ttcd_dtype out_dtype;
+} ttcd_attn_desc;
+
+size_t ttcd_dual_window_attn_workspace_size(const ttcd_attn_desc* desc);
+
+ttcd_status ttcd_dual_window_attn(const ttcd_attn_desc* desc,
+                                  const void* q, const void* k, const void* v,
+                                  void* o_teacher, void* o_student,
+                                  float* lse_teacher, float* lse_student,
+                                  void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/* ------------------------------------------------------------------------
+ * Chunk-wise fast-weight update of W_down (IP-TTCD, off-policy).
+ *
+ * From the papernotes.org notes, key design 3 (the practical update, the
+ * paper's Eq. 12 in the podcast transcript) and key design 2 (off-policy
+ * activations at W_down^(0), causal prefix over chunks):
+ *   Zbar_T = conv_T(Z_T), Zbar_S = conv_S(Z_S)   depthwise causal conv over
+ *            the whole sequence, zero left padding, tap kc-1 multiplies the
+ *            current token, no bias;
+ *   r_t    = W_down0 W_proj (Zbar_T[t] - Zbar_S[t])                 [d]
+ *   k_t    = Zbar_S[t] / max(||Zbar_S[t]||_2, l2_eps)               [f]
+ *   dW_i   = beta[i] * sum_{t in chunk i} r_t k_t^T                 [d x f]
+ *   S_0    = W_down0,  S_{i+1} = S_i + dW_i
+ *   y_t    = S_{floor(t/chunk)} z_main[t]       (writes act on later chunks)
+ *
+ *   z_teacher, z_student, z_main  [batch, seq, d_ff]  in_dtype
+ *            (z_main may alias z_teacher or z_student)
+ *   conv_t, conv_s  [d_ff, conv_k]  in_dtype
+ *   w_down0 [d_model, d_ff], w_proj [d_ff, d_ff]     in_dtype
+ *   beta    [batch, ceil(seq/chunk)] fp32 (the exact coefficient of R_i K_i^T)
+ *   y       [batch, seq, d_model]  out_dtype
+ *   state_out [batch, d_model, d_ff] fp32 or NULL: S after every chunk's
+ *            write (the weight a decode step continues from).
+ * Requires chunk % 16 == 0, d_model % 8 == 0, d_ff % 8 == 0, conv_k in [1,8].
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t batch;
+  int32_t seq;
+  int32_t d_model;
+  int32_t d_ff;
+  int32_t chunk;
+  int32_t conv_k;
+  float l2_eps;          /* <= 0 -> 1e-12 */
+  ttcd_dtype in_dtype;
+  ttcd_dtype out_dtype;
+} ttcd_fw_desc;
+
+size_t ttcd_fastweight_scan_workspace_size(const ttcd_fw_desc* desc);
+
+ttcd_status ttcd_fastweight_scan(const ttcd_fw_desc* desc,
+                                 const void* z_teacher, const void* z_student,
+                                 const void* z_main,
+                                 const void* conv_t, const void* conv_s,
+                                 const void* w_down0, const void* w_proj,
+                                 const float* beta,
+                                 void* y, float* state_out,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/* ------------------------------------------------------------------------
+ * Whole IP-TTCD layer forward from Q/K/V onward.
+ *
+ * Per path p in {teacher, student} (the glue around attention and the MLP
+ * is a standard pre-norm decoder block; the pages do not describe it):
+ *   h_p = x + concat_heads(O_p) W_o^T
+ *   Z_p = silu(RMSNorm(h_p) W_gate^T) * (RMSNorm(h_p) W_up^T)
+ * then the fast-weight update above with z_main = Z_main and
+ *   out = h_main + y.
+ *
+ *   w_o [d_model, n_q_heads*head_dim], rms_gamma [d_model] (NULL = ones),
+ *   w_gate, w_up [d_ff, d_model], w_down0 [d_model, d_ff],
+ *   w_proj [d_ff, d_ff], conv_t, conv_s [d_ff, conv_k]: attn.in_dtype;
+ *   beta [batch, ceil(seq/chunk)] fp32.
+ *   x   [batch, seq_q, d_model]  attn.in_dtype (residual stream)
+ *   out [batch, seq_q, d_model]  fp32
+ *
+ * Prefill: dec == NULL, attn.seq_q == attn.seq_k, attn.q_pos0 == 0.
+ * Decode:  dec != NULL, attn.seq_q == 1, attn.q_pos0 = L, attn.seq_k = L+1
+ *          (the new token's k/v already written at row L of the cache).
+ *          The fast weight is W_down0 + sum_j beta_list[j] R_j^T K_j over
+ *          the dec->n_chunks completed chunks (low-rank lists), or
+ *          dec->state_dense when it is not NULL.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  const void* w_o;
+  const void* rms_gamma;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down0;
+  const void* w_proj;
+  const void* conv_t;
+  const void* conv_s;
+  const float* beta;
+} ttcd_layer_weights;
+
+typedef struct {
+  ttcd_attn_desc attn;
+  int32_t d_model;
+  int32_t d_ff;
+  int32_t chunk;
+  int32_t conv_k;
+  float rms_eps;          /* <= 0 -> 1e-6 */
+  float l2_eps;           /* <= 0 -> 1e-12 */
+  ttcd_main_path main_path;
+} ttcd_layer_desc;
+
+typedef struct {
+  const float* state_dense;  /* [batch, d_model, d_ff] fp32, or NULL        */
+  const void* r_list;        /* [batch, n_chunks*chunk, d_model] in_dtype   */
+  const void* k_list;        /* [batch, n_chunks*chunk, d_ff] in_dtype (unit keys) */
+  const float* beta_list;    /* [batch, n_chunks]                           */
+  int32_t n_chunks;
+} ttcd_fw_state;
+
+/* Optional intermediate outputs (any member may be NULL). */
+typedef struct {
+  void* o_teacher;      /* [batch, seq_q, n_q_heads, head_dim] attn.out_dtype */
+  void* o_student;
+  float* lse_teacher;   /* [batch, n_q_heads, seq_q] */
+  float* lse_student;
+  void* z_teacher;      /* [batch, seq_q, d_ff] attn.in_dtype */
+  void* z_student;      /* prefill only */
+  float* y;             /* [batch, seq_q, d_model] fast-weight MLP output */
+  float* state_out;     /* prefill only: [batch, d_model, d_ff] */
+} ttcd_layer_aux;
+
+size_t ttcd_layer_forward_workspace_size(const ttcd_layer_desc* desc,
+                                         const ttcd_fw_state* dec);
+
+ttcd_status ttcd_layer_forward(const ttcd_layer_desc* desc,
+                               const ttcd_layer_weights* weights,
+                               const void* q, const void* k, const void* v,
+                               const void* x, float* out,
+                               const ttcd_fw_state* dec,
+                               const ttcd_layer_aux* aux,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* ------------------------------------------------------------------------
+ * Fold low-rank chunk lists into a dense fast weight (decode set-up):
+ *   state_out[b] = W_down0 + sum_{j < n_chunks} beta_list[b,j] R_j^T K_j
+ * with R_j = r_list[b, j*chunk:(j+1)*chunk], K_j likewise (the prefix sum of
+ * the papernotes.org notes, key design 2, evaluated once).
+ * desc->seq is ignored; desc->in_dtype is the list/weight type.
+ * ---------------------------------------------------------------------- */
+size_t ttcd_fastweight_fold_workspace_size(const ttcd_fw_desc* desc, int32_t n_chunks);
+
+ttcd_status ttcd_fastweight_fold(const ttcd_fw_desc* desc, const void* w_down0,
+                                 const void* r_list, const void* k_list,
+                                 const float* beta_list, int32_t n_chunks,
+                                 float* state_out,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* ttcd_status_string(ttcd_status status);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char* ttcd_last_error(void);
+
+/* Library version string, e.g. "0.1.0 gfx950". */
+const char* ttcd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTCD_H */

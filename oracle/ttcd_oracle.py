@@ -387,7 +387,8 @@ def decode_step(q, k_cache, v_cache, x, w, pos: int, w_teacher: int, w_student: 
     key_offset .. key_offset+M-1 (the new token's key included, at ``pos``).
     The fast weight is taken straight from the chunk lists (low-rank form):
         y = W_down^(0) z + sum_j beta_j R_j^T (K_j z)
-    r_list [B, n*C, d], k_list [B, n*C, f] (unit keys), beta_list [B, n].
+    r_list [B, n*C, d], k_list [B, n*C, f] (unit keys), beta_list [B, n];
+    the lists may be sequences of per-batch arrays (converted slice by slice).
     """
     B = q.shape[0]
     # positions relative to the slice held in the cache arrays
@@ -397,12 +398,12 @@ def decode_step(q, k_cache, v_cache, x, w, pos: int, w_teacher: int, w_student: 
     h = attn_out_residual(x, o_t, w["w_o"])
     z = swiglu_hidden(rmsnorm(h, w.get("gamma"), rms_eps), w["w_gate"], w["w_up"])
     y = z @ _f64(w["w_down0"]).T
-    r_list, k_list = _f64(r_list), _f64(k_list)
     n = beta_list.shape[1]
     for b in range(B):
+        rb, kb = r_list[b], k_list[b]
         for j in range(n):
             a, e = j * C, (j + 1) * C
-            y[b] += float(beta_list[b, j]) * ((z[b] @ k_list[b, a:e].T) @ r_list[b, a:e])
+            y[b] += float(beta_list[b, j]) * ((z[b] @ _f64(kb[a:e]).T) @ _f64(rb[a:e]))
     return {"out": h + y, "o_t": o_t, "o_s": o_s, "lse_t": lse_t, "lse_s": lse_s,
             "h": h, "z": z, "y": y}
 

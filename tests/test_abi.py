@@ -1,0 +1,130 @@
+"""The C-ABI library loads on the host, exports every symbol the header
+declares, sizes workspaces and rejects bad arguments before touching the GPU.
+CPU only: no call here reaches a kernel launch."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ttcd.h")
+LIB = os.path.join(ROOT, "dual_window_attention_amd", "libttcd.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libttcd.so not built")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[\w\s\*]*?\b(ttcd_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_function_is_exported():
+    lib = C.CDLL(LIB)
+    names = header_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    from dual_window_attention_amd import ttcd
+    assert sorted(ttcd.EXPORTS) == names
+
+
+def test_version_and_status_strings():
+    from dual_window_attention_amd import ttcd
+    assert "gfx950" in ttcd.version()
+    lib = ttcd.lib()
+    assert lib.ttcd_status_string(0) == b"TTCD_OK"
+    assert lib.ttcd_status_string(4) == b"TTCD_ERR_WORKSPACE_TOO_SMALL"
+
+
+def _attn(**kw):
+    from dual_window_attention_amd import ttcd
+    base = dict(batch=1, seq_q=65536, seq_k=65536, kv_rows=0, q_pos0=0, n_q_heads=16,
+                n_kv_heads=8, head_dim=128, w_teacher=8192, w_student=512, scale=0.0,
+                in_dtype=1, out_dtype=1)
+    base.update(kw)
+    return ttcd.AttnDesc(**base)
+
+
+def test_workspace_sizes():
+    from dual_window_attention_amd import ttcd
+    lib = ttcd.lib()
+    d = _attn()
+    # the transposed V staging copy: B * Hkv * D * T bf16
+    assert lib.ttcd_dual_window_attn_workspace_size(C.byref(d)) == 8 * 128 * 65536 * 2
+    dd = _attn(seq_q=1, q_pos0=65536, seq_k=65537, batch=32)
+    assert 0 < lib.ttcd_dual_window_attn_workspace_size(C.byref(dd)) < 64 << 20
+    fw = ttcd.FwDesc(1, 65536, 1024, 3072, 1024, 4, 0.0, 1, 0)
+    n = lib.ttcd_fastweight_scan_workspace_size(C.byref(fw))
+    # dbar + zbar^T (2 x T f) + 63 prefix weights (d f) + ...
+    assert n > (2 * 65536 * 3072 + 63 * 1024 * 3072) * 2
+    bad = _attn(head_dim=96)
+    assert lib.ttcd_dual_window_attn_workspace_size(C.byref(bad)) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), 3),
+    (dict(w_student=9000), 2),
+    (dict(w_student=0), 2),
+    (dict(n_q_heads=12, n_kv_heads=8), 2),
+    (dict(seq_q=10, seq_k=5), 2),
+    (dict(in_dtype=7), 3),
+])
+def test_attention_rejects_bad_descriptors(kw, status):
+    from dual_window_attention_amd import ttcd
+    lib = ttcd.lib()
+    d = _attn(**kw)
+    fake = C.c_void_p(1 << 20)
+    st = lib.ttcd_dual_window_attn(C.byref(d), fake, fake, fake, fake, fake, None, None, fake,
+                                   1 << 40, None)
+    assert st == status, lib.ttcd_last_error()
+    assert lib.ttcd_last_error() != b""
+
+
+def test_attention_rejects_null_misaligned_and_small_workspace():
+    from dual_window_attention_amd import ttcd
+    lib = ttcd.lib()
+    d = _attn()
+    fake = C.c_void_p(1 << 20)
+    assert lib.ttcd_dual_window_attn(C.byref(d), None, fake, fake, fake, fake, None, None, fake,
+                                     1 << 40, None) == 1
+    odd = C.c_void_p((1 << 20) + 2)
+    assert lib.ttcd_dual_window_attn(C.byref(d), fake, odd, fake, fake, fake, None, None, fake,
+                                     1 << 40, None) == 5
+    assert lib.ttcd_dual_window_attn(C.byref(d), fake, fake, fake, fake, fake, None, None, fake,
+                                     16, None) == 4
+    assert b"workspace" in lib.ttcd_last_error()
+
+
+def test_fastweight_and_layer_reject_bad_shapes():
+    from dual_window_attention_amd import ttcd
+    lib = ttcd.lib()
+    fake = C.c_void_p(1 << 20)
+    fw = ttcd.FwDesc(1, 100, 1024, 3072, 24, 4, 0.0, 1, 0)     # chunk not a multiple of 16
+    assert lib.ttcd_fastweight_scan(C.byref(fw), *([fake] * 10), fake, 1 << 40, None) == 2
+    fw = ttcd.FwDesc(1, 100, 1024, 3072, 64, 9, 0.0, 1, 0)      # conv_k > 8
+    assert lib.ttcd_fastweight_scan(C.byref(fw), *([fake] * 10), fake, 1 << 40, None) == 2
+    a = _attn(seq_q=128, seq_k=128)
+    ld = ttcd.LayerDesc(a, 1004, 3072, 1024, 4, 0.0, 0.0, 0)   # d_model not a multiple of 8
+    w = ttcd.LayerWeights(*([1 << 20] * 8), 1 << 20)
+    assert lib.ttcd_layer_forward(C.byref(ld), C.byref(w), fake, fake, fake, fake, fake, None,
+                                  None, fake, 1 << 40, None) == 2
+    ld = ttcd.LayerDesc(_attn(seq_q=1, seq_k=128, q_pos0=127), 1024, 3072, 1024, 4, 0.0, 0.0, 0)
+    # one query without a decode state is not a prefill
+    assert lib.ttcd_layer_forward(C.byref(ld), C.byref(w), fake, fake, fake, fake, fake, None,
+                                  None, fake, 1 << 40, None) == 2
+    dec = ttcd.FwState(None, None, None, None, 3)
+    assert lib.ttcd_layer_forward(C.byref(ld), C.byref(w), fake, fake, fake, fake, fake,
+                                  C.byref(dec), None, fake, 1 << 40, None) == 1
+
+
+def test_no_oracle_import_in_product_code():
+    """The product path (package + C sources) never imports the oracle."""
+    pkg = os.path.join(ROOT, "dual_window_attention_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle", text, flags=re.M), fn
+                assert "ttcd_oracle" not in text, fn

@@ -1,0 +1,82 @@
+"""The whole IP-TTCD layer forward on the GPU against the fp64 oracle."""
+import numpy as np
+import pytest
+
+from dual_window_attention_amd import inputs as I
+from oracle import ttcd_oracle as O
+from tests.gpu_helpers import assert_close, say, to_np, tol_for
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def run_layer(cfg, main_path="teacher", aux=True):
+    from dual_window_attention_amd import ttcd
+    att = I.attention_inputs(cfg)
+    w = I.layer_weights(cfg)
+    beta = I.beta_for(cfg)
+    x = I.residual_input(cfg)
+    q, k, v = (I.to_torch(att[n]) for n in ("q", "k", "v"))
+    wd = {n: I.to_torch(t) for n, t in w.items()}
+    wd["beta"] = I.f32_to_torch(beta)
+    res = ttcd.layer_forward(q, k, v, I.to_torch(x), wd, cfg.w_teacher, cfg.w_student, cfg.chunk,
+                             main_path=main_path, aux=aux)
+    torch.cuda.synchronize()
+    wo = {n: t.f64() for n, t in w.items()}
+    wo["beta"] = beta.astype(np.float64)
+    return res, (att, wo, x)
+
+
+def oracle_layer(cfg, att, wo, x, main_path="teacher"):
+    return O.layer_forward(att["q"].f64(), att["k"].f64(), att["v"].f64(), x.f64(), wo,
+                           cfg.w_teacher, cfg.w_student, cfg.chunk, main_path=main_path)
+
+
+def check_layer(cfg, main_path="teacher"):
+    say(f"layer {cfg.name} T={cfg.seq} main={main_path}: GPU")
+    (out, aux), (att, wo, x) = run_layer(cfg, main_path)
+    say("  oracle")
+    ref = oracle_layer(cfg, att, wo, x, main_path)
+    tol = tol_for(cfg.dtype)
+    assert_close(to_np(out), ref["out"], tol, "out")
+    assert_close(to_np(aux["o_teacher"]), ref["o_t"], tol, "O_teacher")
+    assert_close(to_np(aux["o_student"]), ref["o_s"], tol, "O_student")
+    assert_close(to_np(aux["z_teacher"]), ref["z_t"], tol, "Z_teacher")
+    assert_close(to_np(aux["z_student"]), ref["z_s"], tol, "Z_student")
+    assert_close(to_np(aux["y"]), ref["y"], tol, "y (fast-weight MLP output)")
+    # the fast-weight correction alone (y - W0 z) to a relative bound
+    zm = ref["z_t"] if main_path == "teacher" else ref["z_s"]
+    corr_ref = ref["y"] - zm @ wo["w_down0"].T
+    corr = to_np(aux["y"]) - to_np(aux["z_teacher" if main_path == "teacher" else "z_student"]) @ wo["w_down0"].T
+    rel = np.linalg.norm(corr - corr_ref) / max(np.linalg.norm(corr_ref), 1e-30)
+    say(f"  fast-weight correction relL2={rel:.3e} (|corr|={np.linalg.norm(corr_ref):.3e})")
+    assert rel <= 5e-2 if cfg.dtype == "bf16" else rel <= 1e-4
+    st = to_np(aux["state_out"])
+    assert_close(st, ref["state"], (tol[0], tol[1]), "state after all writes")
+
+
+def test_tiny_fp32_layer():
+    check_layer(I.CONFIGS[1])
+
+
+def test_small_bf16_layer_ragged_chunks():
+    cfg = I.CONFIGS[3].scaled(batch=2, seq=700, n_q_heads=4, n_kv_heads=2, d_model=256,
+                              d_ff=384, w_teacher=300, w_student=40, chunk=128, seed=11)
+    check_layer(cfg)
+
+
+def test_small_bf16_layer_student_main_path():
+    cfg = I.CONFIGS[2].scaled(seq=640, d_model=192, d_ff=256, w_teacher=256, w_student=32,
+                              chunk=128, seed=12)
+    check_layer(cfg, main_path="student")
+
+
+def test_small_chunk_uses_generic_apply():
+    cfg = I.CONFIGS[3].scaled(seq=300, n_q_heads=2, n_kv_heads=1, d_model=64, d_ff=96,
+                              w_teacher=90, w_student=10, chunk=48, seed=13)
+    check_layer(cfg)
+
+
+def test_smollm2_16k_layer_full():
+    check_layer(I.CONFIGS[2])
