@@ -1,0 +1,170 @@
+"""Benchmark: IP-TTCD layer forward on one MI355X.
+
+Default workload: the Qwen3-0.6B-shaped layer at 64K context (batch 1,
+65536 tokens, 16 q heads / 8 kv heads, head_dim 128, d_model 1024, d_ff
+3072, w_T 8192, w_S 512, chunk 1024, conv 4), bf16 inputs, synthetic data.
+
+Prints ONE JSON line: whole-layer tokens/s, the roofline of the dominant
+kernel (the dual-window attention, bf16 MFMA) measured with HIP events on
+the stream it runs on, and the fp64 CPU oracle timed on a bounded sample of
+the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6       # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+
+
+def attention_flops(cfg, wT):
+    """Algorithmic flops: 4*D per (query, key) pair inside the teacher
+    window (2D for QK^T, 2D for PV); the student band is a subset of it."""
+    T, Hq, D, B = cfg.seq, cfg.n_q_heads, cfg.head_dim, cfg.batch
+    full = max(0, T - wT) * wT
+    ramp = sum(min(t + 1, wT) for t in range(min(T, wT)))
+    return 4.0 * D * Hq * B * (full + ramp)
+
+
+def scan_bytes(cfg):
+    """Algorithmic bytes of the fast-weight stream: read Z_T, Z_S, write
+    the residual difference and the keys (bf16): 8 B T f."""
+    return 8.0 * cfg.batch * cfg.seq * cfg.d_ff
+
+
+def cpu_baseline(cfg, sample_tokens):
+    """The fp64 oracle, as it stands, on the first ``sample_tokens`` tokens
+    of the same inputs (same shapes, weights and windows)."""
+    from dual_window_attention_amd import inputs as I
+    from oracle import ttcd_oracle as O
+
+    sc = cfg.scaled(seq=sample_tokens)
+    att = I.attention_inputs(sc)
+    w = {n: t.f64() for n, t in I.layer_weights(sc).items()}
+    w["beta"] = I.beta_for(sc).astype(np.float64)
+    x = I.residual_input(sc).f64()
+    q, k, v = att["q"].f64(), att["k"].f64(), att["v"].f64()
+    t0 = time.perf_counter()
+    O.layer_forward(q, k, v, x, w, sc.w_teacher, sc.w_student, sc.chunk)
+    wall = time.perf_counter() - t0
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {"value": sample_tokens * sc.batch / wall, "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"fp64 NumPy oracle, full layer forward over the first {sample_tokens} "
+                      f"tokens of the same config (windows fill up over the first "
+                      f"{sc.w_teacher} tokens), wall {wall:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--cpu-sample", type=int, default=9216,
+                    help="tokens of the oracle CPU baseline sample (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only (no collectives); "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from dual_window_attention_amd import inputs as I
+    from dual_window_attention_amd import ttcd
+
+    cfg = I.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    att = I.attention_inputs(cfg)
+    q, k, v = (I.to_torch(att[n], dev) for n in ("q", "k", "v"))
+    del att
+    w = I.layer_weights(cfg)
+    wd = {n: I.to_torch(t, dev) for n, t in w.items()}
+    wd["beta"] = I.f32_to_torch(I.beta_for(cfg), dev)
+    x = I.to_torch(I.residual_input(cfg), dev)
+    B, T = cfg.batch, cfg.seq
+    ws_bytes = ttcd.layer_workspace_bytes(q, k, cfg.d_model, cfg.d_ff, cfg.w_teacher,
+                                          cfg.w_student, cfg.chunk, cfg.conv_k)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((B, T, cfg.d_model), dtype=torch.float32, device=dev)
+
+    def step():
+        ttcd.layer_forward(q, k, v, x, wd, cfg.w_teacher, cfg.w_student, cfg.chunk, out=out,
+                           workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    tokens_per_s = B * T / dt
+    assert torch.isfinite(out).all().item()
+
+    # dominant kernel: dual-window attention, timed with events on its stream
+    stream = torch.cuda.current_stream()
+    o_t = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    o_s = torch.empty_like(o_t)
+    aws = torch.empty(max(256, ttcd.lib().ttcd_dual_window_attn_workspace_size(
+        ttcd.attn_desc(q, k, cfg.w_teacher, cfg.w_student))), dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        ttcd.dual_window_attn(q, k, v, cfg.w_teacher, cfg.w_student, with_lse=False,
+                              out=(o_t, o_s), workspace=aws)
+    n_att = max(3, args.steps)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_att)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        ttcd.dual_window_attn(q, k, v, cfg.w_teacher, cfg.w_student, with_lse=False,
+                              out=(o_t, o_s), workspace=aws)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    att_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    flops = attention_flops(cfg, cfg.w_teacher)
+    achieved = flops / (att_ms * 1e-3) / 1e12
+
+    res = {
+        "metric": "IP-TTCD layer fwd tokens/s at 64K ctx; % bf16 MFMA peak (attn), % HBM BW (scan)",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dt * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian inputs, fan-in scaled random weights)",
+        "config": {"workload": f"{cfg.name}: IP-TTCD layer forward, batch {B}, seq {T}, "
+                               f"{cfg.n_q_heads}/{cfg.n_kv_heads} heads x {cfg.head_dim}, "
+                               f"d_model {cfg.d_model}, d_ff {cfg.d_ff}, w_T {cfg.w_teacher}, "
+                               f"w_S {cfg.w_student}, chunk {cfg.chunk}",
+                   "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "dual-window attention (ttcd_dual_window_attn)",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "ms_per_launch": att_ms, "algorithmic_tflop": flops / 1e12},
+    }
+    if args.cpu_sample > 0:
+        res["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_sample, cfg.seq))
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

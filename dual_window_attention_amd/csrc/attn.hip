@@ -5,25 +5,30 @@
 // at position t, the teacher attends to keys j with 0 <= t-j < w_T and the
 // student to keys with 0 <= t-j < w_S, over one shared Q/K/V.  The README's
 // "Fused inference kernels" section describes producing both in one pass
-// over K/V; the LSE-combination variant merges a student-window result and
-// a far-band result exactly through their log-sum-exp.
+// over K/V with the student recovered through the online-softmax rescaling.
 //
-// Design here (CDNA4, bf16 MFMA 32x32x16):
+// Design here (CDNA4, bf16 MFMA 32x32x16, fp32 accumulate):
 //   * S^T = K Q^T and O^T = V^T P^T, so each lane owns ONE query (a column
 //     of the MFMA output) and every softmax reduction over keys is in-lane
 //     plus one swap between the two lane halves.
-//   * One workgroup = 4 waves x 32 query rows of one (batch, kv head); the
-//     rows are (position, q head) pairs of that kv group, so GQA heads share
-//     every K/V tile staged in LDS.
-//   * Two online-softmax states per row: the student band [t-w_S+1, t] and
-//     the far band [t-w_T+1, t-w_S].  Each score belongs to exactly one of
-//     them.  Tiles are walked newest to oldest; tiles outside a wave's
-//     bands are skipped; masking only happens on edge sub-blocks.  The
-//     teacher result is the exact LSE merge of the two states, and equals
-//     the student result bit for bit when the far band is empty.
-//   * Lazy rescaling: a state's running max only moves when a new score
-//     exceeds it by more than 2^8, which keeps the fp32 accumulators exact
-//     in value while skipping most rescales.
+//   * One workgroup = 8 waves x 32 query rows of one (batch, kv head); the
+//     rows are (position, q head) pairs of that kv group, so all GQA heads
+//     share every K/V tile staged in LDS.
+//   * K/V tiles of 64 keys go straight from global memory into LDS
+//     (global_load_lds_dwordx4) in a 3-deep ring, XOR-swizzled so that the
+//     MFMA operand reads are free of bank conflicts.  V arrives
+//     pre-transposed (d-major) with the keys of every 16-key group permuted
+//     so that one 16-byte LDS read yields the 8 keys an MFMA lane needs.
+//   * ONE online-softmax state per row, walked newest to oldest: first the
+//     student band (masked only on edge sub-blocks); when a wave passes its
+//     oldest student sub-block the student output is written, the far-band
+//     part of the (at most two) edge sub-blocks is added -- they are still
+//     in the LDS ring -- and the walk continues through the far band to the
+//     teacher output.  Tiles outside a wave's bands are skipped.  Rows whose
+//     far band is empty finish with bit-identical teacher and student
+//     results.
+//   * Lazy rescaling: the running max only moves when a new score exceeds
+//     it by more than 2^8; the result is unchanged up to rounding.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -32,37 +37,98 @@ namespace ttcd {
 namespace {
 
 constexpr int BN = 64;          // keys per LDS tile
+constexpr int NBUF = 3;         // LDS ring depth
 constexpr float TAU = 8.0f;     // lazy-rescale threshold (log2 domain)
 constexpr float NEG_INF = -__builtin_inff();
+constexpr float LN2 = 0.69314718055994530942f;
 
-template <int D, int NW>
-struct AttnLds {
-  static constexpr int KS = D + 8;     // K row stride (bf16)
-  static constexpr int VS = BN + 4;    // V^T row stride (bf16)
-  static constexpr int K_ELEMS = BN * KS;
-  static constexpr int V_ELEMS = D * VS;
-  static constexpr int BUF = K_ELEMS + V_ELEMS;
-  static constexpr size_t BYTES = 2 * BUF * sizeof(bf16_t);
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// 16 bytes per lane, global -> LDS; lane i lands at lds_wave_base + 16 i.
+TTCD_DEV void g2l16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds_wave_base, 16, 0, 0);
+}
+
+template <int D>
+struct Tile {
+  static constexpr int CPR = D / 8;                 // 16B chunks per K row
+  static constexpr int KPOS = BN * CPR;             // 16B positions, K region
+  static constexpr int VPOS = D * (BN / 8);         // 16B positions, V^T region
+  static constexpr int BYTES = (KPOS + VPOS) * 16;
+  static TTCD_DEV int kswz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+  static TTCD_DEV int vswz(int d) { return (d >> 1) & 7; }
 };
+
+enum Mask { M_NONE = 0, M_S = 1, M_F = 2, M_T = 3 };
 
 struct SoftState {
   float m;   // running max (log2 domain, scaled)
   float l;   // this lane's partial denominator
 };
 
-// One 32-key sub-block update of a state.  s: the 16 raw scores of this
-// lane (MFMA output layout), msk: which of them belong to this state.
-template <int NB, bool MASKED>
-TTCD_DEV void state_update(SoftState& st, f32x16* acc, const f32x16& s, uint32_t msk,
-                           float c, bf16x8& p0, bf16x8& p1) {
+template <int D, int NW>
+TTCD_DEV void issue_tile(char* buf, const bf16_t* kbase, size_t kstride, const bf16_t* vbase,
+                         int vt_ld, int j0, int jlo, int jhi, int wave, int lane) {
+  using TL = Tile<D>;
+  static_assert(TL::KPOS % (64 * NW) == 0 && TL::VPOS % (64 * NW) == 0, "tile/wave split");
+#pragma unroll
+  for (int i = 0; i < TL::KPOS / (64 * NW); ++i) {
+    const int p0 = (i * NW + wave) * 64;
+    const int p = p0 + lane;
+    const int row = p / TL::CPR, cp = p % TL::CPR;
+    const int c = cp ^ TL::kswz(row);
+    const int j = min(max(j0 + row, jlo), jhi);   // never read outside the band
+    g2l16(kbase + (size_t)j * kstride + c * 8, buf + p0 * 16);
+  }
+  char* vb = buf + TL::KPOS * 16;
+#pragma unroll
+  for (int i = 0; i < TL::VPOS / (64 * NW); ++i) {
+    const int p0 = (i * NW + wave) * 64;
+    const int p = p0 + lane;
+    const int d = p >> 3, cp = p & 7;
+    const int c = cp ^ TL::vswz(d);
+    g2l16(vbase + (size_t)d * vt_ld + j0 + 8 * c, vb + p0 * 16);
+  }
+}
+
+// One 32-key sub-block: S^T = K Q^T, online-softmax update, O^T += V^T P^T.
+template <int D, int MASK>
+TTCD_DEV void process(const char* buf, int sb, int j0, int t, int wS, int wT, float c,
+                      const bf16x8* qf, SoftState& st, f32x16* acc, int lane) {
+  using TL = Tile<D>;
+  constexpr int NB = D / 32;
+  constexpr int KSTEP = D / 16;
+  const int h = lane >> 5, r = lane & 31;
+
+  f32x16 s = zero16();
+  {
+    const int row = 32 * sb + r;
+    const char* krow = buf + row * (TL::CPR * 16);
+    const int sw = TL::kswz(row);
+#pragma unroll
+    for (int ks = 0; ks < KSTEP; ++ks)
+      s = mfma32(as_bf16x8(ld16(krow + (((2 * ks + h) ^ sw) << 4))), qf[ks], s);
+  }
+
+  uint32_t msk = 0xFFFFu;
+  if (MASK != M_NONE) {
+    msk = 0u;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int dlt = t - (j0 + 8 * (v >> 2) + 4 * h + (v & 3));
+      bool in;
+      if (MASK == M_S) in = dlt >= 0 && dlt < wS;
+      else if (MASK == M_F) in = dlt >= wS && dlt < wT;
+      else in = dlt < wT;
+      msk |= (in ? 1u : 0u) << v;
+    }
+  }
+  // row max (raw scores; c > 0)
   float mx = NEG_INF;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    float x = s[v] * c;
-    if (MASKED) x = ((msk >> v) & 1u) ? x : NEG_INF;
-    mx = fmaxf(mx, x);
-  }
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  for (int v = 0; v < 16; ++v) mx = fmaxf(mx, ((msk >> v) & 1u) ? s[v] : NEG_INF);
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
   const bool need = mx > st.m + TAU;
   if (__builtin_expect(__any(need), 0)) {
     const float mnew = need ? mx : st.m;
@@ -73,54 +139,71 @@ TTCD_DEV void state_update(SoftState& st, f32x16* acc, const f32x16& s, uint32_t
     st.m = mnew;
   }
   const float negm = -st.m;
-  float p[16];
+  bf16x8 p0, p1;
   float lsum = 0.f;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     float e = fast_exp2(__builtin_fmaf(s[v], c, negm));
-    if (MASKED) e = ((msk >> v) & 1u) ? e : 0.f;
-    p[v] = e;
+    if (MASK != M_NONE) e = ((msk >> v) & 1u) ? e : 0.f;
     lsum += e;
+    if (v < 8) p0[v] = (__bf16)e;
+    else p1[v - 8] = (__bf16)e;
   }
   st.l += lsum;
+
+  // O^T += V^T P^T : one 16B read gives the 8 (permuted) keys of a lane
+  const char* vb = buf + TL::KPOS * 16;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    p0[j] = (__bf16)p[j];
-    p1[j] = (__bf16)p[8 + j];
+  for (int b = 0; b < NB; ++b) {
+    const int d = 32 * b + r;
+    const char* vrow = vb + d * (BN * 2);
+    const int sw = TL::vswz(d);
+    const bf16x8 v0 = as_bf16x8(ld16(vrow + (((4 * sb + 0 + h) ^ sw) << 4)));
+    const bf16x8 v1 = as_bf16x8(ld16(vrow + (((4 * sb + 2 + h) ^ sw) << 4)));
+    acc[b] = mfma32(v0, p0, acc[b]);
+    acc[b] = mfma32(v1, p1, acc[b]);
   }
 }
 
 template <int NB>
-TTCD_DEV void pv_update(f32x16* acc, const bf16_t* vt_lds, int vs, int sb, int lane,
-                        const bf16x8& p0, const bf16x8& p1) {
-  const int h = lane >> 5;
-  const int r = lane & 31;
+TTCD_DEV void store_out(void* o, float* lse, int out_bf16, bool row_ok, size_t obase, size_t li,
+                        const SoftState& st, const f32x16* acc, int h) {
+  const float l = st.l + __shfl_xor(st.l, 32, 64);
+  const float inv = 1.f / l;
+  if (!row_ok) return;
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const bf16_t* row = vt_lds + (32 * b + r) * vs + 32 * sb + 4 * h;
+  for (int bb = 0; bb < NB; ++bb) {
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      u32x2 lo = *reinterpret_cast<const u32x2*>(row + 16 * m);
-      u32x2 hi = *reinterpret_cast<const u32x2*>(row + 16 * m + 8);
-      u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-      acc[b] = mfma32(as_bf16x8(w), m == 0 ? p0 : p1, acc[b]);
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = 32 * bb + 8 * g4 + 4 * h;
+      float ov[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ov[e] = acc[bb][4 * g4 + e] * inv;
+      if (out_bf16) {
+        *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(o) + obase + d) =
+            u32x2{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
+      } else {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(o) + obase + d) =
+            f32x4{ov[0], ov[1], ov[2], ov[3]};
+      }
     }
   }
+  if (h == 0 && lse) lse[li] = (st.m + fast_log2(l)) * LN2;
 }
 
 template <int D, int NW>
-__global__ void __launch_bounds__(64 * NW, (D == 128 ? 1 : 2))
+__global__ void __launch_bounds__(64 * NW)
 dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                       const bf16_t* __restrict__ vt, int vt_ld,
                       void* __restrict__ o_t, void* __restrict__ o_s,
                       float* __restrict__ lse_t, float* __restrict__ lse_s,
                       int B, int Tq, int Tk, int kv_rows, int q_pos0, int Hq, int Hkv,
                       int wT, int wS, float c, int out_bf16, int nblk) {
-  using L = AttnLds<D, NW>;
-  constexpr int NB = D / 32;      // 32-wide d blocks of O^T
-  constexpr int KSTEP = D / 16;   // k-steps of S^T
+  using TL = Tile<D>;
+  constexpr int NB = D / 32;
+  constexpr int KSTEP = D / 16;
   constexpr int ROWS = 32 * NW;
-  extern __shared__ __align__(16) bf16_t lds[];
+  extern __shared__ __align__(16) char lds[];
 
   const int G = Hq / Hkv;
   const int R = Tq * G;
@@ -136,7 +219,7 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   const int lane = tid & 63;
   const int h = lane >> 5;
 
-  // ---- this lane's query row
+  // ---- this lane's query row: (position, head) pair of the kv group
   const int row0 = blk * ROWS;
   const int rw0 = row0 + 32 * wave;
   int r = rw0 + (lane & 31);
@@ -147,197 +230,81 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   const int t = q_pos0 + qi;
 
   // wave / workgroup position ranges
-  const int wr_hi = min(rw0 + 31, R - 1);
   const int a_w = q_pos0 + min(rw0, R - 1) / G;
-  const int b_w = q_pos0 + wr_hi / G;
+  const int b_w = q_pos0 + min(rw0 + 31, R - 1) / G;
   const int A = q_pos0 + row0 / G;
   const int Bp = q_pos0 + min(row0 + ROWS - 1, R - 1) / G;
   const int jlo = max(0, A - wT + 1);
   const int jhi = min(Bp, Tk - 1);
+  const int sLo = a_w - wS + 1;                 // oldest key of any row's student band
+  const int fLo = max(a_w - wT + 1, 0);         // oldest key of any row's teacher band
+  const int j0_lastS = max(sLo, 0) & ~31;       // the wave's oldest student sub-block
 
-  // ---- Q fragments (B operand of S^T = K Q^T)
   bf16x8 qf[KSTEP];
   {
     const bf16_t* qp = q + ((size_t)(b * Tq + qi) * Hq + qh) * D + 8 * h;
 #pragma unroll
     for (int s = 0; s < KSTEP; ++s) qf[s] = as_bf16x8(ld16(qp + 16 * s));
   }
-
-  f32x16 accS[NB], accF[NB];
+  f32x16 acc[NB];
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    accS[i] = zero16();
-    accF[i] = zero16();
-  }
-  SoftState stS = {NEG_INF, 0.f}, stF = {NEG_INF, 0.f};
+  for (int i = 0; i < NB; ++i) acc[i] = zero16();
+  SoftState st = {NEG_INF, 0.f};
 
-  // ---- tile loaders (registers -> LDS, double buffered)
-  constexpr int KCH = BN * D / 8 / (64 * NW);   // 16B chunks per thread (K)
-  constexpr int VCH = D * BN / 8 / (64 * NW);   // 16B chunks per thread (V^T)
-  static_assert(KCH >= 1 && VCH >= 1, "tile too small for the workgroup");
-  u32x4 kreg[KCH], vreg[VCH];
   const bf16_t* kbase = k + ((size_t)b * kv_rows * Hkv + g) * D;
   const size_t kstride = (size_t)Hkv * D;
   const bf16_t* vbase = vt + (size_t)(b * Hkv + g) * D * vt_ld;
-
-  auto load_regs = [&](int n) {
-    const int j0 = n * BN;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int cidx = tid + i * 64 * NW;
-      const int key = cidx / (D / 8), dc = cidx % (D / 8);
-      const int j = j0 + key;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (j >= jlo && j <= jhi) val = ld16(kbase + (size_t)j * kstride + dc * 8);
-      kreg[i] = val;
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int cidx = tid + i * 64 * NW;
-      const int d = cidx / (BN / 8), kc = cidx % (BN / 8);
-      const int j = j0 + kc * 8;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (j + 7 >= jlo && j <= jhi) {
-        val = ld16(vbase + (size_t)d * vt_ld + j);
-        if (j < jlo || j + 7 > jhi) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int ja = j + 2 * e, jb = ja + 1;
-            uint32_t w = val[e];
-            if (ja < jlo || ja > jhi) w &= 0xFFFF0000u;
-            if (jb < jlo || jb > jhi) w &= 0x0000FFFFu;
-            val[e] = w;
-          }
-        }
-      }
-      vreg[i] = val;
-    }
-  };
-  auto store_lds = [&](int buf) {
-    bf16_t* kl = lds + buf * L::BUF;
-    bf16_t* vl = kl + L::K_ELEMS;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int cidx = tid + i * 64 * NW;
-      const int key = cidx / (D / 8), dc = cidx % (D / 8);
-      st16(kl + key * L::KS + dc * 8, kreg[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int cidx = tid + i * 64 * NW;
-      const int d = cidx / (BN / 8), kc = cidx % (BN / 8);
-      u32x2* p = reinterpret_cast<u32x2*>(vl + d * L::VS + kc * 8);
-      p[0] = u32x2{vreg[i][0], vreg[i][1]};
-      p[1] = u32x2{vreg[i][2], vreg[i][3]};
-    }
-  };
+  const size_t obase = ((size_t)(b * Tq + qi) * Hq + qh) * D;
+  const size_t li = (size_t)(b * Hq + qh) * Tq + qi;
 
   const int n_hi = jhi / BN, n_lo = jlo / BN;
-  load_regs(n_hi);
-  store_lds(0);
+  issue_tile<D, NW>(lds + (n_hi % NBUF) * TL::BYTES, kbase, kstride, vbase, vt_ld, n_hi * BN,
+                    jlo, jhi, wave, lane);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  int it = 0;
-  for (int n = n_hi; n >= n_lo; --n, ++it) {
-    const int cur = it & 1;
-    const bool has_next = n > n_lo;
-    if (has_next) load_regs(n - 1);
-
-    const bf16_t* kl = lds + cur * L::BUF;
-    const bf16_t* vl = kl + L::K_ELEMS;
+  for (int n = n_hi; n >= n_lo; --n) {
+    if (n > n_lo)
+      issue_tile<D, NW>(lds + ((n - 1) % NBUF) * TL::BYTES, kbase, kstride, vbase, vt_ld,
+                        (n - 1) * BN, jlo, jhi, wave, lane);
+    const char* buf = lds + (n % NBUF) * TL::BYTES;
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
+    for (int sb = 1; sb >= 0; --sb) {
       const int j0 = n * BN + 32 * sb;
       const int j1 = j0 + 31;
-      // wave-uniform classification of this 32-key sub-block
-      if (j0 > b_w || j1 < a_w - wT + 1) continue;
-      const bool anyS = (j0 <= b_w) && (j1 >= a_w - wS + 1);
-      const bool anyF = (a_w - j1 <= wT - 1) && (b_w - j0 >= wS);
-      const bool allS = (a_w - j1 >= 0) && (b_w - j0 <= wS - 1);
-      const bool allF = (a_w - j1 >= wS) && (b_w - j0 <= wT - 1);
-
-      f32x16 s = zero16();
-      const bf16_t* krow = kl + (32 * sb + (lane & 31)) * L::KS + 8 * h;
+      if (j0 > b_w || j1 < fLo) continue;        // outside every row's teacher band
+      if (j1 >= sLo) {
+        // student band (plus the causal diagonal)
+        if (j1 <= a_w && j0 >= b_w - wS + 1)
+          process<D, M_NONE>(buf, sb, j0, t, wS, wT, c, qf, st, acc, lane);
+        else
+          process<D, M_S>(buf, sb, j0, t, wS, wT, c, qf, st, acc, lane);
+        if (j0 == j0_lastS) {
+          // student complete: write it, then add the far part of the edge
+          store_out<NB>(o_s, lse_s, out_bf16, row_ok, obase, li, st, acc, h);
+          if (wT > wS) {
 #pragma unroll
-      for (int ks = 0; ks < KSTEP; ++ks) s = mfma32(as_bf16x8(ld16(krow + 16 * ks)), qf[ks], s);
-
-      bf16x8 p0, p1;
-      if (allS) {
-        state_update<NB, false>(stS, accS, s, 0xFFFFu, c, p0, p1);
-        pv_update<NB>(accS, vl, L::VS, sb, lane, p0, p1);
-      } else if (allF) {
-        state_update<NB, false>(stF, accF, s, 0xFFFFu, c, p0, p1);
-        pv_update<NB>(accF, vl, L::VS, sb, lane, p0, p1);
+            for (int e = 0; e < 2; ++e) {
+              const int je = j0_lastS + 32 * e;
+              if (je <= b_w - wS) {
+                const char* eb = lds + ((je / BN) % NBUF) * TL::BYTES;
+                process<D, M_F>(eb, (je / 32) & 1, je, t, wS, wT, c, qf, st, acc, lane);
+              }
+            }
+          }
+        }
       } else {
-        uint32_t mS = 0u, mF = 0u;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int j = j0 + 8 * (v >> 2) + 4 * h + (v & 3);
-          const int dlt = t - j;
-          if (dlt >= 0 && dlt < wS) mS |= 1u << v;
-          if (dlt >= wS && dlt < wT) mF |= 1u << v;
-        }
-        if (anyS) {
-          state_update<NB, true>(stS, accS, s, mS, c, p0, p1);
-          pv_update<NB>(accS, vl, L::VS, sb, lane, p0, p1);
-        }
-        if (anyF) {
-          state_update<NB, true>(stF, accF, s, mF, c, p0, p1);
-          pv_update<NB>(accF, vl, L::VS, sb, lane, p0, p1);
-        }
+        // far band only: every key is >= w_S behind every row of the wave
+        if (j0 >= b_w - wT + 1)
+          process<D, M_NONE>(buf, sb, j0, t, wS, wT, c, qf, st, acc, lane);
+        else
+          process<D, M_T>(buf, sb, j0, t, wS, wT, c, qf, st, acc, lane);
       }
     }
-
-    if (has_next) store_lds(cur ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
-
-  // ---- merge and store
-  const float lS = stS.l + __shfl_xor(stS.l, 32, 64);
-  const float lF = stF.l + __shfl_xor(stF.l, 32, 64);
-  const float mT = fmaxf(stS.m, stF.m);
-  const float aS = (stS.m == NEG_INF) ? 0.f : fast_exp2(stS.m - mT);
-  const float aF = (stF.m == NEG_INF) ? 0.f : fast_exp2(stF.m - mT);
-  const float lT = lS * aS + lF * aF;
-  const bool far_empty = (lF == 0.f);
-  const float invS = 1.f / lS;
-  const float invT = 1.f / lT;
-  constexpr float LN2 = 0.69314718055994530942f;
-
-  if (row_ok) {
-    const size_t obase = ((size_t)(b * Tq + qi) * Hq + qh) * D;
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = 32 * bb + 8 * g4 + 4 * h;
-        float os[4], ot[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float vs = accS[bb][4 * g4 + e];
-          os[e] = vs * invS;
-          ot[e] = far_empty ? os[e] : (vs * aS + accF[bb][4 * g4 + e] * aF) * invT;
-        }
-        if (out_bf16) {
-          u32x2 ws = {pack_bf16x2(os[0], os[1]), pack_bf16x2(os[2], os[3])};
-          u32x2 wt = {pack_bf16x2(ot[0], ot[1]), pack_bf16x2(ot[2], ot[3])};
-          *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(o_s) + obase + d) = ws;
-          *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(o_t) + obase + d) = wt;
-        } else {
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(o_s) + obase + d) =
-              f32x4{os[0], os[1], os[2], os[3]};
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(o_t) + obase + d) =
-              f32x4{ot[0], ot[1], ot[2], ot[3]};
-        }
-      }
-    }
-    if (h == 0) {
-      const size_t li = (size_t)(b * Hq + qh) * Tq + qi;
-      const float lseS = (stS.m + fast_log2(lS)) * LN2;
-      if (lse_s) lse_s[li] = lseS;
-      if (lse_t) lse_t[li] = far_empty ? lseS : (mT + fast_log2(lT)) * LN2;
-    }
-  }
+  store_out<NB>(o_t, lse_t, out_bf16, row_ok, obase, li, st, acc, h);
 }
 
 // --------------------------------------------------------------------------
@@ -445,18 +412,21 @@ dual_window_attn_simple(const T* __restrict__ q, const T* __restrict__ k,
 
 template <int D>
 hipError_t launch_mfma(const AttnArgs& a, hipStream_t s) {
-  constexpr int NW = 4;
-  using L = AttnLds<D, NW>;
+  constexpr int NW = 8;
+  const size_t lds = (size_t)NBUF * Tile<D>::BYTES;
+  static hipError_t attr = hipFuncSetAttribute((const void*)dual_window_attn_mfma<D, NW>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)lds);
+  if (attr != hipSuccess) return attr;
   const int G = a.Hq / a.Hkv;
   const int R = a.Tq * G;
   const int nblk = (R + 32 * NW - 1) / (32 * NW);
   const long total = (long)a.B * a.Hkv * nblk;
   const float c = a.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((dual_window_attn_mfma<D, NW>), dim3((unsigned)total), dim3(64 * NW),
-                     L::BYTES, s, (const bf16_t*)a.q, (const bf16_t*)a.k,
-                     (const bf16_t*)a.vt, a.vt_ld, a.o_t, a.o_s, a.lse_t, a.lse_s, a.B, a.Tq,
-                     a.Tk, a.kv_rows, a.q_pos0, a.Hq, a.Hkv, a.wT, a.wS, c,
-                     a.out_dt == BF16 ? 1 : 0, nblk);
+  hipLaunchKernelGGL((dual_window_attn_mfma<D, NW>), dim3((unsigned)total), dim3(64 * NW), lds,
+                     s, (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.vt, a.vt_ld,
+                     a.o_t, a.o_s, a.lse_t, a.lse_s, a.B, a.Tq, a.Tk, a.kv_rows, a.q_pos0, a.Hq,
+                     a.Hkv, a.wT, a.wS, c, a.out_dt == BF16 ? 1 : 0, nblk);
   return hipGetLastError();
 }
 
@@ -483,17 +453,10 @@ size_t attn_vt_bytes(int B, int Hkv, int D, int Tk, int in_dt) {
 
 hipError_t launch_dual_window_attn(const AttnArgs& a, hipStream_t s) {
   if (a.in_dt == BF16 && (a.D == 64 || a.D == 128)) {
-    static bool attr_set = false;
-    if (!attr_set) {
-      (void)hipFuncSetAttribute((const void*)dual_window_attn_mfma<64, 4>,
-                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)AttnLds<64, 4>::BYTES);
-      (void)hipFuncSetAttribute((const void*)dual_window_attn_mfma<128, 4>,
-                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)AttnLds<128, 4>::BYTES);
-      attr_set = true;
-    }
-    hipError_t e = launch_v_transpose(a.v, a.vt, a.B, a.Tk, a.kv_rows, a.Hkv, a.D, a.vt_ld, 2, s);
+    // V^T with the keys every query may read: [max(0, q_pos0 - w_T + 1), Tk)
+    const int jlo_all = a.q_pos0 - a.wT + 1 > 0 ? a.q_pos0 - a.wT + 1 : 0;
+    hipError_t e = launch_v_transpose(a.v, a.vt, a.B, a.Tk, jlo_all, a.kv_rows, a.Hkv, a.D,
+                                      a.vt_ld, s);
     if (e != hipSuccess) return e;
     return a.D == 64 ? launch_mfma<64>(a, s) : launch_mfma<128>(a, s);
   }

@@ -4,7 +4,7 @@ import pytest
 
 from dual_window_attention_amd import inputs as I
 from oracle import ttcd_oracle as O
-from tests.gpu_helpers import assert_close, say, to_np, tol_for
+from tests.gpu_helpers import assert_close, assert_close_stored, say, to_np, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -40,10 +40,10 @@ def check_layer(cfg, main_path="teacher"):
     ref = oracle_layer(cfg, att, wo, x, main_path)
     tol = tol_for(cfg.dtype)
     assert_close(to_np(out), ref["out"], tol, "out")
-    assert_close(to_np(aux["o_teacher"]), ref["o_t"], tol, "O_teacher")
-    assert_close(to_np(aux["o_student"]), ref["o_s"], tol, "O_student")
-    assert_close(to_np(aux["z_teacher"]), ref["z_t"], tol, "Z_teacher")
-    assert_close(to_np(aux["z_student"]), ref["z_s"], tol, "Z_student")
+    assert_close_stored(to_np(aux["o_teacher"]), ref["o_t"], tol, "O_teacher", cfg.dtype)
+    assert_close_stored(to_np(aux["o_student"]), ref["o_s"], tol, "O_student", cfg.dtype)
+    assert_close_stored(to_np(aux["z_teacher"]), ref["z_t"], tol, "Z_teacher", cfg.dtype)
+    assert_close_stored(to_np(aux["z_student"]), ref["z_s"], tol, "Z_student", cfg.dtype)
     assert_close(to_np(aux["y"]), ref["y"], tol, "y (fast-weight MLP output)")
     # the fast-weight correction alone (y - W0 z) to a relative bound
     zm = ref["z_t"] if main_path == "teacher" else ref["z_s"]
