@@ -74,6 +74,9 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--cpu-sample", type=int, default=9216,
                     help="tokens of the oracle CPU baseline sample (0 = skip)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one plain 1 GiB device-to-device copy (a reference "
+                         "kernel of known traffic for scaling memory counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only (no collectives); "
@@ -104,6 +107,13 @@ def main():
     def step():
         ttcd.layer_forward(q, k, v, x, wd, cfg.w_teacher, cfg.w_student, cfg.chunk, out=out,
                            workspace=ws)
+
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
 
     for _ in range(args.warmup):
         step()

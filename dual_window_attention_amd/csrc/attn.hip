@@ -37,7 +37,7 @@ namespace ttcd {
 namespace {
 
 constexpr int BN = 64;          // keys per LDS tile
-constexpr int NBUF = 3;         // LDS ring depth
+constexpr int NBUF = 4;         // LDS ring depth: current, previous, two in flight
 constexpr float TAU = 8.0f;     // lazy-rescale threshold (log2 domain)
 constexpr float NEG_INF = -__builtin_inff();
 constexpr float LN2 = 0.69314718055994530942f;
@@ -50,6 +50,20 @@ TTCD_DEV void g2l16(const void* src, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds_wave_base, 16, 0, 0);
 }
 
+// Workgroup barrier that does not drain this wave's in-flight tile fetches
+// (a fenced barrier would wait for every outstanding memory operation).  LDS
+// ordering: every wave waits for the tile it needs with wait_vm first, and
+// all LDS reads of a buffer are consumed by MFMAs before the barrier that
+// precedes the fetch overwriting it.
+TTCD_DEV void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+TTCD_DEV void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 template <int D>
 struct Tile {
   static constexpr int CPR = D / 8;                 // 16B chunks per K row
@@ -59,8 +73,6 @@ struct Tile {
   static TTCD_DEV int kswz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
   static TTCD_DEV int vswz(int d) { return (d >> 1) & 7; }
 };
-
-enum Mask { M_NONE = 0, M_S = 1, M_F = 2, M_T = 3 };
 
 struct SoftState {
   float m;   // running max (log2 domain, scaled)
@@ -93,42 +105,105 @@ TTCD_DEV void issue_tile(char* buf, const bf16_t* kbase, size_t kstride, const b
 }
 
 // One 32-key sub-block: S^T = K Q^T, online-softmax update, O^T += V^T P^T.
-template <int D, int MASK>
-TTCD_DEV void process(const char* buf, int sb, int j0, int t, int wS, int wT, float c,
-                      const bf16x8* qf, SoftState& st, f32x16* acc, int lane) {
+// Operand fragments are read from LDS in groups ahead of their MFMAs so that
+// one LDS latency covers eight MFMAs, and the V^T fragments are in flight
+// while the softmax runs.  masked (wave-uniform): only keys with
+// lo <= t - j < hi take part.
+template <int D>
+TTCD_DEV void process(const char* buf, int sb, int j0, int t, bool masked, int lo, int hi,
+                      float c, const bf16x8* qf, SoftState& st, f32x16* acc, int lane) {
   using TL = Tile<D>;
   constexpr int NB = D / 32;
   constexpr int KSTEP = D / 16;
   const int h = lane >> 5, r = lane & 31;
 
-  f32x16 s = zero16();
+  bf16x8 kf[KSTEP];
   {
     const int row = 32 * sb + r;
     const char* krow = buf + row * (TL::CPR * 16);
     const int sw = TL::kswz(row);
 #pragma unroll
-    for (int ks = 0; ks < KSTEP; ++ks)
-      s = mfma32(as_bf16x8(ld16(krow + (((2 * ks + h) ^ sw) << 4))), qf[ks], s);
+    for (int ks = 0; ks < KSTEP; ++ks) kf[ks] = as_bf16x8(ld16(krow + (((2 * ks + h) ^ sw) << 4)));
   }
-
-  uint32_t msk = 0xFFFFu;
-  if (MASK != M_NONE) {
-    msk = 0u;
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 s = zero16();
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int dlt = t - (j0 + 8 * (v >> 2) + 4 * h + (v & 3));
-      bool in;
-      if (MASK == M_S) in = dlt >= 0 && dlt < wS;
-      else if (MASK == M_F) in = dlt >= wS && dlt < wT;
-      else in = dlt < wT;
-      msk |= (in ? 1u : 0u) << v;
+  for (int ks = 0; ks < KSTEP; ++ks) s = mfma32(kf[ks], qf[ks], s);
+
+  bf16x8 vf[NB][2];
+  {
+    const char* vb = buf + TL::KPOS * 16;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int d = 32 * b + r;
+      const char* vrow = vb + d * (BN * 2);
+      const int sw = TL::vswz(d);
+      vf[b][0] = as_bf16x8(ld16(vrow + (((4 * sb + 0 + h) ^ sw) << 4)));
+      vf[b][1] = as_bf16x8(ld16(vrow + (((4 * sb + 2 + h) ^ sw) << 4)));
     }
   }
-  // row max (raw scores; c > 0)
+  __builtin_amdgcn_sched_barrier(0);
+
+  if (masked) {
+    // lo <= t - j < hi  <=>  (unsigned)(t - j - lo) < (unsigned)(hi - lo)
+    const uint32_t d0 = (uint32_t)(t - j0 - 4 * h - lo), span = (uint32_t)(hi - lo);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const uint32_t dl = d0 - (uint32_t)(8 * (v >> 2) + (v & 3));
+      s[v] = dl < span ? s[v] : NEG_INF;
+    }
+  }
+  // row max over the 32 keys (raw scores; c > 0): in-lane, then swap halves
   float mx = NEG_INF;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) mx = fmaxf(mx, ((msk >> v) & 1u) ? s[v] : NEG_INF);
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+  for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[v]);
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                     false, false);
+    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+  }
+  const bool need = mx > st.m + TAU;
+  if (__builtin_expect(__any(need), 0)) {
+    const float mnew = need ? mx : st.m;
+    const float alpha = (st.m == NEG_INF) ? 0.f : fast_exp2(st.m - mnew);
+    st.l *= alpha;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] *= alpha;
+    st.m = mnew;
+  }
+  // masked scores are -inf: exp2(-inf) = 0 (a row without any key here has
+  // m = -inf only if it never had one, and then every score is -inf too)
+  const float negm = st.m == NEG_INF ? 0.f : -st.m;
+  bf16x8 p0, p1;
+  float lsum = 0.f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const float e = fast_exp2(__builtin_fmaf(s[v], c, negm));
+    lsum += e;
+    if (v < 8) p0[v] = (__bf16)e;
+    else p1[v - 8] = (__bf16)e;
+  }
+  st.l += lsum;
+
+  // O^T += V^T P^T
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    acc[b] = mfma32(vf[b][0], p0, acc[b]);
+    acc[b] = mfma32(vf[b][1], p1, acc[b]);
+  }
+}
+
+// softmax step of one unmasked 32-key sub-block: lazy max update, p = 2^(s c - m)
+template <int NB>
+TTCD_DEV void softmax32(f32x16& s, float c, SoftState& st, f32x16* acc, bf16x8& p0, bf16x8& p1) {
+  float mx = NEG_INF;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[v]);
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                     false, false);
+    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+  }
   const bool need = mx > st.m + TAU;
   if (__builtin_expect(__any(need), 0)) {
     const float mnew = need ? mx : st.m;
@@ -139,36 +214,88 @@ TTCD_DEV void process(const char* buf, int sb, int j0, int t, int wS, int wT, fl
     st.m = mnew;
   }
   const float negm = -st.m;
-  bf16x8 p0, p1;
   float lsum = 0.f;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    float e = fast_exp2(__builtin_fmaf(s[v], c, negm));
-    if (MASK != M_NONE) e = ((msk >> v) & 1u) ? e : 0.f;
+    const float e = fast_exp2(__builtin_fmaf(s[v], c, negm));
     lsum += e;
     if (v < 8) p0[v] = (__bf16)e;
     else p1[v - 8] = (__bf16)e;
   }
   st.l += lsum;
+}
 
-  // O^T += V^T P^T : one 16B read gives the 8 (permuted) keys of a lane
+// Both 32-key sub-blocks of a tile, no masking, software-pipelined so the
+// MFMA pipe always has queued work while the VALU runs a softmax:
+//   QK(1) | QK(0) + softmax(1) | PV(1) + softmax(0) | PV(0)
+template <int D>
+TTCD_DEV void process_pair(const char* buf, float c, const bf16x8* qf, SoftState& st,
+                           f32x16* acc, int lane) {
+  using TL = Tile<D>;
+  constexpr int NB = D / 32;
+  constexpr int KSTEP = D / 16;
+  const int h = lane >> 5, r = lane & 31;
   const char* vb = buf + TL::KPOS * 16;
+  bf16x8 kf[KSTEP];
+  bf16x8 vf[NB][2];
+  f32x16 s1 = zero16(), s0 = zero16();
+  bf16x8 p0, p1;
+
+  auto load_k = [&](int sb) {
+    const int row = 32 * sb + r;
+    const char* krow = buf + row * (TL::CPR * 16);
+    const int sw = TL::kswz(row);
+#pragma unroll
+    for (int ks = 0; ks < KSTEP; ++ks) kf[ks] = as_bf16x8(ld16(krow + (((2 * ks + h) ^ sw) << 4)));
+  };
+  auto load_v = [&](int sb) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int d = 32 * b + r;
+      const char* vrow = vb + d * (BN * 2);
+      const int sw = TL::vswz(d);
+      vf[b][0] = as_bf16x8(ld16(vrow + (((4 * sb + 0 + h) ^ sw) << 4)));
+      vf[b][1] = as_bf16x8(ld16(vrow + (((4 * sb + 2 + h) ^ sw) << 4)));
+    }
+  };
+
+  load_k(1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int ks = 0; ks < KSTEP; ++ks) s1 = mfma32(kf[ks], qf[ks], s1);
+  __builtin_amdgcn_sched_barrier(0);
+  load_k(0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int ks = 0; ks < KSTEP; ++ks) s0 = mfma32(kf[ks], qf[ks], s0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_v(1);
+  __builtin_amdgcn_sched_barrier(0);
+  softmax32<NB>(s1, c, st, acc, p0, p1);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const int d = 32 * b + r;
-    const char* vrow = vb + d * (BN * 2);
-    const int sw = TL::vswz(d);
-    const bf16x8 v0 = as_bf16x8(ld16(vrow + (((4 * sb + 0 + h) ^ sw) << 4)));
-    const bf16x8 v1 = as_bf16x8(ld16(vrow + (((4 * sb + 2 + h) ^ sw) << 4)));
-    acc[b] = mfma32(v0, p0, acc[b]);
-    acc[b] = mfma32(v1, p1, acc[b]);
+    acc[b] = mfma32(vf[b][0], p0, acc[b]);
+    acc[b] = mfma32(vf[b][1], p1, acc[b]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  load_v(0);
+  __builtin_amdgcn_sched_barrier(0);
+  softmax32<NB>(s0, c, st, acc, p0, p1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    acc[b] = mfma32(vf[b][0], p0, acc[b]);
+    acc[b] = mfma32(vf[b][1], p1, acc[b]);
   }
 }
 
 template <int NB>
 TTCD_DEV void store_out(void* o, float* lse, int out_bf16, bool row_ok, size_t obase, size_t li,
                         const SoftState& st, const f32x16* acc, int h) {
-  const float l = st.l + __shfl_xor(st.l, 32, 64);
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.l), __float_as_uint(st.l),
+                                                   false, false);
+  const float l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   const float inv = 1.f / l;
   if (!row_ok) return;
 #pragma unroll
@@ -215,7 +342,7 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   const int b = bg / Hkv;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int lane = tid & 63;
   const int h = lane >> 5;
 
@@ -257,52 +384,94 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   const size_t obase = ((size_t)(b * Tq + qi) * Hq + qh) * D;
   const size_t li = (size_t)(b * Hq + qh) * Tq + qi;
 
+  // tiles are fetched two ahead of the one being computed
+  constexpr int LPW = (TL::KPOS + TL::VPOS) / (64 * NW);   // 16B loads per wave and tile
   const int n_hi = jhi / BN, n_lo = jlo / BN;
   issue_tile<D, NW>(lds + (n_hi % NBUF) * TL::BYTES, kbase, kstride, vbase, vt_ld, n_hi * BN,
                     jlo, jhi, wave, lane);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  if (n_hi - 1 >= n_lo) {
+    issue_tile<D, NW>(lds + ((n_hi - 1) % NBUF) * TL::BYTES, kbase, kstride, vbase, vt_ld,
+                      (n_hi - 1) * BN, jlo, jhi, wave, lane);
+    wait_vm<LPW>();
+  } else {
+    wait_vm<0>();
+  }
+  ring_barrier();
 
   for (int n = n_hi; n >= n_lo; --n) {
-    if (n > n_lo)
-      issue_tile<D, NW>(lds + ((n - 1) % NBUF) * TL::BYTES, kbase, kstride, vbase, vt_ld,
-                        (n - 1) * BN, jlo, jhi, wave, lane);
+    const bool fetch = n - 2 >= n_lo;
+    if (fetch)
+      issue_tile<D, NW>(lds + ((n - 2) % NBUF) * TL::BYTES, kbase, kstride, vbase, vt_ld,
+                        (n - 2) * BN, jlo, jhi, wave, lane);
     const char* buf = lds + (n % NBUF) * TL::BYTES;
-#pragma unroll
-    for (int sb = 1; sb >= 0; --sb) {
-      const int j0 = n * BN + 32 * sb;
-      const int j1 = j0 + 31;
-      if (j0 > b_w || j1 < fLo) continue;        // outside every row's teacher band
-      if (j1 >= sLo) {
-        // student band (plus the causal diagonal)
-        if (j1 <= a_w && j0 >= b_w - wS + 1)
-          process<D, M_NONE>(buf, sb, j0, t, wS, wT, c, qf, st, acc, lane);
-        else
-          process<D, M_S>(buf, sb, j0, t, wS, wT, c, qf, st, acc, lane);
-        if (j0 == j0_lastS) {
-          // student complete: write it, then add the far part of the edge
+    // work items of this tile, newest first: sub-block 1, sub-block 0, and
+    // right after the wave's oldest student sub-block the far part of its
+    // (at most two) edge sub-blocks
+    int sbq = 1, pend = 0;
+    {
+      // fast path: both sub-blocks inside one band for every row of the wave
+      const int j0b = n * BN;                                 // sub-block 0
+      const int j0a = j0b + 32;                               // sub-block 1 (newer)
+      const bool a_in = !(j0a > b_w || j0a + 31 < fLo);
+      const bool b_in = !(j0b > b_w || j0b + 31 < fLo);
+      auto unmasked = [&](int j0) {
+        return (j0 + 31 >= sLo) ? (j0 + 31 <= a_w && j0 >= b_w - wS + 1) : (j0 >= b_w - wT + 1);
+      };
+      if (a_in && b_in && j0a != j0_lastS && unmasked(j0a) && unmasked(j0b)) {
+        process_pair<D>(buf, c, qf, st, acc, lane);
+        sbq = -1;
+        if (j0b == j0_lastS) {
           store_out<NB>(o_s, lse_s, out_bf16, row_ok, obase, li, st, acc, h);
-          if (wT > wS) {
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const int je = j0_lastS + 32 * e;
-              if (je <= b_w - wS) {
-                const char* eb = lds + ((je / BN) % NBUF) * TL::BYTES;
-                process<D, M_F>(eb, (je / 32) & 1, je, t, wS, wT, c, qf, st, acc, lane);
-              }
-            }
-          }
+          pend = wT > wS ? 2 : 0;
         }
-      } else {
-        // far band only: every key is >= w_S behind every row of the wave
-        if (j0 >= b_w - wT + 1)
-          process<D, M_NONE>(buf, sb, j0, t, wS, wT, c, qf, st, acc, lane);
-        else
-          process<D, M_T>(buf, sb, j0, t, wS, wT, c, qf, st, acc, lane);
       }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+#pragma unroll 1
+    while (true) {
+      int j0, lo, hi;
+      bool masked, main_item;
+      const char* b;
+      if (pend > 0) {
+        j0 = j0_lastS + 32 * (2 - pend);
+        --pend;
+        if (j0 > b_w - wS) continue;
+        b = lds + ((j0 / BN) % NBUF) * TL::BYTES;
+        masked = true;
+        lo = wS;
+        hi = wT;
+        main_item = false;
+      } else if (sbq >= 0) {
+        j0 = n * BN + 32 * sbq;
+        --sbq;
+        const int j1 = j0 + 31;
+        if (j0 > b_w || j1 < fLo) continue;      // outside every row's teacher band
+        b = buf;
+        main_item = true;
+        if (j1 >= sLo) {                          // student band (and causal diagonal)
+          masked = !(j1 <= a_w && j0 >= b_w - wS + 1);
+          lo = 0;
+          hi = wS;
+        } else {                                  // far band: >= w_S behind every row
+          masked = !(j0 >= b_w - wT + 1);
+          lo = wS;
+          hi = wT;
+        }
+      } else {
+        break;
+      }
+      process<D>(b, (j0 >> 5) & 1, j0, t, masked, lo, hi, c, qf, st, acc, lane);
+      if (main_item && j0 == j0_lastS) {
+        // the student band is complete: write it, then add the far edge
+        store_out<NB>(o_s, lse_s, out_bf16, row_ok, obase, li, st, acc, h);
+        pend = wT > wS ? 2 : 0;
+      }
+    }
+    // tile n-1 must be in LDS; tile n-2 may still be in flight
+    if (fetch)
+      wait_vm<LPW>();
+    else
+      wait_vm<0>();
+    ring_barrier();
   }
   store_out<NB>(o_t, lse_t, out_bf16, row_ok, obase, li, st, acc, h);
 }
