@@ -353,6 +353,190 @@ __global__ void __launch_bounds__(256) fw_states_simple(StateArgs a) {
   }
 }
 
+
+// --------------------------------------------------------------------------
+// Large-tile NT GEMM: 256 x 128 workgroup tile, 4 waves each owning a
+// 128 x 64 block (8 MFMAs per 6 KB of LDS operand reads), BK = 32.  Operand
+// tiles go straight from global memory into LDS (global_load_lds_dwordx4) in
+// an XOR-swizzled layout that keeps the MFMA operand reads free of bank
+// conflicts; a 3-stage ring is fetched two stages ahead, and two workgroups
+// share a CU.  Requires K % 32 == 0 and 16-byte aligned rows.
+// --------------------------------------------------------------------------
+namespace big {
+constexpr int BM = 256, BN = 128, BK = 32, NW = 4, NTH = 64 * NW, NST = 3;
+constexpr int AB = BM * BK * 2, BB = BN * BK * 2;   // operand bytes per stage
+constexpr int STAGE = AB + BB;
+constexpr size_t LDS = (size_t)NST * STAGE;          // 72 KB
+constexpr int ALD = BM * BK / 8 / (64 * NW);         // 16B loads per wave (A)
+constexpr int BLD = BN * BK / 8 / (64 * NW);         // 16B loads per wave (B)
+constexpr int LPW = ALD + BLD;
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+TTCD_DEV void g2l16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds_wave_base, 16, 0, 0);
+}
+// barrier that leaves the in-flight stage fetches alone; every wave waits
+// for the stage it needs with wait_vm before it
+TTCD_DEV void barrier() { asm volatile("s_barrier" ::: "memory"); }
+template <int N>
+TTCD_DEV void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// rows of 64 bytes (4 chunks): chunk c of row r lives at c ^ ((r >> 2) & 3)
+TTCD_DEV int swz(int row) { return (row >> 2) & 3; }
+
+template <int NLD, class RowPtr>
+TTCD_DEV void issue(char* dst, const RowPtr& row_ptr, long k0, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int p0 = (i * NW + wave) * 64;
+    const int p = p0 + lane;
+    const int row = p >> 2, cp = p & 3;
+    const int c = cp ^ swz(row);
+    g2l16(row_ptr(row) + k0 + 8 * c, dst + p0 * 16);
+  }
+}
+
+template <typename OutT>
+__global__ void __launch_bounds__(NTH, 2)
+gemm_nt_big(GemmArgs g) {
+  extern __shared__ __align__(16) char lds[];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, r = lane & 31;
+  const int z = blockIdx.z;
+  const bool swiglu = g.epi == EPI_SWIGLU;
+  const int ncols = swiglu ? BN / 2 : BN;                   // output columns per tile
+  const int ntn = (g.N + ncols - 1) / ncols;
+  const int ntm = (g.M + BM - 1) / BM;
+  const uint32_t lid = xcd_remap(blockIdx.x, (uint32_t)(ntm * ntn));
+  const long m0 = (long)(lid / ntn) * BM;
+  const long n0 = (long)(lid % ntn) * ncols;
+
+  const bf16_t* A = (const bf16_t*)g.A + z * g.sA;
+  const bf16_t* Bm = (const bf16_t*)g.B + z * g.sB;
+  const bf16_t* B2 = g.B2 ? (const bf16_t*)g.B2 + z * g.sB : nullptr;
+  if (g.chunk > 0) {
+    const long c = m0 / g.chunk;
+    if (c > 0) Bm = (const bf16_t*)g.Bchunks + z * g.sBchunksBatch + (c - 1) * g.sBchunk;
+  }
+  const long mmax = g.M - 1, nmax = g.N - 1;
+  const long lda = g.lda, ldb = g.ldb;
+  auto a_row = [&](int rr) { return A + min(m0 + rr, mmax) * lda; };
+  auto b_row = [&](int rr) {
+    if (swiglu) {
+      // LDS row blocks of 32 alternate gate / up for the same 32 columns
+      const int blk = rr >> 5;
+      const long col = min(n0 + 32 * (blk >> 1) + (rr & 31), nmax);
+      return ((blk & 1) ? B2 : Bm) + col * ldb;
+    }
+    return Bm + min(n0 + rr, nmax) * ldb;
+  };
+  auto fetch = [&](int kt) {
+    char* st = lds + (kt % NST) * STAGE;
+    issue<ALD>(st, a_row, (long)kt * BK, wave, lane);
+    issue<BLD>(st + AB, b_row, (long)kt * BK, wave, lane);
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
+
+  const int nk = g.K / BK;
+  fetch(0);
+  if (nk > 1) {
+    fetch(1);
+    wait_vm<LPW>();
+  } else {
+    wait_vm<0>();
+  }
+  barrier();
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool ahead = kt + 2 < nk;
+    if (ahead) fetch(kt + 2);
+    const char* as = lds + (kt % NST) * STAGE;
+    const char* bs = as + AB;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 af[4], bfr[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 128 * wm + 32 * i + r;
+        af[i] = as_bf16x8(ld16(as + row * (BK * 2) + (((2 * ks + h) ^ swz(row)) << 4)));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int row = 64 * wn + 32 * j + r;
+        bfr[j] = as_bf16x8(ld16(bs + row * (BK * 2) + (((2 * ks + h) ^ swz(row)) << 4)));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+    }
+    // stage kt+1 must have landed; stage kt+2 may still be in flight
+    if (ahead)
+      wait_vm<LPW>();
+    else
+      wait_vm<0>();
+    barrier();
+  }
+
+  OutT* C = (OutT*)g.C + z * g.sC;
+  if (swiglu) {
+    const long n = n0 + 32 * wn + r;
+    if (n > nmax) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const long m = m0 + 128 * wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (m <= mmax) stf(C + m * g.ldc + n, silu(acc[i][0][v]) * acc[i][1][v]);
+      }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const long n = n0 + 64 * wn + 32 * j + r;
+    if (n > nmax) continue;
+    float cs = 1.f;
+    if (g.epi == EPI_STORE && g.colscale) cs = g.colscale[z * g.sScale + n];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const long m = m0 + 128 * wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (m > mmax) continue;
+        float val = acc[i][j][v];
+        if (g.epi == EPI_RESIDUAL) {
+          const long rm = (m % g.res_rows) * g.ldr + n + z * g.sRes;
+          val += g.res_dt == BF16 ? bf2f(((const bf16_t*)g.res)[rm]) : ((const float*)g.res)[rm];
+        } else {
+          val *= cs;
+        }
+        stf(C + m * g.ldc + n, val);
+      }
+  }
+}
+}  // namespace big
+
+bool big_ok(const GemmArgs& g) {
+  if (g.in_dt != BF16) return false;
+  if (g.K % big::BK || g.lda % 8 || g.ldb % 8) return false;
+  if (g.chunk > 0 && g.chunk % big::BM) return false;
+  // enough tiles to fill the chip
+  const long tiles = (long)((g.M + big::BM - 1) / big::BM) *
+                     ((g.N + big::BN - 1) / (g.epi == EPI_SWIGLU ? big::BN / 2 : big::BN)) *
+                     (g.batch > 0 ? g.batch : 1);
+  return tiles >= 256;
+}
+
 bool mfma_ok(const GemmArgs& g) {
   if (g.in_dt != BF16) return false;
   if (g.K % 8 || g.lda % 8 || g.ldb % 8) return false;
@@ -365,6 +549,24 @@ bool mfma_ok(const GemmArgs& g) {
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   const int nb = g.batch > 0 ? g.batch : 1;
+  if (big_ok(g)) {
+    static hipError_t a1 = hipFuncSetAttribute((const void*)big::gemm_nt_big<float>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)big::LDS);
+    static hipError_t a2 = hipFuncSetAttribute((const void*)big::gemm_nt_big<bf16_t>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)big::LDS);
+    if (a1 != hipSuccess) return a1;
+    if (a2 != hipSuccess) return a2;
+    const int ncols = g.epi == EPI_SWIGLU ? big::BN / 2 : big::BN;
+    const unsigned tiles = (unsigned)(((g.M + big::BM - 1) / big::BM) * ((g.N + ncols - 1) / ncols));
+    dim3 grid(tiles, 1, nb);
+    if (g.out_dt == BF16)
+      hipLaunchKernelGGL(big::gemm_nt_big<bf16_t>, grid, dim3(big::NTH), big::LDS, s, g);
+    else
+      hipLaunchKernelGGL(big::gemm_nt_big<float>, grid, dim3(big::NTH), big::LDS, s, g);
+    return hipGetLastError();
+  }
   if (mfma_ok(g)) {
     static bool attr = false;
     if (!attr) {
