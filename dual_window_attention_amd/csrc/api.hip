@@ -152,7 +152,7 @@ ttcd_status check_fw(const ttcd_fw_desc* d) {
 
 struct FwBufs {
   void *dbar, *zbt, *wpt, *m, *rst, *states;
-  float* sc;
+  float *sc, *part;
   int Tpad, N;
 };
 
@@ -163,6 +163,7 @@ void plan_fw(int B, int T, int d, int f, int C, int dt, Plan& p, FwBufs& w) {
   w.dbar = p.take((size_t)B * w.Tpad * f * es);
   w.zbt = p.take((size_t)B * f * w.Tpad * es);
   w.sc = (float*)p.take((size_t)B * w.Tpad * sizeof(float));
+  w.part = (float*)p.take(fw_stream_part_bytes(B, T, f));
   w.wpt = p.take((size_t)f * f * es);
   w.m = p.take((size_t)d * f * es);
   w.rst = p.take((size_t)B * d * w.Tpad * es);
@@ -181,7 +182,7 @@ hipError_t run_fw(int B, int T, int d, int f, int C, int kc, float eps, int dt,
   // (1) conv, difference, key norms
   StreamArgs sa{};
   sa.zt = zt; sa.zs = zs; sa.conv_t = conv_t; sa.conv_s = conv_s; sa.beta = beta;
-  sa.dbar = w.dbar; sa.zbt = w.zbt; sa.sc = w.sc;
+  sa.dbar = w.dbar; sa.zbt = w.zbt; sa.sc = w.sc; sa.part = w.part;
   sa.B = B; sa.T = T; sa.f = f; sa.kc = kc; sa.chunk = C; sa.nchunks = N; sa.eps = eps;
   sa.in_dt = dt;
   if ((e = launch_fw_stream(sa, s)) != hipSuccess) return e;

@@ -105,11 +105,13 @@ struct StreamArgs {
   const void* conv_t; const void* conv_s;
   const float* beta;
   void* dbar; void* zbt; float* sc;
+  float* part;                    // workspace: partial key norms (fw_stream_part_bytes)
   int B, T, f, kc, chunk, nchunks;
   float eps;
   int in_dt;
 };
 hipError_t launch_fw_stream(const StreamArgs& a, hipStream_t s);
+size_t fw_stream_part_bytes(int B, int T, int f);
 
 // out [cols, rows] = in [rows, cols]^T (per batch), 2- or 4-byte elements
 hipError_t launch_transpose(const void* in, void* out, int rows, int cols, long ld_in,

@@ -13,10 +13,6 @@ namespace ttcd {
 namespace {
 
 // --------------------------------------------------------------- fw stream
-constexpr int ST_T = 64;     // tokens per workgroup
-constexpr int ST_F = 64;     // features per slab
-constexpr int MAXK = 8;      // max conv taps
-
 template <typename T>
 struct Vec16;
 template <>
@@ -50,111 +46,149 @@ struct Vec16<float> {
   }
 };
 
+// Fast-weight stream, one 64-token x 128-feature tile per workgroup.  Thread
+// (tg, fc) owns 4 consecutive tokens x 8 features: it loads its kc+3 input
+// rows of both paths at once (the conv halo comes from L2), writes dbar
+// token-major, stages conv_S(Z_S) in LDS for the feature-major store, and
+// leaves a partial sum of squares per token for this feature tile.
+constexpr int S2_TT = 64, S2_FF = 128;
+
+// Element i of a run of T values held as raw 32-bit words in registers.
 template <typename T>
-__global__ void __launch_bounds__(256)
-fw_stream_kernel(const T* __restrict__ zt, const T* __restrict__ zs,
-                 const T* __restrict__ conv_t, const T* __restrict__ conv_s,
-                 const float* __restrict__ beta, T* __restrict__ dbar, T* __restrict__ zbt,
-                 float* __restrict__ sc, int T_, int Tpad, int f, int kc, int chunk,
-                 int nchunks, float eps) {
-  constexpr int VN = Vec16<T>::N;
-  __shared__ float zts[ST_T + MAXK - 1][ST_F + 1];
-  __shared__ float zss[ST_T + MAXK - 1][ST_F + 1];
-  __shared__ float tap_t[ST_F][MAXK];
-  __shared__ float tap_s[ST_F][MAXK];
-  __shared__ float zbT[ST_F][ST_T + 1];
+TTCD_DEV float raw_el(const uint32_t* w, int i);
+template <>
+TTCD_DEV float raw_el<bf16_t>(const uint32_t* w, int i) {
+  return (i & 1) ? __uint_as_float(w[i >> 1] & 0xFFFF0000u) : __uint_as_float(w[i >> 1] << 16);
+}
+template <>
+TTCD_DEV float raw_el<float>(const uint32_t* w, int i) { return __uint_as_float(w[i]); }
 
-  const int b = blockIdx.y;
-  const int t0 = blockIdx.x * ST_T;
+// Four waves per SIMD where the rows fit in 128 registers (bf16, up to 4 taps),
+// else two.
+template <typename T, int KC>
+constexpr int stream_waves() { return (sizeof(T) == 2 && KC <= 4) ? 4 : 2; }
+
+template <typename T, int KC>
+__global__ void __launch_bounds__(256, (stream_waves<T, KC>()))
+fw_stream2_kernel(const T* __restrict__ zt, const T* __restrict__ zs,
+                  const T* __restrict__ conv_t, const T* __restrict__ conv_s,
+                  T* __restrict__ dbar, T* __restrict__ zbt, float* __restrict__ part,
+                  int T_, int Tpad, int f) {
+  constexpr int kc = KC;
+  constexpr int VN = Vec16<T>::N;          // elements per 16-byte vector
+  constexpr int NV = 8 / VN;               // vectors per 8 features
+  constexpr int RW = 8 * sizeof(T) / 4;    // 32-bit words per row of 8 features
+  constexpr int WW = KC * RW;              // words of 8 features x KC taps
+  __shared__ float zb[S2_FF][S2_TT + 1];
+  const int b = blockIdx.z;
+  const int t0 = blockIdx.x * S2_TT;
+  const int ft = blockIdx.y;
   const int tid = threadIdx.x;
-  const int tok = tid >> 2, fq = tid & 3;      // compute mapping
-  const int t = t0 + tok;
-  const int halo = kc - 1;
-  const int nrows = ST_T + halo;
+  const int fc = tid & 15, tg = tid >> 4;
+  const int c0 = ft * S2_FF + fc * 8;      // first of this thread's 8 features
+  const int tf = t0 + 4 * tg;              // first of its 4 tokens
+  const bool fok = c0 < f;                 // f % 8 == 0: all 8 or none
   const size_t zoff = (size_t)b * T_ * f;
-  const T* ztb = zt + zoff;
-  const T* zsb = zs + zoff;
-  float ssq = 0.f;
 
-  for (int c0 = 0; c0 < f; c0 += ST_F) {
-    __syncthreads();
-    // stage the slab (rows t0-halo .. t0+63) of both paths
-    constexpr int CPR = ST_F / VN;   // vector chunks per row
-    for (int e = tid; e < nrows * CPR; e += 256) {
-      const int row = e / CPR, cc = e % CPR;
-      const int tt = t0 - halo + row;
-      const int c = c0 + cc * VN;
-      float a[VN], bb[VN];
-      if (tt >= 0 && tt < T_ && c < f) {
-        Vec16<T>::load(ztb + (size_t)tt * f + c, a);
-        Vec16<T>::load(zsb + (size_t)tt * f + c, bb);
-      } else {
+  // taps of the 8 features: conv[c][k] is contiguous over (c, k)
+  uint32_t wt[WW], ws[WW];
+  uint32_t xt[KC + 3][RW], xs[KC + 3][RW];
+  constexpr int nrow = KC + 3;
+  if (fok) {
 #pragma unroll
-        for (int i = 0; i < VN; ++i) a[i] = bb[i] = 0.f;
-      }
+    for (int v = 0; v < WW / 4; ++v) {
+      const u32x4 a = ld16(conv_t + (size_t)c0 * kc + v * (16 / sizeof(T)));
+      const u32x4 c = ld16(conv_s + (size_t)c0 * kc + v * (16 / sizeof(T)));
 #pragma unroll
-      for (int i = 0; i < VN; ++i) {
-        zts[row][cc * VN + i] = a[i];
-        zss[row][cc * VN + i] = bb[i];
+      for (int j = 0; j < 4; ++j) { wt[4 * v + j] = a[j]; ws[4 * v + j] = c[j]; }
+    }
+#pragma unroll
+    for (int rr = 0; rr < nrow; ++rr) {
+      const int tt = tf - (kc - 1) + rr;
+      const bool in = tt >= 0 && tt < T_;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+        if (in) {
+          a = ld16(zt + zoff + (size_t)tt * f + c0 + v * VN);
+          c = ld16(zs + zoff + (size_t)tt * f + c0 + v * VN);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { xt[rr][4 * v + j] = a[j]; xs[rr][4 * v + j] = c[j]; }
       }
     }
-    for (int e = tid; e < ST_F * kc; e += 256) {
-      const int cc = e / kc, k = e % kc;
-      const int c = c0 + cc;
-      tap_t[cc][k] = c < f ? ldf(conv_t + (size_t)c * kc + k) : 0.f;
-      tap_s[cc][k] = c < f ? ldf(conv_s + (size_t)c * kc + k) : 0.f;
-    }
-    __syncthreads();
-
-    // conv of 16 features of one token
-    float dv[16];
-    const bool tok_ok = t < T_;
+  }
+  float ssq[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int cc = fq * 16 + i;
+  for (int i = 0; i < 4; ++i) {
+    const int t = tf + i;
+    float dv[8];
+    float sq = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
       float at = 0.f, as = 0.f;
-      for (int k = 0; k < kc; ++k) {
-        at = __builtin_fmaf(tap_t[cc][k], zts[tok + k][cc], at);
-        as = __builtin_fmaf(tap_s[cc][k], zss[tok + k][cc], as);
+      if (fok) {
+#pragma unroll
+        for (int k = 0; k < kc; ++k) {
+          at = __builtin_fmaf(raw_el<T>(wt, e * KC + k), raw_el<T>(xt[i + k], e), at);
+          as = __builtin_fmaf(raw_el<T>(ws, e * KC + k), raw_el<T>(xs[i + k], e), as);
+        }
       }
-      if (!tok_ok) at = as = 0.f;
-      dv[i] = at - as;
-      zbT[cc][tok] = as;
-      ssq = __builtin_fmaf(as, as, ssq);
+      if (t >= T_) at = as = 0.f;
+      dv[e] = at - as;
+      zb[fc * 8 + e][4 * tg + i] = as;
+      sq = __builtin_fmaf(as, as, sq);
     }
-    if (t < Tpad) {
-      T* dp = dbar + ((size_t)b * Tpad + t) * f + c0 + fq * 16;
+    ssq[i] = sq;
+    if (fok && t < Tpad) {
+      T* dp = dbar + ((size_t)b * Tpad + t) * f + c0;
 #pragma unroll
-      for (int i = 0; i < 16; i += VN)
-        if (c0 + fq * 16 + i < f) Vec16<T>::store(dp + i, dv + i);
-    }
-    __syncthreads();
-    // transposed write: feature row fr, 16 tokens per thread
-    {
-      const int fr = tid >> 2, tq = tid & 3;
-      const int c = c0 + fr;
-      if (c < f) {
-        T* zp = zbt + ((size_t)b * f + c) * Tpad + t0 + tq * 16;
-        float v[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = zbT[fr][tq * 16 + i];
-#pragma unroll
-        for (int i = 0; i < 16; i += VN)
-          if (t0 + tq * 16 + i < Tpad) Vec16<T>::store(zp + i, v + i);
-      }
+      for (int v = 0; v < NV; ++v) Vec16<T>::store(dp + v * VN, dv + v * VN);
     }
   }
-  // per-token norm -> scale beta_i / max(||zbar_s||, eps)
-  ssq += __shfl_xor(ssq, 1, 64);
-  ssq += __shfl_xor(ssq, 2, 64);
-  if (fq == 0 && t < Tpad) {
-    float v = 0.f;
-    if (t < T_) {
-      const int ci = min(t / chunk, nchunks - 1);
-      v = beta[(size_t)b * nchunks + ci] / fmaxf(sqrtf(ssq), eps);
-    }
-    sc[(size_t)b * Tpad + t] = v;
+  // partial l2 norms of this feature tile: reduce over the 16 feature chunks
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) ssq[i] += __shfl_xor(ssq[i], o, 64);
   }
+  if (fc == 0) {
+    float* pp = part + ((size_t)b * gridDim.y + ft) * Tpad + tf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pp[i] = ssq[i];
+  }
+  __syncthreads();
+  // feature-major store of conv_S(Z_S): row = feature, 32 tokens per thread
+  {
+    const int fr = tid >> 1, half = tid & 1;
+    const int c = ft * S2_FF + fr;
+    if (c < f) {
+      T* zp = zbt + ((size_t)b * f + c) * Tpad + t0 + 32 * half;
+      float v[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = zb[fr][32 * half + i];
+#pragma unroll
+      for (int i = 0; i < 32; i += VN) Vec16<T>::store(zp + i, v + i);
+    }
+  }
+}
+
+// sc[b, t] = beta[b, t / chunk] / max(sqrt(sum of the partial norms), eps)
+__global__ void __launch_bounds__(256)
+fw_key_scale_kernel(const float* __restrict__ part, const float* __restrict__ beta,
+                    float* __restrict__ sc, int nft, int T_, int Tpad, int chunk, int nchunks,
+                    float eps) {
+  const int b = blockIdx.y;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= Tpad) return;
+  float v = 0.f;
+  if (t < T_) {
+    float ss = 0.f;
+    for (int y = 0; y < nft; ++y) ss += part[((size_t)b * nft + y) * Tpad + t];
+    const int ci = min(t / chunk, nchunks - 1);
+    v = beta[(size_t)b * nchunks + ci] / fmaxf(sqrtf(ss), eps);
+  }
+  sc[(size_t)b * Tpad + t] = v;
 }
 
 // --------------------------------------------------------------- rmsnorm
@@ -284,19 +318,38 @@ __global__ void convert_kernel(const float* in, OutT* out, long n) {
 
 }  // namespace
 
+size_t fw_stream_part_bytes(int B, int T, int f) {
+  const size_t Tpad = ((size_t)T + 63) / 64 * 64;
+  return (size_t)B * ((f + S2_FF - 1) / S2_FF) * Tpad * sizeof(float);
+}
+
 hipError_t launch_fw_stream(const StreamArgs& a, hipStream_t s) {
   const int Tpad = (a.T + 63) / 64 * 64;
-  dim3 grid(Tpad / ST_T, a.B);
-  if (a.in_dt == BF16)
-    hipLaunchKernelGGL(fw_stream_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)a.zt,
-                       (const bf16_t*)a.zs, (const bf16_t*)a.conv_t, (const bf16_t*)a.conv_s,
-                       a.beta, (bf16_t*)a.dbar, (bf16_t*)a.zbt, a.sc, a.T, Tpad, a.f, a.kc,
-                       a.chunk, a.nchunks, a.eps);
-  else
-    hipLaunchKernelGGL(fw_stream_kernel<float>, grid, dim3(256), 0, s, (const float*)a.zt,
-                       (const float*)a.zs, (const float*)a.conv_t, (const float*)a.conv_s,
-                       a.beta, (float*)a.dbar, (float*)a.zbt, a.sc, a.T, Tpad, a.f, a.kc,
-                       a.chunk, a.nchunks, a.eps);
+  const int nft = (a.f + S2_FF - 1) / S2_FF;
+  dim3 grid(Tpad / S2_TT, nft, a.B);
+  switch (a.kc) {
+#define TTCD_STREAM_KC(K)                                                                        \
+  case K:                                                                                        \
+    if (a.in_dt == BF16)                                                                         \
+      hipLaunchKernelGGL((fw_stream2_kernel<bf16_t, K>), grid, dim3(256), 0, s,                  \
+                         (const bf16_t*)a.zt, (const bf16_t*)a.zs, (const bf16_t*)a.conv_t,      \
+                         (const bf16_t*)a.conv_s, (bf16_t*)a.dbar, (bf16_t*)a.zbt, a.part, a.T,  \
+                         Tpad, a.f);                                                             \
+    else                                                                                         \
+      hipLaunchKernelGGL((fw_stream2_kernel<float, K>), grid, dim3(256), 0, s,                   \
+                         (const float*)a.zt, (const float*)a.zs, (const float*)a.conv_t,         \
+                         (const float*)a.conv_s, (float*)a.dbar, (float*)a.zbt, a.part, a.T,     \
+                         Tpad, a.f);                                                             \
+    break;
+    TTCD_STREAM_KC(1) TTCD_STREAM_KC(2) TTCD_STREAM_KC(3) TTCD_STREAM_KC(4)
+    TTCD_STREAM_KC(5) TTCD_STREAM_KC(6) TTCD_STREAM_KC(7) TTCD_STREAM_KC(8)
+#undef TTCD_STREAM_KC
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fw_key_scale_kernel, dim3(Tpad / 256 + 1, a.B), dim3(256), 0, s, a.part,
+                     a.beta, a.sc, nft, a.T, Tpad, a.chunk, a.nchunks, a.eps);
   return hipGetLastError();
 }
 
