@@ -206,7 +206,7 @@ typedef struct {
 
 /* Optional intermediate outputs (any member may be NULL). */
 typedef struct {
-  void* o_teacher;      /* [batch, seq_q, n_q_heads, head_dim] attn.out_dtype */
+  void* o_teacher;      /* [batch, seq_q, n_q_heads, head_dim] attn.in_dtype */
   void* o_student;
   float* lse_teacher;   /* [batch, n_q_heads, seq_q] */
   float* lse_student;
