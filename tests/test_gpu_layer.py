@@ -80,3 +80,52 @@ def test_small_chunk_uses_generic_apply():
 
 def test_smollm2_16k_layer_full():
     check_layer(I.CONFIGS[2])
+
+
+def test_qwen3_64k_layer_full_against_stored_oracle_rows():
+    """The 64K workload at full size, in the launch configuration of the
+    benchmark, against oracle rows written by tests/golden/make_layer_golden.py."""
+    from dual_window_attention_amd import ttcd
+    from tests.golden import make_layer_golden as G
+    ref = np.load(G.OUT)
+    cfg = I.CONFIGS[3]
+    say("layer qwen3 64K: inputs")
+    att = I.attention_inputs(cfg)
+    w = I.layer_weights(cfg)
+    beta = I.beta_for(cfg)
+    x = I.residual_input(cfg)
+    fp = G.fingerprint({"q": att["q"].f64(),
+                        "k": att["k"].f64(), "v": att["v"].f64(), "x": x.f64(),
+                        **{n: t.f64() for n, t in w.items()}, "beta": beta.astype(np.float64)})
+    for n, a in fp.items():
+        np.testing.assert_allclose(a, ref[n], rtol=1e-12, err_msg=f"stored rows are stale ({n})")
+    q, k, v = (I.to_torch(att[n]) for n in ("q", "k", "v"))
+    del att
+    wd = {n: I.to_torch(t) for n, t in w.items()}
+    wd["beta"] = I.f32_to_torch(beta)
+    xd = I.to_torch(x)
+    rows = torch.from_numpy(ref["rows"]).cuda()
+    tol = tol_for(cfg.dtype)
+    say("  GPU, benchmark launch configuration (no intermediates)")
+    out = ttcd.layer_forward(q, k, v, xd, wd, cfg.w_teacher, cfg.w_student, cfg.chunk)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all().item()
+    assert_close(to_np(out[0, rows]), ref["out"], tol, "out (sampled rows)")
+    del out
+    say("  GPU, with intermediates")
+    out, aux = ttcd.layer_forward(q, k, v, xd, wd, cfg.w_teacher, cfg.w_student, cfg.chunk,
+                                  aux=True)
+    torch.cuda.synchronize()
+    assert_close(to_np(out[0, rows]), ref["out"], tol, "out (sampled rows)")
+    assert_close(to_np(aux["y"][0, rows]), ref["y"], tol, "y (sampled rows)")
+    assert_close_stored(to_np(aux["o_teacher"][0, rows]).reshape(len(rows), -1),
+                        ref["o_t"].reshape(len(rows), -1), tol, "O_teacher", cfg.dtype)
+    assert_close_stored(to_np(aux["o_student"][0, rows]).reshape(len(rows), -1),
+                        ref["o_s"].reshape(len(rows), -1), tol, "O_student", cfg.dtype)
+    assert_close(to_np(aux["lse_teacher"][0][:, rows]), ref["lse_t"], (1e-3, 1e-5), "LSE_T")
+    assert_close(to_np(aux["lse_student"][0][:, rows]), ref["lse_s"], (1e-3, 1e-5), "LSE_S")
+    assert_close_stored(to_np(aux["z_teacher"][0, rows]), ref["z_t"], tol, "Z_teacher", cfg.dtype)
+    assert_close_stored(to_np(aux["z_student"][0, rows]), ref["z_s"], tol, "Z_student", cfg.dtype)
+    si = torch.from_numpy(ref["state_i"]).cuda()
+    sj = torch.from_numpy(ref["state_j"]).cuda()
+    assert_close(to_np(aux["state_out"][0, si, sj]), ref["state"], tol, "final state (sampled)")

@@ -34,3 +34,16 @@ def test_outlier_keys_fraction():
     rms = np.sqrt((k.astype(np.float64) ** 2).mean(-1))
     frac = (rms > 4.0).mean()
     assert 0.04 < frac < 0.06
+
+
+def test_stored_64k_layer_rows_match_the_generators():
+    """The stored oracle rows of the 64K layer were written from exactly the
+    inputs the generators produce now (else rerun make_layer_golden.py)."""
+    from tests.golden import make_layer_golden as G
+    ref = np.load(G.OUT)
+    cfg = I.CONFIGS[3]
+    q, k, v, x, w = G.inputs64(cfg)
+    fp = G.fingerprint({"q": q, "k": k, "v": v, "x": x, **w})
+    assert sorted(fp) == sorted(n for n in ref.files if n.startswith("fp_"))
+    for n, a in fp.items():
+        np.testing.assert_allclose(a, ref[n], rtol=1e-12, err_msg=n)
