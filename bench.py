@@ -23,6 +23,46 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2516.6       # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_qwen3_64k.txt")
+# the sources whose kernels each traffic figure was measured on
+TRAFFIC_SOURCES = {
+    "attention": ["dual_window_attention_amd/csrc/attn.hip", "dual_window_attention_amd/csrc/common.hpp"],
+    "scan": ["dual_window_attention_amd/csrc/stream.hip", "dual_window_attention_amd/csrc/common.hpp"],
+}
+
+
+def source_digest(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(part):
+    """HBM bytes per launch of ``part`` from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known size), or
+    None when the kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    sec, vals = None, {}
+    for ln in lines:
+        ln = ln.strip()
+        if ln.startswith("[") and ln.endswith("]"):
+            sec = ln[1:-1]
+        elif sec == part and ":" in ln and not ln.startswith("#"):
+            k_, v_ = ln.split(":", 1)
+            vals[k_.strip()] = v_.strip()
+    if vals.get("sources_sha256") != source_digest(TRAFFIC_SOURCES[part]):
+        return None
+    try:
+        return float(vals["bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def attention_flops(cfg, wT):
@@ -38,6 +78,118 @@ def scan_bytes(cfg):
     """Algorithmic bytes of the fast-weight stream: read Z_T, Z_S, write
     the residual difference and the keys (bf16): 8 B T f."""
     return 8.0 * cfg.batch * cfg.seq * cfg.d_ff
+
+
+def time_events(fn, n, stream, warmup=5):
+    """Mean device time of ``fn`` over ``n`` calls, from HIP events recorded
+    on ``stream`` (the stream the library launches on).  The warmup calls
+    bring the clocks back up after host-side set-up left the GPU idle."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+
+
+def scan_roofline(cfg, dev, n):
+    """The fast-weight stream (HBM-bound) at the workload's size, timed alone."""
+    import torch
+    from dual_window_attention_amd import inputs as I
+    from dual_window_attention_amd import ttcd
+
+    z = I.hidden_activations(cfg)
+    w = I.layer_weights(cfg)
+    zt, zs = I.to_torch(z["z_t"], dev), I.to_torch(z["z_s"], dev)
+    del z
+    ct, cs = I.to_torch(w["conv_t"], dev), I.to_torch(w["conv_s"], dev)
+    beta = I.f32_to_torch(I.beta_for(cfg), dev)
+    out = ttcd.fastweight_stream(zt, zs, ct, cs, beta, cfg.chunk)
+    ws = torch.empty(max(256, ttcd.lib().ttcd_fastweight_stream_workspace_size(
+        ttcd.fw_desc(zt, 8, cfg.chunk, cfg.conv_k))), dtype=torch.uint8, device=dev)
+
+    def run():
+        ttcd.fastweight_stream(zt, zs, ct, cs, beta, cfg.chunk, out=out, workspace=ws)
+
+    ms = time_events(run, n, torch.cuda.current_stream(), warmup=20)
+    gb = scan_bytes(cfg) / 1e9
+    return {"bound": "hbm", "kernel": "fast-weight stream (ttcd_fastweight_stream)",
+            "achieved": gb / (ms * 1e-3), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": gb / (ms * 1e-3) / PEAK_HBM_GBS, "traffic": measured_traffic("scan"),
+            "ms_per_launch": ms, "algorithmic_gb": gb}
+
+
+def decode_bench(dev, n):
+    """One decode token per sequence at the batch-32, 64K-cache workload:
+    low-rank lists and folded dense state; the fold itself timed once."""
+    import torch
+    from dual_window_attention_amd import inputs as I
+    from dual_window_attention_amd import ttcd
+
+    cfg = I.CONFIGS[5]
+    B, L = cfg.batch, cfg.cache_len
+    dec = I.decode_inputs(cfg)
+    m = 2      # sequence b takes the lists and write coefficients of sequence b % 2
+    dec["beta_list"] = np.ascontiguousarray(dec["beta_list"][np.arange(B) % m])
+    sets = [I.decode_lists(cfg, s) for s in range(m)]
+    on = [(I.to_torch(r, dev), I.to_torch(k, dev)) for r, k in sets]
+    del sets
+    r_l = torch.stack([on[b % m][0] for b in range(B)])
+    k_l = torch.stack([on[b % m][1] for b in range(B)])
+    del on
+    w = I.layer_weights(cfg)
+    wd = {k_: I.to_torch(t, dev) for k_, t in w.items()}
+    start = dec["window_start"]
+
+    def cache(win):
+        t = I.to_torch(win, dev)
+        c = torch.full((B, L + 1) + tuple(t.shape[2:]), float("nan"), dtype=t.dtype, device=dev)
+        c[:, start:start + t.shape[1]] = t
+        return c
+
+    kc, vc = cache(dec["k_win"]), cache(dec["v_win"])
+    q, x = I.to_torch(dec["q"], dev), I.to_torch(dec["x"], dev)
+    bl = I.f32_to_torch(dec["beta_list"], dev)
+    stream = torch.cuda.current_stream()
+    fold_ws = torch.empty(max(256, ttcd.lib().ttcd_fastweight_fold_workspace_size(
+        ttcd.FwDesc(B, L, cfg.d_model, cfg.d_ff, cfg.chunk, 1, 0.0, 1, 0), L // cfg.chunk)),
+        dtype=torch.uint8, device=dev)
+    dense = ttcd.fastweight_fold(wd["w_down0"], r_l, k_l, bl, cfg.chunk, workspace=fold_ws)
+    fold_ms = time_events(lambda: ttcd.fastweight_fold(wd["w_down0"], r_l, k_l, bl, cfg.chunk,
+                                                       workspace=fold_ws), 2, stream, warmup=1)
+    out = torch.empty((B, 1, cfg.d_model), dtype=torch.float32, device=dev)
+    res = {}
+    win_bytes = 2.0 * B * min(cfg.w_teacher, L + 1) * cfg.n_kv_heads * cfg.head_dim * 2
+    w_bytes = sum(int(wd[n_].numel()) * 2 for n_ in ("w_o", "w_gate", "w_up", "w_down0"))
+    for form, d in (("dense", {"pos": L, "state_dense": dense, "beta_list": bl}),
+                    ("lists", {"pos": L, "r_list": r_l, "k_list": k_l, "beta_list": bl})):
+        need = ttcd.layer_workspace_bytes(q, kc, cfg.d_model, cfg.d_ff, cfg.w_teacher,
+                                          cfg.w_student, cfg.chunk,
+                                          decode_chunks=L // cfg.chunk, pos=L)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+
+        def step(d=d, ws=ws):
+            ttcd.layer_forward(q, kc, vc, x, wd, cfg.w_teacher, cfg.w_student, cfg.chunk,
+                               decode=d, out=out, workspace=ws)
+
+        ms = time_events(step, n, stream, warmup=10)
+        st_bytes = (B * cfg.d_model * cfg.d_ff * 4.0 if form == "dense"
+                    else float(r_l.numel() + k_l.numel()) * 2)
+        gb = (win_bytes + w_bytes + st_bytes) / 1e9
+        res[form] = {"ms_per_step": ms, "tokens_per_s": B / (ms * 1e-3),
+                     "algorithmic_gb": gb, "achieved_gbs": gb / (ms * 1e-3),
+                     "hbm_frac": gb / (ms * 1e-3) / PEAK_HBM_GBS}
+        assert torch.isfinite(out).all().item()
+    res["fold_ms"] = fold_ms
+    res["fold_tflops"] = 2.0 * B * L * cfg.d_model * cfg.d_ff / (fold_ms * 1e-3) / 1e12
+    res["workload"] = (f"{cfg.name}: decode step, batch {B}, 64K cache (NaN outside the "
+                       f"w_T={cfg.w_teacher} window), {L // cfg.chunk} chunk lists")
+    return res
 
 
 def cpu_baseline(cfg, sample_tokens):
@@ -72,8 +224,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=3)
-    ap.add_argument("--cpu-sample", type=int, default=9216,
+    ap.add_argument("--cpu-sample", type=int, default=20480,
                     help="tokens of the oracle CPU baseline sample (0 = skip)")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step section")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (a reference "
                          "kernel of known traffic for scaling memory counters)")
@@ -132,19 +285,10 @@ def main():
     o_s = torch.empty_like(o_t)
     aws = torch.empty(max(256, ttcd.lib().ttcd_dual_window_attn_workspace_size(
         ttcd.attn_desc(q, k, cfg.w_teacher, cfg.w_student))), dtype=torch.uint8, device=dev)
-    for _ in range(2):
-        ttcd.dual_window_attn(q, k, v, cfg.w_teacher, cfg.w_student, with_lse=False,
-                              out=(o_t, o_s), workspace=aws)
-    n_att = max(3, args.steps)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n_att)]
-    for e0, e1 in evs:
-        e0.record(stream)
-        ttcd.dual_window_attn(q, k, v, cfg.w_teacher, cfg.w_student, with_lse=False,
-                              out=(o_t, o_s), workspace=aws)
-        e1.record(stream)
-    torch.cuda.synchronize()
-    att_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    n_att = max(10, args.steps)
+    att_ms = time_events(lambda: ttcd.dual_window_attn(q, k, v, cfg.w_teacher, cfg.w_student,
+                                                       with_lse=False, out=(o_t, o_s),
+                                                       workspace=aws), n_att, stream)
     flops = attention_flops(cfg, cfg.w_teacher)
     achieved = flops / (att_ms * 1e-3) / 1e12
 
@@ -168,9 +312,16 @@ def main():
                    "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "dual-window attention (ttcd_dual_window_attn)",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic("attention"),
                      "ms_per_launch": att_ms, "algorithmic_tflop": flops / 1e12},
     }
+    del q, k, v, wd, x, out, ws, o_t, o_s, aws
+    torch.cuda.empty_cache()
+    res["scan"] = scan_roofline(cfg, dev, n_att)
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        res["decode"] = decode_bench(dev, n_att)
+        torch.cuda.empty_cache()
     if args.cpu_sample > 0:
         res["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_sample, cfg.seq))
     print(json.dumps(res), flush=True)

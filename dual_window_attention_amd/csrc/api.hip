@@ -362,6 +362,38 @@ ttcd_status ttcd_fastweight_scan(const ttcd_fw_desc* d, const void* zt, const vo
   return ok();
 }
 
+size_t ttcd_fastweight_stream_workspace_size(const ttcd_fw_desc* d) {
+  if (check_fw(d) != TTCD_OK) return 0;
+  return fw_stream_part_bytes(d->batch, d->seq, d->d_ff);
+}
+
+ttcd_status ttcd_fastweight_stream(const ttcd_fw_desc* d, const void* zt, const void* zs,
+                                   const void* conv_t, const void* conv_s, const float* beta,
+                                   void* dbar, void* zbar_s_t, float* key_scale, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  ttcd_status st = check_fw(d);
+  if (st != TTCD_OK) return st;
+  REQ_PTR(zt); REQ_PTR(zs); REQ_PTR(conv_t); REQ_PTR(conv_s); REQ_PTR(dbar);
+  REQ_PTR(zbar_s_t);
+  if (!beta) return fail(TTCD_ERR_NULL_POINTER, "beta is NULL");
+  if (!key_scale) return fail(TTCD_ERR_NULL_POINTER, "key_scale is NULL");
+  OPT_PTR4(beta); OPT_PTR4(key_scale);
+  const size_t need = ttcd_fastweight_stream_workspace_size(d);
+  if (ws_bytes < need)
+    return fail(TTCD_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (!ws) return fail(TTCD_ERR_NULL_POINTER, "workspace is NULL");
+  OPT_PTR(ws);
+  StreamArgs sa{};
+  sa.zt = zt; sa.zs = zs; sa.conv_t = conv_t; sa.conv_s = conv_s; sa.beta = beta;
+  sa.dbar = dbar; sa.zbt = zbar_s_t; sa.sc = key_scale; sa.part = (float*)ws;
+  sa.B = d->batch; sa.T = d->seq; sa.f = d->d_ff; sa.kc = d->conv_k; sa.chunk = d->chunk;
+  sa.nchunks = (d->seq + d->chunk - 1) / d->chunk;
+  sa.eps = d->l2_eps > 0.f ? d->l2_eps : 1e-12f;
+  sa.in_dt = d->in_dtype;
+  HIPCHK(launch_fw_stream(sa, (hipStream_t)stream));
+  return ok();
+}
+
 size_t ttcd_layer_forward_workspace_size(const ttcd_layer_desc* d, const ttcd_fw_state* dec) {
   if (check_layer(d, dec) != TTCD_OK) return 0;
   Plan p(nullptr);

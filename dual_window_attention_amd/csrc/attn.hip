@@ -599,6 +599,47 @@ hipError_t launch_mfma(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// V^T operand of the PV product: vt[b, g, d, c] = v[b, key(c), g, d], where
+// storage column c holds key c with bits 2 and 3 swapped inside each group
+// of 16, so that one 16-byte LDS read gives a lane the 8 keys of its MFMA
+// operand.  Keys outside [jlo, Tk) are written as zero.  One workgroup per
+// 64 keys x 64 dims, 16-byte loads and stores through an LDS tile.
+__global__ void __launch_bounds__(256)
+v_transpose_kernel(const uint16_t* __restrict__ v, uint16_t* __restrict__ vt, int Tk, int jlo,
+                   int kv_rows, int Hkv, int D, int vt_ld) {
+  __shared__ __align__(16) uint16_t tile[64][64 + 8];   // [key][dim]
+  const int bg = blockIdx.z;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const long j0 = (long)blockIdx.x * 64;
+  const int d0 = blockIdx.y * 64;
+  const uint16_t* vp = v + ((size_t)b * kv_rows * Hkv + g) * D + d0;
+  uint16_t* op = vt + ((size_t)bg * D + d0) * vt_ld + j0;
+  const int t = threadIdx.x;
+  const int c = t & 7;                       // 16-byte piece of a 64-element row
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int i = (t >> 3) + 32 * it;        // key row of the tile
+    const long j = j0 + i;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (j >= jlo && j < Tk) val = ld16(vp + j * Hkv * D + c * 8);
+    *reinterpret_cast<u32x4*>(&tile[i][c * 8]) = val;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int dd = (t >> 3) + 32 * it;       // dim row of the output
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int c0 = c * 8 + e, c1 = c0 + 1;
+      const int k0 = (c0 & ~12) | ((c0 & 4) << 1) | ((c0 & 8) >> 1);
+      const int k1 = (c1 & ~12) | ((c1 & 4) << 1) | ((c1 & 8) >> 1);
+      o[e / 2] = (uint32_t)tile[k0][dd] | ((uint32_t)tile[k1][dd] << 16);
+    }
+    st16(op + (size_t)dd * vt_ld + c * 8, o);
+  }
+}
+
 template <typename T, int D>
 hipError_t launch_simple(const AttnArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
@@ -624,8 +665,11 @@ hipError_t launch_dual_window_attn(const AttnArgs& a, hipStream_t s) {
   if (a.in_dt == BF16 && (a.D == 64 || a.D == 128)) {
     // V^T with the keys every query may read: [max(0, q_pos0 - w_T + 1), Tk)
     const int jlo_all = a.q_pos0 - a.wT + 1 > 0 ? a.q_pos0 - a.wT + 1 : 0;
-    hipError_t e = launch_v_transpose(a.v, a.vt, a.B, a.Tk, jlo_all, a.kv_rows, a.Hkv, a.D,
-                                      a.vt_ld, s);
+    // grid covers vt_ld (a multiple of 64) keys and D (64 or 128) dims
+    hipLaunchKernelGGL(v_transpose_kernel, dim3(a.vt_ld / 64, a.D / 64, a.B * a.Hkv), dim3(256),
+                       0, s, (const uint16_t*)a.v, (uint16_t*)a.vt, a.Tk, jlo_all, a.kv_rows,
+                       a.Hkv, a.D, a.vt_ld);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return a.D == 64 ? launch_mfma<64>(a, s) : launch_mfma<128>(a, s);
   }

@@ -124,8 +124,6 @@ hipError_t launch_transpose_scale(const void* in, void* out, int rows, int cols,
                                   hipStream_t s);
 // V [B, kv_rows, Hkv, D] (bf16) -> vt [B, Hkv, D, vt_ld]: keys in [jlo, Tk), the
 // keys of each 16-group permuted for the attention kernel's MFMA operand reads
-hipError_t launch_v_transpose(const void* v, void* vt, int B, int Tk, int jlo, int kv_rows,
-                              int Hkv, int D, int vt_ld, hipStream_t s);
 
 // decode fast-weight apply from low-rank lists:
 //   c[b, t]  = k_list[b, t] . z[b]          (t < n*chunk)

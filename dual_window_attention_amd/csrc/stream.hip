@@ -240,35 +240,6 @@ transpose_kernel(const E* __restrict__ in, E* __restrict__ out, int rows, int co
   }
 }
 
-// V [B, kv_rows, Hkv, D] -> vt [B, Hkv, D, vt_ld] (bf16), the keys of every
-// aligned group of 16 stored in the order that makes the 8 keys one MFMA lane
-// needs contiguous (bits 2 and 3 of the key index swapped).  Only keys in
-// [jlo, Tk) are read; the other columns are zero.
-__global__ void __launch_bounds__(256)
-v_transpose_kernel(const uint16_t* __restrict__ v, uint16_t* __restrict__ vt, int Tk, int jlo,
-                   int kv_rows, int Hkv, int D, int vt_ld) {
-  __shared__ uint16_t tile[64][65];
-  const int bg = blockIdx.z;
-  const int b = bg / Hkv, g = bg % Hkv;
-  const long j0 = (long)blockIdx.x * 64;
-  const int d0 = blockIdx.y * 64;
-  const uint16_t* vp = v + ((size_t)b * kv_rows * Hkv + g) * D;
-  uint16_t* op = vt + (size_t)bg * D * vt_ld;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const long j = j0 + i;
-    const int d = d0 + tx;
-    tile[i][tx] = (j >= jlo && j < Tk && d < D) ? vp[j * Hkv * D + d] : (uint16_t)0;
-  }
-  __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int d = d0 + i;
-    const int col = tx;                                   // storage column within the tile
-    const int key = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);
-    if (d < D && j0 + col < vt_ld) op[(size_t)d * vt_ld + j0 + col] = tile[key][i];
-  }
-}
-
 // out[b][c][r] = in[b][r][c] * (scale ? scale[b * nscale + r / rows_per_scale] : 1)
 template <typename T>
 __global__ void __launch_bounds__(256)
@@ -384,14 +355,6 @@ hipError_t launch_transpose(const void* in, void* out, int rows, int cols, long 
   else
     hipLaunchKernelGGL(transpose_kernel<uint32_t>, grid, dim3(256), 0, s, (const uint32_t*)in,
                        (uint32_t*)out, rows, cols, ld_in, ld_out, s_in, s_out);
-  return hipGetLastError();
-}
-
-hipError_t launch_v_transpose(const void* v, void* vt, int B, int Tk, int jlo, int kv_rows, int Hkv,
-                              int D, int vt_ld, hipStream_t s) {
-  dim3 grid(vt_ld / 64, (D + 63) / 64, B * Hkv);
-  hipLaunchKernelGGL(v_transpose_kernel, grid, dim3(256), 0, s, (const uint16_t*)v, (uint16_t*)vt,
-                     Tk, jlo, kv_rows, Hkv, D, vt_ld);
   return hipGetLastError();
 }
 

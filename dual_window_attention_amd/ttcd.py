@@ -34,6 +34,7 @@ STATUS = {
 EXPORTS = (
     "ttcd_dual_window_attn_workspace_size", "ttcd_dual_window_attn",
     "ttcd_fastweight_scan_workspace_size", "ttcd_fastweight_scan",
+    "ttcd_fastweight_stream_workspace_size", "ttcd_fastweight_stream",
     "ttcd_layer_forward_workspace_size", "ttcd_layer_forward",
     "ttcd_fastweight_fold_workspace_size", "ttcd_fastweight_fold",
     "ttcd_status_string", "ttcd_last_error", "ttcd_version",
@@ -86,6 +87,9 @@ _sig = {
     "ttcd_fastweight_scan_workspace_size": (_sz, [C.POINTER(FwDesc)]),
     "ttcd_fastweight_scan": (C.c_int, [C.POINTER(FwDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _vp, _vp, _vp, _sz, _vp]),
+    "ttcd_fastweight_stream_workspace_size": (_sz, [C.POINTER(FwDesc)]),
+    "ttcd_fastweight_stream": (C.c_int, [C.POINTER(FwDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                         _vp, _vp, _sz, _vp]),
     "ttcd_layer_forward_workspace_size": (_sz, [C.POINTER(LayerDesc), C.POINTER(FwState)]),
     "ttcd_layer_forward": (C.c_int, [C.POINTER(LayerDesc), C.POINTER(LayerWeights), _vp, _vp,
                                      _vp, _vp, _vp, C.POINTER(FwState), C.POINTER(LayerAux),
@@ -233,6 +237,33 @@ def fastweight_scan(z_teacher, z_student, z_main, conv_t, conv_s, w_down0, w_pro
                                      _ptr(beta), _ptr(y), _ptr(st), _ptr(ws), ws.numel(),
                                      _stream(stream)), "ttcd_fastweight_scan")
     return y, st
+
+
+def stream_pad(seq: int) -> int:
+    return (seq + 63) // 64 * 64
+
+
+def fastweight_stream(z_teacher, z_student, conv_t, conv_s, beta, chunk: int, *,
+                      l2_eps: float = 0.0, out=None, workspace=None, stream=None):
+    """The stream step alone.  Returns (dbar [B,Tp,f], zbar_s_t [B,f,Tp],
+    key_scale [B,Tp]) with Tp = stream_pad(T); rows >= T are zero."""
+    B, T, f = z_teacher.shape
+    kc = conv_t.shape[1]
+    d = fw_desc(z_teacher, 8, chunk, kc, l2_eps)
+    Tp = stream_pad(T)
+    dev, dt = z_teacher.device, z_teacher.dtype
+    if out is None:
+        out = (torch.empty((B, Tp, f), dtype=dt, device=dev),
+               torch.empty((B, f, Tp), dtype=dt, device=dev),
+               torch.empty((B, Tp), dtype=torch.float32, device=dev))
+    dbar, zbt, ks = out
+    need = _lib.ttcd_fastweight_stream_workspace_size(C.byref(d))
+    ws = _workspace(need, dev, workspace)
+    _check(_lib.ttcd_fastweight_stream(C.byref(d), _ptr(z_teacher), _ptr(z_student), _ptr(conv_t),
+                                       _ptr(conv_s), _ptr(beta), _ptr(dbar), _ptr(zbt), _ptr(ks),
+                                       _ptr(ws), ws.numel(), _stream(stream)),
+           "ttcd_fastweight_stream")
+    return dbar, zbt, ks
 
 
 def fastweight_fold(w_down0, r_list, k_list, beta_list, chunk: int, *, workspace=None,

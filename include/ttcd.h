@@ -150,6 +150,33 @@ ttcd_status ttcd_fastweight_scan(const ttcd_fw_desc* desc,
                                  void* stream);
 
 /* ------------------------------------------------------------------------
+ * The fast-weight stream alone: the first, memory-bound step of
+ * ttcd_fastweight_scan (papernotes.org notes, key design 3: the short
+ * causal convs of both paths, their difference and the per-token l2 norm of
+ * the student activations).  Same conv and norm conventions as above.
+ *
+ *   desc: batch, seq, d_ff, chunk, conv_k, l2_eps, in_dtype (d_model and
+ *         out_dtype are ignored)
+ *   z_teacher, z_student [batch, seq, d_ff], conv_t, conv_s [d_ff, conv_k],
+ *         beta [batch, ceil(seq/chunk)] fp32
+ * Outputs, with seq_pad = 64 * ceil(seq / 64):
+ *   dbar      [batch, seq_pad, d_ff] in_dtype: Zbar_T - Zbar_S, token-major
+ *   zbar_s_t  [batch, d_ff, seq_pad] in_dtype: Zbar_S, feature-major
+ *   key_scale [batch, seq_pad] fp32: beta[t/chunk] / max(||Zbar_S[t]||, eps),
+ *             so the scaled key beta_i k_t is key_scale[t] * Zbar_S[t]
+ * Rows t >= seq of every output are zero.
+ * ---------------------------------------------------------------------- */
+size_t ttcd_fastweight_stream_workspace_size(const ttcd_fw_desc* desc);
+
+ttcd_status ttcd_fastweight_stream(const ttcd_fw_desc* desc,
+                                   const void* z_teacher, const void* z_student,
+                                   const void* conv_t, const void* conv_s,
+                                   const float* beta,
+                                   void* dbar, void* zbar_s_t, float* key_scale,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/* ------------------------------------------------------------------------
  * Whole IP-TTCD layer forward from Q/K/V onward.
  *
  * Per path p in {teacher, student} (the glue around attention and the MLP

@@ -146,3 +146,52 @@ def test_fold_no_chunks_is_w0():
     torch.cuda.synchronize()
     for b in range(2):
         np.testing.assert_array_equal(to_np(got)[b], w0.f64())
+
+
+# --------------------------------------------------------------------- stream
+def check_stream(cfg):
+    from dual_window_attention_amd import ttcd
+    say(f"stream {cfg.dtype} B={cfg.batch} T={cfg.seq} f={cfg.d_ff} C={cfg.chunk} kc={cfg.conv_k}")
+    z, w, beta = scan_inputs(cfg)
+    dbar, zbt, ks = ttcd.fastweight_stream(I.to_torch(z["z_t"]), I.to_torch(z["z_s"]),
+                                           I.to_torch(w["conv_t"]), I.to_torch(w["conv_s"]),
+                                           I.f32_to_torch(beta), cfg.chunk)
+    torch.cuda.synchronize()
+    T, Tp = cfg.seq, ttcd.stream_pad(cfg.seq)
+    tol = tol_for(cfg.dtype)
+    dbar_g, zbt_g, ks_g = to_np(dbar), to_np(zbt), to_np(ks)
+    assert not dbar_g[:, T:].any() and not zbt_g[:, :, T:].any() and not ks_g[:, T:].any(), \
+        "padding rows must be zero"
+    c0 = O.chunk_bounds(T, cfg.chunk)
+    for b in range(cfg.batch):
+        zb_t = O.causal_depthwise_conv(z["z_t"].f64()[b], w["conv_t"].f64())
+        zb_s = O.causal_depthwise_conv(z["z_s"].f64()[b], w["conv_s"].f64())
+        assert_close_stored(dbar_g[b, :T], zb_t - zb_s, tol, "dbar", cfg.dtype)
+        assert_close_stored(zbt_g[b, :, :T].T, zb_s, tol, "conv_S(Z_S)", cfg.dtype)
+        nrm = np.maximum(np.linalg.norm(zb_s, axis=-1), 1e-12)
+        bt = np.concatenate([np.full(e - a, beta[b, i], dtype=np.float64)
+                             for i, (a, e) in enumerate(c0)])
+        want = bt / nrm
+        rel = np.abs(ks_g[b, :T] - want) / want
+        say(f"  key scale: max rel err {rel.max():.3e}")
+        assert rel.max() <= 1e-4
+        # the scaled keys against beta * l2_normalize(conv_S(Z_S))
+        kt = ks_g[b, :T, None] * zbt_g[b, :, :T].T
+        kref = bt[:, None] * O.l2_normalize(zb_s, 1e-12)
+        err = np.linalg.norm(kt - kref, axis=-1) / np.linalg.norm(kref, axis=-1)
+        say(f"  scaled keys: max per-token rel L2 {err.max():.3e}")
+        assert err.max() <= (1e-2 if cfg.dtype == "bf16" else 1e-5)
+
+
+@pytest.mark.parametrize("case", [
+    dict(dtype="bf16", batch=2, seq=517, d_ff=384, chunk=128, conv_k=4, seed=51),
+    dict(dtype="f32", batch=1, seq=200, d_ff=136, chunk=64, conv_k=3, seed=52),
+    dict(dtype="bf16", batch=1, seq=64, d_ff=8, chunk=16, conv_k=8, seed=53),
+], ids=["bf16-B2-ragged", "f32-f136", "bf16-f8-kc8"])
+def test_stream_small(case):
+    check_stream(BASE.scaled(**case))
+
+
+def test_stream_qwen3_64k_full():
+    """The stream step at the 64K workload's full size (T 65536, d_ff 3072)."""
+    check_stream(BASE.scaled(batch=1))
