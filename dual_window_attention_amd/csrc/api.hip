@@ -152,7 +152,7 @@ ttcd_status check_fw(const ttcd_fw_desc* d) {
 
 struct FwBufs {
   void *dbar, *zbt, *wpt, *m, *rst, *states;
-  float *sc, *part;
+  float *sc, *part, *dw;
   int Tpad, N;
 };
 
@@ -168,6 +168,7 @@ void plan_fw(int B, int T, int d, int f, int C, int dt, Plan& p, FwBufs& w) {
   w.m = p.take((size_t)d * f * es);
   w.rst = p.take((size_t)B * d * w.Tpad * es);
   w.states = p.take((size_t)B * (w.N > 1 ? w.N - 1 : 0) * d * f * es);
+  w.dw = (float*)p.take((size_t)B * w.N * d * f * sizeof(float));
 }
 
 // Runs the fast-weight stream, residual projection, prefix states and the
@@ -200,17 +201,35 @@ hipError_t run_fw(int B, int T, int d, int f, int C, int kc, float eps, int dt,
   g.colscale = w.sc; g.batch = B; g.sA = 0; g.sB = (long)w.Tpad * f;
   g.sC = (long)d * w.Tpad; g.sScale = w.Tpad;
   if ((e = launch_gemm(g, s)) != hipSuccess) return e;
-  // (4) prefix states S_1 .. S_{N-1} (and S_N when asked for)
+  // (4) chunk writes dW_j = Rs^T_j Zbar_S,j^T (fp32, all chunks at once), then the causal
+  //     prefix S_{j+1} = W0 + sum_{i<=j} dW_i: states S_1 .. S_{N-1} (and S_N when asked for)
   const int nstates = N - 1;
   const int nwrites = state_out ? N : nstates;
   if (nwrites > 0) {
-    StateArgs st{};
-    st.A = w.rst; st.lda = w.Tpad; st.B = w.zbt; st.ldb = w.Tpad; st.W0 = w0;
-    st.states = w.states; st.final_out = state_out;
-    st.d = d; st.f = f; st.T = T; st.chunk = C; st.nstates = nstates; st.nwrites = nwrites;
-    st.in_dt = dt; st.st_dt = dt; st.batch = B; st.sA = (long)d * w.Tpad;
-    st.sB = (long)f * w.Tpad; st.sStates = (long)nstates * d * f; st.sFinal = (long)d * f;
-    if ((e = launch_fw_states(st, s)) != hipSuccess) return e;
+    const int nfull = std::min(nwrites, T / C);     // chunks holding all C tokens
+    for (int b = 0; b < B; ++b) {
+      const char* ab = (const char*)w.rst + (size_t)b * d * w.Tpad * dsize(dt);
+      const char* bb = (const char*)w.zbt + (size_t)b * f * w.Tpad * dsize(dt);
+      float* cb = w.dw + (size_t)b * N * d * f;
+      g = GemmArgs{};
+      g.lda = w.Tpad; g.ldb = w.Tpad; g.ldc = f; g.M = d; g.N = f;
+      g.in_dt = dt; g.out_dt = F32; g.epi = EPI_STORE;
+      if (nfull > 0) {
+        g.A = ab; g.B = bb; g.C = cb; g.K = C;
+        g.batch = nfull; g.sA = C; g.sB = C; g.sC = (long)d * f;
+        if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+      }
+      if (nwrites > nfull) {
+        // the short last chunk: its columns past T are zero up to Tpad
+        const long j0 = (long)nfull * C;
+        g.A = ab + j0 * dsize(dt); g.B = bb + j0 * dsize(dt);
+        g.C = cb + (size_t)nfull * d * f; g.K = (int)(w.Tpad - j0); g.batch = 1;
+        if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+      }
+    }
+    if ((e = launch_state_prefix(w.dw, (long)N, w0, w.states, state_out, (long)d * f, nstates,
+                                 nwrites, B, dt, dt, s)) != hipSuccess)
+      return e;
   }
   // (5) apply: out = [res +] Z_main S_{t/C}^T
   g = GemmArgs{};
@@ -553,14 +572,14 @@ ttcd_status ttcd_fastweight_fold(const ttcd_fw_desc* d, const void* w_down0, con
     HIPCHK(launch_transpose_scale(r_list, rst, (int)rows, dm, B, beta_list, C, n_chunks, dt, s));
     HIPCHK(launch_transpose_scale(k_list, kt, (int)rows, f, B, nullptr, 1, 0, dt, s));
   }
-  StateArgs st{};
-  st.A = rst; st.lda = rows; st.B = kt; st.ldb = rows; st.W0 = w_down0;
-  st.states = nullptr; st.final_out = state_out;
-  st.d = dm; st.f = f; st.T = (int)rows; st.chunk = C; st.nstates = 0; st.nwrites = n_chunks;
-  st.in_dt = dt; st.st_dt = F32; st.batch = B; st.sA = (long)dm * rows; st.sB = (long)f * rows;
-  st.sStates = 0; st.sFinal = (long)dm * f;
   if (n_chunks > 0) {
-    HIPCHK(launch_fw_states(st, s));
+    // state_out[b] = W0 + Rs^T[b] K^T[b]^T: one GEMM over all list rows, W0 as residual
+    GemmArgs g{};
+    g.A = rst; g.lda = rows; g.B = kt; g.ldb = rows; g.C = state_out; g.ldc = f;
+    g.M = dm; g.N = f; g.K = (int)rows; g.in_dt = dt; g.out_dt = F32; g.epi = EPI_RESIDUAL;
+    g.res = w_down0; g.ldr = f; g.res_rows = dm; g.res_dt = dt; g.sRes = 0;
+    g.batch = B; g.sA = (long)dm * rows; g.sB = (long)f * rows; g.sC = (long)dm * f;
+    HIPCHK(launch_gemm(g, s));
   } else {
     HIPCHK(launch_widen_repeat(w_down0, state_out, (long)dm * f, B, dt, s));
   }

@@ -1,11 +1,9 @@
 // Dense contractions of the IP-TTCD layer on gfx950:
 //   C = A B^T with A [M, K] and B [N, K] both K-contiguous ("NT"), bf16 in,
 //   fp32 MFMA accumulate, with fused epilogues (residual add, SwiGLU,
-//   per-column scale, chunk-indexed weights), and the fast-weight prefix
-//   kernel that keeps a d x f tile of the weight in registers while it
-//   walks the chunks in order (papernotes.org notes on "Learning What to
-//   Remember", key design 2: causal prefix sum of the chunk updates;
-//   key design 3: dW_i = beta_i R_i K_i^T).
+//   per-column scale, chunk-indexed weights).  The chunk writes of the fast
+//   weight (papernotes.org notes on "Learning What to Remember", key design
+//   3: dW_i = beta_i R_i K_i^T) are one batched call over the chunks.
 #include <algorithm>
 
 #include "common.hpp"
@@ -185,62 +183,6 @@ gemm_nt_mfma(GemmArgs g) {
   }
 }
 
-// Fast-weight prefix: one 128 x 128 tile of the d x f weight per workgroup.
-template <typename StT>
-__global__ void __launch_bounds__(NT, 1)
-fw_states_mfma(StateArgs a) {
-  extern __shared__ __align__(16) bf16_t lds[];
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int h = lane >> 5, r = lane & 31;
-  const int z = blockIdx.z;
-  const int ncol_tiles = gridDim.y;
-  const uint32_t tiles = gridDim.x * ncol_tiles;
-  const uint32_t lid = xcd_remap(blockIdx.y * gridDim.x + blockIdx.x, tiles);
-  const long m0 = (long)(lid / ncol_tiles) * BM;
-  const long n0 = (long)(lid % ncol_tiles) * BN;
-  const bf16_t* A = (const bf16_t*)a.A + z * a.sA;
-  const bf16_t* Bm = (const bf16_t*)a.B + z * a.sB;
-  const bf16_t* W0 = (const bf16_t*)a.W0;
-
-  Tile t;
-#pragma unroll
-  for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-    for (int bn = 0; bn < 2; ++bn)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const long m = m0 + 64 * wm + 32 * bm + 8 * (v >> 2) + 4 * h + (v & 3);
-        const long n = n0 + 64 * wn + 32 * bn + r;
-        t.acc[bm][bn][v] = (m < a.d && n < a.f) ? bf2f(W0[m * a.f + n]) : 0.f;
-      }
-
-  for (int i = 0; i < a.nwrites; ++i) {
-    const long kb = (long)i * a.chunk;
-    const long ke = min((long)(i + 1) * a.chunk, (long)a.T);
-    mainloop(t, A, a.lda, m0, a.d, Bm, nullptr, a.ldb, n0, a.f, kb, ke, lds, 64 * wn,
-             64 * wn + 32);
-    StT* S = nullptr;
-    if (i < a.nstates) S = (StT*)a.states + z * a.sStates + (long)i * a.d * a.f;
-    float* Fo = (i == a.nwrites - 1 && a.final_out) ? a.final_out + z * a.sFinal : nullptr;
-    if (!S && !Fo) continue;
-#pragma unroll
-    for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-      for (int bn = 0; bn < 2; ++bn)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const long m = m0 + 64 * wm + 32 * bm + 8 * (v >> 2) + 4 * h + (v & 3);
-          const long n = n0 + 64 * wn + 32 * bn + r;
-          if (m < a.d && n < a.f) {
-            if (S) stf(S + m * a.f + n, t.acc[bm][bn][v]);
-            if (Fo) Fo[m * a.f + n] = t.acc[bm][bn][v];
-          }
-        }
-  }
-}
-
 // --------------------------------------------------------------------------
 // Plain tiled FMA kernels (fp32 inputs, shapes the MFMA path does not take)
 // --------------------------------------------------------------------------
@@ -320,40 +262,6 @@ __global__ void __launch_bounds__(256) gemm_nt_simple(GemmArgs g) {
     }
 }
 
-template <typename InT, typename StT>
-__global__ void __launch_bounds__(256) fw_states_simple(StateArgs a) {
-  const int z = blockIdx.z;
-  const long m0 = (long)blockIdx.x * SB, n0 = (long)blockIdx.y * SB;
-  const InT* A = (const InT*)a.A + z * a.sA;
-  const InT* Bm = (const InT*)a.B + z * a.sB;
-  const InT* W0 = (const InT*)a.W0;
-  const int tr = threadIdx.x / 16, tc = threadIdx.x % 16;
-  float acc[4][4], dummy[4][4] = {};
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const long m = m0 + tr * 4 + i, n = n0 + tc * 4 + j;
-      acc[i][j] = (m < a.d && n < a.f) ? ldf(W0 + m * a.f + n) : 0.f;
-    }
-  for (int c = 0; c < a.nwrites; ++c) {
-    const long kb = (long)c * a.chunk, ke = min((long)(c + 1) * a.chunk, (long)a.T);
-    simple_tile<InT>(acc, dummy, A, a.lda, m0, a.d, Bm, nullptr, a.ldb, n0, a.f, kb, ke);
-    StT* S = c < a.nstates ? (StT*)a.states + z * a.sStates + (long)c * a.d * a.f : nullptr;
-    float* Fo = (c == a.nwrites - 1 && a.final_out) ? a.final_out + z * a.sFinal : nullptr;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const long m = m0 + tr * 4 + i, n = n0 + tc * 4 + j;
-        if (m >= a.d || n >= a.f) continue;
-        if (S) stf(S + m * a.f + n, acc[i][j]);
-        if (Fo) Fo[m * a.f + n] = acc[i][j];
-      }
-  }
-}
-
-
 // --------------------------------------------------------------------------
 // Large-tile NT GEMM: 256 x 128 workgroup tile, 4 waves each owning a
 // 128 x 64 block (8 MFMAs per 6 KB of LDS operand reads), BK = 32.  Operand
@@ -370,6 +278,8 @@ constexpr size_t LDS = (size_t)NST * STAGE;          // 72 KB
 constexpr int ALD = BM * BK / 8 / (64 * NW);         // 16B loads per wave (A)
 constexpr int BLD = BN * BK / 8 / (64 * NW);         // 16B loads per wave (B)
 constexpr int LPW = ALD + BLD;
+constexpr int EPS = 72;                              // epilogue slab row stride (floats)
+static_assert(NW * 32 * EPS * 4 <= (int)LDS, "epilogue slabs fit in the operand ring");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
@@ -426,17 +336,20 @@ gemm_nt_big(GemmArgs g) {
   }
   const long mmax = g.M - 1, nmax = g.N - 1;
   const long lda = g.lda, ldb = g.ldb;
-  auto a_row = [&](int rr) { return A + min(m0 + rr, mmax) * lda; };
-  auto b_row = [&](int rr) {
+  // (captured by value: by reference, the two B pointers land in a stack
+  // array whose scratch load would wait on every prefetch in flight)
+  auto a_row = [=](int rr) { return A + min(m0 + rr, mmax) * lda; };
+  const long b2_off = swiglu ? (long)(B2 - Bm) : 0;   // up rows relative to gate rows
+  auto b_row = [=](int rr) {
     if (swiglu) {
       // LDS row blocks of 32 alternate gate / up for the same 32 columns
       const int blk = rr >> 5;
       const long col = min(n0 + 32 * (blk >> 1) + (rr & 31), nmax);
-      return ((blk & 1) ? B2 : Bm) + col * ldb;
+      return Bm + ((blk & 1) ? b2_off : 0) + col * ldb;
     }
     return Bm + min(n0 + rr, nmax) * ldb;
   };
-  auto fetch = [&](int kt) {
+  auto fetch = [=](int kt) {
     char* st = lds + (kt % NST) * STAGE;
     issue<ALD>(st, a_row, (long)kt * BK, wave, lane);
     issue<BLD>(st + AB, b_row, (long)kt * BK, wave, lane);
@@ -488,40 +401,84 @@ gemm_nt_big(GemmArgs g) {
     barrier();
   }
 
+  // Epilogue through a wave-private LDS slab (the operand ring is idle after
+  // the last barrier): one 32-row block row of the wave's tile at a time is
+  // written as the MFMA layout leaves it and read back row-major, so each
+  // lane stores 16 bytes of consecutive columns and loads the residual the
+  // same way.
   OutT* C = (OutT*)g.C + z * g.sC;
-  if (swiglu) {
-    const long n = n0 + 32 * wn + r;
-    if (n > nmax) return;
+  float* slab = reinterpret_cast<float*>(lds) + wave * (32 * EPS);
+  const int ocols = swiglu ? 32 : 64;                 // output columns of the wave
+  const int per_row = ocols / 4;                      // 4-column pieces per row
+  const long nw0 = swiglu ? n0 + 32 * wn : n0 + 64 * wn;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const long m = m0 + 128 * wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (m <= mmax) stf(C + m * g.ldc + n, silu(acc[i][0][v]) * acc[i][1][v]);
+    for (int v = 0; v < 16; ++v) {
+      const int row = 8 * (v >> 2) + 4 * h + (v & 3);
+      if (swiglu) {
+        slab[row * EPS + r] = silu(acc[i][0][v]) * acc[i][1][v];
+      } else {
+        slab[row * EPS + r] = acc[i][0][v];
+        slab[row * EPS + 32 + r] = acc[i][1][v];
       }
-    return;
-  }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const long mb = m0 + 128 * wm + 32 * i;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const long n = n0 + 64 * wn + 32 * j + r;
-    if (n > nmax) continue;
-    float cs = 1.f;
-    if (g.epi == EPI_STORE && g.colscale) cs = g.colscale[z * g.sScale + n];
+    for (int t = 0; t < 8; ++t) {
+      const int idx = lane + 64 * t;
+      if (idx < 32 * per_row) {
+        const int rr = idx / per_row, c4 = 4 * (idx % per_row);
+        const long m = mb + rr, n = nw0 + c4;
+        if (m <= mmax && n <= nmax) {
+          f32x4 val = *reinterpret_cast<const f32x4*>(slab + rr * EPS + c4);
+          const bool full = n + 3 <= nmax;
+          if (g.epi == EPI_RESIDUAL) {
+            const long rm = (m % g.res_rows) * g.ldr + n + z * g.sRes;
+            float rv[4];
+            if (full && g.res_dt == BF16) {
+              const uint2 u = *reinterpret_cast<const uint2*>((const bf16_t*)g.res + rm);
+              rv[0] = __uint_as_float(u.x << 16); rv[1] = __uint_as_float(u.x & 0xFFFF0000u);
+              rv[2] = __uint_as_float(u.y << 16); rv[3] = __uint_as_float(u.y & 0xFFFF0000u);
+            } else if (full) {
+              const f32x4 f = *reinterpret_cast<const f32x4*>((const float*)g.res + rm);
+              rv[0] = f[0]; rv[1] = f[1]; rv[2] = f[2]; rv[3] = f[3];
+            } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+              for (int e = 0; e < 4; ++e)
+                rv[e] = n + e > nmax ? 0.f
+                        : g.res_dt == BF16 ? bf2f(((const bf16_t*)g.res)[rm + e])
+                                           : ((const float*)g.res)[rm + e];
+            }
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const long m = m0 + 128 * wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (m > mmax) continue;
-        float val = acc[i][j][v];
-        if (g.epi == EPI_RESIDUAL) {
-          const long rm = (m % g.res_rows) * g.ldr + n + z * g.sRes;
-          val += g.res_dt == BF16 ? bf2f(((const bf16_t*)g.res)[rm]) : ((const float*)g.res)[rm];
-        } else {
-          val *= cs;
+            for (int e = 0; e < 4; ++e) val[e] += rv[e];
+          } else if (g.epi == EPI_STORE && g.colscale) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e <= nmax) val[e] *= g.colscale[z * g.sScale + n + e];
+          }
+          OutT* cp = C + m * g.ldc + n;
+          if (full) {
+            if constexpr (sizeof(OutT) == 4) {
+              *reinterpret_cast<f32x4*>(cp) = val;
+            } else {
+              *reinterpret_cast<uint2*>(cp) =
+                  uint2{pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e <= nmax) stf(cp + e, val[e]);
+          }
         }
-        stf(C + m * g.ldc + n, val);
       }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 }  // namespace big
@@ -529,6 +486,9 @@ gemm_nt_big(GemmArgs g) {
 bool big_ok(const GemmArgs& g) {
   if (g.in_dt != BF16) return false;
   if (g.K % big::BK || g.lda % 8 || g.ldb % 8) return false;
+  // the epilogue moves 4 consecutive columns per access
+  if (g.ldc % 4 || g.sC % 4) return false;
+  if (g.epi == EPI_RESIDUAL && (g.ldr % 4 || g.sRes % 4)) return false;
   if (g.chunk > 0 && g.chunk % big::BM) return false;
   // enough tiles to fill the chip
   const long tiles = (long)((g.M + big::BM - 1) / big::BM) *
@@ -620,41 +580,6 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
       hipLaunchKernelGGL((gemm_nt_simple<float, bf16_t>), grid, dim3(256), 0, s, g);
     else
       hipLaunchKernelGGL((gemm_nt_simple<float, float>), grid, dim3(256), 0, s, g);
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_fw_states(const StateArgs& a, hipStream_t s) {
-  if (a.nwrites <= 0) return hipSuccess;
-  const int nb = a.batch > 0 ? a.batch : 1;
-  const bool mf = a.in_dt == BF16 && a.lda % 8 == 0 && a.ldb % 8 == 0 && a.chunk % 8 == 0;
-  if (mf) {
-    static bool attr = false;
-    if (!attr) {
-      (void)hipFuncSetAttribute((const void*)fw_states_mfma<float>,
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)GEMM_LDS);
-      (void)hipFuncSetAttribute((const void*)fw_states_mfma<bf16_t>,
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)GEMM_LDS);
-      attr = true;
-    }
-    dim3 grid((a.d + BM - 1) / BM, (a.f + BN - 1) / BN, nb);
-    if (a.st_dt == BF16)
-      hipLaunchKernelGGL(fw_states_mfma<bf16_t>, grid, dim3(NT), GEMM_LDS, s, a);
-    else
-      hipLaunchKernelGGL(fw_states_mfma<float>, grid, dim3(NT), GEMM_LDS, s, a);
-    return hipGetLastError();
-  }
-  dim3 grid((a.d + SB - 1) / SB, (a.f + SB - 1) / SB, nb);
-  if (a.in_dt == BF16) {
-    if (a.st_dt == BF16)
-      hipLaunchKernelGGL((fw_states_simple<bf16_t, bf16_t>), grid, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((fw_states_simple<bf16_t, float>), grid, dim3(256), 0, s, a);
-  } else {
-    if (a.st_dt == BF16)
-      hipLaunchKernelGGL((fw_states_simple<float, bf16_t>), grid, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((fw_states_simple<float, float>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

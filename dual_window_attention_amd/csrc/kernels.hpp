@@ -79,17 +79,14 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
 //   acc = W0 (fp32); for i in [0, nstates): acc += A_i B_i^T over tokens of
 //   chunk i; states[i] = acc  (state i = weight after chunk i's write).
 // A = Rs^T [d, T] (lda = T), B = Zb^T [f, T] (ldb = T).
-struct StateArgs {
-  const void* A; long lda;
-  const void* B; long ldb;
-  const void* W0;                  // [d, f] in_dt
-  void* states;                    // [nstates, d, f] st_dt
-  float* final_out;                // optional [d, f] fp32: weight after all writes
-  int d, f, T, chunk, nstates, nwrites;
-  int in_dt, st_dt;
-  int batch; long sA, sB, sStates, sFinal;
-};
-hipError_t launch_fw_states(const StateArgs& a, hipStream_t s);
+// Causal prefix of the chunk writes (papernotes.org notes, key design 2):
+//   S_{j+1} = W0 + sum_{i <= j} dW_i, kept in fp32 while walking j;
+//   states[b, j] = S_{j+1} (st_dt) for j < nstates, final_out[b] = S_{nwrites}.
+//   dw [B, dw_chunks, n] fp32 (the first nwrites chunks of each batch element
+//   are read), w0 [n] w0_dt, states [B, nstates, n], final_out [B, n], n = d * f.
+hipError_t launch_state_prefix(const float* dw, long dw_chunks, const void* w0, void* states,
+                               float* final_out, long n, int nstates, int nwrites, int batch,
+                               int w0_dt, int st_dt, hipStream_t s);
 
 // ---------------------------------------------------------------- elementwise / stream
 // u = rmsnorm(h) * gamma, h fp32 [rows, d] -> u [rows, d] out_dt

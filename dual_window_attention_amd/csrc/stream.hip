@@ -191,6 +191,49 @@ fw_key_scale_kernel(const float* __restrict__ part, const float* __restrict__ be
   sc[(size_t)b * Tpad + t] = v;
 }
 
+// --------------------------------------------------------------- state prefix
+// Each thread owns 4 consecutive weight entries and walks the chunk writes in
+// order, 8 loads in flight at a time; the running sum never leaves fp32.
+template <typename W0T, typename StT>
+__global__ void __launch_bounds__(256)
+state_prefix_kernel(const float* __restrict__ dw, long dw_chunks, const W0T* __restrict__ w0,
+                    StT* __restrict__ states, float* __restrict__ final_out, long n,
+                    int nstates, int nwrites) {
+  const int b = blockIdx.y;
+  const long e = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= n) return;
+  float acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = ldf(w0 + e + i);
+  const float* src = dw + (size_t)b * dw_chunks * n + e;
+  StT* dst = states + (size_t)b * nstates * n + e;
+  constexpr int U = 8;
+  for (int j0 = 0; j0 < nwrites; j0 += U) {
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (j0 + u < nwrites) v[u] = *reinterpret_cast<const f32x4*>(src + (size_t)(j0 + u) * n);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u;
+      if (j >= nwrites) break;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += v[u][i];
+      if (j < nstates) {
+        StT* o = dst + (size_t)j * n;
+        if constexpr (sizeof(StT) == 2) {
+          uint2 pk = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+          *reinterpret_cast<uint2*>(o) = pk;
+        } else {
+          *reinterpret_cast<f32x4*>(o) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+        }
+      }
+    }
+  }
+  if (final_out)
+    *reinterpret_cast<f32x4*>(final_out + (size_t)b * n + e) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+}
+
 // --------------------------------------------------------------- rmsnorm
 template <typename GT, typename OutT>
 __global__ void __launch_bounds__(256)
@@ -321,6 +364,24 @@ hipError_t launch_fw_stream(const StreamArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fw_key_scale_kernel, dim3(Tpad / 256 + 1, a.B), dim3(256), 0, s, a.part,
                      a.beta, a.sc, nft, a.T, Tpad, a.chunk, a.nchunks, a.eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_prefix(const float* dw, long dw_chunks, const void* w0, void* states,
+                               float* final_out, long n, int nstates, int nwrites, int batch,
+                               int w0_dt, int st_dt, hipStream_t s) {
+  if (nwrites <= 0 || n % 4) return nwrites <= 0 ? hipSuccess : hipErrorInvalidValue;
+  dim3 grid((unsigned)((n / 4 + 255) / 256), batch);
+  if (w0_dt == BF16 && st_dt == BF16)
+    hipLaunchKernelGGL((state_prefix_kernel<bf16_t, bf16_t>), grid, dim3(256), 0, s, dw,
+                       dw_chunks, (const bf16_t*)w0, (bf16_t*)states, final_out, n, nstates,
+                       nwrites);
+  else if (w0_dt == F32 && st_dt == F32)
+    hipLaunchKernelGGL((state_prefix_kernel<float, float>), grid, dim3(256), 0, s, dw,
+                       dw_chunks, (const float*)w0, (float*)states, final_out, n, nstates,
+                       nwrites);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
