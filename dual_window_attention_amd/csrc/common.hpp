@@ -68,6 +68,19 @@ TTCD_DEV float wave_sum(float v) {
 TTCD_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 TTCD_DEV float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Logical tile id -> (tile row, tile column), gm tile rows at a time with the
+// row index fastest: the few dozen workgroups an XCD runs at once then cover a
+// gm x (that / gm) block of output tiles and share its A and B panels in L2,
+// instead of one A panel and a sweep over every B panel.
+TTCD_DEV void grouped_tile(uint32_t lid, int ntm, int ntn, int gm, int& tm, int& tn) {
+  const int per_group = gm * ntn;
+  const int first = (int)(lid / per_group) * gm;
+  const int gsz = ntm - first < gm ? ntm - first : gm;
+  const int in = (int)(lid % per_group);
+  tm = first + in % gsz;
+  tn = in / gsz;
+}
+
 // Map a linear workgroup id onto a logical tile id so that the tiles each
 // XCD receives (hardware dispatches workgroup w to XCD w % 8) are
 // contiguous in logical order: neighbouring tiles then share that XCD's L2.

@@ -5,6 +5,7 @@
 //   weight (papernotes.org notes on "Learning What to Remember", key design
 //   3: dW_i = beta_i R_i K_i^T) are one batched call over the chunks.
 #include <algorithm>
+#include <cstdlib>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -266,20 +267,22 @@ __global__ void __launch_bounds__(256) gemm_nt_simple(GemmArgs g) {
 // Large-tile NT GEMM: 256 x 128 workgroup tile, 4 waves each owning a
 // 128 x 64 block (8 MFMAs per 6 KB of LDS operand reads), BK = 32.  Operand
 // tiles go straight from global memory into LDS (global_load_lds_dwordx4) in
-// an XOR-swizzled layout that keeps the MFMA operand reads free of bank
-// conflicts; a 3-stage ring is fetched two stages ahead, and two workgroups
-// share a CU.  Requires K % 32 == 0 and 16-byte aligned rows.
+// an XOR-swizzled layout that keeps the MFMA operand reads nearly free of
+// bank conflicts; the ring (2 stages: three workgroups per CU, or 3) is
+// fetched one stage less than its depth ahead.  Output tiles are visited in
+// 8-row groups per XCD for L2 reuse.  Requires K % 32 == 0 and 16-byte
+// aligned rows.
 // --------------------------------------------------------------------------
 namespace big {
-constexpr int BM = 256, BN = 128, BK = 32, NW = 4, NTH = 64 * NW, NST = 3;
+constexpr int BM = 256, BN = 128, BK = 32, NW = 4, NTH = 64 * NW;
 constexpr int AB = BM * BK * 2, BB = BN * BK * 2;   // operand bytes per stage
-constexpr int STAGE = AB + BB;
-constexpr size_t LDS = (size_t)NST * STAGE;          // 72 KB
+constexpr int STAGE = AB + BB;                       // 24 KB
+constexpr size_t lds_bytes(int nst) { return (size_t)nst * STAGE; }
 constexpr int ALD = BM * BK / 8 / (64 * NW);         // 16B loads per wave (A)
 constexpr int BLD = BN * BK / 8 / (64 * NW);         // 16B loads per wave (B)
 constexpr int LPW = ALD + BLD;
 constexpr int EPS = 72;                              // epilogue slab row stride (floats)
-static_assert(NW * 32 * EPS * 4 <= (int)LDS, "epilogue slabs fit in the operand ring");
+static_assert(NW * 32 * EPS * 4 <= 2 * STAGE, "epilogue slabs fit in the operand ring");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
@@ -296,6 +299,9 @@ TTCD_DEV void wait_vm() {
 }
 // rows of 64 bytes (4 chunks): chunk c of row r lives at c ^ ((r >> 2) & 3)
 TTCD_DEV int swz(int row) { return (row >> 2) & 3; }
+// the wave's LDS accesses so far are complete (and the compiler may not move
+// memory accesses across): enough for lanes of one wave to exchange data
+TTCD_DEV void lds_wave_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <int NLD, class RowPtr>
 TTCD_DEV void issue(char* dst, const RowPtr& row_ptr, long k0, int wave, int lane) {
@@ -309,7 +315,20 @@ TTCD_DEV void issue(char* dst, const RowPtr& row_ptr, long k0, int wave, int lan
   }
 }
 
-template <typename OutT>
+// stages still in flight after the one waited for
+template <int NST>
+TTCD_DEV void wait_pending(int pending) {
+  if (NST > 2 && pending >= 2)
+    wait_vm<2 * LPW>();
+  else if (pending >= 1)
+    wait_vm<LPW>();
+  else
+    wait_vm<0>();
+}
+
+// NST-stage ring: 2 stages (48 KB) let three workgroups share a CU, 3 stages
+// (72 KB) two.
+template <typename OutT, int NST>
 __global__ void __launch_bounds__(NTH, 2)
 gemm_nt_big(GemmArgs g) {
   extern __shared__ __align__(16) char lds[];
@@ -324,8 +343,10 @@ gemm_nt_big(GemmArgs g) {
   const int ntn = (g.N + ncols - 1) / ncols;
   const int ntm = (g.M + BM - 1) / BM;
   const uint32_t lid = xcd_remap(blockIdx.x, (uint32_t)(ntm * ntn));
-  const long m0 = (long)(lid / ntn) * BM;
-  const long n0 = (long)(lid % ntn) * ncols;
+  int tm, tn;
+  grouped_tile(lid, ntm, ntn, 8, tm, tn);
+  const long m0 = (long)tm * BM;
+  const long n0 = (long)tn * ncols;
 
   const bf16_t* A = (const bf16_t*)g.A + z * g.sA;
   const bf16_t* Bm = (const bf16_t*)g.B + z * g.sB;
@@ -362,17 +383,13 @@ gemm_nt_big(GemmArgs g) {
     for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
 
   const int nk = g.K / BK;
-  fetch(0);
-  if (nk > 1) {
-    fetch(1);
-    wait_vm<LPW>();
-  } else {
-    wait_vm<0>();
-  }
+  const int npro = nk < NST - 1 ? nk : NST - 1;
+  for (int kt = 0; kt < npro; ++kt) fetch(kt);
+  wait_pending<NST>(npro - 1);
   barrier();
   for (int kt = 0; kt < nk; ++kt) {
-    const bool ahead = kt + 2 < nk;
-    if (ahead) fetch(kt + 2);
+    // the buffer refilled here held stage kt-1, finished before the last barrier
+    if (kt + NST - 1 < nk) fetch(kt + NST - 1);
     const char* as = lds + (kt % NST) * STAGE;
     const char* bs = as + AB;
 #pragma unroll
@@ -393,11 +410,9 @@ gemm_nt_big(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
     }
-    // stage kt+1 must have landed; stage kt+2 may still be in flight
-    if (ahead)
-      wait_vm<LPW>();
-    else
-      wait_vm<0>();
+    // stage kt+1 must have landed; later ones may still be in flight
+    const int last = kt + NST - 1 < nk ? kt + NST - 1 : nk - 1;
+    wait_pending<NST>(last - (kt + 1));
     barrier();
   }
 
@@ -423,9 +438,7 @@ gemm_nt_big(GemmArgs g) {
         slab[row * EPS + 32 + r] = acc[i][1][v];
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    lds_wave_sync();
     const long mb = m0 + 128 * wm + 32 * i;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -476,9 +489,7 @@ gemm_nt_big(GemmArgs g) {
         }
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    lds_wave_sync();
   }
 }
 }  // namespace big
@@ -506,26 +517,43 @@ bool mfma_ok(const GemmArgs& g) {
 
 }  // namespace
 
+// Ring depth of the 256 x 128 kernel: 2 stages (three workgroups per CU,
+// measured faster on the 64K layer) unless TTCD_GEMM_STAGES=3 asks for the
+// 3-stage ring (two workgroups per CU).
+int gemm_stage_choice() {
+  static const int v = [] {
+    const char* e = getenv("TTCD_GEMM_STAGES");
+    return e && atoi(e) == 3 ? 3 : 2;
+  }();
+  return v;
+}
+
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   const int nb = g.batch > 0 ? g.batch : 1;
   if (big_ok(g)) {
-    static hipError_t a1 = hipFuncSetAttribute((const void*)big::gemm_nt_big<float>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)big::LDS);
-    static hipError_t a2 = hipFuncSetAttribute((const void*)big::gemm_nt_big<bf16_t>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)big::LDS);
-    if (a1 != hipSuccess) return a1;
-    if (a2 != hipSuccess) return a2;
+    const int nst = gemm_stage_choice();
+    const void* kf = nst == 2 ? (const void*)big::gemm_nt_big<float, 2>
+                              : (const void*)big::gemm_nt_big<float, 3>;
+    const void* kb = nst == 2 ? (const void*)big::gemm_nt_big<bf16_t, 2>
+                              : (const void*)big::gemm_nt_big<bf16_t, 3>;
+    const size_t lds = big::lds_bytes(nst);
+    static hipError_t a[4] = {
+        hipFuncSetAttribute((const void*)big::gemm_nt_big<float, 2>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)big::lds_bytes(2)),
+        hipFuncSetAttribute((const void*)big::gemm_nt_big<float, 3>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)big::lds_bytes(3)),
+        hipFuncSetAttribute((const void*)big::gemm_nt_big<bf16_t, 2>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)big::lds_bytes(2)),
+        hipFuncSetAttribute((const void*)big::gemm_nt_big<bf16_t, 3>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)big::lds_bytes(3))};
+    for (hipError_t e : a)
+      if (e != hipSuccess) return e;
     const int ncols = g.epi == EPI_SWIGLU ? big::BN / 2 : big::BN;
     const unsigned tiles = (unsigned)(((g.M + big::BM - 1) / big::BM) * ((g.N + ncols - 1) / ncols));
     dim3 grid(tiles, 1, nb);
-    if (g.out_dt == BF16)
-      hipLaunchKernelGGL(big::gemm_nt_big<bf16_t>, grid, dim3(big::NTH), big::LDS, s, g);
-    else
-      hipLaunchKernelGGL(big::gemm_nt_big<float>, grid, dim3(big::NTH), big::LDS, s, g);
-    return hipGetLastError();
+    void* args[] = {(void*)&g};
+    return hipLaunchKernel(g.out_dt == BF16 ? kb : kf, grid, dim3(big::NTH), args, lds, s);
   }
   if (mfma_ok(g)) {
     static bool attr = false;
