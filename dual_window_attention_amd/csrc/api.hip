@@ -271,6 +271,8 @@ struct LayerBufs {
   void *o[2], *u, *z[2], *zdec;
   float *h[2], *lse[2], *y;
   float* cbuf;
+  float* sk = nullptr;          // decode: split-K partial sums of the few-row GEMMs
+  size_t sk_floats = 0;
   FwBufs fw;
 };
 
@@ -294,6 +296,13 @@ void plan_layer(const ttcd_layer_desc* d, const ttcd_fw_state* dec, Plan& p, Lay
     const long nseg = (rows + 255) / 256;
     b.cbuf = (float*)p.take(((size_t)a.batch * rows + (size_t)a.batch * nseg * d->d_model) *
                             sizeof(float));
+    if (a.batch <= 32) {
+      size_t n = gemm_skinny_ws_floats(a.batch, d->d_model, (int)HD, EPI_RESIDUAL);
+      n = std::max(n, gemm_skinny_ws_floats(a.batch, d->d_ff, d->d_model, EPI_SWIGLU));
+      n = std::max(n, gemm_skinny_ws_floats(a.batch, d->d_model, d->d_ff, EPI_STORE));
+      b.sk_floats = n;
+      b.sk = (float*)p.take(n * sizeof(float));
+    }
   } else {
     plan_fw(a.batch, a.seq_q, d->d_model, d->d_ff, d->chunk, dt, p, b.fw);
   }
@@ -483,12 +492,14 @@ ttcd_status ttcd_layer_forward(const ttcd_layer_desc* d, const ttcd_layer_weight
     g.A = o[path]; g.lda = HD; g.B = wt->w_o; g.ldb = HD; g.C = b.h[path]; g.ldc = dm;
     g.M = (int)BT; g.N = dm; g.K = HD; g.in_dt = dt; g.out_dt = F32; g.epi = EPI_RESIDUAL;
     g.res = x; g.ldr = dm; g.res_rows = (int)BT; g.res_dt = dt; g.batch = 1;
+    g.ws = b.sk; g.ws_floats = b.sk_floats;
     HIPCHK(launch_gemm(g, s));
     HIPCHK(launch_rmsnorm(b.h[path], wt->rms_gamma, b.u, (int)BT, dm, rms_eps, dt, dt, s));
     g = GemmArgs{};
     g.A = b.u; g.lda = dm; g.B = wt->w_gate; g.B2 = wt->w_up; g.ldb = dm; g.C = z[path];
     g.ldc = f; g.M = (int)BT; g.N = f; g.K = dm; g.in_dt = dt; g.out_dt = dt;
     g.epi = EPI_SWIGLU; g.batch = 1;
+    g.ws = b.sk; g.ws_floats = b.sk_floats;
     HIPCHK(launch_gemm(g, s));
   }
 
@@ -515,6 +526,7 @@ ttcd_status ttcd_layer_forward(const ttcd_layer_desc* d, const ttcd_layer_weight
     GemmArgs g{};
     g.A = z[main]; g.lda = f; g.B = wt->w_down0; g.ldb = f; g.C = y; g.ldc = dm;
     g.M = B; g.N = dm; g.K = f; g.in_dt = dt; g.out_dt = F32; g.epi = EPI_STORE; g.batch = 1;
+    g.ws = b.sk; g.ws_floats = b.sk_floats;
     HIPCHK(launch_gemm(g, s));
     if (dec->n_chunks > 0) {
       ListApplyArgs la{};

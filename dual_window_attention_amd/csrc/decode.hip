@@ -67,17 +67,44 @@ decode_attn_split(const T* __restrict__ q, const T* __restrict__ k, const T* __r
   const size_t rs = (size_t)Hkv * D;
   const T* kb = k + ((size_t)b * kv_rows * Hkv + g) * D + dc * 8;
   const T* vb = v + ((size_t)b * kv_rows * Hkv + g) * D + dc * 8;
+  // this lane's 8 elements of key j's K and V rows (16-byte loads for bf16),
+  // one key step loaded ahead of the one being used
+  using Raw = u32x4[sizeof(T) == 2 ? 1 : 2];
+  auto fetch = [&](int j, Raw& rk, Raw& rv) {
+#pragma unroll
+    for (int h2 = 0; h2 < (int)(sizeof(T) == 2 ? 1 : 2); ++h2) {
+      rk[h2] = ld16(kb + (size_t)j * rs + h2 * 4);
+      rv[h2] = ld16(vb + (size_t)j * rs + h2 * 4);
+    }
+  };
+  auto unpack = [&](const Raw& r, float* o) {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[2 * e] = __uint_as_float(r[0][e] << 16);
+        o[2 * e + 1] = __uint_as_float(r[0][e] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = __uint_as_float(r[e / 4][e % 4]);
+    }
+  };
+  Raw nk, nv;
+  {
+    const int j = ks + wave * KPW + kg;
+    fetch(j < ke ? j : ks, nk, nv);
+  }
   for (int j0 = ks + wave * KPW; j0 < ke; j0 += 4 * KPW) {
     const int j = j0 + kg;
     const bool ok = j < ke;
     float kv[8], vv[8];
-    if (ok) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        kv[e] = ldf(kb + (size_t)j * rs + e);
-        vv[e] = ldf(vb + (size_t)j * rs + e);
-      }
-    } else {
+    unpack(nk, kv);
+    unpack(nv, vv);
+    {
+      const int jn = j + 4 * KPW;
+      fetch(jn < ke ? jn : ks, nk, nv);       // (a valid row either way)
+    }
+    if (!ok) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) kv[e] = vv[e] = 0.f;
     }
@@ -251,6 +278,128 @@ list_raccum(const T* __restrict__ rlist, const float* __restrict__ cbuf, float* 
   }
 }
 
+// bf16 fast paths of the two list passes.  K rows: z lives in registers (NCH
+// 16-byte column chunks per lane), four rows' loads are in flight at once.
+// R rows: 16-byte loads of 8 consecutive features, eight rows in flight per
+// thread, the row groups of a workgroup summed through LDS.
+template <int NCH>
+__global__ void __launch_bounds__(256)
+list_kdot_reg(const bf16_t* __restrict__ klist, const bf16_t* __restrict__ z,
+              const float* __restrict__ beta, float* __restrict__ cbuf, int rows, int f,
+              int chunk, int n) {
+  constexpr int RG = 4;                     // rows in flight per wave
+  const int b = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float zr[NCH][8];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = lane * 8 + 512 * i;
+    if (c < f) {
+      const u32x4 v = ld16(z + (size_t)b * f + c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        zr[i][2 * e] = __uint_as_float(v[e] << 16);
+        zr[i][2 * e + 1] = __uint_as_float(v[e] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zr[i][e] = 0.f;
+    }
+  }
+  const long t0 = ((long)blockIdx.x * 4 + wave) * RG;
+  u32x4 kv[RG][NCH];
+#pragma unroll
+  for (int r = 0; r < RG; ++r) {
+    const long t = t0 + r < rows ? t0 + r : rows - 1;
+    const bf16_t* kr = klist + ((size_t)b * rows + t) * f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane * 8 + 512 * i;
+      kv[r][i] = c < f ? ld16(kr + c) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RG; ++r) {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = __builtin_fmaf(__uint_as_float(kv[r][i][e] << 16), zr[i][2 * e], acc);
+        acc = __builtin_fmaf(__uint_as_float(kv[r][i][e] & 0xFFFF0000u), zr[i][2 * e + 1], acc);
+      }
+    acc = wave_sum(acc);
+    const long t = t0 + r;
+    if (lane == 0 && t < rows) cbuf[(size_t)b * rows + t] = acc * beta[(size_t)b * n + t / chunk];
+  }
+}
+
+__global__ void __launch_bounds__(256)
+list_raccum_v(const bf16_t* __restrict__ rlist, const float* __restrict__ cbuf,
+              float* __restrict__ ypart, int rows, int d) {
+  __shared__ float cs[SEG];
+  __shared__ float red[256 * 8];
+  const int seg = blockIdx.x, b = blockIdx.y;
+  const long t0 = (long)seg * SEG;
+  for (int i = threadIdx.x; i < SEG; i += 256) {
+    const long t = t0 + i;
+    cs[i] = t < rows ? cbuf[(size_t)b * rows + t] : 0.f;
+  }
+  __syncthreads();
+  const int nseg = gridDim.x;
+  const int CH = d / 8;                              // 8-feature chunks (d % 8 == 0)
+  const int CHP = CH < 256 ? CH : 256;               // threads per row group
+  const int NRG = 256 / CHP;                         // row groups
+  const int fc = threadIdx.x % CHP, rg = threadIdx.x / CHP;
+  const int tend = (int)min((long)SEG, rows - t0);
+  const int niter = (CH + CHP - 1) / CHP;            // the same for every thread (barriers)
+  for (int it = 0; it < niter; ++it) {
+    const int c0 = fc + it * CHP;
+    const bool cok = c0 < CH;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    if (rg < NRG && cok) {
+      const bf16_t* rb = rlist + ((size_t)b * rows + t0) * d + 8 * c0;
+      int i = rg;
+      for (; i + 7 * NRG < tend; i += 8 * NRG) {
+        u32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = ld16(rb + (size_t)(i + u * NRG) * d);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float cv = cs[i + u * NRG];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[2 * e] = __builtin_fmaf(cv, __uint_as_float(v[u][e] << 16), acc[2 * e]);
+            acc[2 * e + 1] = __builtin_fmaf(cv, __uint_as_float(v[u][e] & 0xFFFF0000u), acc[2 * e + 1]);
+          }
+        }
+      }
+      for (; i < tend; i += NRG) {
+        const u32x4 v = ld16(rb + (size_t)i * d);
+        const float cv = cs[i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] = __builtin_fmaf(cv, __uint_as_float(v[e] << 16), acc[2 * e]);
+          acc[2 * e + 1] = __builtin_fmaf(cv, __uint_as_float(v[e] & 0xFFFF0000u), acc[2 * e + 1]);
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[threadIdx.x * 8 + e] = acc[e];
+    __syncthreads();
+    if (rg == 0 && cok) {
+      for (int g2 = 1; g2 < NRG; ++g2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += red[(g2 * CHP + fc) * 8 + e];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ypart[((size_t)b * nseg + seg) * d + 8 * c0 + e] = acc[e];
+    }
+  }
+}
+
 __global__ void __launch_bounds__(256)
 list_reduce(const float* __restrict__ ypart, float* __restrict__ y, int nseg, int d) {
   const int b = blockIdx.y;
@@ -341,11 +490,26 @@ hipError_t launch_list_apply(const ListApplyArgs& a, hipStream_t s) {
   const size_t zl = (size_t)a.f * sizeof(float);
   const int nseg = (rows + SEG - 1) / SEG;
   float* ypart = a.cbuf + (size_t)a.B * rows;
-  if (a.in_dt == BF16) {
+  const int nch = (a.f + 511) / 512;
+  if (a.in_dt == BF16 && nch <= 8) {
+    dim3 gk((rows + 15) / 16, a.B);               // 4 waves x 4 rows per workgroup
+    switch (nch) {
+#define TTCD_KDOT(N)                                                                          \
+  case N:                                                                                     \
+    hipLaunchKernelGGL(list_kdot_reg<N>, gk, dim3(256), 0, s, (const bf16_t*)a.k_list,        \
+                       (const bf16_t*)a.z, a.beta, a.cbuf, rows, a.f, a.chunk, a.n);          \
+    break;
+      TTCD_KDOT(1) TTCD_KDOT(2) TTCD_KDOT(3) TTCD_KDOT(4)
+      TTCD_KDOT(5) TTCD_KDOT(6) TTCD_KDOT(7) TTCD_KDOT(8)
+#undef TTCD_KDOT
+    }
+    hipLaunchKernelGGL(list_raccum_v, dim3(nseg, a.B), dim3(256), 0, s, (const bf16_t*)a.r_list,
+                       a.cbuf, ypart, rows, a.d);
+  } else if (a.in_dt == BF16) {
     hipLaunchKernelGGL(list_kdot<bf16_t>, g1, dim3(256), zl, s, (const bf16_t*)a.k_list,
                        (const bf16_t*)a.z, a.beta, a.cbuf, rows, a.f, a.chunk, a.n);
-    hipLaunchKernelGGL(list_raccum<bf16_t>, dim3(nseg, a.B), dim3(256), 0, s,
-                       (const bf16_t*)a.r_list, a.cbuf, ypart, rows, a.d);
+    hipLaunchKernelGGL(list_raccum_v, dim3(nseg, a.B), dim3(256), 0, s, (const bf16_t*)a.r_list,
+                       a.cbuf, ypart, rows, a.d);
   } else {
     hipLaunchKernelGGL(list_kdot<float>, g1, dim3(256), zl, s, (const float*)a.k_list,
                        (const float*)a.z, a.beta, a.cbuf, rows, a.f, a.chunk, a.n);

@@ -494,6 +494,95 @@ gemm_nt_big(GemmArgs g) {
 }
 }  // namespace big
 
+// --------------------------------------------------------------------------
+// Few-row NT GEMM (a decode step: one row per sequence), M <= 32.  One wave
+// per 32-column tile and K slice: the MFMA operands come straight from
+// global memory (every A and B row is read once per slice), so enough waves
+// exist to stream the weight matrix at full bandwidth; the slices' fp32
+// partial sums go to the workspace and a second kernel adds them and applies
+// the epilogue.  For SwiGLU the gate columns are [0, N) and the up columns
+// [N, 2N) of the partial sums.
+// --------------------------------------------------------------------------
+namespace skinny {
+constexpr int TARGET_WAVES = 1024;
+
+TTCD_DEV bf16x8 ld_frag(const bf16_t* row, long k, long kend) {
+  return k < kend ? as_bf16x8(ld16(row + k)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+}
+
+__global__ void __launch_bounds__(64)
+gemm_skinny_part(GemmArgs g, int kslice, int ncols) {
+  const int tn = blockIdx.x, ks = blockIdx.y;
+  const int lane = threadIdx.x, r = lane & 31, h = lane >> 5;
+  const bool swiglu = g.epi == EPI_SWIGLU;
+  const int n = min(tn * 32 + r, ncols - 1);           // this lane's B row (output column)
+  const bf16_t* br = (swiglu && n >= g.N) ? (const bf16_t*)g.B2 + (size_t)(n - g.N) * g.ldb
+                                           : (const bf16_t*)g.B + (size_t)n * g.ldb;
+  const bf16_t* ar = (const bf16_t*)g.A + (size_t)min(r, g.M - 1) * g.lda;
+  const long k0 = (long)ks * kslice;
+  const long k1 = min(k0 + (long)kslice, (long)g.K);
+  f32x16 acc = zero16();
+  for (long kk = k0; kk < k1; kk += 64) {
+    bf16x8 af[4], bf[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const long k = kk + 16 * u + 8 * h;
+      af[u] = ld_frag(ar, k, k1);
+      bf[u] = ld_frag(br, k, k1);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc = mfma32(af[u], bf[u], acc);
+  }
+  // lane: column tn*32 + r, rows 8(v/4) + 4h + v%4
+  const int col = tn * 32 + r;
+  if (col >= ncols) return;
+  float* part = g.ws + (size_t)ks * g.M * ncols;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int m = 8 * (v >> 2) + 4 * h + (v & 3);
+    if (m < g.M) part[(size_t)m * ncols + col] = acc[v];
+  }
+}
+
+template <typename OutT>
+__global__ void __launch_bounds__(256)
+gemm_skinny_reduce(GemmArgs g, int nks, int ncols) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long)g.M * g.N) return;
+  const int m = (int)(i / g.N), n = (int)(i % g.N);
+  float a = 0.f, u = 0.f;
+  for (int ks = 0; ks < nks; ++ks) {
+    const float* part = g.ws + (size_t)ks * g.M * ncols + (size_t)m * ncols;
+    a += part[n];
+    if (g.epi == EPI_SWIGLU) u += part[g.N + n];
+  }
+  float val;
+  if (g.epi == EPI_SWIGLU) {
+    val = silu(a) * u;
+  } else if (g.epi == EPI_RESIDUAL) {
+    const long rm = (long)(m % g.res_rows) * g.ldr + n;
+    val = a + (g.res_dt == BF16 ? bf2f(((const bf16_t*)g.res)[rm]) : ((const float*)g.res)[rm]);
+  } else {
+    val = g.colscale ? a * g.colscale[n] : a;
+  }
+  stf((OutT*)g.C + (size_t)m * g.ldc + n, val);
+}
+
+int ksplit_for(int N, int K, int epi) {
+  const int ncols = epi == EPI_SWIGLU ? 2 * N : N;
+  const int tiles = (ncols + 31) / 32;
+  const int max_split = (K + 63) / 64;
+  int ks = (TARGET_WAVES + tiles - 1) / tiles;
+  return ks < 1 ? 1 : (ks > max_split ? max_split : ks);
+}
+}  // namespace skinny
+
+bool skinny_ok(const GemmArgs& g) {
+  return g.ws && g.M <= 32 && g.in_dt == BF16 && g.batch <= 1 && g.chunk == 0 &&
+         g.K % 8 == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
+         gemm_skinny_ws_floats(g.M, g.N, g.K, g.epi) <= g.ws_floats;
+}
+
 bool big_ok(const GemmArgs& g) {
   if (g.in_dt != BF16) return false;
   if (g.K % big::BK || g.lda % 8 || g.ldb % 8) return false;
@@ -528,9 +617,32 @@ int gemm_stage_choice() {
   return v;
 }
 
+size_t gemm_skinny_ws_floats(int M, int N, int K, int epi) {
+  const int ncols = epi == EPI_SWIGLU ? 2 * N : N;
+  return (size_t)skinny::ksplit_for(N, K, epi) * M * ncols;
+}
+
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   const int nb = g.batch > 0 ? g.batch : 1;
+  if (skinny_ok(g)) {
+    const int ncols = g.epi == EPI_SWIGLU ? 2 * g.N : g.N;
+    const int nks = skinny::ksplit_for(g.N, g.K, g.epi);
+    const int kslice = ((g.K + nks - 1) / nks + 63) / 64 * 64;
+    const int nks_used = (g.K + kslice - 1) / kslice;
+    hipLaunchKernelGGL(skinny::gemm_skinny_part, dim3((ncols + 31) / 32, nks_used), dim3(64), 0,
+                       s, g, kslice, ncols);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned nblk = (unsigned)(((long)g.M * g.N + 255) / 256);
+    if (g.out_dt == BF16)
+      hipLaunchKernelGGL(skinny::gemm_skinny_reduce<bf16_t>, dim3(nblk), dim3(256), 0, s, g,
+                         nks_used, ncols);
+    else
+      hipLaunchKernelGGL(skinny::gemm_skinny_reduce<float>, dim3(nblk), dim3(256), 0, s, g,
+                         nks_used, ncols);
+    return hipGetLastError();
+  }
   if (big_ok(g)) {
     const int nst = gemm_stage_choice();
     const void* kf = nst == 2 ? (const void*)big::gemm_nt_big<float, 2>

@@ -72,8 +72,12 @@ struct GemmArgs {
   // chunked B (fast-weight apply): rows [c*chunk, (c+1)*chunk) of each batch
   // use B = (c == 0 ? B : Bchunks + (c-1) * sBchunk); 0 disables
   int chunk; const void* Bchunks; long sBchunk; long sBchunksBatch;
+  // optional fp32 workspace for the few-row (M <= 32) split-K path; NULL
+  // disables it (gemm_skinny_ws_floats gives the size it needs)
+  float* ws; size_t ws_floats;
 };
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
+size_t gemm_skinny_ws_floats(int M, int N, int K, int epi);
 
 // Fast-weight prefix states:
 //   acc = W0 (fp32); for i in [0, nstates): acc += A_i B_i^T over tokens of
