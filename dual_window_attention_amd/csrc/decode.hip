@@ -248,7 +248,7 @@ list_kdot(const T* __restrict__ klist, const T* __restrict__ z, const float* __r
 }
 
 // ypart[b, seg, a] = sum_{t in seg} c[b, t] r_list[b, t, a]
-constexpr int SEG = 256;
+constexpr int SEG = 1024;
 template <typename T>
 __global__ void __launch_bounds__(256)
 list_raccum(const T* __restrict__ rlist, const float* __restrict__ cbuf, float* __restrict__ ypart,
