@@ -15,18 +15,20 @@
 //     rows are (position, q head) pairs of that kv group, so all GQA heads
 //     share every K/V tile staged in LDS.
 //   * K/V tiles of 64 keys go straight from global memory into LDS
-//     (global_load_lds_dwordx4) in a 3-deep ring, XOR-swizzled so that the
+//     (global_load_lds_dwordx4) in a 4-slot ring, XOR-swizzled so that the
 //     MFMA operand reads are free of bank conflicts.  V arrives
 //     pre-transposed (d-major) with the keys of every 16-key group permuted
 //     so that one 16-byte LDS read yields the 8 keys an MFMA lane needs.
+//   * The two groups of four waves (one wave of each per SIMD) run half a
+//     step apart: while one wave of a SIMD issues the QK and PV products,
+//     the other computes a softmax (see the kernel's comment).
 //   * ONE online-softmax state per row, walked newest to oldest: first the
-//     student band (masked only on edge sub-blocks); when a wave passes its
-//     oldest student sub-block the student output is written, the far-band
-//     part of the (at most two) edge sub-blocks is added -- they are still
-//     in the LDS ring -- and the walk continues through the far band to the
-//     teacher output.  Tiles outside a wave's bands are skipped.  Rows whose
-//     far band is empty finish with bit-identical teacher and student
-//     results.
+//     student band (masked only on edge sub-blocks); once the wave's oldest
+//     student sub-block is in, the student output is written and the walk
+//     continues through the far band.  The far part of the (at most two)
+//     sub-blocks at the w_S edge is added at the end, from global memory.
+//     Rows whose far band is empty finish with bit-identical teacher and
+//     student results.
 //   * Lazy rescaling: the running max only moves when a new score exceeds
 //     it by more than 2^8; the result is unchanged up to rounding.
 #include "common.hpp"
@@ -37,7 +39,6 @@ namespace ttcd {
 namespace {
 
 constexpr int BN = 64;          // keys per LDS tile
-constexpr int NBUF = 4;         // LDS ring depth: current, previous, two in flight
 constexpr float TAU = 8.0f;     // lazy-rescale threshold (log2 domain)
 constexpr float NEG_INF = -__builtin_inff();
 constexpr float LN2 = 0.69314718055994530942f;
@@ -52,9 +53,9 @@ TTCD_DEV void g2l16(const void* src, void* lds_wave_base) {
 
 // Workgroup barrier that does not drain this wave's in-flight tile fetches
 // (a fenced barrier would wait for every outstanding memory operation).  LDS
-// ordering: every wave waits for the tile it needs with wait_vm first, and
-// all LDS reads of a buffer are consumed by MFMAs before the barrier that
-// precedes the fetch overwriting it.
+// ordering: the waves that fetch a tile wait for it with wait_vm before the
+// barrier that publishes it, and every wave's LDS reads of a slot are
+// complete (lgkmcnt 0) before the barrier after which the slot is refilled.
 TTCD_DEV void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // wait until at most N vector-memory operations of this wave are outstanding
@@ -78,217 +79,6 @@ struct SoftState {
   float m;   // running max (log2 domain, scaled)
   float l;   // this lane's partial denominator
 };
-
-template <int D, int NW>
-TTCD_DEV void issue_tile(char* buf, const bf16_t* kbase, size_t kstride, const bf16_t* vbase,
-                         int vt_ld, int j0, int jlo, int jhi, int wave, int lane) {
-  using TL = Tile<D>;
-  static_assert(TL::KPOS % (64 * NW) == 0 && TL::VPOS % (64 * NW) == 0, "tile/wave split");
-#pragma unroll
-  for (int i = 0; i < TL::KPOS / (64 * NW); ++i) {
-    const int p0 = (i * NW + wave) * 64;
-    const int p = p0 + lane;
-    const int row = p / TL::CPR, cp = p % TL::CPR;
-    const int c = cp ^ TL::kswz(row);
-    const int j = min(max(j0 + row, jlo), jhi);   // never read outside the band
-    g2l16(kbase + (size_t)j * kstride + c * 8, buf + p0 * 16);
-  }
-  char* vb = buf + TL::KPOS * 16;
-#pragma unroll
-  for (int i = 0; i < TL::VPOS / (64 * NW); ++i) {
-    const int p0 = (i * NW + wave) * 64;
-    const int p = p0 + lane;
-    const int d = p >> 3, cp = p & 7;
-    const int c = cp ^ TL::vswz(d);
-    g2l16(vbase + (size_t)d * vt_ld + j0 + 8 * c, vb + p0 * 16);
-  }
-}
-
-// One 32-key sub-block: S^T = K Q^T, online-softmax update, O^T += V^T P^T.
-// Operand fragments are read from LDS in groups ahead of their MFMAs so that
-// one LDS latency covers eight MFMAs, and the V^T fragments are in flight
-// while the softmax runs.  masked (wave-uniform): only keys with
-// lo <= t - j < hi take part.
-template <int D>
-TTCD_DEV void process(const char* buf, int sb, int j0, int t, bool masked, int lo, int hi,
-                      float c, const bf16x8* qf, SoftState& st, f32x16* acc, int lane) {
-  using TL = Tile<D>;
-  constexpr int NB = D / 32;
-  constexpr int KSTEP = D / 16;
-  const int h = lane >> 5, r = lane & 31;
-
-  bf16x8 kf[KSTEP];
-  {
-    const int row = 32 * sb + r;
-    const char* krow = buf + row * (TL::CPR * 16);
-    const int sw = TL::kswz(row);
-#pragma unroll
-    for (int ks = 0; ks < KSTEP; ++ks) kf[ks] = as_bf16x8(ld16(krow + (((2 * ks + h) ^ sw) << 4)));
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  f32x16 s = zero16();
-#pragma unroll
-  for (int ks = 0; ks < KSTEP; ++ks) s = mfma32(kf[ks], qf[ks], s);
-
-  bf16x8 vf[NB][2];
-  {
-    const char* vb = buf + TL::KPOS * 16;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int d = 32 * b + r;
-      const char* vrow = vb + d * (BN * 2);
-      const int sw = TL::vswz(d);
-      vf[b][0] = as_bf16x8(ld16(vrow + (((4 * sb + 0 + h) ^ sw) << 4)));
-      vf[b][1] = as_bf16x8(ld16(vrow + (((4 * sb + 2 + h) ^ sw) << 4)));
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-
-  if (masked) {
-    // lo <= t - j < hi  <=>  (unsigned)(t - j - lo) < (unsigned)(hi - lo)
-    const uint32_t d0 = (uint32_t)(t - j0 - 4 * h - lo), span = (uint32_t)(hi - lo);
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const uint32_t dl = d0 - (uint32_t)(8 * (v >> 2) + (v & 3));
-      s[v] = dl < span ? s[v] : NEG_INF;
-    }
-  }
-  // row max over the 32 keys (raw scores; c > 0): in-lane, then swap halves
-  float mx = NEG_INF;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[v]);
-  {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                     false, false);
-    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
-  }
-  const bool need = mx > st.m + TAU;
-  if (__builtin_expect(__any(need), 0)) {
-    const float mnew = need ? mx : st.m;
-    const float alpha = (st.m == NEG_INF) ? 0.f : fast_exp2(st.m - mnew);
-    st.l *= alpha;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] *= alpha;
-    st.m = mnew;
-  }
-  // masked scores are -inf: exp2(-inf) = 0 (a row without any key here has
-  // m = -inf only if it never had one, and then every score is -inf too)
-  const float negm = st.m == NEG_INF ? 0.f : -st.m;
-  bf16x8 p0, p1;
-  float lsum = 0.f;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const float e = fast_exp2(__builtin_fmaf(s[v], c, negm));
-    lsum += e;
-    if (v < 8) p0[v] = (__bf16)e;
-    else p1[v - 8] = (__bf16)e;
-  }
-  st.l += lsum;
-
-  // O^T += V^T P^T
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    acc[b] = mfma32(vf[b][0], p0, acc[b]);
-    acc[b] = mfma32(vf[b][1], p1, acc[b]);
-  }
-}
-
-// softmax step of one unmasked 32-key sub-block: lazy max update, p = 2^(s c - m)
-template <int NB>
-TTCD_DEV void softmax32(f32x16& s, float c, SoftState& st, f32x16* acc, bf16x8& p0, bf16x8& p1) {
-  float mx = NEG_INF;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[v]);
-  {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                     false, false);
-    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
-  }
-  const bool need = mx > st.m + TAU;
-  if (__builtin_expect(__any(need), 0)) {
-    const float mnew = need ? mx : st.m;
-    const float alpha = (st.m == NEG_INF) ? 0.f : fast_exp2(st.m - mnew);
-    st.l *= alpha;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] *= alpha;
-    st.m = mnew;
-  }
-  const float negm = -st.m;
-  float lsum = 0.f;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const float e = fast_exp2(__builtin_fmaf(s[v], c, negm));
-    lsum += e;
-    if (v < 8) p0[v] = (__bf16)e;
-    else p1[v - 8] = (__bf16)e;
-  }
-  st.l += lsum;
-}
-
-// Both 32-key sub-blocks of a tile, no masking, software-pipelined so the
-// MFMA pipe always has queued work while the VALU runs a softmax:
-//   QK(1) | QK(0) + softmax(1) | PV(1) + softmax(0) | PV(0)
-template <int D>
-TTCD_DEV void process_pair(const char* buf, float c, const bf16x8* qf, SoftState& st,
-                           f32x16* acc, int lane) {
-  using TL = Tile<D>;
-  constexpr int NB = D / 32;
-  constexpr int KSTEP = D / 16;
-  const int h = lane >> 5, r = lane & 31;
-  const char* vb = buf + TL::KPOS * 16;
-  bf16x8 kf[KSTEP];
-  bf16x8 vf[NB][2];
-  f32x16 s1 = zero16(), s0 = zero16();
-  bf16x8 p0, p1;
-
-  auto load_k = [&](int sb) {
-    const int row = 32 * sb + r;
-    const char* krow = buf + row * (TL::CPR * 16);
-    const int sw = TL::kswz(row);
-#pragma unroll
-    for (int ks = 0; ks < KSTEP; ++ks) kf[ks] = as_bf16x8(ld16(krow + (((2 * ks + h) ^ sw) << 4)));
-  };
-  auto load_v = [&](int sb) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int d = 32 * b + r;
-      const char* vrow = vb + d * (BN * 2);
-      const int sw = TL::vswz(d);
-      vf[b][0] = as_bf16x8(ld16(vrow + (((4 * sb + 0 + h) ^ sw) << 4)));
-      vf[b][1] = as_bf16x8(ld16(vrow + (((4 * sb + 2 + h) ^ sw) << 4)));
-    }
-  };
-
-  load_k(1);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int ks = 0; ks < KSTEP; ++ks) s1 = mfma32(kf[ks], qf[ks], s1);
-  __builtin_amdgcn_sched_barrier(0);
-  load_k(0);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int ks = 0; ks < KSTEP; ++ks) s0 = mfma32(kf[ks], qf[ks], s0);
-  __builtin_amdgcn_sched_barrier(0);
-  load_v(1);
-  __builtin_amdgcn_sched_barrier(0);
-  softmax32<NB>(s1, c, st, acc, p0, p1);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    acc[b] = mfma32(vf[b][0], p0, acc[b]);
-    acc[b] = mfma32(vf[b][1], p1, acc[b]);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  load_v(0);
-  __builtin_amdgcn_sched_barrier(0);
-  softmax32<NB>(s0, c, st, acc, p0, p1);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    acc[b] = mfma32(vf[b][0], p0, acc[b]);
-    acc[b] = mfma32(vf[b][1], p1, acc[b]);
-  }
-}
 
 template <int NB>
 TTCD_DEV void store_out(void* o, float* lse, int out_bf16, bool row_ok, size_t obase, size_t li,
@@ -318,54 +108,179 @@ TTCD_DEV void store_out(void* o, float* lse, int out_bf16, bool row_ok, size_t o
   if (h == 0 && lse) lse[li] = (st.m + fast_log2(l)) * LN2;
 }
 
-template <int D, int NW>
-__global__ void __launch_bounds__(64 * NW)
+// --------------------------------------------------------------------------
+// Two groups of four waves, one wave of each group per SIMD.  Each wave
+// walks the workgroup's sub-blocks of 32 keys (newest first) as alternating
+// segments, every one ended by a workgroup barrier:
+//   M(k): PV of sub-block k-1 with the K fragments of sub-block k loaded
+//         behind it, then S(k) = K(k) Q^T with the V^T fragments of k loaded
+//         behind it, then the mask and row max of S(k);
+//   X(k): the lazy rescale and P(k) = 2^(S(k) c - m) on the vector ALU.
+// Group 1 runs one segment behind group 0 (it passes one extra barrier at
+// the start, group 0 one at the end), so on each SIMD one wave feeds the
+// matrix cores while the other runs a softmax.
+//
+// Keys that are far (w_S <= t-j) for some rows but lie in the two sub-blocks
+// at the w_S edge are walked with the student mask only; their far part is
+// added after the walk, from global memory, once the student output is out.
+//
+// Tile ring (NBUF slots of 64 keys), filled by group 0: tile i is read in
+// M(2i) and M(2i+1); group 0 waits for it at the end of X(2i-1) and issues
+// tile i+NBUF into its slot in X(2i+2), after every wave's reads of tile i
+// have completed.
+// --------------------------------------------------------------------------
+template <int D>
+struct MfmaCfg {
+  static constexpr int NB = D / 32;
+  static constexpr int KSTEP = D / 16;
+  static constexpr int NW = 8;
+  static constexpr int ROWS = 32 * NW;
+  static constexpr int NBUF = 4;
+  static constexpr int ISSUERS = 4;
+  static constexpr int LPT = (Tile<D>::KPOS + Tile<D>::VPOS) / (64 * ISSUERS);
+};
+
+TTCD_DEV void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// vmcnt wait with a run-time count among {0, L, 2L, 3L}
+template <int L>
+TTCD_DEV void wait_vm_tiles(int ntiles) {
+  if (ntiles >= 3)
+    wait_vm<3 * L>();
+  else if (ntiles == 2)
+    wait_vm<2 * L>();
+  else if (ntiles == 1)
+    wait_vm<L>();
+  else
+    wait_vm<0>();
+}
+
+// row max of one 32-key sub-block (raw scores times c > 0)
+TTCD_DEV float row_max32(const f32x16& s, float c) {
+  float mx = NEG_INF;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[v]);
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                   false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+}
+
+// keys with lo <= t - j < hi keep their score, the others become -inf
+TTCD_DEV void mask32(f32x16& s, int t, int j0, int h, int lo, int hi) {
+  const uint32_t d0 = (uint32_t)(t - j0 - 4 * h - lo), span = (uint32_t)(hi - lo);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const uint32_t dl = d0 - (uint32_t)(8 * (v >> 2) + (v & 3));
+    s[v] = dl < span ? s[v] : NEG_INF;
+  }
+}
+
+// lazy rescale against the sub-block max, then P = 2^(s c - m) in bf16 and
+// its fp32 sum into the denominator
+template <int NB>
+TTCD_DEV void softmax_p(const f32x16& s, float mx, float c, SoftState& st, f32x16* acc,
+                        bf16x8& p0, bf16x8& p1) {
+  const bool need = mx > st.m + TAU;
+  if (__builtin_expect(__any(need), 0)) {
+    const float mnew = need ? mx : st.m;
+    const float alpha = (st.m == NEG_INF) ? 0.f : fast_exp2(st.m - mnew);
+    st.l *= alpha;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] *= alpha;
+    st.m = mnew;
+  }
+  const float negm = st.m == NEG_INF ? 0.f : -st.m;
+  float la = 0.f, lb = 0.f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const float e = fast_exp2(__builtin_fmaf(s[v], c, negm));
+    if (v & 1)
+      lb += e;
+    else
+      la += e;
+    if (v < 8)
+      p0[v] = (__bf16)e;
+    else
+      p1[v - 8] = (__bf16)e;
+  }
+  st.l += la + lb;
+}
+
+// which keys of the sub-block starting at j0 this wave takes in the walk:
+// 0 = none, 1 = student band (w_S edge blocks included), 2 = far band
+struct Band {
+  int a_w, b_w, sLo, fLo, wS, wT;
+  TTCD_DEV int kind(int j0, bool& masked, int& lo, int& hi) const {
+    const int j1 = j0 + 31;
+    if (j0 > b_w || j1 < fLo) return 0;
+    if (j1 >= sLo) {
+      masked = !(j1 <= a_w && j0 >= b_w - wS + 1);
+      lo = 0;
+      hi = wS;
+      return 1;
+    }
+    masked = !(j0 >= b_w - wT + 1);
+    lo = wS;
+    hi = wT;
+    return 2;
+  }
+};
+
+template <int D>
+__global__ void __launch_bounds__(512)
 dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-                      const bf16_t* __restrict__ vt, int vt_ld,
-                      void* __restrict__ o_t, void* __restrict__ o_s,
-                      float* __restrict__ lse_t, float* __restrict__ lse_s,
-                      int B, int Tq, int Tk, int kv_rows, int q_pos0, int Hq, int Hkv,
-                      int wT, int wS, float c, int out_bf16, int nblk) {
+                    const bf16_t* __restrict__ vt, int vt_ld, void* __restrict__ o_t,
+                    void* __restrict__ o_s, float* __restrict__ lse_t,
+                    float* __restrict__ lse_s, int B, int Tq, int Tk, int kv_rows, int q_pos0,
+                    int Hq, int Hkv, int wT, int wS, float c, int out_bf16, int nblk) {
   using TL = Tile<D>;
-  constexpr int NB = D / 32;
-  constexpr int KSTEP = D / 16;
-  constexpr int ROWS = 32 * NW;
+  using CF = MfmaCfg<D>;
+  constexpr int NB = CF::NB;
+  constexpr int KSTEP = CF::KSTEP;
+  constexpr int ROWS = CF::ROWS;
+  constexpr int NBUF = CF::NBUF;
+  constexpr int LPT = CF::LPT;
   extern __shared__ __align__(16) char lds[];
 
   const int G = Hq / Hkv;
   const int R = Tq * G;
   const uint32_t total = (uint32_t)B * Hkv * nblk;
   const uint32_t lid = xcd_remap(blockIdx.x, total);
-  const int blk = lid % nblk;
+  // position blocks run newest first: the workgroups an XCD starts together
+  // then have full windows of equal length, stay in step, and re-read each
+  // other's K/V tiles from L2 a few tiles apart
+  const int blk = nblk - 1 - (int)(lid % nblk);
   const int bg = lid / nblk;
   const int g = bg % Hkv;
   const int b = bg / Hkv;
 
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool issuer = wave < CF::ISSUERS;        // group 0
   const int lane = tid & 63;
-  const int h = lane >> 5;
+  const int h = lane >> 5, r32 = lane & 31;
 
-  // ---- this lane's query row: (position, head) pair of the kv group
   const int row0 = blk * ROWS;
   const int rw0 = row0 + 32 * wave;
-  int r = rw0 + (lane & 31);
+  int r = rw0 + r32;
   const bool row_ok = r < R;
   r = row_ok ? r : R - 1;
   const int qi = r / G;
   const int qh = g * G + (r % G);
   const int t = q_pos0 + qi;
 
-  // wave / workgroup position ranges
-  const int a_w = q_pos0 + min(rw0, R - 1) / G;
-  const int b_w = q_pos0 + min(rw0 + 31, R - 1) / G;
+  Band bd;
+  bd.a_w = q_pos0 + min(rw0, R - 1) / G;
+  bd.b_w = q_pos0 + min(rw0 + 31, R - 1) / G;
+  bd.sLo = bd.a_w - wS + 1;
+  bd.fLo = max(bd.a_w - wT + 1, 0);
+  bd.wS = wS;
+  bd.wT = wT;
   const int A = q_pos0 + row0 / G;
   const int Bp = q_pos0 + min(row0 + ROWS - 1, R - 1) / G;
   const int jlo = max(0, A - wT + 1);
   const int jhi = min(Bp, Tk - 1);
-  const int sLo = a_w - wS + 1;                 // oldest key of any row's student band
-  const int fLo = max(a_w - wT + 1, 0);         // oldest key of any row's teacher band
-  const int j0_lastS = max(sLo, 0) & ~31;       // the wave's oldest student sub-block
+  const int j0_lastS = max(bd.sLo, 0) & ~31;
 
   bf16x8 qf[KSTEP];
   {
@@ -384,96 +299,213 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   const size_t obase = ((size_t)(b * Tq + qi) * Hq + qh) * D;
   const size_t li = (size_t)(b * Hq + qh) * Tq + qi;
 
-  // tiles are fetched two ahead of the one being computed
-  constexpr int LPW = (TL::KPOS + TL::VPOS) / (64 * NW);   // 16B loads per wave and tile
   const int n_hi = jhi / BN, n_lo = jlo / BN;
-  issue_tile<D, NW>(lds + (n_hi % NBUF) * TL::BYTES, kbase, kstride, vbase, vt_ld, n_hi * BN,
-                    jlo, jhi, wave, lane);
-  if (n_hi - 1 >= n_lo) {
-    issue_tile<D, NW>(lds + ((n_hi - 1) % NBUF) * TL::BYTES, kbase, kstride, vbase, vt_ld,
-                      (n_hi - 1) * BN, jlo, jhi, wave, lane);
-    wait_vm<LPW>();
-  } else {
-    wait_vm<0>();
+  const int NT = n_hi - n_lo + 1;            // tiles, newest first
+  const int K = 2 * NT;                       // sub-blocks
+  auto j0_of = [&](int x) { return (n_hi - (x >> 1)) * BN + ((x & 1) ? 0 : 32); };
+  // the walk position of the oldest student sub-block
+  const int kL = 2 * (n_hi - j0_lastS / BN) + (((j0_lastS >> 5) & 1) ? 0 : 1);
+
+  // LDS operand addresses.  The swizzled chunk of a K row or V^T row is
+  // (logical chunk) ^ (per-lane swizzle); the k-step, key-half and sub-block
+  // parts of the logical chunk occupy address bits that no other part uses,
+  // so every fragment address is  uniform base + (lane part ^ constant).
+  //   K, sub-block x, k-step i:  ring(x) + 32 sb(x) CPR 16 + (klane ^ 32 i)
+  //   V^T, MFMA i of PV:         ring(x) + KPOS 16 + 4096 (i/2)
+  //                              + (vlane ^ (64 sb(x) + 32 (i%2)))
+  const uint32_t klane = (uint32_t)(r32 * (TL::CPR * 16) + ((h ^ TL::kswz(r32)) << 4));
+  const uint32_t vlane = (uint32_t)(r32 * (BN * 2) + ((h ^ TL::vswz(r32)) << 4));
+  auto ring = [&](int x) { return (uint32_t)(((x >> 1) % NBUF) * TL::BYTES); };
+  auto sbit = [&](int x) { return (x & 1) ? 0 : 1; };
+  auto load_k1 = [&](uint32_t kl, int x, int i, bf16x8& dst) {
+    const uint32_t base = ring(x) + (uint32_t)(sbit(x) * 32 * TL::CPR * 16);
+    dst = as_bf16x8(ld16(lds + base + (kl ^ (uint32_t)(32 * i))));
+  };
+  auto load_v1 = [&](uint32_t vl, int x, int i, bf16x8& dst) {
+    const uint32_t base = ring(x) + (uint32_t)(TL::KPOS * 16 + 4096 * (i >> 1));
+    dst = as_bf16x8(ld16(lds + base + (vl ^ (uint32_t)(64 * sbit(x) + 32 * (i & 1)))));
+  };
+
+  // Tile fetch by the four group-0 waves, 16 bytes per lane straight into
+  // LDS.  For K, load i of a wave covers rows (i*4 + wave) * 64/CPR + lane/CPR
+  // and its swizzled chunk does not depend on i; for V^T, dims
+  // (i*4 + wave) * 8 + lane/8.  Only the newest tile can reach past the last
+  // key; its rows are clamped there (they are masked).
+  constexpr int KLD = TL::KPOS / (64 * CF::ISSUERS), VLD = TL::VPOS / (64 * CF::ISSUERS);
+  constexpr int KRPL = 64 / TL::CPR;          // K rows per load instruction
+  const int wv4 = issuer ? wave : 0;
+  const int krow_l = wv4 * KRPL + lane / TL::CPR;
+  const int kchunk = (lane % TL::CPR) ^ TL::kswz(krow_l);
+  const uint32_t koff_l = (uint32_t)(krow_l * kstride + kchunk * 8);
+  const int vd_l = wv4 * 8 + lane / 8;
+  const uint32_t voff_l = (uint32_t)(vd_l * vt_ld + 8 * ((lane % 8) ^ TL::vswz(vd_l)));
+  auto issue = [&](int i) {
+    char* buf = lds + (i % NBUF) * TL::BYTES;
+    const int j0 = (n_hi - i) * BN;
+    if (j0 + BN - 1 < Tk) {
+#pragma unroll
+      for (int u = 0; u < KLD; ++u) {
+        const bf16_t* src = kbase + (size_t)(j0 + u * CF::ISSUERS * KRPL) * kstride;
+        g2l16(src + koff_l, buf + (u * CF::ISSUERS + wv4) * 64 * 16);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < KLD; ++u) {
+        const int j = min(j0 + u * CF::ISSUERS * KRPL + krow_l, Tk - 1);
+        g2l16(kbase + (size_t)j * kstride + kchunk * 8, buf + (u * CF::ISSUERS + wv4) * 64 * 16);
+      }
+    }
+    char* vb = buf + TL::KPOS * 16;
+#pragma unroll
+    for (int u = 0; u < VLD; ++u) {
+      const bf16_t* src = vbase + (size_t)(u * CF::ISSUERS * 8) * vt_ld + j0;
+      g2l16(src + voff_l, vb + (u * CF::ISSUERS + wv4) * 64 * 16);
+    }
+  };
+
+  // ---- prologue: tiles 0 .. NBUF-1 in flight, tile 0 visible
+  const int npro = min(NBUF, NT);
+  if (issuer) {
+    for (int i = 0; i < npro; ++i) issue(i);
+    wait_vm_tiles<LPT>(npro - 1);
   }
   ring_barrier();
 
-  for (int n = n_hi; n >= n_lo; --n) {
-    const bool fetch = n - 2 >= n_lo;
-    if (fetch)
-      issue_tile<D, NW>(lds + ((n - 2) % NBUF) * TL::BYTES, kbase, kstride, vbase, vt_ld,
-                        (n - 2) * BN, jlo, jhi, wave, lane);
-    const char* buf = lds + (n % NBUF) * TL::BYTES;
-    // work items of this tile, newest first: sub-block 1, sub-block 0, and
-    // right after the wave's oldest student sub-block the far part of its
-    // (at most two) edge sub-blocks
-    int sbq = 1, pend = 0;
-    {
-      // fast path: both sub-blocks inside one band for every row of the wave
-      const int j0b = n * BN;                                 // sub-block 0
-      const int j0a = j0b + 32;                               // sub-block 1 (newer)
-      const bool a_in = !(j0a > b_w || j0a + 31 < fLo);
-      const bool b_in = !(j0b > b_w || j0b + 31 < fLo);
-      auto unmasked = [&](int j0) {
-        return (j0 + 31 >= sLo) ? (j0 + 31 <= a_w && j0 >= b_w - wS + 1) : (j0 >= b_w - wT + 1);
-      };
-      if (a_in && b_in && j0a != j0_lastS && unmasked(j0a) && unmasked(j0b)) {
-        process_pair<D>(buf, c, qf, st, acc, lane);
-        sbq = -1;
-        if (j0b == j0_lastS) {
-          store_out<NB>(o_s, lse_s, out_bf16, row_ok, obase, li, st, acc, h);
-          pend = wT > wS ? 2 : 0;
-        }
-      }
-    }
+  bf16x8 vf[NB][2];        // V^T fragments of the sub-block whose PV comes next
+  bf16x8 p0, p1;           // its P (zero when the wave skips it)
+#pragma unroll
+  for (int v = 0; v < 8; ++v) p0[v] = p1[v] = (__bf16)0.f;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) vf[i][0] = vf[i][1] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  bool m_c = false;
+  int lo_c = 0, hi_c = 0;
+  int kind_p = 0;
+  if (!issuer) ring_barrier();                 // group 1 runs one segment behind
+
 #pragma unroll 1
-    while (true) {
-      int j0, lo, hi;
-      bool masked, main_item;
-      const char* b;
-      if (pend > 0) {
-        j0 = j0_lastS + 32 * (2 - pend);
-        --pend;
-        if (j0 > b_w - wS) continue;
-        b = lds + ((j0 / BN) % NBUF) * TL::BYTES;
-        masked = true;
-        lo = wS;
-        hi = wT;
-        main_item = false;
-      } else if (sbq >= 0) {
-        j0 = n * BN + 32 * sbq;
-        --sbq;
-        const int j1 = j0 + 31;
-        if (j0 > b_w || j1 < fLo) continue;      // outside every row's teacher band
-        b = buf;
-        main_item = true;
-        if (j1 >= sLo) {                          // student band (and causal diagonal)
-          masked = !(j1 <= a_w && j0 >= b_w - wS + 1);
-          lo = 0;
-          hi = wS;
-        } else {                                  // far band: >= w_S behind every row
-          masked = !(j0 >= b_w - wT + 1);
-          lo = wS;
-          hi = wT;
-        }
-      } else {
-        break;
-      }
-      process<D>(b, (j0 >> 5) & 1, j0, t, masked, lo, hi, c, qf, st, acc, lane);
-      if (main_item && j0 == j0_lastS) {
-        // the student band is complete: write it, then add the far edge
-        store_out<NB>(o_s, lse_s, out_bf16, row_ok, obase, li, st, acc, h);
-        pend = wT > wS ? 2 : 0;
+  for (int kk = 0; kk <= K; ++kk) {
+    // ================= M(kk): matrix segment
+    const int kind_c = kk < K ? bd.kind(j0_of(kk), m_c, lo_c, hi_c) : 0;
+    const bool act_p = kind_p != 0, act_c = kind_c != 0;
+    // The lane parts pass through an empty asm so that the per-fragment
+    // addresses are recomputed here (one VALU each) rather than all held in
+    // registers across the loop.
+    uint32_t kl = klane, vl = vlane;
+    asm volatile("" : "+v"(kl), "+v"(vl));
+    // PV(kk-1) with the K fragments of sub-block kk loaded behind it, then
+    // QK(kk) with the V^T fragments of sub-block kk loaded behind it: each
+    // load reuses the registers of the fragment the MFMA before it read, and
+    // has a whole MFMA chain to land.
+    // Sub-blocks the wave skips go through the same code (their P is zero
+    // and their scores are not used).
+    bf16x8 kf[KSTEP];
+#pragma unroll
+    for (int i = 0; i < KSTEP; ++i) {
+      acc[i >> 1] = mfma32(vf[i >> 1][i & 1], (i & 1) ? p1 : p0, acc[i >> 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      load_k1(kl, kk, i, kf[i]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    f32x16 s = zero16();
+#pragma unroll
+    for (int i = 0; i < KSTEP; ++i) {
+      s = mfma32(kf[i], qf[i], s);
+      __builtin_amdgcn_sched_barrier(0);
+      load_v1(vl, kk, i, vf[i >> 1][i & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (m_c && act_c) mask32(s, t, j0_of(kk), h, lo_c, hi_c);
+    const float mx = row_max32(s, c);
+    ring_barrier();
+    if (kk == K) break;
+
+    // ================= X(kk): softmax segment
+    if (kk - 1 == kL) {
+      // PV(kL) is in, P(kL+1) not yet: every student sub-block and nothing
+      // else -- write the student output
+      store_out<NB>(o_s, lse_s, out_bf16, row_ok, obase, li, st, acc, h);
+    }
+    if (act_c) {
+      softmax_p<NB>(s, mx, c, st, acc, p0, p1);
+    } else {
+#pragma unroll
+      for (int v = 0; v < 8; ++v) p0[v] = p1[v] = (__bf16)0.f;
+    }
+    if (issuer) {
+      if ((kk & 1) == 0 && kk >= 2) {
+        const int i = kk / 2 - 1 + NBUF;       // the slot of tile i - NBUF is free
+        if (i < NT) issue(i);
+      } else if (kk & 1) {
+        const int i = (kk + 1) / 2;            // tile read first by M(kk + 1)
+        if (i < NT) wait_vm_tiles<LPT>(min(i + NBUF - 2, NT - 1) - i);
       }
     }
-    // tile n-1 must be in LDS; tile n-2 may still be in flight
-    if (fetch)
-      wait_vm<LPW>();
-    else
-      wait_vm<0>();
+    // this wave's LDS reads of the ring are complete before the barrier
+    // after which a slot may be refilled
+    lds_wait_all();
     ring_barrier();
+    kind_p = kind_c;
+  }
+  if (issuer) ring_barrier();                  // group 0's extra barrier
+  if (kL == K - 1) {
+    // the oldest walked sub-block was the last student one
+    store_out<NB>(o_s, lse_s, out_bf16, row_ok, obase, li, st, acc, h);
+  }
+
+  // ---- far part of the (at most two) sub-blocks at the w_S edge, from
+  // global memory: keys with w_S <= t - j < w_T that the walk left out
+  if (wT > wS) {
+#pragma unroll 1
+    for (int e = 0; e < 2; ++e) {
+      const int j0 = j0_lastS + 32 * e;
+      if (j0 > bd.b_w - wS) continue;
+      bf16x8 kf[KSTEP];
+      {
+        const int j = min(max(j0 + r32, jlo), jhi);
+        const bf16_t* kp = kbase + (size_t)j * kstride + 8 * h;
+#pragma unroll
+        for (int ks = 0; ks < KSTEP; ++ks) kf[ks] = as_bf16x8(ld16(kp + 16 * ks));
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+          const bf16_t* vp = vbase + (size_t)(32 * bb + r32) * vt_ld + j0 + 8 * h;
+          vf[bb][0] = as_bf16x8(ld16(vp));
+          vf[bb][1] = as_bf16x8(ld16(vp + 16));
+        }
+      }
+      f32x16 s = zero16();
+#pragma unroll
+      for (int i = 0; i < KSTEP; ++i) s = mfma32(kf[i], qf[i], s);
+      mask32(s, t, j0, h, wS, wT);
+      const float mx = row_max32(s, c);
+      softmax_p<NB>(s, mx, c, st, acc, p0, p1);
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        acc[bb] = mfma32(vf[bb][0], p0, acc[bb]);
+        acc[bb] = mfma32(vf[bb][1], p1, acc[bb]);
+      }
+    }
   }
   store_out<NB>(o_t, lse_t, out_bf16, row_ok, obase, li, st, acc, h);
+}
+
+template <int D>
+hipError_t launch_mfma(const AttnArgs& a, hipStream_t s) {
+  using CF = MfmaCfg<D>;
+  const size_t lds = (size_t)CF::NBUF * Tile<D>::BYTES;
+  static hipError_t attr = hipFuncSetAttribute((const void*)dual_window_attn_mfma<D>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)lds);
+  if (attr != hipSuccess) return attr;
+  const int G = a.Hq / a.Hkv;
+  const int R = a.Tq * G;
+  const int nblk = (R + CF::ROWS - 1) / CF::ROWS;
+  const long total = (long)a.B * a.Hkv * nblk;
+  const float c = a.scale * 1.4426950408889634f;
+  hipLaunchKernelGGL((dual_window_attn_mfma<D>), dim3((unsigned)total), dim3(64 * CF::NW), lds, s,
+                     (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.vt, a.vt_ld, a.o_t,
+                     a.o_s, a.lse_t, a.lse_s, a.B, a.Tq, a.Tk, a.kv_rows, a.q_pos0, a.Hq, a.Hkv,
+                     a.wT, a.wS, c, a.out_dt == BF16 ? 1 : 0, nblk);
+  return hipGetLastError();
 }
 
 // --------------------------------------------------------------------------
@@ -577,26 +609,6 @@ dual_window_attn_simple(const T* __restrict__ q, const T* __restrict__ k,
   const float lseS = mS + logf(lS);
   if (lse_s) lse_s[li] = lseS;
   if (lse_t) lse_t[li] = far_empty ? lseS : mT + logf(lT);
-}
-
-template <int D>
-hipError_t launch_mfma(const AttnArgs& a, hipStream_t s) {
-  constexpr int NW = 8;
-  const size_t lds = (size_t)NBUF * Tile<D>::BYTES;
-  static hipError_t attr = hipFuncSetAttribute((const void*)dual_window_attn_mfma<D, NW>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)lds);
-  if (attr != hipSuccess) return attr;
-  const int G = a.Hq / a.Hkv;
-  const int R = a.Tq * G;
-  const int nblk = (R + 32 * NW - 1) / (32 * NW);
-  const long total = (long)a.B * a.Hkv * nblk;
-  const float c = a.scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((dual_window_attn_mfma<D, NW>), dim3((unsigned)total), dim3(64 * NW), lds,
-                     s, (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.vt, a.vt_ld,
-                     a.o_t, a.o_s, a.lse_t, a.lse_s, a.B, a.Tq, a.Tk, a.kv_rows, a.q_pos0, a.Hq,
-                     a.Hkv, a.wT, a.wS, c, a.out_dt == BF16 ? 1 : 0, nblk);
-  return hipGetLastError();
 }
 
 // V^T operand of the PV product: vt[b, g, d, c] = v[b, key(c), g, d], where
