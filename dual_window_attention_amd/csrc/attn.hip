@@ -88,22 +88,28 @@ TTCD_DEV void store_out(void* o, float* lse, int out_bf16, bool row_ok, size_t o
   const float l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   const float inv = 1.f / l;
   if (!row_ok) return;
+  // lane (r, h) holds dims 32 bb + 8 g4 + 4 h + e of its row
+  if (out_bf16) {
+    bf16_t* op = reinterpret_cast<bf16_t*>(o) + obase + 4 * h;
 #pragma unroll
-  for (int bb = 0; bb < NB; ++bb) {
+    for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d = 32 * bb + 8 * g4 + 4 * h;
-      float ov[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ov[e] = acc[bb][4 * g4 + e] * inv;
-      if (out_bf16) {
-        *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(o) + obase + d) =
-            u32x2{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
-      } else {
-        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(o) + obase + d) =
-            f32x4{ov[0], ov[1], ov[2], ov[3]};
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x16& a = acc[bb];
+        *reinterpret_cast<u32x2*>(op + 32 * bb + 8 * g4) =
+            u32x2{pack_bf16x2(a[4 * g4] * inv, a[4 * g4 + 1] * inv),
+                  pack_bf16x2(a[4 * g4 + 2] * inv, a[4 * g4 + 3] * inv)};
       }
-    }
+  } else {
+    float* op = reinterpret_cast<float*>(o) + obase + 4 * h;
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x16& a = acc[bb];
+        *reinterpret_cast<f32x4*>(op + 32 * bb + 8 * g4) =
+            f32x4{a[4 * g4] * inv, a[4 * g4 + 1] * inv, a[4 * g4 + 2] * inv, a[4 * g4 + 3] * inv};
+      }
   }
   if (h == 0 && lse) lse[li] = (st.m + fast_log2(l)) * LN2;
 }
@@ -206,23 +212,26 @@ TTCD_DEV void softmax_p(const f32x16& s, float mx, float c, SoftState& st, f32x1
   st.l += la + lb;
 }
 
-// which keys of the sub-block starting at j0 this wave takes in the walk:
-// 0 = none, 1 = student band (w_S edge blocks included), 2 = far band
+// How this wave takes the sub-block of 32 keys starting at j0 in the walk:
+// not at all, or with keys lo <= t - j < hi for the student band (w_S edge
+// blocks included: lo = 0, hi = w_S) or the far band (lo = w_S, hi = w_T),
+// masked when some row of the wave sees only part of the sub-block.  All
+// values are wave-uniform; selects, no branches.
+struct Item {
+  bool act, masked;
+  int lo, hi;
+};
 struct Band {
   int a_w, b_w, sLo, fLo, wS, wT;
-  TTCD_DEV int kind(int j0, bool& masked, int& lo, int& hi) const {
+  TTCD_DEV Item item(int j0) const {
     const int j1 = j0 + 31;
-    if (j0 > b_w || j1 < fLo) return 0;
-    if (j1 >= sLo) {
-      masked = !(j1 <= a_w && j0 >= b_w - wS + 1);
-      lo = 0;
-      hi = wS;
-      return 1;
-    }
-    masked = !(j0 >= b_w - wT + 1);
-    lo = wS;
-    hi = wT;
-    return 2;
+    const bool stud = j1 >= sLo;
+    Item it;
+    it.act = j0 <= b_w && j1 >= fLo;
+    it.masked = stud ? !(j1 <= a_w && j0 >= b_w - wS + 1) : !(j0 >= b_w - wT + 1);
+    it.lo = stud ? 0 : wS;
+    it.hi = stud ? wS : wT;
+    return it;
   }
 };
 
@@ -377,27 +386,19 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   for (int v = 0; v < 8; ++v) p0[v] = p1[v] = (__bf16)0.f;
 #pragma unroll
   for (int i = 0; i < NB; ++i) vf[i][0] = vf[i][1] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-  bool m_c = false;
-  int lo_c = 0, hi_c = 0;
-  int kind_p = 0;
-  if (!issuer) ring_barrier();                 // group 1 runs one segment behind
 
-#pragma unroll 1
-  for (int kk = 0; kk <= K; ++kk) {
-    // ================= M(kk): matrix segment
-    const int kind_c = kk < K ? bd.kind(j0_of(kk), m_c, lo_c, hi_c) : 0;
-    const bool act_p = kind_p != 0, act_c = kind_c != 0;
-    // The lane parts pass through an empty asm so that the per-fragment
+  // M(kk): PV(kk-1) with the K fragments of sub-block kk loaded behind it,
+  // then QK(kk) with the V^T fragments of kk loaded behind it: each load
+  // reuses the registers of the fragment the MFMA before it read and has a
+  // whole MFMA chain to land.  Sub-blocks the wave skips go through the
+  // same code (their P is zero and their scores are not used).  Returns the
+  // scaled row max of S(kk).
+  auto seg_m = [&](int kk, const Item& ic, f32x16& s) __attribute__((always_inline)) {
+    // the lane parts pass through an empty asm so that the per-fragment
     // addresses are recomputed here (one VALU each) rather than all held in
-    // registers across the loop.
+    // registers across the loop
     uint32_t kl = klane, vl = vlane;
     asm volatile("" : "+v"(kl), "+v"(vl));
-    // PV(kk-1) with the K fragments of sub-block kk loaded behind it, then
-    // QK(kk) with the V^T fragments of sub-block kk loaded behind it: each
-    // load reuses the registers of the fragment the MFMA before it read, and
-    // has a whole MFMA chain to land.
-    // Sub-blocks the wave skips go through the same code (their P is zero
-    // and their scores are not used).
     bf16x8 kf[KSTEP];
 #pragma unroll
     for (int i = 0; i < KSTEP; ++i) {
@@ -406,7 +407,7 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
       load_k1(kl, kk, i, kf[i]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    f32x16 s = zero16();
+    s = zero16();
 #pragma unroll
     for (int i = 0; i < KSTEP; ++i) {
       s = mfma32(kf[i], qf[i], s);
@@ -414,37 +415,58 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
       load_v1(vl, kk, i, vf[i >> 1][i & 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (m_c && act_c) mask32(s, t, j0_of(kk), h, lo_c, hi_c);
-    const float mx = row_max32(s, c);
-    ring_barrier();
-    if (kk == K) break;
-
-    // ================= X(kk): softmax segment
-    if (kk - 1 == kL) {
-      // PV(kL) is in, P(kL+1) not yet: every student sub-block and nothing
-      // else -- write the student output
+    if (ic.act && ic.masked) mask32(s, t, j0_of(kk), h, ic.lo, ic.hi);
+    return row_max32(s, c);
+  };
+  // X(kk): the student output right after PV(kL) (P(kL+1) is not in yet),
+  // then the softmax of S(kk)
+  auto seg_x = [&](int kk, const Item& ic, const f32x16& s, float mx) __attribute__((always_inline)) {
+    if (kk - 1 == kL)
       store_out<NB>(o_s, lse_s, out_bf16, row_ok, obase, li, st, acc, h);
-    }
-    if (act_c) {
+    if (ic.act) {
       softmax_p<NB>(s, mx, c, st, acc, p0, p1);
     } else {
 #pragma unroll
       for (int v = 0; v < 8; ++v) p0[v] = p1[v] = (__bf16)0.f;
     }
-    if (issuer) {
-      if ((kk & 1) == 0 && kk >= 2) {
-        const int i = kk / 2 - 1 + NBUF;       // the slot of tile i - NBUF is free
-        if (i < NT) issue(i);
-      } else if (kk & 1) {
-        const int i = (kk + 1) / 2;            // tile read first by M(kk + 1)
-        if (i < NT) wait_vm_tiles<LPT>(min(i + NBUF - 2, NT - 1) - i);
-      }
-    }
-    // this wave's LDS reads of the ring are complete before the barrier
-    // after which a slot may be refilled
+  };
+
+  if (!issuer) ring_barrier();                 // group 1 runs one segment behind
+  // tile it holds sub-blocks 2 it (newer half) and 2 it + 1
+#pragma unroll 1
+  for (int it = 0; it < NT; ++it) {
+    const int k0 = 2 * it, k1 = k0 + 1;
+    const Item i0 = bd.item(j0_of(k0)), i1 = bd.item(j0_of(k1));
+    f32x16 s;
+    float mx = seg_m(k0, i0, s);
+    ring_barrier();
+    seg_x(k0, i0, s, mx);
+    // the slot of tile it - 1 is free (every wave's reads of it completed
+    // before the last barrier): refill it with tile it - 1 + NBUF
+    if (issuer && it >= 1 && it - 1 + NBUF < NT) issue(it - 1 + NBUF);
     lds_wait_all();
     ring_barrier();
-    kind_p = kind_c;
+    mx = seg_m(k1, i1, s);
+    ring_barrier();
+    seg_x(k1, i1, s, mx);
+    // tile it + 1 is read first by the next M: wait for it (the tiles
+    // issued after it may stay in flight, except near the end)
+    if (issuer && it + 1 < NT) {
+      if (it + NBUF - 1 < NT)
+        wait_vm<(NBUF - 2) * LPT>();
+      else
+        wait_vm<0>();
+    }
+    lds_wait_all();
+    ring_barrier();
+  }
+  {
+    // M(K): the PV of the last sub-block
+    Item none;
+    none.act = false;
+    f32x16 s;
+    seg_m(K, none, s);
+    ring_barrier();
   }
   if (issuer) ring_barrier();                  // group 0's extra barrier
   if (kL == K - 1) {
