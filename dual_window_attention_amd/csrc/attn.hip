@@ -394,6 +394,9 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   // same code (their P is zero and their scores are not used).  Returns the
   // scaled row max of S(kk).
   auto seg_m = [&](int kk, const Item& ic, f32x16& s) __attribute__((always_inline)) {
+    // while this wave feeds the matrix cores it takes the issue slots first;
+    // the other wave of the SIMD runs its softmax in the gaps
+    __builtin_amdgcn_s_setprio(2);
     // the lane parts pass through an empty asm so that the per-fragment
     // addresses are recomputed here (one VALU each) rather than all held in
     // registers across the loop
@@ -415,6 +418,7 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
       load_v1(vl, kk, i, vf[i >> 1][i & 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
     if (ic.act && ic.masked) mask32(s, t, j0_of(kk), h, ic.lo, ic.hi);
     return row_max32(s, c);
   };
