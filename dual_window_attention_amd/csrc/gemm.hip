@@ -7,6 +7,9 @@
 #include <algorithm>
 #include <cstdlib>
 
+#include <mutex>
+#include <vector>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -105,7 +108,12 @@ TTCD_DEV void mainloop(Tile& t, const bf16_t* A, long lda, long m0, long mlim,
   }
 }
 
-TTCD_DEV float silu(float a) { return a / (1.f + __expf(-a)); }
+// silu(a) = a / (1 + e^-a) with the hardware reciprocal (about 1 ulp)
+// rather than the correctly rounded division sequence; e^-a -> inf for very
+// negative a gives rcp = 0 and silu = -0
+TTCD_DEV float silu(float a) {
+  return a * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * a));
+}
 
 template <typename OutT>
 __global__ void __launch_bounds__(NT, 2)
@@ -315,20 +323,19 @@ TTCD_DEV void issue(char* dst, const RowPtr& row_ptr, long k0, int wave, int lan
   }
 }
 
-// stages still in flight after the one waited for
-template <int NST>
+// stages still in flight after the one waited for (0 or 1)
 TTCD_DEV void wait_pending(int pending) {
-  if (NST > 2 && pending >= 2)
-    wait_vm<2 * LPW>();
-  else if (pending >= 1)
+  if (pending >= 1)
     wait_vm<LPW>();
   else
     wait_vm<0>();
 }
 
-// NST-stage ring: 2 stages (48 KB) let three workgroups share a CU, 3 stages
-// (72 KB) two.
-template <typename OutT, int NST>
+// 2-stage ring (48 KB): three workgroups share a CU.  (A 3-stage ring with
+// two workgroups per CU and register double buffering of the fragments
+// measured no faster.)
+constexpr int NST = 2;
+template <typename OutT, int EPI>
 __global__ void __launch_bounds__(NTH, 2)
 gemm_nt_big(GemmArgs g) {
   extern __shared__ __align__(16) char lds[];
@@ -338,7 +345,7 @@ gemm_nt_big(GemmArgs g) {
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5, r = lane & 31;
   const int z = blockIdx.z;
-  const bool swiglu = g.epi == EPI_SWIGLU;
+  constexpr bool swiglu = EPI == EPI_SWIGLU;
   const int ncols = swiglu ? BN / 2 : BN;                   // output columns per tile
   const int ntn = (g.N + ncols - 1) / ncols;
   const int ntm = (g.M + BM - 1) / BM;
@@ -385,34 +392,41 @@ gemm_nt_big(GemmArgs g) {
   const int nk = g.K / BK;
   const int npro = nk < NST - 1 ? nk : NST - 1;
   for (int kt = 0; kt < npro; ++kt) fetch(kt);
-  wait_pending<NST>(npro - 1);
+  wait_pending(npro - 1);
   barrier();
+  // MFMA operand fragments of k-step ks (16 wide) of the stage at as
+  auto ldfrag = [&](const char* as, int ks, bf16x8* af, bf16x8* bfr) __attribute__((always_inline)) {
+    const char* bs = as + AB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 128 * wm + 32 * i + r;
+      af[i] = as_bf16x8(ld16(as + row * (BK * 2) + (((2 * ks + h) ^ swz(row)) << 4)));
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = 64 * wn + 32 * j + r;
+      bfr[j] = as_bf16x8(ld16(bs + row * (BK * 2) + (((2 * ks + h) ^ swz(row)) << 4)));
+    }
+  };
+  auto mma = [&](const bf16x8* af, const bf16x8* bfr) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+  };
   for (int kt = 0; kt < nk; ++kt) {
     // the buffer refilled here held stage kt-1, finished before the last barrier
     if (kt + NST - 1 < nk) fetch(kt + NST - 1);
     const char* as = lds + (kt % NST) * STAGE;
-    const char* bs = as + AB;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       bf16x8 af[4], bfr[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 128 * wm + 32 * i + r;
-        af[i] = as_bf16x8(ld16(as + row * (BK * 2) + (((2 * ks + h) ^ swz(row)) << 4)));
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int row = 64 * wn + 32 * j + r;
-        bfr[j] = as_bf16x8(ld16(bs + row * (BK * 2) + (((2 * ks + h) ^ swz(row)) << 4)));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+      ldfrag(as, ks, af, bfr);
+      mma(af, bfr);
     }
     // stage kt+1 must have landed; later ones may still be in flight
     const int last = kt + NST - 1 < nk ? kt + NST - 1 : nk - 1;
-    wait_pending<NST>(last - (kt + 1));
+    wait_pending(last - (kt + 1));
     barrier();
   }
 
@@ -420,18 +434,48 @@ gemm_nt_big(GemmArgs g) {
   // the last barrier): one 32-row block row of the wave's tile at a time is
   // written as the MFMA layout leaves it and read back row-major, so each
   // lane stores 16 bytes of consecutive columns and loads the residual the
-  // same way.
+  // same way.  Tiles fully inside C skip the per-element bounds checks.
   OutT* C = (OutT*)g.C + z * g.sC;
   float* slab = reinterpret_cast<float*>(lds) + wave * (32 * EPS);
-  const int ocols = swiglu ? 32 : 64;                 // output columns of the wave
-  const int per_row = ocols / 4;                      // 4-column pieces per row
+  constexpr int ocols = swiglu ? 32 : 64;             // output columns of the wave
+  constexpr int per_row = ocols / 4;                  // 4-column pieces per row
+  constexpr int npieces = 32 * per_row;               // per 32-row block
   const long nw0 = swiglu ? n0 + 32 * wn : n0 + 64 * wn;
+  const bool full_tile = m0 + BM - 1 <= mmax && n0 + ncols - 1 <= nmax;
+  const float* res = (const float*)g.res;
+  const bf16_t* resb = (const bf16_t*)g.res;
+  const bool res_bf16 = g.res_dt == BF16;
+  const float* cscale = g.colscale ? g.colscale + z * g.sScale : nullptr;
+  auto finish = [&](long m, long n, f32x4 val) __attribute__((always_inline)) {
+    if constexpr (EPI == EPI_RESIDUAL) {
+      const long rm = (m % g.res_rows) * g.ldr + n + z * g.sRes;
+      if (res_bf16) {
+        const uint2 u = *reinterpret_cast<const uint2*>(resb + rm);
+        val[0] += __uint_as_float(u.x << 16);
+        val[1] += __uint_as_float(u.x & 0xFFFF0000u);
+        val[2] += __uint_as_float(u.y << 16);
+        val[3] += __uint_as_float(u.y & 0xFFFF0000u);
+      } else {
+        const f32x4 f = *reinterpret_cast<const f32x4*>(res + rm);
+        val += f;
+      }
+    } else if constexpr (EPI == EPI_STORE) {
+      if (cscale) val *= *reinterpret_cast<const f32x4*>(cscale + n);
+    }
+    OutT* cp = C + m * g.ldc + n;
+    if constexpr (sizeof(OutT) == 4) {
+      *reinterpret_cast<f32x4*>(cp) = val;
+    } else {
+      *reinterpret_cast<uint2*>(cp) =
+          uint2{pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
+    }
+  };
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int row = 8 * (v >> 2) + 4 * h + (v & 3);
-      if (swiglu) {
+      if constexpr (swiglu) {
         slab[row * EPS + r] = silu(acc[i][0][v]) * acc[i][1][v];
       } else {
         slab[row * EPS + r] = acc[i][0][v];
@@ -440,52 +484,37 @@ gemm_nt_big(GemmArgs g) {
     }
     lds_wave_sync();
     const long mb = m0 + 128 * wm + 32 * i;
+    if (full_tile) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int idx = lane + 64 * t;
-      if (idx < 32 * per_row) {
+      for (int t = 0; t < npieces / 64; ++t) {
+        const int idx = lane + 64 * t;
+        const int rr = idx / per_row, c4 = 4 * (idx % per_row);
+        finish(mb + rr, nw0 + c4, *reinterpret_cast<const f32x4*>(slab + rr * EPS + c4));
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < npieces / 64; ++t) {
+        const int idx = lane + 64 * t;
         const int rr = idx / per_row, c4 = 4 * (idx % per_row);
         const long m = mb + rr, n = nw0 + c4;
-        if (m <= mmax && n <= nmax) {
-          f32x4 val = *reinterpret_cast<const f32x4*>(slab + rr * EPS + c4);
-          const bool full = n + 3 <= nmax;
-          if (g.epi == EPI_RESIDUAL) {
-            const long rm = (m % g.res_rows) * g.ldr + n + z * g.sRes;
-            float rv[4];
-            if (full && g.res_dt == BF16) {
-              const uint2 u = *reinterpret_cast<const uint2*>((const bf16_t*)g.res + rm);
-              rv[0] = __uint_as_float(u.x << 16); rv[1] = __uint_as_float(u.x & 0xFFFF0000u);
-              rv[2] = __uint_as_float(u.y << 16); rv[3] = __uint_as_float(u.y & 0xFFFF0000u);
-            } else if (full) {
-              const f32x4 f = *reinterpret_cast<const f32x4*>((const float*)g.res + rm);
-              rv[0] = f[0]; rv[1] = f[1]; rv[2] = f[2]; rv[3] = f[3];
-            } else {
+        if (m > mmax || n > nmax) continue;
+        f32x4 val = *reinterpret_cast<const f32x4*>(slab + rr * EPS + c4);
+        if (n + 3 <= nmax) {
+          finish(m, n, val);
+          continue;
+        }
+        // ragged right edge: element by element
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                rv[e] = n + e > nmax ? 0.f
-                        : g.res_dt == BF16 ? bf2f(((const bf16_t*)g.res)[rm + e])
-                                           : ((const float*)g.res)[rm + e];
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) val[e] += rv[e];
-          } else if (g.epi == EPI_STORE && g.colscale) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (n + e <= nmax) val[e] *= g.colscale[z * g.sScale + n + e];
+        for (int e = 0; e < 4; ++e) {
+          if (n + e > nmax) break;
+          float x = val[e];
+          if constexpr (EPI == EPI_RESIDUAL) {
+            const long rm = (m % g.res_rows) * g.ldr + n + e + z * g.sRes;
+            x += res_bf16 ? bf2f(resb[rm]) : res[rm];
+          } else if constexpr (EPI == EPI_STORE) {
+            if (cscale) x *= cscale[n + e];
           }
-          OutT* cp = C + m * g.ldc + n;
-          if (full) {
-            if constexpr (sizeof(OutT) == 4) {
-              *reinterpret_cast<f32x4*>(cp) = val;
-            } else {
-              *reinterpret_cast<uint2*>(cp) =
-                  uint2{pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (n + e <= nmax) stf(cp + e, val[e]);
-          }
+          stf(C + m * g.ldc + n + e, x);
         }
       }
     }
@@ -606,21 +635,37 @@ bool mfma_ok(const GemmArgs& g) {
 
 }  // namespace
 
-// Ring depth of the 256 x 128 kernel: 2 stages (three workgroups per CU,
-// measured faster on the 64K layer) unless TTCD_GEMM_STAGES=3 asks for the
-// 3-stage ring (two workgroups per CU).
-int gemm_stage_choice() {
-  static const int v = [] {
-    const char* e = getenv("TTCD_GEMM_STAGES");
-    return e && atoi(e) == 3 ? 3 : 2;
-  }();
-  return v;
-}
-
 size_t gemm_skinny_ws_floats(int M, int N, int K, int epi) {
   const int ncols = epi == EPI_SWIGLU ? 2 * N : N;
   return (size_t)skinny::ksplit_for(N, K, epi) * M * ncols;
 }
+
+namespace {
+template <typename OutT>
+const void* big_kernel_epi(int epi) {
+  switch (epi) {
+    case EPI_STORE: return (const void*)big::gemm_nt_big<OutT, EPI_STORE>;
+    case EPI_RESIDUAL: return (const void*)big::gemm_nt_big<OutT, EPI_RESIDUAL>;
+    case EPI_SWIGLU: return (const void*)big::gemm_nt_big<OutT, EPI_SWIGLU>;
+    default: return nullptr;
+  }
+}
+const void* big_kernel(bool out_bf16, int epi) {
+  return out_bf16 ? big_kernel_epi<bf16_t>(epi) : big_kernel_epi<float>(epi);
+}
+// the dynamic LDS limit of each kernel is raised once, on its first launch
+hipError_t big_attr(const void* kern) {
+  static std::mutex mu;
+  static std::vector<const void*> done;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const void* k : done)
+    if (k == kern) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)big::lds_bytes(big::NST));
+  if (e == hipSuccess) done.push_back(kern);
+  return e;
+}
+}  // namespace
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
@@ -644,28 +689,16 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
     return hipGetLastError();
   }
   if (big_ok(g)) {
-    const int nst = gemm_stage_choice();
-    const void* kf = nst == 2 ? (const void*)big::gemm_nt_big<float, 2>
-                              : (const void*)big::gemm_nt_big<float, 3>;
-    const void* kb = nst == 2 ? (const void*)big::gemm_nt_big<bf16_t, 2>
-                              : (const void*)big::gemm_nt_big<bf16_t, 3>;
-    const size_t lds = big::lds_bytes(nst);
-    static hipError_t a[4] = {
-        hipFuncSetAttribute((const void*)big::gemm_nt_big<float, 2>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)big::lds_bytes(2)),
-        hipFuncSetAttribute((const void*)big::gemm_nt_big<float, 3>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)big::lds_bytes(3)),
-        hipFuncSetAttribute((const void*)big::gemm_nt_big<bf16_t, 2>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)big::lds_bytes(2)),
-        hipFuncSetAttribute((const void*)big::gemm_nt_big<bf16_t, 3>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)big::lds_bytes(3))};
-    for (hipError_t e : a)
-      if (e != hipSuccess) return e;
+    const size_t lds = big::lds_bytes(big::NST);
+    const void* kern = big_kernel(g.out_dt == BF16, g.epi);
+    if (!kern) return hipErrorInvalidValue;
+    const hipError_t e = big_attr(kern);
+    if (e != hipSuccess) return e;
     const int ncols = g.epi == EPI_SWIGLU ? big::BN / 2 : big::BN;
     const unsigned tiles = (unsigned)(((g.M + big::BM - 1) / big::BM) * ((g.N + ncols - 1) / ncols));
     dim3 grid(tiles, 1, nb);
     void* args[] = {(void*)&g};
-    return hipLaunchKernel(g.out_dt == BF16 ? kb : kf, grid, dim3(big::NTH), args, lds, s);
+    return hipLaunchKernel(kern, grid, dim3(big::NTH), args, lds, s);
   }
   if (mfma_ok(g)) {
     static bool attr = false;
