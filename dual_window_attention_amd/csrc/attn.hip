@@ -89,27 +89,22 @@ TTCD_DEV void store_out(void* o, float* lse, int out_bf16, bool row_ok, size_t o
   const float inv = 1.f / l;
   if (!row_ok) return;
   // lane (r, h) holds dims 32 bb + 8 g4 + 4 h + e of its row
-  if (out_bf16) {
-    bf16_t* op = reinterpret_cast<bf16_t*>(o) + obase + 4 * h;
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb)
+  for (int bb = 0; bb < NB; ++bb) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x16& a = acc[bb];
-        *reinterpret_cast<u32x2*>(op + 32 * bb + 8 * g4) =
-            u32x2{pack_bf16x2(a[4 * g4] * inv, a[4 * g4 + 1] * inv),
-                  pack_bf16x2(a[4 * g4 + 2] * inv, a[4 * g4 + 3] * inv)};
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = 32 * bb + 8 * g4 + 4 * h;
+      float ov[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ov[e] = acc[bb][4 * g4 + e] * inv;
+      if (out_bf16) {
+        *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(o) + obase + d) =
+            u32x2{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
+      } else {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(o) + obase + d) =
+            f32x4{ov[0], ov[1], ov[2], ov[3]};
       }
-  } else {
-    float* op = reinterpret_cast<float*>(o) + obase + 4 * h;
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x16& a = acc[bb];
-        *reinterpret_cast<f32x4*>(op + 32 * bb + 8 * g4) =
-            f32x4{a[4 * g4] * inv, a[4 * g4 + 1] * inv, a[4 * g4 + 2] * inv, a[4 * g4 + 3] * inv};
-      }
+    }
   }
   if (h == 0 && lse) lse[li] = (st.m + fast_log2(l)) * LN2;
 }
@@ -196,18 +191,23 @@ TTCD_DEV void softmax_p(const f32x16& s, float mx, float c, SoftState& st, f32x1
     st.m = mnew;
   }
   const float negm = st.m == NEG_INF ? 0.f : -st.m;
+  // in place, stage by stage: every element keeps its own register, so the
+  // sixteen fma -> exp chains stay independent
+  f32x16 x = s;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) x[v] = __builtin_fmaf(x[v], c, negm);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) x[v] = fast_exp2(x[v]);
   float la = 0.f, lb = 0.f;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const float e = fast_exp2(__builtin_fmaf(s[v], c, negm));
-    if (v & 1)
-      lb += e;
-    else
-      la += e;
-    if (v < 8)
-      p0[v] = (__bf16)e;
-    else
-      p1[v - 8] = (__bf16)e;
+  for (int v = 0; v < 16; v += 2) {
+    la += x[v];
+    lb += x[v + 1];
+  }
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    p0[v] = (__bf16)x[v];
+    p1[v] = (__bf16)x[v + 8];
   }
   st.l += la + lb;
 }
