@@ -127,8 +127,9 @@ TTCD_DEV void store_out(void* o, float* lse, int out_bf16, bool row_ok, size_t o
 //
 // Tile ring (NBUF slots of 64 keys), filled by group 0: tile i is read in
 // M(2i) and M(2i+1); group 0 waits for it at the end of X(2i-1) and issues
-// tile i+NBUF into its slot in X(2i+2), after every wave's reads of tile i
-// have completed.
+// tile i+NBUF into its slot in M(2i+3), between its two MFMA chains, after
+// every wave's reads of tile i have completed (each wave drains its LDS
+// reads at the end of every X segment).
 // --------------------------------------------------------------------------
 template <int D>
 struct MfmaCfg {
@@ -393,7 +394,7 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   // whole MFMA chain to land.  Sub-blocks the wave skips go through the
   // same code (their P is zero and their scores are not used).  Returns the
   // scaled row max of S(kk).
-  auto seg_m = [&](int kk, const Item& ic, f32x16& s) __attribute__((always_inline)) {
+  auto seg_m = [&](int kk, const Item& ic, f32x16& s, int fill) __attribute__((always_inline)) {
     // while this wave feeds the matrix cores it takes the issue slots first;
     // the other wave of the SIMD runs its softmax in the gaps
     __builtin_amdgcn_s_setprio(2);
@@ -410,6 +411,9 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
       load_k1(kl, kk, i, kf[i]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // group 0 refills a ring slot here, between the two MFMA chains
+    if (fill >= 0) issue(fill);
+    __builtin_amdgcn_sched_barrier(0);
     s = zero16();
 #pragma unroll
     for (int i = 0; i < KSTEP; ++i) {
@@ -442,15 +446,15 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
     const int k0 = 2 * it, k1 = k0 + 1;
     const Item i0 = bd.item(j0_of(k0)), i1 = bd.item(j0_of(k1));
     f32x16 s;
-    float mx = seg_m(k0, i0, s);
+    float mx = seg_m(k0, i0, s, -1);
     ring_barrier();
     seg_x(k0, i0, s, mx);
-    // the slot of tile it - 1 is free (every wave's reads of it completed
-    // before the last barrier): refill it with tile it - 1 + NBUF
-    if (issuer && it >= 1 && it - 1 + NBUF < NT) issue(it - 1 + NBUF);
     lds_wait_all();
     ring_barrier();
-    mx = seg_m(k1, i1, s);
+    // every wave's reads of tile it - 1 completed before the last barrier:
+    // group 0 refills its slot with tile it - 1 + NBUF
+    const int fill = issuer && it >= 1 && it - 1 + NBUF < NT ? it - 1 + NBUF : -1;
+    mx = seg_m(k1, i1, s, fill);
     ring_barrier();
     seg_x(k1, i1, s, mx);
     // tile it + 1 is read first by the next M: wait for it (the tiles
@@ -469,7 +473,7 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
     Item none;
     none.act = false;
     f32x16 s;
-    seg_m(K, none, s);
+    seg_m(K, none, s, -1);
     ring_barrier();
   }
   if (issuer) ring_barrier();                  // group 0's extra barrier
