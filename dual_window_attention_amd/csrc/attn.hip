@@ -115,8 +115,9 @@ TTCD_DEV void store_out(void* o, float* lse, int out_bf16, bool row_ok, size_t o
 // segments, every one ended by a workgroup barrier:
 //   M(k): PV of sub-block k-1 with the K fragments of sub-block k loaded
 //         behind it, then S(k) = K(k) Q^T with the V^T fragments of k loaded
-//         behind it, then the mask and row max of S(k);
-//   X(k): the lazy rescale and P(k) = 2^(S(k) c - m) on the vector ALU.
+//         behind it;
+//   X(k): the mask and row max of S(k), the lazy rescale and
+//         P(k) = 2^(S(k) c - m) on the vector ALU.
 // Group 1 runs one segment behind group 0 (it passes one extra barrier at
 // the start, group 0 one at the end), so on each SIMD one wave feeds the
 // matrix cores while the other runs a softmax.
@@ -392,9 +393,8 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   // then QK(kk) with the V^T fragments of kk loaded behind it: each load
   // reuses the registers of the fragment the MFMA before it read and has a
   // whole MFMA chain to land.  Sub-blocks the wave skips go through the
-  // same code (their P is zero and their scores are not used).  Returns the
-  // scaled row max of S(kk).
-  auto seg_m = [&](int kk, const Item& ic, f32x16& s, int fill) __attribute__((always_inline)) {
+  // same code (their P is zero and their scores are not used).
+  auto seg_m = [&](int kk, f32x16& s, int fill) __attribute__((always_inline)) {
     // while this wave feeds the matrix cores it takes the issue slots first;
     // the other wave of the SIMD runs its softmax in the gaps
     __builtin_amdgcn_s_setprio(2);
@@ -423,16 +423,16 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
-    if (ic.act && ic.masked) mask32(s, t, j0_of(kk), h, ic.lo, ic.hi);
-    return row_max32(s, c);
   };
   // X(kk): the student output right after PV(kL) (P(kL+1) is not in yet),
-  // then the softmax of S(kk)
-  auto seg_x = [&](int kk, const Item& ic, const f32x16& s, float mx) __attribute__((always_inline)) {
+  // then the mask, row max and softmax of S(kk) (here rather than at the
+  // end of M, whose last MFMA result they would wait for)
+  auto seg_x = [&](int kk, const Item& ic, f32x16& s) __attribute__((always_inline)) {
     if (kk - 1 == kL)
       store_out<NB>(o_s, lse_s, out_bf16, row_ok, obase, li, st, acc, h);
     if (ic.act) {
-      softmax_p<NB>(s, mx, c, st, acc, p0, p1);
+      if (ic.masked) mask32(s, t, j0_of(kk), h, ic.lo, ic.hi);
+      softmax_p<NB>(s, row_max32(s, c), c, st, acc, p0, p1);
     } else {
 #pragma unroll
       for (int v = 0; v < 8; ++v) p0[v] = p1[v] = (__bf16)0.f;
@@ -446,17 +446,17 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
     const int k0 = 2 * it, k1 = k0 + 1;
     const Item i0 = bd.item(j0_of(k0)), i1 = bd.item(j0_of(k1));
     f32x16 s;
-    float mx = seg_m(k0, i0, s, -1);
+    seg_m(k0, s, -1);
     ring_barrier();
-    seg_x(k0, i0, s, mx);
+    seg_x(k0, i0, s);
     lds_wait_all();
     ring_barrier();
     // every wave's reads of tile it - 1 completed before the last barrier:
     // group 0 refills its slot with tile it - 1 + NBUF
     const int fill = issuer && it >= 1 && it - 1 + NBUF < NT ? it - 1 + NBUF : -1;
-    mx = seg_m(k1, i1, s, fill);
+    seg_m(k1, s, fill);
     ring_barrier();
-    seg_x(k1, i1, s, mx);
+    seg_x(k1, i1, s);
     // tile it + 1 is read first by the next M: wait for it (the tiles
     // issued after it may stay in flight, except near the end)
     if (issuer && it + 1 < NT) {
@@ -470,10 +470,8 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   }
   {
     // M(K): the PV of the last sub-block
-    Item none;
-    none.act = false;
     f32x16 s;
-    seg_m(K, none, s, -1);
+    seg_m(K, s, -1);
     ring_barrier();
   }
   if (issuer) ring_barrier();                  // group 0's extra barrier
