@@ -44,11 +44,23 @@ constexpr float NEG_INF = -__builtin_inff();
 constexpr float LN2 = 0.69314718055994530942f;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4_t;
+
+// 16-byte LDS read at a byte address.  The MFMA kernel has no static LDS, so
+// its dynamic LDS starts at address 0 and an offset into it is the address.
+TTCD_DEV u32x4 lds16(uint32_t addr) { return *reinterpret_cast<lds_u32x4_t*>((size_t)addr); }
 
 // 16 bytes per lane, global -> LDS; lane i lands at lds_wave_base + 16 i.
+// Written as inline asm rather than the compiler builtin: the compiler counts
+// a builtin LDS DMA as an outstanding LDS operation of unknown order, and
+// then waits for every LDS read of a chain (lgkmcnt 0) before the first MFMA
+// that needs only the oldest.  The hardware counts the DMA in vmcnt alone,
+// and the kernel orders it explicitly (wait_vm before the publishing barrier).
+// M0 takes the LDS address (bound as an operand, so the compiler writes it);
+// one wait state separates that write from the DMA.
 TTCD_DEV void g2l16(const void* src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds_wave_base, 16, 0, 0);
+  const uint32_t m = (uint32_t)(size_t)(lds_void_t*)lds_wave_base;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(m) : "memory");
 }
 
 // Workgroup barrier that does not drain this wave's in-flight tile fetches
@@ -76,8 +88,11 @@ struct Tile {
 };
 
 struct SoftState {
-  float m;   // running max (log2 domain, scaled)
-  float l;   // this lane's partial denominator
+  float m;      // running max (log2 domain, scaled)
+  float l;      // this lane's partial denominator
+  float negm;   // -m, or 0 while m = -inf (the exponent offset)
+  float thr;    // 2^TAU, or -1 while m = -inf: a sub-block sum above it
+                // raises m (lazy rescale)
 };
 
 template <int NB>
@@ -158,14 +173,18 @@ TTCD_DEV void wait_vm_tiles(int ntiles) {
     wait_vm<0>();
 }
 
-// row max of one 32-key sub-block (raw scores times c > 0)
-TTCD_DEV float row_max32(const f32x16& s, float c) {
+// row max of the raw scores of one 32-key sub-block
+TTCD_DEV float row_max32(const f32x16& s) {
   float mx = NEG_INF;
 #pragma unroll
   for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[v]);
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                    false, false);
-  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+  // the two halves' maxima; a plain v_max_f32 (fmaxf would first quiet
+  // both operands, which come back from the swap as integers)
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(sw[0]), "v"(sw[1]));
+  return r;
 }
 
 // keys with lo <= t - j < hi keep their score, the others become -inf
@@ -178,40 +197,51 @@ TTCD_DEV void mask32(f32x16& s, int t, int j0, int h, int lo, int hi) {
   }
 }
 
-// lazy rescale against the sub-block max, then P = 2^(s c - m) in bf16 and
-// its fp32 sum into the denominator
+// 2^(s c + negm) of this lane's 16 scores, stage by stage (sixteen
+// independent fma -> exp chains), and their fp32 sum
+TTCD_DEV float exp_sum16(const f32x16& s, float c, float negm, f32x16& x) {
+#pragma unroll
+  for (int v = 0; v < 16; ++v) x[v] = __builtin_fmaf(s[v], c, negm);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) x[v] = fast_exp2(x[v]);
+  float la = x[0], lb = x[1];
+#pragma unroll
+  for (int v = 2; v < 16; v += 2) {
+    la += x[v];
+    lb += x[v + 1];
+  }
+  return la + lb;
+}
+
+// P = 2^(s c - m) in bf16 and its fp32 sum into the denominator, against the
+// running max m as it stands.  The rescale is lazy and needs no row max in
+// the common case: only when some lane's sum exceeds 2^TAU (then one of its
+// terms exceeds 2^TAU / 16, or overflowed), or the lane has no finite max
+// yet, does the wave raise m to the sub-block's row max, rescale its
+// accumulators and recompute the terms.  Every term used is therefore at
+// most 2^TAU.
 template <int NB>
-TTCD_DEV void softmax_p(const f32x16& s, float mx, float c, SoftState& st, f32x16* acc,
-                        bf16x8& p0, bf16x8& p1) {
-  const bool need = mx > st.m + TAU;
-  if (__builtin_expect(__any(need), 0)) {
-    const float mnew = need ? mx : st.m;
+TTCD_DEV void softmax_p(const f32x16& s, float c, SoftState& st, f32x16* acc, bf16x8& p0,
+                        bf16x8& p1) {
+  f32x16 x;
+  float sum = exp_sum16(s, c, st.negm, x);
+  if (__builtin_expect(__any(sum > st.thr), 0)) {
+    const float mnew = fmaxf(st.m, row_max32(s) * c);
     const float alpha = (st.m == NEG_INF) ? 0.f : fast_exp2(st.m - mnew);
     st.l *= alpha;
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[b] *= alpha;
     st.m = mnew;
-  }
-  const float negm = st.m == NEG_INF ? 0.f : -st.m;
-  // in place, stage by stage: every element keeps its own register, so the
-  // sixteen fma -> exp chains stay independent
-  f32x16 x = s;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) x[v] = __builtin_fmaf(x[v], c, negm);
-#pragma unroll
-  for (int v = 0; v < 16; ++v) x[v] = fast_exp2(x[v]);
-  float la = 0.f, lb = 0.f;
-#pragma unroll
-  for (int v = 0; v < 16; v += 2) {
-    la += x[v];
-    lb += x[v + 1];
+    st.negm = mnew == NEG_INF ? 0.f : -mnew;
+    st.thr = mnew == NEG_INF ? -1.f : __builtin_exp2f(TAU);
+    sum = exp_sum16(s, c, st.negm, x);
   }
 #pragma unroll
   for (int v = 0; v < 8; ++v) {
     p0[v] = (__bf16)x[v];
     p1[v] = (__bf16)x[v + 8];
   }
-  st.l += la + lb;
+  st.l += sum;
 }
 
 // How this wave takes the sub-block of 32 keys starting at j0 in the walk:
@@ -302,7 +332,7 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   f32x16 acc[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) acc[i] = zero16();
-  SoftState st = {NEG_INF, 0.f};
+  SoftState st = {NEG_INF, 0.f, 0.f, -1.f};
 
   const bf16_t* kbase = k + ((size_t)b * kv_rows * Hkv + g) * D;
   const size_t kstride = (size_t)Hkv * D;
@@ -324,17 +354,24 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   //   K, sub-block x, k-step i:  ring(x) + 32 sb(x) CPR 16 + (klane ^ 32 i)
   //   V^T, MFMA i of PV:         ring(x) + KPOS 16 + 4096 (i/2)
   //                              + (vlane ^ (64 sb(x) + 32 (i%2)))
+  // For K the bases are multiples of the 32-row block (KSB bytes, a power of
+  // two) and klane stays below it; for V^T the bases are multiples of 4 KB
+  // and vlane stays below that.  So the XOR can follow the add: one add per
+  // segment and one XOR per fragment.
   const uint32_t klane = (uint32_t)(r32 * (TL::CPR * 16) + ((h ^ TL::kswz(r32)) << 4));
   const uint32_t vlane = (uint32_t)(r32 * (BN * 2) + ((h ^ TL::vswz(r32)) << 4));
   auto ring = [&](int x) { return (uint32_t)(((x >> 1) % NBUF) * TL::BYTES); };
   auto sbit = [&](int x) { return (x & 1) ? 0 : 1; };
-  auto load_k1 = [&](uint32_t kl, int x, int i, bf16x8& dst) {
-    const uint32_t base = ring(x) + (uint32_t)(sbit(x) * 32 * TL::CPR * 16);
-    dst = as_bf16x8(ld16(lds + base + (kl ^ (uint32_t)(32 * i))));
+  constexpr int KSB = 32 * TL::CPR * 16;
+  static_assert((KSB & (KSB - 1)) == 0 && TL::BYTES % KSB == 0 && 32 * KSTEP <= KSB &&
+                (TL::KPOS * 16) % 4096 == 0 && 32 * BN * 2 <= 4096, "fragment address layout");
+  auto kseg = [&](uint32_t kl, int x) { return kl + ring(x) + (uint32_t)(sbit(x) * KSB); };
+  auto vseg = [&](uint32_t vl, int x) { return vl + ring(x) + (uint32_t)(TL::KPOS * 16); };
+  auto load_k1 = [&](uint32_t kb, int i, bf16x8& dst) {
+    dst = as_bf16x8(lds16(kb ^ (uint32_t)(32 * i)));
   };
-  auto load_v1 = [&](uint32_t vl, int x, int i, bf16x8& dst) {
-    const uint32_t base = ring(x) + (uint32_t)(TL::KPOS * 16 + 4096 * (i >> 1));
-    dst = as_bf16x8(ld16(lds + base + (vl ^ (uint32_t)(64 * sbit(x) + 32 * (i & 1)))));
+  auto load_v1 = [&](uint32_t vb, int x, int i, bf16x8& dst) {
+    dst = as_bf16x8(lds16((vb ^ (uint32_t)(64 * sbit(x) + 32 * (i & 1))) + 4096 * (i >> 1)));
   };
 
   // Tile fetch by the four group-0 waves, 16 bytes per lane straight into
@@ -398,17 +435,13 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
     // while this wave feeds the matrix cores it takes the issue slots first;
     // the other wave of the SIMD runs its softmax in the gaps
     __builtin_amdgcn_s_setprio(2);
-    // the lane parts pass through an empty asm so that the per-fragment
-    // addresses are recomputed here (one VALU each) rather than all held in
-    // registers across the loop
-    uint32_t kl = klane, vl = vlane;
-    asm volatile("" : "+v"(kl), "+v"(vl));
+    const uint32_t kb = kseg(klane, kk), vb = vseg(vlane, kk);
     bf16x8 kf[KSTEP];
 #pragma unroll
     for (int i = 0; i < KSTEP; ++i) {
       acc[i >> 1] = mfma32(vf[i >> 1][i & 1], (i & 1) ? p1 : p0, acc[i >> 1]);
       __builtin_amdgcn_sched_barrier(0);
-      load_k1(kl, kk, i, kf[i]);
+      load_k1(kb, i, kf[i]);
       __builtin_amdgcn_sched_barrier(0);
     }
     // group 0 refills a ring slot here, between the two MFMA chains
@@ -419,7 +452,7 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
     for (int i = 0; i < KSTEP; ++i) {
       s = mfma32(kf[i], qf[i], s);
       __builtin_amdgcn_sched_barrier(0);
-      load_v1(vl, kk, i, vf[i >> 1][i & 1]);
+      load_v1(vb, kk, i, vf[i >> 1][i & 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
@@ -432,7 +465,7 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
       store_out<NB>(o_s, lse_s, out_bf16, row_ok, obase, li, st, acc, h);
     if (ic.act) {
       if (ic.masked) mask32(s, t, j0_of(kk), h, ic.lo, ic.hi);
-      softmax_p<NB>(s, row_max32(s, c), c, st, acc, p0, p1);
+      softmax_p<NB>(s, c, st, acc, p0, p1);
     } else {
 #pragma unroll
       for (int v = 0; v < 8; ++v) p0[v] = p1[v] = (__bf16)0.f;
@@ -504,8 +537,7 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
 #pragma unroll
       for (int i = 0; i < KSTEP; ++i) s = mfma32(kf[i], qf[i], s);
       mask32(s, t, j0, h, wS, wT);
-      const float mx = row_max32(s, c);
-      softmax_p<NB>(s, mx, c, st, acc, p0, p1);
+      softmax_p<NB>(s, c, st, acc, p0, p1);
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb) {
         acc[bb] = mfma32(vf[bb][0], p0, acc[bb]);
