@@ -62,6 +62,13 @@ TTCD_DEV void g2l16(const void* src, void* lds_wave_base) {
   const uint32_t m = (uint32_t)(size_t)(lds_void_t*)lds_wave_base;
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(m) : "memory");
 }
+// The same from a wave-uniform base (scalar registers) plus a per-lane byte
+// offset, so that only scalar arithmetic moves the source from load to load.
+TTCD_DEV void g2l16s(const void* sbase, uint32_t voff, void* lds_wave_base) {
+  const uint32_t m = (uint32_t)(size_t)(lds_void_t*)lds_wave_base;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase), "{m0}"(m)
+               : "memory");
+}
 
 // Workgroup barrier that does not drain this wave's in-flight tile fetches
 // (a fenced barrier would wait for every outstanding memory operation).  LDS
@@ -131,8 +138,8 @@ TTCD_DEV void store_out(void* o, float* lse, int out_bf16, bool row_ok, size_t o
 //   M(k): PV of sub-block k-1 with the K fragments of sub-block k loaded
 //         behind it, then S(k) = K(k) Q^T with the V^T fragments of k loaded
 //         behind it;
-//   X(k): the mask and row max of S(k), the lazy rescale and
-//         P(k) = 2^(S(k) c - m) on the vector ALU.
+//   X(k): the mask of S(k), P(k) = 2^(S(k) c - m) and its sum on the
+//         vector ALU, with the lazy rescale.
 // Group 1 runs one segment behind group 0 (it passes one extra barrier at
 // the start, group 0 one at the end), so on each SIMD one wave feeds the
 // matrix cores while the other runs a softmax.
@@ -141,11 +148,14 @@ TTCD_DEV void store_out(void* o, float* lse, int out_bf16, bool row_ok, size_t o
 // at the w_S edge are walked with the student mask only; their far part is
 // added after the walk, from global memory, once the student output is out.
 //
-// Tile ring (NBUF slots of 64 keys), filled by group 0: tile i is read in
-// M(2i) and M(2i+1); group 0 waits for it at the end of X(2i-1) and issues
-// tile i+NBUF into its slot in M(2i+3), between its two MFMA chains, after
-// every wave's reads of tile i have completed (each wave drains its LDS
-// reads at the end of every X segment).
+// Tile ring (NBUF slots of 64 keys): group 0 fetches the K part of every
+// tile, group 1 the V^T part.  Tile i is read in M(2i) and M(2i+1).  Each
+// group issues its part of tile i+NBUF into the slot of tile i in its
+// M(2i+3), between the two MFMA chains, after every wave's reads of tile i
+// have completed (each wave drains its LDS reads at the end of every X
+// segment), and waits for its part of tile i before the barrier that
+// publishes it: group 0 at the end of X(2i-1), group 1 (one segment
+// behind) at the end of its M(2i-1).
 // --------------------------------------------------------------------------
 template <int D>
 struct MfmaCfg {
@@ -154,8 +164,9 @@ struct MfmaCfg {
   static constexpr int NW = 8;
   static constexpr int ROWS = 32 * NW;
   static constexpr int NBUF = 4;
-  static constexpr int ISSUERS = 4;
-  static constexpr int LPT = (Tile<D>::KPOS + Tile<D>::VPOS) / (64 * ISSUERS);
+  static constexpr int ISSUERS = 4;     // waves per group; group 0 fetches K, group 1 V^T
+  static constexpr int LPT = Tile<D>::KPOS / (64 * ISSUERS);   // loads per wave per tile
+  static_assert(Tile<D>::KPOS == Tile<D>::VPOS, "K and V^T parts of a tile are equal");
 };
 
 TTCD_DEV void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
@@ -374,49 +385,50 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
     dst = as_bf16x8(lds16((vb ^ (uint32_t)(64 * sbit(x) + 32 * (i & 1))) + 4096 * (i >> 1)));
   };
 
-  // Tile fetch by the four group-0 waves, 16 bytes per lane straight into
-  // LDS.  For K, load i of a wave covers rows (i*4 + wave) * 64/CPR + lane/CPR
-  // and its swizzled chunk does not depend on i; for V^T, dims
-  // (i*4 + wave) * 8 + lane/8.  Only the newest tile can reach past the last
-  // key; its rows are clamped there (they are masked).
-  constexpr int KLD = TL::KPOS / (64 * CF::ISSUERS), VLD = TL::VPOS / (64 * CF::ISSUERS);
+  // Tile fetch, 16 bytes per lane straight into LDS, by the four waves of a
+  // group (w = wave % 4).  For K, load u of a wave covers rows
+  // (u*4 + w) * 64/CPR + lane/CPR and its swizzled chunk does not depend on
+  // u; for V^T, dims (u*4 + w) * 8 + lane/8.  Only the newest tile can reach
+  // past the last key; its rows are clamped there (they are masked).
   constexpr int KRPL = 64 / TL::CPR;          // K rows per load instruction
-  const int wv4 = issuer ? wave : 0;
+  const int wv4 = wave & 3;
   const int krow_l = wv4 * KRPL + lane / TL::CPR;
   const int kchunk = (lane % TL::CPR) ^ TL::kswz(krow_l);
-  const uint32_t koff_l = (uint32_t)(krow_l * kstride + kchunk * 8);
+  const uint32_t koff_b = (uint32_t)(2 * (krow_l * kstride + kchunk * 8));
   const int vd_l = wv4 * 8 + lane / 8;
-  const uint32_t voff_l = (uint32_t)(vd_l * vt_ld + 8 * ((lane % 8) ^ TL::vswz(vd_l)));
+  const uint32_t voff_b = (uint32_t)(2 * (vd_l * vt_ld + 8 * ((lane % 8) ^ TL::vswz(vd_l))));
+  // group 0 fetches the K part of tile i, group 1 its V^T part
   auto issue = [&](int i) {
     char* buf = lds + (i % NBUF) * TL::BYTES;
     const int j0 = (n_hi - i) * BN;
-    if (j0 + BN - 1 < Tk) {
+    if (issuer) {
+      if (j0 + BN - 1 < Tk) {
+        const char* tb = reinterpret_cast<const char*>(kbase + (size_t)j0 * kstride);
 #pragma unroll
-      for (int u = 0; u < KLD; ++u) {
-        const bf16_t* src = kbase + (size_t)(j0 + u * CF::ISSUERS * KRPL) * kstride;
-        g2l16(src + koff_l, buf + (u * CF::ISSUERS + wv4) * 64 * 16);
+        for (int u = 0; u < LPT; ++u)
+          g2l16s(tb + (size_t)u * CF::ISSUERS * KRPL * kstride * 2, koff_b,
+                 buf + (u * CF::ISSUERS + wv4) * 64 * 16);
+      } else {
+#pragma unroll
+        for (int u = 0; u < LPT; ++u) {
+          const int j = min(j0 + u * CF::ISSUERS * KRPL + krow_l, Tk - 1);
+          g2l16(kbase + (size_t)j * kstride + kchunk * 8, buf + (u * CF::ISSUERS + wv4) * 64 * 16);
+        }
       }
     } else {
+      const char* tb = reinterpret_cast<const char*>(vbase + j0);
+      char* vb = buf + TL::KPOS * 16;
 #pragma unroll
-      for (int u = 0; u < KLD; ++u) {
-        const int j = min(j0 + u * CF::ISSUERS * KRPL + krow_l, Tk - 1);
-        g2l16(kbase + (size_t)j * kstride + kchunk * 8, buf + (u * CF::ISSUERS + wv4) * 64 * 16);
-      }
-    }
-    char* vb = buf + TL::KPOS * 16;
-#pragma unroll
-    for (int u = 0; u < VLD; ++u) {
-      const bf16_t* src = vbase + (size_t)(u * CF::ISSUERS * 8) * vt_ld + j0;
-      g2l16(src + voff_l, vb + (u * CF::ISSUERS + wv4) * 64 * 16);
+      for (int u = 0; u < LPT; ++u)
+        g2l16s(tb + (size_t)u * CF::ISSUERS * 8 * vt_ld * 2, voff_b,
+               vb + (u * CF::ISSUERS + wv4) * 64 * 16);
     }
   };
 
   // ---- prologue: tiles 0 .. NBUF-1 in flight, tile 0 visible
   const int npro = min(NBUF, NT);
-  if (issuer) {
-    for (int i = 0; i < npro; ++i) issue(i);
-    wait_vm_tiles<LPT>(npro - 1);
-  }
+  for (int i = 0; i < npro; ++i) issue(i);
+  wait_vm_tiles<LPT>(npro - 1);
   ring_barrier();
 
   bf16x8 vf[NB][2];        // V^T fragments of the sub-block whose PV comes next
@@ -444,7 +456,8 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
       load_k1(kb, i, kf[i]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // group 0 refills a ring slot here, between the two MFMA chains
+    // each group refills its part of a ring slot here, between the two
+    // MFMA chains
     if (fill >= 0) issue(fill);
     __builtin_amdgcn_sched_barrier(0);
     s = zero16();
@@ -485,13 +498,21 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
     lds_wait_all();
     ring_barrier();
     // every wave's reads of tile it - 1 completed before the last barrier:
-    // group 0 refills its slot with tile it - 1 + NBUF
-    const int fill = issuer && it >= 1 && it - 1 + NBUF < NT ? it - 1 + NBUF : -1;
+    // each group refills its part of the slot with tile it - 1 + NBUF
+    const int fill = it >= 1 && it - 1 + NBUF < NT ? it - 1 + NBUF : -1;
     seg_m(k1, s, fill);
+    // group 1 runs one segment behind, so the barrier after its M(k1) is the
+    // one that publishes tile it + 1: its V^T part must have landed
+    if (!issuer && it + 1 < NT) {
+      if (it + NBUF - 1 < NT)
+        wait_vm<(NBUF - 2) * LPT>();
+      else
+        wait_vm<0>();
+    }
     ring_barrier();
     seg_x(k1, i1, s);
-    // tile it + 1 is read first by the next M: wait for it (the tiles
-    // issued after it may stay in flight, except near the end)
+    // tile it + 1 is read first by the next M: group 0 waits for its K part
+    // (the tiles issued after it may stay in flight, except near the end)
     if (issuer && it + 1 < NT) {
       if (it + NBUF - 1 < NT)
         wait_vm<(NBUF - 2) * LPT>();
