@@ -24,8 +24,11 @@ TTCD_DEV bf16_t f2bf(float f) {
   return __builtin_bit_cast(bf16_t, h);
 }
 
+// two values in one packed conversion (v_cvt_pk_bf16_f32), lo in bits 0..15
 TTCD_DEV uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){lo, hi}, bf16x2v));
 }
 
 template <typename T> struct elem;

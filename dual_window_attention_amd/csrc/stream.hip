@@ -8,6 +8,8 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <type_traits>
+
 namespace ttcd {
 
 namespace {
@@ -90,62 +92,95 @@ fw_stream2_kernel(const T* __restrict__ zt, const T* __restrict__ zs,
   const bool fok = c0 < f;                 // f % 8 == 0: all 8 or none
   const size_t zoff = (size_t)b * T_ * f;
 
-  // taps of the 8 features: conv[c][k] is contiguous over (c, k)
-  uint32_t wt[WW], ws[WW];
-  uint32_t xt[KC + 3][RW], xs[KC + 3][RW];
-  constexpr int nrow = KC + 3;
-  if (fok) {
+  constexpr int DW = RW;                   // raw words per token row of 8 features
+  float ssq[4] = {0.f, 0.f, 0.f, 0.f};
+  // Interior tiles (whole feature tile, every halo row and token inside the
+  // sequence) take a path with no per-lane bounds logic.
+  const bool interior = (ft + 1) * S2_FF <= f && t0 >= KC - 1 && t0 + S2_TT <= T_;
+  auto body = [&](auto interior_tag) __attribute__((always_inline)) {
+    constexpr bool IN = decltype(interior_tag)::value;
+    // taps of the 8 features: conv[c][k] is contiguous over (c, k)
+    uint32_t wt[WW], ws[WW];
+    uint32_t xt[KC + 3][RW], xs[KC + 3][RW];
+    if (IN || fok) {
 #pragma unroll
-    for (int v = 0; v < WW / 4; ++v) {
-      const u32x4 a = ld16(conv_t + (size_t)c0 * kc + v * (16 / sizeof(T)));
-      const u32x4 c = ld16(conv_s + (size_t)c0 * kc + v * (16 / sizeof(T)));
+      for (int v = 0; v < WW / 4; ++v) {
+        const u32x4 a = ld16(conv_t + (size_t)c0 * kc + v * (16 / sizeof(T)));
+        const u32x4 c = ld16(conv_s + (size_t)c0 * kc + v * (16 / sizeof(T)));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) { wt[4 * v + j] = a[j]; ws[4 * v + j] = c[j]; }
-    }
+        for (int j = 0; j < 4; ++j) { wt[4 * v + j] = a[j]; ws[4 * v + j] = c[j]; }
+      }
 #pragma unroll
-    for (int rr = 0; rr < nrow; ++rr) {
-      const int tt = tf - (kc - 1) + rr;
-      const bool in = tt >= 0 && tt < T_;
+      for (int rr = 0; rr < KC + 3; ++rr) {
+        const int tt = tf - (kc - 1) + rr;
+        const bool in = IN || (tt >= 0 && tt < T_);
 #pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
-        if (in) {
-          a = ld16(zt + zoff + (size_t)tt * f + c0 + v * VN);
-          c = ld16(zs + zoff + (size_t)tt * f + c0 + v * VN);
+        for (int v = 0; v < NV; ++v) {
+          u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+          if (in) {
+            a = ld16(zt + zoff + (size_t)tt * f + c0 + v * VN);
+            c = ld16(zs + zoff + (size_t)tt * f + c0 + v * VN);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) { xt[rr][4 * v + j] = a[j]; xs[rr][4 * v + j] = c[j]; }
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) { xt[rr][4 * v + j] = a[j]; xs[rr][4 * v + j] = c[j]; }
       }
     }
-  }
-  float ssq[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = tf + i;
-    float dv[8];
-    float sq = 0.f;
+    // Feature by feature: each tap weight and input element is unpacked to
+    // fp32 once and serves all four tokens; dw holds the output rows in the
+    // storage type's raw words (bf16 pairs packed once both halves are in).
+    uint32_t dw[4][DW];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float at = 0.f, as = 0.f;
-      if (fok) {
+      float w_t[KC], w_s[KC], x_t[KC + 3], x_s[KC + 3];
 #pragma unroll
-        for (int k = 0; k < kc; ++k) {
-          at = __builtin_fmaf(raw_el<T>(wt, e * KC + k), raw_el<T>(xt[i + k], e), at);
-          as = __builtin_fmaf(raw_el<T>(ws, e * KC + k), raw_el<T>(xs[i + k], e), as);
+      for (int k = 0; k < KC; ++k) {
+        w_t[k] = raw_el<T>(wt, e * KC + k);
+        w_s[k] = raw_el<T>(ws, e * KC + k);
+      }
+#pragma unroll
+      for (int rr = 0; rr < KC + 3; ++rr) {
+        x_t[rr] = raw_el<T>(xt[rr], e);
+        x_s[rr] = raw_el<T>(xs[rr], e);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float at = 0.f, as = 0.f;
+#pragma unroll
+        for (int k = 0; k < KC; ++k) {
+          at = __builtin_fmaf(w_t[k], x_t[i + k], at);
+          as = __builtin_fmaf(w_s[k], x_s[i + k], as);
+        }
+        if (!IN && (!fok || tf + i >= T_)) at = as = 0.f;
+        const float dv = at - as;
+        zb[fc * 8 + e][4 * tg + i] = as;
+        ssq[i] = __builtin_fmaf(as, as, ssq[i]);
+        if constexpr (sizeof(T) == 2) {
+          if (e & 1)
+            dw[i][e >> 1] = pack_bf16x2(__uint_as_float(dw[i][e >> 1]), dv);
+          else
+            dw[i][e >> 1] = __float_as_uint(dv);
+        } else {
+          dw[i][e] = __float_as_uint(dv);
         }
       }
-      if (t >= T_) at = as = 0.f;
-      dv[e] = at - as;
-      zb[fc * 8 + e][4 * tg + i] = as;
-      sq = __builtin_fmaf(as, as, sq);
     }
-    ssq[i] = sq;
-    if (fok && t < Tpad) {
-      T* dp = dbar + ((size_t)b * Tpad + t) * f + c0;
 #pragma unroll
-      for (int v = 0; v < NV; ++v) Vec16<T>::store(dp + v * VN, dv + v * VN);
+    for (int i = 0; i < 4; ++i) {
+      const int t = tf + i;
+      if (IN || (fok && t < Tpad)) {
+        T* dp = dbar + ((size_t)b * Tpad + t) * f + c0;
+#pragma unroll
+        for (int v = 0; v < DW / 4; ++v)
+          st16(dp + v * (16 / sizeof(T)),
+               u32x4{dw[i][4 * v], dw[i][4 * v + 1], dw[i][4 * v + 2], dw[i][4 * v + 3]});
+      }
     }
-  }
+  };
+  if (interior)
+    body(std::true_type{});
+  else
+    body(std::false_type{});
   // partial l2 norms of this feature tile: reduce over the 16 feature chunks
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -173,18 +208,28 @@ fw_stream2_kernel(const T* __restrict__ zt, const T* __restrict__ zs,
   }
 }
 
-// sc[b, t] = beta[b, t / chunk] / max(sqrt(sum of the partial norms), eps)
-__global__ void __launch_bounds__(256)
+// sc[b, t] = beta[b, t / chunk] / max(sqrt(sum of the partial norms), eps).
+// One token per lane; the partials are loaded eight at a time (all in
+// flight together) and added in feature-tile order.
+__global__ void __launch_bounds__(64)
 fw_key_scale_kernel(const float* __restrict__ part, const float* __restrict__ beta,
                     float* __restrict__ sc, int nft, int T_, int Tpad, int chunk, int nchunks,
                     float eps) {
   const int b = blockIdx.y;
-  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int t = blockIdx.x * 64 + threadIdx.x;
   if (t >= Tpad) return;
   float v = 0.f;
   if (t < T_) {
     float ss = 0.f;
-    for (int y = 0; y < nft; ++y) ss += part[((size_t)b * nft + y) * Tpad + t];
+    const float* pp = part + (size_t)b * nft * Tpad + t;
+    for (int y0 = 0; y0 < nft; y0 += 8) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = y0 + j < nft ? pp[(size_t)(y0 + j) * Tpad] : 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (y0 + j < nft) ss += x[j];
+    }
     const int ci = min(t / chunk, nchunks - 1);
     v = beta[(size_t)b * nchunks + ci] / fmaxf(sqrtf(ss), eps);
   }
@@ -362,7 +407,7 @@ hipError_t launch_fw_stream(const StreamArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fw_key_scale_kernel, dim3(Tpad / 256 + 1, a.B), dim3(256), 0, s, a.part,
+  hipLaunchKernelGGL(fw_key_scale_kernel, dim3(Tpad / 64, a.B), dim3(64), 0, s, a.part,
                      a.beta, a.sc, nft, a.T, Tpad, a.chunk, a.nchunks, a.eps);
   return hipGetLastError();
 }
