@@ -8,6 +8,7 @@
 #include <cstdlib>
 
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 #include "common.hpp"
@@ -446,80 +447,97 @@ gemm_nt_big(GemmArgs g) {
   const bf16_t* resb = (const bf16_t*)g.res;
   const bool res_bf16 = g.res_dt == BF16;
   const float* cscale = g.colscale ? g.colscale + z * g.sScale : nullptr;
-  auto finish = [&](long m, long n, f32x4 val) __attribute__((always_inline)) {
-    if constexpr (EPI == EPI_RESIDUAL) {
-      const long rm = (m % g.res_rows) * g.ldr + n + z * g.sRes;
-      if (res_bf16) {
-        const uint2 u = *reinterpret_cast<const uint2*>(resb + rm);
-        val[0] += __uint_as_float(u.x << 16);
-        val[1] += __uint_as_float(u.x & 0xFFFF0000u);
-        val[2] += __uint_as_float(u.y << 16);
-        val[3] += __uint_as_float(u.y & 0xFFFF0000u);
-      } else {
-        const f32x4 f = *reinterpret_cast<const f32x4*>(res + rm);
-        val += f;
+  // The residual row of output row m needs a 64-bit remainder only when the
+  // residual has fewer rows than C; the epilogue is compiled twice and the
+  // wave takes the copy without it otherwise (every call in the layer passes
+  // one residual row per output row).
+  auto epilogue = [&](auto wrap_tag) __attribute__((always_inline)) {
+    constexpr bool WRAP = decltype(wrap_tag)::value;
+    auto res_row = [&](long m) __attribute__((always_inline)) {
+      if constexpr (WRAP)
+        return m % g.res_rows;
+      else
+        return m;
+    };
+    auto finish = [&](long m, long n, f32x4 val) __attribute__((always_inline)) {
+      if constexpr (EPI == EPI_RESIDUAL) {
+        const long rm = res_row(m) * g.ldr + n + z * g.sRes;
+        if (res_bf16) {
+          const uint2 u = *reinterpret_cast<const uint2*>(resb + rm);
+          val[0] += __uint_as_float(u.x << 16);
+          val[1] += __uint_as_float(u.x & 0xFFFF0000u);
+          val[2] += __uint_as_float(u.y << 16);
+          val[3] += __uint_as_float(u.y & 0xFFFF0000u);
+        } else {
+          const f32x4 f = *reinterpret_cast<const f32x4*>(res + rm);
+          val += f;
+        }
+      } else if constexpr (EPI == EPI_STORE) {
+        if (cscale) val *= *reinterpret_cast<const f32x4*>(cscale + n);
       }
-    } else if constexpr (EPI == EPI_STORE) {
-      if (cscale) val *= *reinterpret_cast<const f32x4*>(cscale + n);
-    }
-    OutT* cp = C + m * g.ldc + n;
-    if constexpr (sizeof(OutT) == 4) {
-      *reinterpret_cast<f32x4*>(cp) = val;
-    } else {
-      *reinterpret_cast<uint2*>(cp) =
-          uint2{pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
+      OutT* cp = C + m * g.ldc + n;
+      if constexpr (sizeof(OutT) == 4) {
+        *reinterpret_cast<f32x4*>(cp) = val;
+      } else {
+        *reinterpret_cast<uint2*>(cp) =
+            uint2{pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
+      }
+    };
+  #pragma unroll
+    for (int i = 0; i < 4; ++i) {
+  #pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = 8 * (v >> 2) + 4 * h + (v & 3);
+        if constexpr (swiglu) {
+          slab[row * EPS + r] = silu(acc[i][0][v]) * acc[i][1][v];
+        } else {
+          slab[row * EPS + r] = acc[i][0][v];
+          slab[row * EPS + 32 + r] = acc[i][1][v];
+        }
+      }
+      lds_wave_sync();
+      const long mb = m0 + 128 * wm + 32 * i;
+      if (full_tile) {
+  #pragma unroll
+        for (int t = 0; t < npieces / 64; ++t) {
+          const int idx = lane + 64 * t;
+          const int rr = idx / per_row, c4 = 4 * (idx % per_row);
+          finish(mb + rr, nw0 + c4, *reinterpret_cast<const f32x4*>(slab + rr * EPS + c4));
+        }
+      } else {
+  #pragma unroll
+        for (int t = 0; t < npieces / 64; ++t) {
+          const int idx = lane + 64 * t;
+          const int rr = idx / per_row, c4 = 4 * (idx % per_row);
+          const long m = mb + rr, n = nw0 + c4;
+          if (m > mmax || n > nmax) continue;
+          f32x4 val = *reinterpret_cast<const f32x4*>(slab + rr * EPS + c4);
+          if (n + 3 <= nmax) {
+            finish(m, n, val);
+            continue;
+          }
+          // ragged right edge: element by element
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (n + e > nmax) break;
+            float x = val[e];
+            if constexpr (EPI == EPI_RESIDUAL) {
+              const long rm = res_row(m) * g.ldr + n + e + z * g.sRes;
+              x += res_bf16 ? bf2f(resb[rm]) : res[rm];
+            } else if constexpr (EPI == EPI_STORE) {
+              if (cscale) x *= cscale[n + e];
+            }
+            stf(C + m * g.ldc + n + e, x);
+          }
+        }
+      }
+      lds_wave_sync();
     }
   };
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = 8 * (v >> 2) + 4 * h + (v & 3);
-      if constexpr (swiglu) {
-        slab[row * EPS + r] = silu(acc[i][0][v]) * acc[i][1][v];
-      } else {
-        slab[row * EPS + r] = acc[i][0][v];
-        slab[row * EPS + 32 + r] = acc[i][1][v];
-      }
-    }
-    lds_wave_sync();
-    const long mb = m0 + 128 * wm + 32 * i;
-    if (full_tile) {
-#pragma unroll
-      for (int t = 0; t < npieces / 64; ++t) {
-        const int idx = lane + 64 * t;
-        const int rr = idx / per_row, c4 = 4 * (idx % per_row);
-        finish(mb + rr, nw0 + c4, *reinterpret_cast<const f32x4*>(slab + rr * EPS + c4));
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < npieces / 64; ++t) {
-        const int idx = lane + 64 * t;
-        const int rr = idx / per_row, c4 = 4 * (idx % per_row);
-        const long m = mb + rr, n = nw0 + c4;
-        if (m > mmax || n > nmax) continue;
-        f32x4 val = *reinterpret_cast<const f32x4*>(slab + rr * EPS + c4);
-        if (n + 3 <= nmax) {
-          finish(m, n, val);
-          continue;
-        }
-        // ragged right edge: element by element
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (n + e > nmax) break;
-          float x = val[e];
-          if constexpr (EPI == EPI_RESIDUAL) {
-            const long rm = (m % g.res_rows) * g.ldr + n + e + z * g.sRes;
-            x += res_bf16 ? bf2f(resb[rm]) : res[rm];
-          } else if constexpr (EPI == EPI_STORE) {
-            if (cscale) x *= cscale[n + e];
-          }
-          stf(C + m * g.ldc + n + e, x);
-        }
-      }
-    }
-    lds_wave_sync();
-  }
+  if (EPI == EPI_RESIDUAL && g.res_rows < g.M)
+    epilogue(std::true_type{});
+  else
+    epilogue(std::false_type{});
 }
 }  // namespace big
 
