@@ -291,6 +291,13 @@ def main():
                                                        workspace=aws), n_att, stream)
     flops = attention_flops(cfg, cfg.w_teacher)
     achieved = flops / (att_ms * 1e-3) / 1e12
+    # the same outputs through the LSE-combination path (student call,
+    # shifted far-band call, exact merge), for the fused-versus-split figure
+    sws = torch.empty(max(256, ttcd.lib().ttcd_dual_window_attn_lse_split_workspace_size(
+        ttcd.attn_desc(q, k, cfg.w_teacher, cfg.w_student))), dtype=torch.uint8, device=dev)
+    split_ms = time_events(lambda: ttcd.dual_window_attn_lse_split(
+        q, k, v, cfg.w_teacher, cfg.w_student, with_lse=False, out=(o_t, o_s), workspace=sws),
+        n_att, stream)
 
     res = {
         "metric": "IP-TTCD layer fwd tokens/s at 64K ctx; % bf16 MFMA peak (attn), % HBM BW (scan)",
@@ -314,8 +321,12 @@ def main():
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic("attention"),
                      "ms_per_launch": att_ms, "algorithmic_tflop": flops / 1e12},
+        "lse_split": {"kernel": "LSE-combination path (ttcd_dual_window_attn_lse_split)",
+                      "ms_per_launch": split_ms, "achieved": flops / (split_ms * 1e-3) / 1e12,
+                      "unit": "TFLOP/s", "fused_ms_per_launch": att_ms,
+                      "fused_saving": 1.0 - att_ms / split_ms},
     }
-    del q, k, v, wd, x, out, ws, o_t, o_s, aws
+    del q, k, v, wd, x, out, ws, o_t, o_s, aws, sws
     torch.cuda.empty_cache()
     res["scan"] = scan_roofline(cfg, dev, n_att)
     torch.cuda.empty_cache()

@@ -356,6 +356,59 @@ ttcd_status ttcd_dual_window_attn(const ttcd_attn_desc* d, const void* q, const 
   return ok();
 }
 
+// ---- LSE-combination path
+struct SplitBufs {
+  void* vt = nullptr;
+  float* o_far = nullptr;
+  float* lse_far = nullptr;
+  float* lse_tmp = nullptr;
+};
+
+void plan_split(const ttcd_attn_desc* d, Plan& p, SplitBufs& b) {
+  b.vt = p.take(attn_vt_bytes(d->batch, d->n_kv_heads, d->head_dim, d->seq_k, d->in_dtype));
+  const size_t rows = (size_t)d->batch * d->seq_q * d->n_q_heads;
+  b.o_far = (float*)p.take(rows * d->head_dim * sizeof(float));
+  b.lse_far = (float*)p.take(rows * sizeof(float));
+  b.lse_tmp = (float*)p.take(rows * sizeof(float));
+}
+
+size_t ttcd_dual_window_attn_lse_split_workspace_size(const ttcd_attn_desc* d) {
+  if (check_attn(d) != TTCD_OK) return 0;
+  Plan p(nullptr);
+  SplitBufs b;
+  plan_split(d, p, b);
+  return p.off;
+}
+
+ttcd_status ttcd_dual_window_attn_lse_split(const ttcd_attn_desc* d, const void* q, const void* k,
+                                            const void* v, void* o_t, void* o_s, float* lse_t,
+                                            float* lse_s, void* ws, size_t ws_bytes,
+                                            void* stream) {
+  ttcd_status st = check_attn(d);
+  if (st != TTCD_OK) return st;
+  REQ_PTR(q); REQ_PTR(k); REQ_PTR(v); REQ_PTR(o_t); REQ_PTR(o_s);
+  OPT_PTR4(lse_t); OPT_PTR4(lse_s);
+  if (o_t == o_s) return fail(TTCD_ERR_BAD_SHAPE, "o_teacher and o_student must not alias");
+  const size_t need = ttcd_dual_window_attn_lse_split_workspace_size(d);
+  if (ws_bytes < need)
+    return fail(TTCD_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (!ws) return fail(TTCD_ERR_NULL_POINTER, "workspace is NULL");
+  OPT_PTR(ws);
+  Plan p(ws);
+  SplitBufs b;
+  plan_split(d, p, b);
+  AttnArgs a{};
+  a.q = q; a.k = k; a.v = v; a.vt = b.vt; a.vt_ld = pad64(d->seq_k);
+  a.o_t = o_t; a.o_s = o_s; a.lse_t = lse_t; a.lse_s = lse_s;
+  a.B = d->batch; a.Tq = d->seq_q; a.Tk = d->seq_k; a.kv_rows = d->kv_rows ? d->kv_rows : d->seq_k;
+  a.q_pos0 = d->q_pos0; a.Hq = d->n_q_heads; a.Hkv = d->n_kv_heads; a.D = d->head_dim;
+  a.wT = d->w_teacher; a.wS = d->w_student; a.scale = attn_scale(d); a.in_dt = d->in_dtype;
+  a.out_dt = d->out_dtype;
+  HIPCHK(launch_dual_window_attn_lse_split(a, b.o_far, b.lse_far, b.lse_tmp,
+                                           (hipStream_t)stream));
+  return ok();
+}
+
 size_t ttcd_fastweight_scan_workspace_size(const ttcd_fw_desc* d) {
   if (check_fw(d) != TTCD_OK) return 0;
   Plan p(nullptr);

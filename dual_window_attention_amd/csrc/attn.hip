@@ -102,33 +102,38 @@ struct SoftState {
                 // raises m (lazy rescale)
 };
 
+// O = acc / l and LSE = ln 2 (m + log2 l) of the lane's row; o or lse may be
+// NULL (not wanted).  A row that saw no key (possible only for the shifted
+// band of the LSE-combination path) gets O = 0 and LSE = -inf.
 template <int NB>
 TTCD_DEV void store_out(void* o, float* lse, int out_bf16, bool row_ok, size_t obase, size_t li,
                         const SoftState& st, const f32x16* acc, int h) {
   const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.l), __float_as_uint(st.l),
                                                    false, false);
   const float l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-  const float inv = 1.f / l;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
   if (!row_ok) return;
-  // lane (r, h) holds dims 32 bb + 8 g4 + 4 h + e of its row
+  if (o) {
+    // lane (r, h) holds dims 32 bb + 8 g4 + 4 h + e of its row
 #pragma unroll
-  for (int bb = 0; bb < NB; ++bb) {
+    for (int bb = 0; bb < NB; ++bb) {
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d = 32 * bb + 8 * g4 + 4 * h;
-      float ov[4];
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = 32 * bb + 8 * g4 + 4 * h;
+        float ov[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ov[e] = acc[bb][4 * g4 + e] * inv;
-      if (out_bf16) {
-        *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(o) + obase + d) =
-            u32x2{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
-      } else {
-        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(o) + obase + d) =
-            f32x4{ov[0], ov[1], ov[2], ov[3]};
+        for (int e = 0; e < 4; ++e) ov[e] = acc[bb][4 * g4 + e] * inv;
+        if (out_bf16) {
+          *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(o) + obase + d) =
+              u32x2{pack_bf16x2(ov[0], ov[1]), pack_bf16x2(ov[2], ov[3])};
+        } else {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(o) + obase + d) =
+              f32x4{ov[0], ov[1], ov[2], ov[3]};
+        }
       }
     }
   }
-  if (h == 0 && lse) lse[li] = (st.m + fast_log2(l)) * LN2;
+  if (h == 0 && lse) lse[li] = l > 0.f ? (st.m + fast_log2(l)) * LN2 : NEG_INF;
 }
 
 // --------------------------------------------------------------------------
@@ -675,19 +680,21 @@ dual_window_attn_simple(const T* __restrict__ q, const T* __restrict__ k,
   const float lT = lS * eS + lF * eF;
   const bool far_empty = lF == 0.f;
   const size_t obase = ((size_t)(b * Tq + qi) * Hq + qh) * D;
+  // o_t or o_s may be NULL (not wanted); a row that saw no key (only in the
+  // shifted band of the LSE-combination path) gets O = 0 and LSE = -inf
   for (int d = 0; d < D; ++d) {
-    const float os = aS[d] / lS;
+    const float os = lS > 0.f ? aS[d] / lS : 0.f;
     const float ot = far_empty ? os : (aS[d] * eS + aF[d] * eF) / lT;
     if (out_bf16) {
-      reinterpret_cast<bf16_t*>(o_s)[obase + d] = f2bf(os);
-      reinterpret_cast<bf16_t*>(o_t)[obase + d] = f2bf(ot);
+      if (o_s) reinterpret_cast<bf16_t*>(o_s)[obase + d] = f2bf(os);
+      if (o_t) reinterpret_cast<bf16_t*>(o_t)[obase + d] = f2bf(ot);
     } else {
-      reinterpret_cast<float*>(o_s)[obase + d] = os;
-      reinterpret_cast<float*>(o_t)[obase + d] = ot;
+      if (o_s) reinterpret_cast<float*>(o_s)[obase + d] = os;
+      if (o_t) reinterpret_cast<float*>(o_t)[obase + d] = ot;
     }
   }
   const size_t li = (size_t)(b * Hq + qh) * Tq + qi;
-  const float lseS = mS + logf(lS);
+  const float lseS = lS > 0.f ? mS + logf(lS) : NEG_INF;
   if (lse_s) lse_s[li] = lseS;
   if (lse_t) lse_t[li] = far_empty ? lseS : mT + logf(lT);
 }
@@ -754,18 +761,22 @@ size_t attn_vt_bytes(int B, int Hkv, int D, int Tk, int in_dt) {
   return (size_t)B * Hkv * D * ld * 2;
 }
 
-hipError_t launch_dual_window_attn(const AttnArgs& a, hipStream_t s) {
-  if (a.in_dt == BF16 && (a.D == 64 || a.D == 128)) {
-    // V^T with the keys every query may read: [max(0, q_pos0 - w_T + 1), Tk)
-    const int jlo_all = a.q_pos0 - a.wT + 1 > 0 ? a.q_pos0 - a.wT + 1 : 0;
-    // grid covers vt_ld (a multiple of 64) keys and D (64 or 128) dims
-    hipLaunchKernelGGL(v_transpose_kernel, dim3(a.vt_ld / 64, a.D / 64, a.B * a.Hkv), dim3(256),
-                       0, s, (const uint16_t*)a.v, (uint16_t*)a.vt, a.Tk, jlo_all, a.kv_rows,
-                       a.Hkv, a.D, a.vt_ld);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return a.D == 64 ? launch_mfma<64>(a, s) : launch_mfma<128>(a, s);
-  }
+namespace {
+
+bool mfma_path(const AttnArgs& a) { return a.in_dt == BF16 && (a.D == 64 || a.D == 128); }
+
+// V^T with the keys every query may read: [max(0, q_pos0 - w_T + 1), Tk)
+hipError_t launch_vt(const AttnArgs& a, hipStream_t s) {
+  const int jlo_all = a.q_pos0 - a.wT + 1 > 0 ? a.q_pos0 - a.wT + 1 : 0;
+  // grid covers vt_ld (a multiple of 64) keys and D (64 or 128) dims
+  hipLaunchKernelGGL(v_transpose_kernel, dim3(a.vt_ld / 64, a.D / 64, a.B * a.Hkv), dim3(256), 0,
+                     s, (const uint16_t*)a.v, (uint16_t*)a.vt, a.Tk, jlo_all, a.kv_rows, a.Hkv,
+                     a.D, a.vt_ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_core(const AttnArgs& a, hipStream_t s) {
+  if (mfma_path(a)) return a.D == 64 ? launch_mfma<64>(a, s) : launch_mfma<128>(a, s);
   if (a.in_dt == F32) {
     if (a.D == 64) return launch_simple<float, 64>(a, s);
     if (a.D == 128) return launch_simple<float, 128>(a, s);
@@ -774,6 +785,114 @@ hipError_t launch_dual_window_attn(const AttnArgs& a, hipStream_t s) {
     if (a.D == 128) return launch_simple<bf16_t, 128>(a, s);
   }
   return hipErrorInvalidValue;
+}
+
+// Teacher output and LSE from the student-window result and the far band
+// (keys with w_S <= t - j < w_T), merged exactly through their log-sum-exps
+// (README "Fused inference kernels", the LSE-combination variant): with
+// L = log(e^LSE_S + e^LSE_far), O_T = e^(LSE_S - L) O_S + e^(LSE_far - L) O_far.
+// lse_far == NULL means the far band is empty for every row (w_T == w_S).
+// One thread per 4 head dims of a (row, head); O is [B, Tq, Hq, D], LSE is
+// [B, Hq, Tq].
+__global__ void __launch_bounds__(256)
+lse_merge_kernel(const void* __restrict__ o_s, const float* __restrict__ o_far,
+                 const float* __restrict__ lse_s, const float* __restrict__ lse_far,
+                 void* __restrict__ o_t, float* __restrict__ lse_t, int Tq, int Hq, int D,
+                 long total4, int out_bf16) {
+  const long i4 = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i4 >= total4) return;
+  const long e0 = 4 * i4;                              // first element of the four
+  const int d = (int)(e0 % D);
+  const long row = e0 / D;                             // (b, qi, qh) flattened
+  const int qh = (int)(row % Hq);
+  const long bq = row / Hq;                            // b * Tq + qi
+  const int qi = (int)(bq % Tq);
+  const long b = bq / Tq;
+  const size_t li = ((size_t)b * Hq + qh) * Tq + qi;
+  const float ls = lse_s[li];
+  const float lf = lse_far ? lse_far[li] : NEG_INF;
+  float os[4];
+  if (out_bf16) {
+    const u32x2 u = *reinterpret_cast<const u32x2*>(reinterpret_cast<const bf16_t*>(o_s) + e0);
+    os[0] = __uint_as_float(u[0] << 16);
+    os[1] = __uint_as_float(u[0] & 0xFFFF0000u);
+    os[2] = __uint_as_float(u[1] << 16);
+    os[3] = __uint_as_float(u[1] & 0xFFFF0000u);
+  } else {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(o_s) + e0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) os[j] = v[j];
+  }
+  float ot[4], lt;
+  if (lf == NEG_INF) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ot[j] = os[j];
+    lt = ls;
+  } else {
+    const f32x4 of = *reinterpret_cast<const f32x4*>(o_far + e0);
+    const float mx = fmaxf(ls, lf);
+    const float ws = expf(ls - mx), wf = expf(lf - mx);
+    const float inv = 1.f / (ws + wf);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ot[j] = (ws * os[j] + wf * of[j]) * inv;
+    lt = mx + logf(ws + wf);
+  }
+  if (out_bf16) {
+    *reinterpret_cast<u32x2*>(reinterpret_cast<bf16_t*>(o_t) + e0) =
+        u32x2{pack_bf16x2(ot[0], ot[1]), pack_bf16x2(ot[2], ot[3])};
+  } else {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(o_t) + e0) = f32x4{ot[0], ot[1], ot[2], ot[3]};
+  }
+  if (lse_t && d == 0) lse_t[li] = lt;
+}
+
+}  // namespace
+
+hipError_t launch_dual_window_attn(const AttnArgs& a, hipStream_t s) {
+  if (mfma_path(a)) {
+    hipError_t e = launch_vt(a, s);
+    if (e != hipSuccess) return e;
+  }
+  return launch_core(a, s);
+}
+
+// The LSE-combination path: a student-window call (w = w_S), a call over
+// the far band (queries shifted back by w_S against a window of w_T - w_S:
+// a query at t then sees exactly the keys with w_S <= t - j < w_T), and the
+// exact merge.  o_far [B,Tq,Hq,D] fp32, lse_far and lse_tmp [B,Hq,Tq] fp32
+// are workspace; lse_tmp holds LSE_S when the caller does not want it.
+hipError_t launch_dual_window_attn_lse_split(const AttnArgs& a, float* o_far, float* lse_far,
+                                             float* lse_tmp, hipStream_t s) {
+  if (mfma_path(a)) {
+    hipError_t e = launch_vt(a, s);
+    if (e != hipSuccess) return e;
+  }
+  float* lse_s = a.lse_s ? a.lse_s : lse_tmp;
+  AttnArgs st = a;
+  st.wT = a.wS;
+  st.o_t = nullptr;
+  st.lse_t = nullptr;
+  st.lse_s = lse_s;
+  hipError_t e = launch_core(st, s);
+  if (e != hipSuccess) return e;
+  const bool far = a.wT > a.wS;
+  if (far) {
+    AttnArgs fa = a;
+    fa.q_pos0 = a.q_pos0 - a.wS;
+    fa.wT = fa.wS = a.wT - a.wS;
+    fa.o_t = o_far;
+    fa.lse_t = lse_far;
+    fa.o_s = nullptr;
+    fa.lse_s = nullptr;
+    fa.out_dt = F32;
+    e = launch_core(fa, s);
+    if (e != hipSuccess) return e;
+  }
+  const long total4 = (long)a.B * a.Tq * a.Hq * a.D / 4;
+  hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)((total4 + 255) / 256)), dim3(256), 0, s,
+                     a.o_s, o_far, lse_s, far ? lse_far : nullptr, a.o_t, a.lse_t, a.Tq, a.Hq,
+                     a.D, total4, a.out_dt == BF16 ? 1 : 0);
+  return hipGetLastError();
 }
 
 }  // namespace ttcd

@@ -28,6 +28,10 @@ struct AttnArgs {
 };
 // Returns hipSuccess or the launch error.
 hipError_t launch_dual_window_attn(const AttnArgs& a, hipStream_t s);
+// The same outputs through the LSE-combination path (student call, shifted
+// far-band call, exact merge); o_far, lse_far, lse_tmp are fp32 workspace.
+hipError_t launch_dual_window_attn_lse_split(const AttnArgs& a, float* o_far, float* lse_far,
+                                             float* lse_tmp, hipStream_t s);
 size_t attn_vt_bytes(int B, int Hkv, int D, int Tk, int in_dt);
 
 // ---------------------------------------------------------------- decode attention

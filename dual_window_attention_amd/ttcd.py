@@ -33,6 +33,7 @@ STATUS = {
 
 EXPORTS = (
     "ttcd_dual_window_attn_workspace_size", "ttcd_dual_window_attn",
+    "ttcd_dual_window_attn_lse_split_workspace_size", "ttcd_dual_window_attn_lse_split",
     "ttcd_fastweight_scan_workspace_size", "ttcd_fastweight_scan",
     "ttcd_fastweight_stream_workspace_size", "ttcd_fastweight_stream",
     "ttcd_layer_forward_workspace_size", "ttcd_layer_forward",
@@ -84,6 +85,9 @@ _sig = {
     "ttcd_dual_window_attn_workspace_size": (_sz, [C.POINTER(AttnDesc)]),
     "ttcd_dual_window_attn": (C.c_int, [C.POINTER(AttnDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _vp, _sz, _vp]),
+    "ttcd_dual_window_attn_lse_split_workspace_size": (_sz, [C.POINTER(AttnDesc)]),
+    "ttcd_dual_window_attn_lse_split": (C.c_int, [C.POINTER(AttnDesc), _vp, _vp, _vp, _vp, _vp,
+                                                  _vp, _vp, _vp, _sz, _vp]),
     "ttcd_fastweight_scan_workspace_size": (_sz, [C.POINTER(FwDesc)]),
     "ttcd_fastweight_scan": (C.c_int, [C.POINTER(FwDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _vp, _vp, _vp, _sz, _vp]),
@@ -202,6 +206,33 @@ def dual_window_attn(q, k, v, w_teacher: int, w_student: int, *, scale=None, q_p
     _check(_lib.ttcd_dual_window_attn(C.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o_t), _ptr(o_s),
                                       _ptr(lse_t), _ptr(lse_s), _ptr(ws), ws.numel(),
                                       _stream(stream)), "ttcd_dual_window_attn")
+    return o_t, o_s, lse_t, lse_s
+
+
+def dual_window_attn_lse_split(q, k, v, w_teacher: int, w_student: int, *, scale=None,
+                               q_pos0: int = 0, seq_k: Optional[int] = None, out_dtype=None,
+                               with_lse: bool = True,
+                               out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+                               workspace: Optional[torch.Tensor] = None, stream=None):
+    """The outputs of ``dual_window_attn`` through the LSE-combination path
+    (student call, shifted far-band call, exact merge)."""
+    d = attn_desc(q, k, w_teacher, w_student, scale, q_pos0, seq_k, out_dtype)
+    odt = _tdt(d.out_dtype)
+    if out is None:
+        o_t = torch.empty(q.shape, dtype=odt, device=q.device)
+        o_s = torch.empty(q.shape, dtype=odt, device=q.device)
+    else:
+        o_t, o_s = out
+    lse_t = lse_s = None
+    if with_lse:
+        lse_t = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
+        lse_s = torch.empty_like(lse_t)
+    need = _lib.ttcd_dual_window_attn_lse_split_workspace_size(C.byref(d))
+    ws = _workspace(need, q.device, workspace)
+    _check(_lib.ttcd_dual_window_attn_lse_split(C.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o_t),
+                                                _ptr(o_s), _ptr(lse_t), _ptr(lse_s), _ptr(ws),
+                                                ws.numel(), _stream(stream)),
+           "ttcd_dual_window_attn_lse_split")
     return o_t, o_s, lse_t, lse_s
 
 

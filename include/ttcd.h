@@ -101,6 +101,30 @@ ttcd_status ttcd_dual_window_attn(const ttcd_attn_desc* desc,
                                   void* stream);
 
 /* ------------------------------------------------------------------------
+ * The same attention through the LSE-combination path (README "Fused
+ * inference kernels", the LSE-combination variant): a student-window call,
+ * a call over the far band w_S <= t - j < w_T (the queries shifted back by
+ * w_S against a window of w_T - w_S), and the exact merge of the two
+ * normalised outputs through their log-sum-exps:
+ *   LSE_T = log(e^LSE_S + e^LSE_far),
+ *   O_T   = e^(LSE_S - LSE_T) O_S + e^(LSE_far - LSE_T) O_far.
+ * Arguments, layouts, requirements and errors are those of
+ * ttcd_dual_window_attn; o_teacher and o_student must not alias.  The
+ * workspace (size from ttcd_dual_window_attn_lse_split_workspace_size, never
+ * zero) holds V^T for bf16 inputs, O_far in fp32 and two LSE rows.  The
+ * outputs equal the fused kernel's up to rounding (O_T here is formed from
+ * O_S as stored in out_dtype).
+ * ---------------------------------------------------------------------- */
+size_t ttcd_dual_window_attn_lse_split_workspace_size(const ttcd_attn_desc* desc);
+
+ttcd_status ttcd_dual_window_attn_lse_split(const ttcd_attn_desc* desc,
+                                            const void* q, const void* k, const void* v,
+                                            void* o_teacher, void* o_student,
+                                            float* lse_teacher, float* lse_student,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* stream);
+
+/* ------------------------------------------------------------------------
  * Chunk-wise fast-weight update of W_down (IP-TTCD, off-policy).
  *
  * From the papernotes.org notes, key design 3 (the practical update, the
