@@ -81,20 +81,22 @@ def scan_bytes(cfg):
 
 
 def time_events(fn, n, stream, warmup=5):
-    """Mean device time of ``fn`` over ``n`` calls, from HIP events recorded
-    on ``stream`` (the stream the library launches on).  The warmup calls
-    bring the clocks back up after host-side set-up left the GPU idle."""
+    """Mean device time of ``fn`` over ``n`` back-to-back calls: one HIP event
+    recorded on ``stream`` (the stream the library launches on) before the
+    first call and one after the last, so the average covers the kernels
+    and the gaps between launches but not an event per call.  The warmup
+    calls bring the clocks back up after host-side set-up left the GPU
+    idle."""
     import torch
     for _ in range(warmup):
         fn()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n)]
-    for e0, e1 in evs:
-        e0.record(stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
         fn()
-        e1.record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
-    return float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    return float(e0.elapsed_time(e1)) / n
 
 
 def scan_roofline(cfg, dev, n):
