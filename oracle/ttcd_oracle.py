@@ -418,3 +418,30 @@ def fold_lists(w_down0, r_list, k_list, beta_list, C: int):
             a, e = j * C, (j + 1) * C
             out[b] += float(beta_list[b, j]) * (r_list[b, a:e].T @ k_list[b, a:e])
     return out
+
+
+def decode_append(z_t, z_s, hist_t, hist_s, conv_t, conv_s, w_down0, w_proj,
+                  eps: float = 1e-12):
+    """The per-token write terms of one generated token ([NOTES] key design
+    3; [PODCAST] Eq. 12), from the new token's SwiGLU outputs of both paths
+    and each path's last kc-1 inputs (the history, oldest first).
+
+    z_t, z_s [B, f]; hist_t, hist_s [B, kc-1, f]; taps [f, kc] with tap kc-1
+    on the new token (the reading of the conv above).  Returns
+    (r [B, d], k [B, f], dbar [B, f], new hist_t, new hist_s):
+        zbar_p = sum_i taps_p[:, i] * window_p[i],  window_p = [hist_p; z_p]
+        dbar   = zbar_T - zbar_S,  r = W_down^(0) (W_proj dbar),
+        k      = zbar_S / max(||zbar_S||, eps)
+    and each history with its oldest row dropped and the token appended.
+    """
+    z_t, z_s = _f64(z_t), _f64(z_s)
+    hist_t, hist_s = _f64(hist_t), _f64(hist_s)
+    taps_t, taps_s = _f64(conv_t), _f64(conv_s)
+    win_t = np.concatenate([hist_t, z_t[:, None, :]], axis=1)      # [B, kc, f]
+    win_s = np.concatenate([hist_s, z_s[:, None, :]], axis=1)
+    zb_t = np.einsum("bif,fi->bf", win_t, taps_t)
+    zb_s = np.einsum("bif,fi->bf", win_s, taps_s)
+    dbar = zb_t - zb_s
+    r = (dbar @ _f64(w_proj).T) @ _f64(w_down0).T
+    k = l2_normalize(zb_s, eps)
+    return r, k, dbar, win_t[:, 1:, :], win_s[:, 1:, :]

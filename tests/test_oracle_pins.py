@@ -422,3 +422,47 @@ def test_decode_equals_prefill_row_and_fold_equals_prefix_state():
                                                   pre["z_t"][b], w["w_down0"], C,
                                                   return_states=True)
         np.testing.assert_allclose(folded[b], states[n], atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("kc", [1, 3, 4])
+def test_decode_append_token_by_token_equals_sequence_terms(kc):
+    """Appending tokens one at a time (window = history + token) gives the
+    write terms of the whole-sequence causal conv at every position, from a
+    zero history at the sequence start and from a history handed over
+    mid-sequence.  A slip in the tap orientation, the window order or the
+    history shift breaks it; one token is also checked by an explicit loop."""
+    rng = np.random.default_rng(31 + kc)
+    B, T, d, f = 2, 13, 5, 7
+    z_t, z_s = rnd(rng, B, T, f), rnd(rng, B, T, f)
+    conv_t, conv_s = rnd(rng, f, kc), rnd(rng, f, kc)
+    w0, wp = rnd(rng, d, f), rnd(rng, f, f)
+    ref = [O.fastweight_terms(z_t[b], z_s[b], conv_t, conv_s, w0, wp) for b in range(B)]
+    for start in (0, 6):
+        ht = np.zeros((B, kc - 1, f))
+        hs = np.zeros((B, kc - 1, f))
+        for i in range(kc - 1):
+            tau = start - (kc - 1) + i
+            if tau >= 0:
+                ht[:, i], hs[:, i] = z_t[:, tau], z_s[:, tau]
+        for t in range(start, T):
+            r, k, dbar, ht, hs = O.decode_append(z_t[:, t], z_s[:, t], ht, hs, conv_t, conv_s,
+                                                 w0, wp)
+            for b in range(B):
+                np.testing.assert_allclose(r[b], ref[b][0][t], atol=1e-12, rtol=0)
+                np.testing.assert_allclose(k[b], ref[b][1][t], atol=1e-12, rtol=0)
+                np.testing.assert_allclose(dbar[b], ref[b][2][t], atol=1e-12, rtol=0)
+    # one token by an explicit loop over features and taps
+    t = 9
+    ht = np.stack([z_t[:, t - (kc - 1) + i] for i in range(kc - 1)], axis=1) if kc > 1 else np.zeros((B, 0, f))
+    hs = np.stack([z_s[:, t - (kc - 1) + i] for i in range(kc - 1)], axis=1) if kc > 1 else np.zeros((B, 0, f))
+    r, k, dbar, _, _ = O.decode_append(z_t[:, t], z_s[:, t], ht, hs, conv_t, conv_s, w0, wp)
+    for b in range(B):
+        zb_t = np.zeros(f)
+        zb_s = np.zeros(f)
+        for c in range(f):
+            for i in range(kc):
+                zb_t[c] += conv_t[c, i] * z_t[b, t - (kc - 1) + i, c]
+                zb_s[c] += conv_s[c, i] * z_s[b, t - (kc - 1) + i, c]
+        np.testing.assert_allclose(dbar[b], zb_t - zb_s, atol=1e-12, rtol=0)
+        np.testing.assert_allclose(k[b], zb_s / np.linalg.norm(zb_s), atol=1e-12, rtol=0)
+        np.testing.assert_allclose(r[b], w0 @ (wp @ (zb_t - zb_s)), atol=1e-12, rtol=0)
