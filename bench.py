@@ -187,6 +187,38 @@ def decode_bench(dev, n):
                      "algorithmic_gb": gb, "achieved_gbs": gb / (ms * 1e-3),
                      "hbm_frac": gb / (ms * 1e-3) / PEAK_HBM_GBS}
         assert torch.isfinite(out).all().item()
+    # a generation step that also extends the fast weight: the dense-state
+    # decode step returning both paths' Z, then the token's (r, k) appended
+    # to the pending chunk (conv over a history of kc-1 rows per path)
+    f, C = cfg.d_ff, cfg.chunk
+    ntap = int(wd["conv_t"].shape[1])
+    m_res = ttcd.fastweight_residual_proj(wd["w_down0"], wd["w_proj"])
+    hist_t = torch.zeros((B, ntap - 1, f), dtype=torch.bfloat16, device=dev)
+    hist_s = torch.zeros_like(hist_t)
+    r_pend = torch.zeros((B, C, cfg.d_model), dtype=torch.bfloat16, device=dev)
+    k_pend = torch.zeros((B, C, f), dtype=torch.bfloat16, device=dev)
+    dense_d = {"pos": L, "state_dense": dense, "beta_list": bl}
+    need = ttcd.layer_workspace_bytes(q, kc, cfg.d_model, cfg.d_ff, cfg.w_teacher, cfg.w_student,
+                                      cfg.chunk, decode_chunks=L // cfg.chunk, pos=L)
+    gws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    zpair = {}
+
+    def append():
+        ttcd.fastweight_decode_append(zpair["t"], zpair["s"], hist_t, hist_s, wd["conv_t"],
+                                      wd["conv_s"], m_res, r_pend[:, 0], k_pend[:, 0])
+
+    def gen_step():
+        _, a = ttcd.layer_forward(q, kc, vc, x, wd, cfg.w_teacher, cfg.w_student, cfg.chunk,
+                                  decode=dense_d, out=out, workspace=gws, aux=True)
+        zpair["t"], zpair["s"] = a["z_teacher"][:, 0], a["z_student"][:, 0]
+        append()
+
+    gen_ms = time_events(gen_step, n, stream, warmup=10)
+    app_ms = time_events(append, n, stream, warmup=5)
+    res["generate_dense"] = {"ms_per_step": gen_ms, "tokens_per_s": B / (gen_ms * 1e-3),
+                             "append_ms": app_ms,
+                             "what": "dense-state decode step with both paths' Z, then the "
+                                     "token's (r, k) appended to the pending chunk"}
     res["fold_ms"] = fold_ms
     res["fold_tflops"] = 2.0 * B * L * cfg.d_model * cfg.d_ff / (fold_ms * 1e-3) / 1e12
     res["workload"] = (f"{cfg.name}: decode step, batch {B}, 64K cache (NaN outside the "

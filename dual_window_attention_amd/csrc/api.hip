@@ -475,6 +475,87 @@ ttcd_status ttcd_fastweight_stream(const ttcd_fw_desc* d, const void* zt, const 
   return ok();
 }
 
+// ---- decode-time fast-weight pieces
+size_t ttcd_fastweight_residual_proj_workspace_size(const ttcd_fw_desc* d) {
+  if (check_fw(d) != TTCD_OK) return 0;
+  return (size_t)d->d_ff * d->d_ff * dsize(d->in_dtype);
+}
+
+ttcd_status ttcd_fastweight_residual_proj(const ttcd_fw_desc* d, const void* w_down0,
+                                          const void* w_proj, void* m_out, void* ws,
+                                          size_t ws_bytes, void* stream) {
+  ttcd_status st = check_fw(d);
+  if (st != TTCD_OK) return st;
+  REQ_PTR(w_down0); REQ_PTR(w_proj); REQ_PTR(m_out);
+  const size_t need = ttcd_fastweight_residual_proj_workspace_size(d);
+  if (ws_bytes < need)
+    return fail(TTCD_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (!ws) return fail(TTCD_ERR_NULL_POINTER, "workspace is NULL");
+  OPT_PTR(ws);
+  const int dt = d->in_dtype, dm = d->d_model, f = d->d_ff;
+  hipStream_t s = (hipStream_t)stream;
+  // M = W0 W_proj as an NT product: B operand = W_proj^T
+  HIPCHK(launch_transpose(w_proj, ws, f, f, f, f, 1, 0, 0, (int)dsize(dt), s));
+  GemmArgs g{};
+  g.A = w_down0; g.lda = f; g.B = ws; g.ldb = f; g.C = m_out; g.ldc = f;
+  g.M = dm; g.N = f; g.K = f; g.in_dt = dt; g.out_dt = dt; g.epi = EPI_STORE; g.batch = 1;
+  HIPCHK(launch_gemm(g, s));
+  return ok();
+}
+
+size_t ttcd_fastweight_decode_append_workspace_size(const ttcd_fw_desc* d) {
+  if (check_fw(d) != TTCD_OK) return 0;
+  Plan p(nullptr);
+  p.take((size_t)d->batch * d->d_ff * dsize(d->in_dtype));
+  if (d->batch <= 32)
+    p.take(gemm_skinny_ws_floats(d->batch, d->d_model, d->d_ff, EPI_STORE) * sizeof(float));
+  return p.off;
+}
+
+ttcd_status ttcd_fastweight_decode_append(const ttcd_fw_desc* d, const void* z_t,
+                                          const void* z_s, void* hist_t, void* hist_s,
+                                          const void* conv_t, const void* conv_s, const void* m,
+                                          void* r_out, int64_t r_stride, void* k_out,
+                                          int64_t k_stride, void* ws, size_t ws_bytes,
+                                          void* stream) {
+  ttcd_status st = check_fw(d);
+  if (st != TTCD_OK) return st;
+  REQ_PTR(z_t); REQ_PTR(z_s); REQ_PTR(conv_t); REQ_PTR(conv_s); REQ_PTR(m); REQ_PTR(r_out);
+  REQ_PTR(k_out);
+  if (d->conv_k > 1) {
+    REQ_PTR(hist_t); REQ_PTR(hist_s);
+  }
+  if (r_stride < d->d_model || k_stride < d->d_ff || r_stride % 8 || k_stride % 8)
+    return fail(TTCD_ERR_BAD_SHAPE, "r_stride >= d_model, k_stride >= d_ff, both multiples of 8");
+  const size_t need = ttcd_fastweight_decode_append_workspace_size(d);
+  if (ws_bytes < need)
+    return fail(TTCD_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (!ws) return fail(TTCD_ERR_NULL_POINTER, "workspace is NULL");
+  OPT_PTR(ws);
+  const int dt = d->in_dtype, B = d->batch, dm = d->d_model, f = d->d_ff;
+  hipStream_t s = (hipStream_t)stream;
+  Plan p(ws);
+  void* dbar = p.take((size_t)B * f * dsize(dt));
+  float* sk = nullptr;
+  size_t skf = 0;
+  if (B <= 32) {
+    skf = gemm_skinny_ws_floats(B, dm, f, EPI_STORE);
+    sk = (float*)p.take(skf * sizeof(float));
+  }
+  DecodeAppendArgs a{};
+  a.zt = z_t; a.zs = z_s; a.hist_t = hist_t; a.hist_s = hist_s; a.conv_t = conv_t;
+  a.conv_s = conv_s; a.dbar = dbar; a.k_out = k_out; a.k_stride = (long)k_stride; a.B = B;
+  a.f = f; a.kc = d->conv_k; a.eps = d->l2_eps > 0.f ? d->l2_eps : 1e-12f; a.in_dt = dt;
+  HIPCHK(launch_fw_decode_append(a, s));
+  // r = M dbar  for every sequence: [B, f] x [d, f]^T
+  GemmArgs g{};
+  g.A = dbar; g.lda = f; g.B = m; g.ldb = f; g.C = r_out; g.ldc = (long)r_stride;
+  g.M = B; g.N = dm; g.K = f; g.in_dt = dt; g.out_dt = dt; g.epi = EPI_STORE; g.batch = 1;
+  g.ws = sk; g.ws_floats = skf;
+  HIPCHK(launch_gemm(g, s));
+  return ok();
+}
+
 size_t ttcd_layer_forward_workspace_size(const ttcd_layer_desc* d, const ttcd_fw_state* dec) {
   if (check_layer(d, dec) != TTCD_OK) return 0;
   Plan p(nullptr);
@@ -508,8 +589,7 @@ ttcd_status ttcd_layer_forward(const ttcd_layer_desc* d, const ttcd_layer_weight
   OPT_PTR(aux->o_teacher); OPT_PTR(aux->o_student); OPT_PTR4(aux->lse_teacher);
   OPT_PTR4(aux->lse_student); OPT_PTR(aux->z_teacher); OPT_PTR(aux->z_student);
   OPT_PTR(aux->y); OPT_PTR(aux->state_out);
-  if (dec && (aux->z_student || aux->state_out))
-    return fail(TTCD_ERR_BAD_SHAPE, "z_student / state_out are prefill-only outputs");
+  if (dec && aux->state_out) return fail(TTCD_ERR_BAD_SHAPE, "state_out is a prefill-only output");
   const size_t need = ttcd_layer_forward_workspace_size(d, dec);
   if (ws_bytes < need)
     return fail(TTCD_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
@@ -536,11 +616,12 @@ ttcd_status ttcd_layer_forward(const ttcd_layer_desc* d, const ttcd_layer_weight
   // attention, both windows, O in the layer's element type
   HIPCHK(run_attn(&a, b.at, q, k, v, o[0], o[1], lse[0], lse[1], dt, s));
 
-  // per path: h = x + O W_o^T ; Z = SwiGLU(RMSNorm(h))
-  const int npaths = dec ? 1 : 2;
+  // per path: h = x + O W_o^T ; Z = SwiGLU(RMSNorm(h)).  A decode step
+  // needs the main path, and the other one only when the caller asks for its
+  // Z (both Z are the inputs of the fast-weight append of the token).
   const int main = (d->main_path == TTCD_MAIN_STUDENT) ? 1 : 0;
-  for (int pi = 0; pi < npaths; ++pi) {
-    const int path = dec ? main : pi;
+  for (int path = 0; path < 2; ++path) {
+    if (dec && path != main && !(path == 0 ? aux->z_teacher : aux->z_student)) continue;
     GemmArgs g{};
     g.A = o[path]; g.lda = HD; g.B = wt->w_o; g.ldb = HD; g.C = b.h[path]; g.ldc = dm;
     g.M = (int)BT; g.N = dm; g.K = HD; g.in_dt = dt; g.out_dt = F32; g.epi = EPI_RESIDUAL;

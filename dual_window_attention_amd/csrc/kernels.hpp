@@ -116,6 +116,20 @@ struct StreamArgs {
   int in_dt;
 };
 hipError_t launch_fw_stream(const StreamArgs& a, hipStream_t s);
+
+// One generated token: convs over the history and the token, dbar, the unit
+// key (to k_out + b * k_stride), and the history advanced by one row.
+struct DecodeAppendArgs {
+  const void* zt; const void* zs;       // [B, f]
+  void* hist_t; void* hist_s;           // [B, kc-1, f], updated in place
+  const void* conv_t; const void* conv_s;
+  void* dbar;                           // [B, f] workspace
+  void* k_out; long k_stride;
+  int B, f, kc;
+  float eps;
+  int in_dt;
+};
+hipError_t launch_fw_decode_append(const DecodeAppendArgs& a, hipStream_t s);
 size_t fw_stream_part_bytes(int B, int T, int f);
 
 // out [cols, rows] = in [rows, cols]^T (per batch), 2- or 4-byte elements

@@ -236,6 +236,63 @@ fw_key_scale_kernel(const float* __restrict__ part, const float* __restrict__ be
   sc[(size_t)b * Tpad + t] = v;
 }
 
+// ------------------------------------------------------- decode-time append
+// One generated token per sequence (the fast-weight stream for one row):
+// the short causal convs of both paths over the last kc-1 inputs (the
+// history) and the new one, tap kc-1 on the new token; the difference
+// dbar = conv_T - conv_S in the element type (as the prefill stores it);
+// the unit key k = conv_S / max(||conv_S||_2, eps) in the element type at
+// k_out + b * k_stride; then the history moves on by one row.  One
+// workgroup per sequence; each thread owns features tid, tid + 256, ...
+template <typename T, int KC>
+__global__ void __launch_bounds__(256)
+fw_decode_append_kernel(const T* __restrict__ zt, const T* __restrict__ zs, T* hist_t,
+                        T* hist_s, const T* __restrict__ conv_t, const T* __restrict__ conv_s,
+                        T* __restrict__ dbar, T* __restrict__ k_out, long k_stride, int f,
+                        float eps) {
+  __shared__ float red[4];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const T* zrt = zt + (size_t)b * f;
+  const T* zrs = zs + (size_t)b * f;
+  T* ht = hist_t + (size_t)b * (KC - 1) * f;
+  T* hs = hist_s + (size_t)b * (KC - 1) * f;
+  // conv_S of feature c: rows r < KC-1 from the history, row KC-1 the token
+  auto conv = [&](const T* taps, const T* hist, const T* z, int c) {
+    float acc = 0.f;
+#pragma unroll
+    for (int r = 0; r < KC; ++r) {
+      const float x = r < KC - 1 ? ldf(hist + (size_t)r * f + c) : ldf(z + c);
+      acc = __builtin_fmaf(ldf(taps + (size_t)c * KC + r), x, acc);
+    }
+    return acc;
+  };
+  float ss = 0.f;
+  for (int c = tid; c < f; c += 256) {
+    const float at = conv(conv_t, ht, zrt, c), as = conv(conv_s, hs, zrs, c);
+    elem<T>::st(dbar + (size_t)b * f + c, at - as);
+    ss = __builtin_fmaf(as, as, ss);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  const float inv = 1.f / fmaxf(sqrtf(red[0] + red[1] + red[2] + red[3]), eps);
+  for (int c = tid; c < f; c += 256) {
+    const float as = conv(conv_s, hs, zrs, c);
+    elem<T>::st(k_out + (size_t)b * k_stride + c, as * inv);
+    // the history moves on: row r takes row r+1, the last row the token
+#pragma unroll
+    for (int r = 0; r + 1 < KC - 1; ++r) {
+      ht[(size_t)r * f + c] = ht[(size_t)(r + 1) * f + c];
+      hs[(size_t)r * f + c] = hs[(size_t)(r + 1) * f + c];
+    }
+    if (KC > 1) {
+      ht[(size_t)(KC - 2) * f + c] = zrt[c];
+      hs[(size_t)(KC - 2) * f + c] = zrs[c];
+    }
+  }
+}
+
 // --------------------------------------------------------------- state prefix
 // Each thread owns 4 consecutive weight entries and walks the chunk writes in
 // order, 8 loads in flight at a time; the running sum never leaves fp32.
@@ -409,6 +466,29 @@ hipError_t launch_fw_stream(const StreamArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fw_key_scale_kernel, dim3(Tpad / 64, a.B), dim3(64), 0, s, a.part,
                      a.beta, a.sc, nft, a.T, Tpad, a.chunk, a.nchunks, a.eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_fw_decode_append(const DecodeAppendArgs& a, hipStream_t s) {
+#define TTCD_APPEND_KC(K)                                                                   \
+  case K:                                                                                   \
+    if (a.in_dt == BF16)                                                                    \
+      hipLaunchKernelGGL((fw_decode_append_kernel<bf16_t, K>), dim3(a.B), dim3(256), 0, s,  \
+                         (const bf16_t*)a.zt, (const bf16_t*)a.zs, (bf16_t*)a.hist_t,       \
+                         (bf16_t*)a.hist_s, (const bf16_t*)a.conv_t, (const bf16_t*)a.conv_s, \
+                         (bf16_t*)a.dbar, (bf16_t*)a.k_out, a.k_stride, a.f, a.eps);        \
+    else                                                                                    \
+      hipLaunchKernelGGL((fw_decode_append_kernel<float, K>), dim3(a.B), dim3(256), 0, s,   \
+                         (const float*)a.zt, (const float*)a.zs, (float*)a.hist_t,          \
+                         (float*)a.hist_s, (const float*)a.conv_t, (const float*)a.conv_s,  \
+                         (float*)a.dbar, (float*)a.k_out, a.k_stride, a.f, a.eps);          \
+    break;
+  switch (a.kc) {
+    TTCD_APPEND_KC(1) TTCD_APPEND_KC(2) TTCD_APPEND_KC(3) TTCD_APPEND_KC(4)
+    TTCD_APPEND_KC(5) TTCD_APPEND_KC(6) TTCD_APPEND_KC(7) TTCD_APPEND_KC(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef TTCD_APPEND_KC
   return hipGetLastError();
 }
 

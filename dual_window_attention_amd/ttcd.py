@@ -38,6 +38,8 @@ EXPORTS = (
     "ttcd_fastweight_stream_workspace_size", "ttcd_fastweight_stream",
     "ttcd_layer_forward_workspace_size", "ttcd_layer_forward",
     "ttcd_fastweight_fold_workspace_size", "ttcd_fastweight_fold",
+    "ttcd_fastweight_residual_proj_workspace_size", "ttcd_fastweight_residual_proj",
+    "ttcd_fastweight_decode_append_workspace_size", "ttcd_fastweight_decode_append",
     "ttcd_status_string", "ttcd_last_error", "ttcd_version",
 )
 
@@ -98,6 +100,12 @@ _sig = {
     "ttcd_layer_forward": (C.c_int, [C.POINTER(LayerDesc), C.POINTER(LayerWeights), _vp, _vp,
                                      _vp, _vp, _vp, C.POINTER(FwState), C.POINTER(LayerAux),
                                      _vp, _sz, _vp]),
+    "ttcd_fastweight_residual_proj_workspace_size": (_sz, [C.POINTER(FwDesc)]),
+    "ttcd_fastweight_residual_proj": (C.c_int, [C.POINTER(FwDesc), _vp, _vp, _vp, _vp, _sz, _vp]),
+    "ttcd_fastweight_decode_append_workspace_size": (_sz, [C.POINTER(FwDesc)]),
+    "ttcd_fastweight_decode_append": (C.c_int, [C.POINTER(FwDesc), _vp, _vp, _vp, _vp, _vp, _vp,
+                                                _vp, _vp, C.c_int64, _vp, C.c_int64, _vp, _sz,
+                                                _vp]),
     "ttcd_fastweight_fold_workspace_size": (_sz, [C.POINTER(FwDesc), C.c_int32]),
     "ttcd_fastweight_fold": (C.c_int, [C.POINTER(FwDesc), _vp, _vp, _vp, _vp, C.c_int32, _vp,
                                        _vp, _sz, _vp]),
@@ -141,6 +149,15 @@ def _dt(t: torch.Tensor) -> int:
 
 def _tdt(code: int) -> torch.dtype:
     return torch.bfloat16 if code == TTCD_BF16 else torch.float32
+
+
+def _row_ptr(t: torch.Tensor) -> int:
+    """Pointer of a [B, n] view whose rows are contiguous (any row stride)."""
+    if not t.is_cuda:
+        raise ValueError("tensors must live in GPU memory")
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a [B, n] view with contiguous rows")
+    return t.data_ptr()
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -297,6 +314,43 @@ def fastweight_stream(z_teacher, z_student, conv_t, conv_s, beta, chunk: int, *,
     return dbar, zbt, ks
 
 
+def fastweight_residual_proj(w_down0, w_proj, *, workspace=None, stream=None):
+    """M = W_down0 W_proj [d, f] in the weights' dtype (decode set-up)."""
+    dm, f = w_down0.shape
+    d = FwDesc(1, 1, dm, f, 16, 1, 0.0, _dt(w_down0), TTCD_F32)
+    m = torch.empty((dm, f), dtype=w_down0.dtype, device=w_down0.device)
+    ws = _workspace(_lib.ttcd_fastweight_residual_proj_workspace_size(C.byref(d)),
+                    w_down0.device, workspace)
+    _check(_lib.ttcd_fastweight_residual_proj(C.byref(d), _ptr(w_down0), _ptr(w_proj), _ptr(m),
+                                              _ptr(ws), ws.numel(), _stream(stream)),
+           "ttcd_fastweight_residual_proj")
+    return m
+
+
+def fastweight_decode_append(z_teacher, z_student, hist_t, hist_s, conv_t, conv_s, m,
+                             r_out, k_out, *, l2_eps: float = 0.0, workspace=None,
+                             stream=None):
+    """The fast-weight stream for one generated token per sequence.
+
+    z_teacher, z_student [B, f] (or [B, 1, f]); hist_t, hist_s [B, kc-1, f]
+    advance in place; r_out [B, d] and k_out [B, f] may be row views of
+    chunk-list buffers (stride(1) must be 1).
+    """
+    B, f = r_out.shape[0], k_out.shape[-1]
+    dm = r_out.shape[-1]
+    kc = conv_t.shape[1]
+    if r_out.stride(-1) != 1 or k_out.stride(-1) != 1:
+        raise ValueError("r_out and k_out rows must be contiguous")
+    d = FwDesc(B, 1, dm, f, 16, kc, l2_eps, _dt(z_teacher), TTCD_F32)
+    ws = _workspace(_lib.ttcd_fastweight_decode_append_workspace_size(C.byref(d)),
+                    z_teacher.device, workspace)
+    _check(_lib.ttcd_fastweight_decode_append(
+        C.byref(d), _ptr(z_teacher), _ptr(z_student), _ptr(hist_t), _ptr(hist_s), _ptr(conv_t),
+        _ptr(conv_s), _ptr(m), _row_ptr(r_out), int(r_out.stride(0)), _row_ptr(k_out),
+        int(k_out.stride(0)), _ptr(ws), ws.numel(), _stream(stream)),
+        "ttcd_fastweight_decode_append")
+
+
 def fastweight_fold(w_down0, r_list, k_list, beta_list, chunk: int, *, workspace=None,
                     stream=None):
     """Dense fp32 weight W_down0 + sum_j beta_j R_j^T K_j from chunk lists."""
@@ -372,8 +426,10 @@ def layer_forward(q, k, v, x, w: Dict[str, torch.Tensor], w_teacher: int, w_stud
         aux_t["lse_student"] = torch.empty((B, Hq, Tq), dtype=torch.float32, device=dev)
         aux_t["z_teacher"] = torch.empty((B, Tq, f), dtype=q.dtype, device=dev)
         aux_t["y"] = torch.empty((B, Tq, dm), dtype=torch.float32, device=dev)
+        # in a decode step both Z are returned too: they feed the
+        # fast-weight append of the token (fastweight_decode_append)
+        aux_t["z_student"] = torch.empty((B, Tq, f), dtype=q.dtype, device=dev)
         if decode is None:
-            aux_t["z_student"] = torch.empty((B, Tq, f), dtype=q.dtype, device=dev)
             aux_t["state_out"] = torch.empty((B, dm, f), dtype=torch.float32, device=dev)
         aux_s = LayerAux(*[_ptr(aux_t.get(n)) for n, _ in LayerAux._fields_])
     need = _lib.ttcd_layer_forward_workspace_size(C.byref(desc), dec_p)

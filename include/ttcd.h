@@ -262,7 +262,9 @@ typedef struct {
   float* lse_teacher;   /* [batch, n_q_heads, seq_q] */
   float* lse_student;
   void* z_teacher;      /* [batch, seq_q, d_ff] attn.in_dtype */
-  void* z_student;      /* prefill only */
+  void* z_student;      /* in a decode step the non-main path runs only when
+                           its Z is asked for here (the append below needs
+                           both) */
   float* y;             /* [batch, seq_q, d_model] fast-weight MLP output */
   float* state_out;     /* prefill only: [batch, d_model, d_ff] */
 } ttcd_layer_aux;
@@ -278,6 +280,51 @@ ttcd_status ttcd_layer_forward(const ttcd_layer_desc* desc,
                                const ttcd_layer_aux* aux,
                                void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/* ------------------------------------------------------------------------
+ * Decode-time fast-weight stream: the per-token part of the chunk writes
+ * (papernotes.org notes, key design 3; the paper's Eq. 12 in the podcast
+ * transcript) for a generated token, so that a decode loop can grow the
+ * chunk lists (or fold them with ttcd_fastweight_fold) exactly as a prefill
+ * over the same tokens would.
+ *
+ * ttcd_fastweight_residual_proj:  M = W_down0 W_proj  [d_model, d_ff]
+ *   in_dtype, the matrix that maps the conv difference to the residual
+ *   r_t; computed once per weight set.  Workspace: d_ff * d_ff elements.
+ *
+ * ttcd_fastweight_decode_append: for each sequence b of the batch, with
+ *   z_teacher, z_student [batch, d_ff] the new token's SwiGLU outputs of
+ *   both paths (ttcd_layer_forward in decode returns them through
+ *   ttcd_layer_aux) and hist_t, hist_s [batch, conv_k-1, d_ff] the last
+ *   conv_k-1 rows of each path before it (oldest first; the caller seeds
+ *   them with zeros at the sequence start or with the prefill's last rows):
+ *     zbar_p = sum_r conv_p[:, r] * window_p[r]    (row conv_k-1 = the token)
+ *     dbar   = zbar_T - zbar_S                     (rounded to in_dtype)
+ *     r      = M dbar          -> r_out + b * r_stride   [d_model] in_dtype
+ *     k      = zbar_S / max(||zbar_S||_2, l2_eps)
+ *                              -> k_out + b * k_stride   [d_ff]    in_dtype
+ *   and the histories advance by one row in place.  The strides (elements,
+ *   multiples of 8) let r and k land in row j of chunk-list buffers.  The
+ *   desc supplies batch, d_model, d_ff, conv_k, l2_eps and in_dtype.
+ * ---------------------------------------------------------------------- */
+size_t ttcd_fastweight_residual_proj_workspace_size(const ttcd_fw_desc* desc);
+
+ttcd_status ttcd_fastweight_residual_proj(const ttcd_fw_desc* desc,
+                                          const void* w_down0, const void* w_proj,
+                                          void* m_out, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
+size_t ttcd_fastweight_decode_append_workspace_size(const ttcd_fw_desc* desc);
+
+ttcd_status ttcd_fastweight_decode_append(const ttcd_fw_desc* desc,
+                                          const void* z_teacher, const void* z_student,
+                                          void* hist_t, void* hist_s,
+                                          const void* conv_t, const void* conv_s,
+                                          const void* m,
+                                          void* r_out, int64_t r_stride,
+                                          void* k_out, int64_t k_stride,
+                                          void* workspace, size_t workspace_bytes,
+                                          void* stream);
 
 /* ------------------------------------------------------------------------
  * Fold low-rank chunk lists into a dense fast weight (decode set-up):
