@@ -351,6 +351,37 @@ def fastweight_scan(z_t, z_s, z_main, conv_t, conv_s, w_down0, w_proj, beta,
     return {"y": y, "state": st, "r": rr, "k": kk, "dbar": dd}
 
 
+def fastweight_scan_on_policy(z_t, z_s, z_main, conv_t, conv_s, w_down0, w_proj, beta,
+                              C: int, eps: float = 1e-12):
+    """The sequential recurrence that the off-policy scan approximates
+    ([NOTES] key design 2: chunk i should see the weight left by chunk i-1;
+    [PODCAST] Eq. 12 cue: the parallel scan instead evaluates everything at
+    the base weight).  Chunk by chunk, one sequence at a time:
+
+        y_t     = S_i z_main[t]                      for t in chunk i
+        r_t     = S_i (W_proj dbar_t)                (residual at S_i)
+        S_{i+1} = S_i + beta_i R_i^T K_i,            S_0 = W_down^(0)
+
+    dbar and the unit keys are those of ``fastweight_terms`` (they do not
+    depend on the weight).  Returns dict with y [B,T,d] and state [B,d,f]
+    (= S_N)."""
+    z_t, z_s, z_main = _f64(z_t), _f64(z_s), _f64(z_main)
+    B, T, f = z_t.shape
+    d = w_down0.shape[0]
+    wp = _f64(w_proj)
+    y = np.zeros((B, T, d), F64)
+    st = np.zeros((B, d, f), F64)
+    for b in range(B):
+        _, k, dbar, _ = fastweight_terms(z_t[b], z_s[b], conv_t, conv_s, w_down0, w_proj, eps)
+        S = _f64(w_down0).copy()
+        for i, (a, e) in enumerate(chunk_bounds(T, C)):
+            y[b, a:e] = z_main[b, a:e] @ S.T
+            r = (dbar[a:e] @ wp.T) @ S.T
+            S = S + float(beta[b, i]) * (r.T @ k[a:e])
+        st[b] = S
+    return {"y": y, "state": st}
+
+
 # ==========================================================================
 # full layer (prefill) and one decode step
 # ==========================================================================

@@ -466,3 +466,80 @@ def test_decode_append_token_by_token_equals_sequence_terms(kc):
         np.testing.assert_allclose(dbar[b], zb_t - zb_s, atol=1e-12, rtol=0)
         np.testing.assert_allclose(k[b], zb_s / np.linalg.norm(zb_s), atol=1e-12, rtol=0)
         np.testing.assert_allclose(r[b], w0 @ (wp @ (zb_t - zb_s)), atol=1e-12, rtol=0)
+
+
+def _on_policy_args(s, z_s=None, beta=None):
+    return (s["z_t"][None], (s["z_s"] if z_s is None else z_s)[None], s["z_t"][None],
+            s["conv_t"], s["conv_s"], s["w0"], s["wp"],
+            (s["beta"] if beta is None else beta)[None], s["C"])
+
+
+def test_on_policy_state_is_ordered_product_of_chunk_factors():
+    """S_{i+1} = S_i + beta_i S_i W_proj Dbar_i^T K_i factors as
+    S_i (I + beta_i W_proj Dbar_i^T K_i): the on-policy weights are W0 times
+    the ordered product of per-chunk f x f factors (a ragged last chunk
+    included).  A residual taken at W0 or at S_{i+1}, or the factors in the
+    wrong order, breaks this."""
+    rng = np.random.default_rng(31)
+    s = _scan_inputs(rng, T=30, C=8)
+    _, k, dbar, _ = O.fastweight_terms(s["z_t"], s["z_s"], s["conv_t"], s["conv_s"],
+                                       s["w0"], s["wp"])
+    out = O.fastweight_scan_on_policy(*_on_policy_args(s))
+    f = s["w0"].shape[1]
+    P = np.eye(f)
+    y = np.zeros_like(out["y"][0])
+    for i, (a, b) in enumerate(O.chunk_bounds(30, s["C"])):
+        y[a:b] = s["z_t"][a:b] @ (s["w0"] @ P).T
+        P = P @ (np.eye(f) + s["beta"][i] * (s["wp"] @ dbar[a:b].T @ k[a:b]))
+    scale = np.abs(y).max()
+    np.testing.assert_allclose(out["y"][0], y, atol=1e-12 * scale, rtol=0)
+    np.testing.assert_allclose(out["state"][0], s["w0"] @ P, atol=1e-12 * np.abs(s["w0"] @ P).max(),
+                               rtol=0)
+
+
+def test_on_policy_agrees_with_off_policy_until_the_second_write():
+    """Chunks 0 and 1 see W0 and W0 + beta_0 R_0^T K_0 under both rules
+    (chunk 0's residual is taken at S_0 = W0 either way); from chunk 2 on
+    the rules differ.  With beta = 0 or equal paths nothing is written."""
+    rng = np.random.default_rng(32)
+    s = _scan_inputs(rng, T=40, C=8)
+    on = O.fastweight_scan_on_policy(*_on_policy_args(s))["y"][0]
+    off = O.fastweight_scan(*_on_policy_args(s))["y"][0]
+    np.testing.assert_allclose(on[:16], off[:16], atol=1e-12 * np.abs(off).max(), rtol=0)
+    assert np.abs(on[16:] - off[16:]).max() > 1e-3 * np.abs(off).max()
+    zero = O.fastweight_scan_on_policy(*_on_policy_args(s, beta=np.zeros_like(s["beta"])))
+    np.testing.assert_allclose(zero["y"][0], s["z_t"] @ s["w0"].T, atol=1e-13, rtol=0)
+    np.testing.assert_array_equal(zero["state"][0], s["w0"])
+    same = O.fastweight_scan_on_policy(s["z_t"][None], s["z_t"][None], s["z_t"][None],
+                                       s["conv_t"], s["conv_t"], s["w0"], s["wp"],
+                                       s["beta"][None], s["C"])
+    np.testing.assert_array_equal(same["state"][0], s["w0"])
+
+
+def test_on_policy_equals_pure_loop_per_token_recurrence():
+    """Brute force: scalar loops over tokens and features, the weight
+    updated only at chunk ends, each token's residual read from the weight
+    in force for its chunk."""
+    rng = np.random.default_rng(33)
+    s = _scan_inputs(rng, T=13, C=4, f=5, d=3)
+    _, k, dbar, _ = O.fastweight_terms(s["z_t"], s["z_s"], s["conv_t"], s["conv_s"],
+                                       s["w0"], s["wp"])
+    d, f = s["w0"].shape
+    S = [[float(s["w0"][o, c]) for c in range(f)] for o in range(d)]
+    y = np.zeros((13, d))
+    pend = [[0.0] * f for _ in range(d)]
+    for t in range(13):
+        i = t // 4
+        for o in range(d):
+            y[t, o] = sum(S[o][c] * s["z_t"][t, c] for c in range(f))
+        u = [sum(s["wp"][a, c] * dbar[t, c] for c in range(f)) for a in range(f)]
+        r = [sum(S[o][a] * u[a] for a in range(f)) for o in range(d)]
+        for o in range(d):
+            for c in range(f):
+                pend[o][c] += s["beta"][i] * r[o] * k[t, c]
+        if t % 4 == 3 or t == 12:
+            S = [[S[o][c] + pend[o][c] for c in range(f)] for o in range(d)]
+            pend = [[0.0] * f for _ in range(d)]
+    out = O.fastweight_scan_on_policy(*_on_policy_args(s))
+    np.testing.assert_allclose(out["y"][0], y, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(out["state"][0], np.array(S), atol=1e-12, rtol=0)
