@@ -126,6 +126,37 @@ def scan_roofline(cfg, dev, n):
             "ms_per_launch": ms, "algorithmic_gb": gb}
 
 
+def update_rules_bench(cfg, dev, n):
+    """The fast-weight path (stream, residual projection, writes, prefix,
+    apply) under the off-policy rule (all residuals at W_down^(0), parallel
+    over chunks) and under the on-policy recurrence (chunk after chunk),
+    same inputs, output y in fp32."""
+    import torch
+    from dual_window_attention_amd import inputs as I
+    from dual_window_attention_amd import ttcd
+
+    z = I.hidden_activations(cfg)
+    w = I.layer_weights(cfg)
+    zt, zs = I.to_torch(z["z_t"], dev), I.to_torch(z["z_s"], dev)
+    del z
+    a = [zt, zs, zt] + [I.to_torch(w[k], dev) for k in ("conv_t", "conv_s", "w_down0", "w_proj")]
+    a.append(I.f32_to_torch(I.beta_for(cfg), dev))
+    d = ttcd.fw_desc(zt, cfg.d_model, cfg.chunk, cfg.conv_k, 0.0, torch.float32)
+    lib = ttcd.lib()
+    ws = torch.empty(max(lib.ttcd_fastweight_scan_workspace_size(d),
+                         lib.ttcd_fastweight_scan_on_policy_workspace_size(d)),
+                     dtype=torch.uint8, device=dev)
+    st = torch.cuda.current_stream()
+    off_ms = time_events(lambda: ttcd.fastweight_scan(*a, cfg.chunk, workspace=ws), n, st, 3)
+    on_ms = time_events(lambda: ttcd.fastweight_scan_on_policy(*a, cfg.chunk, workspace=ws),
+                        n, st, 3)
+    del a, ws
+    return {"kernel": "fast-weight path, off-policy (ttcd_fastweight_scan) vs on-policy "
+                      "recurrence (ttcd_fastweight_scan_on_policy)",
+            "off_policy_ms": off_ms, "on_policy_ms": on_ms, "on_over_off": on_ms / off_ms,
+            "tokens": cfg.batch * cfg.seq, "chunks": cfg.n_chunks}
+
+
 def decode_bench(dev, n):
     """One decode token per sequence at the batch-32, 64K-cache workload:
     low-rank lists and folded dense state; the fold itself timed once."""
@@ -363,6 +394,8 @@ def main():
     del q, k, v, wd, x, out, ws, o_t, o_s, aws, sws
     torch.cuda.empty_cache()
     res["scan"] = scan_roofline(cfg, dev, n_att)
+    torch.cuda.empty_cache()
+    res["update_rules"] = update_rules_bench(cfg, dev, 5)
     torch.cuda.empty_cache()
     if not args.no_decode:
         res["decode"] = decode_bench(dev, n_att)

@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/ttcd.h"
 #include "kernels.hpp"
 
@@ -440,6 +442,110 @@ ttcd_status ttcd_fastweight_scan(const ttcd_fw_desc* d, const void* zt, const vo
   HIPCHK(run_fw(d->batch, d->seq, d->d_model, d->d_ff, d->chunk, d->conv_k, eps, d->in_dtype, zt,
                 zs, zmain, conv_t, conv_s, w_down0, w_proj, beta, nullptr, y, d->out_dtype,
                 state_out, w, (hipStream_t)stream));
+  return ok();
+}
+
+// ---- on-policy recurrence (a variant of the update rule)
+// R_i from the running fast weight S_i instead of W_down0:
+//   R~^T_i = ((S_i W_proj) dbar_i^T) * s_i,  dW_i = R~^T_i Zbar_S,i^T,
+//   S_{i+1} = S_i + dW_i,  y_t = S_{t/C} z_main[t].
+// The chunks go one after another (each projection needs the state the
+// previous writes made); the stream, the operands and the apply are those
+// of the off-policy path.  The running state stays fp32 (in state_out when
+// given); its element-type copy is the next projection's and the apply's
+// operand.
+hipError_t run_fw_on_policy(int B, int T, int d, int f, int C, int kc, float eps, int dt,
+                            const void* zt, const void* zs, const void* zmain,
+                            const void* conv_t, const void* conv_s, const void* w0,
+                            const void* wp, const float* beta, void* out, int out_dt,
+                            float* state_out, const FwBufs& w, float* s32_ws, hipStream_t s) {
+  hipError_t e;
+  const int N = w.N;
+  const size_t es = dsize(dt);
+  const long df = (long)d * f;
+  StreamArgs sa{};
+  sa.zt = zt; sa.zs = zs; sa.conv_t = conv_t; sa.conv_s = conv_s; sa.beta = beta;
+  sa.dbar = w.dbar; sa.zbt = w.zbt; sa.sc = w.sc; sa.part = w.part;
+  sa.B = B; sa.T = T; sa.f = f; sa.kc = kc; sa.chunk = C; sa.nchunks = N; sa.eps = eps;
+  sa.in_dt = dt;
+  if ((e = launch_fw_stream(sa, s)) != hipSuccess) return e;
+  if ((e = launch_transpose(wp, w.wpt, f, f, f, f, 1, 0, 0, (int)es, s)) != hipSuccess) return e;
+  const int nstates = N - 1;
+  for (int b = 0; b < B; ++b) {
+    float* s32 = state_out ? state_out + (size_t)b * df : s32_ws;
+    if ((e = launch_state_init(w0, s32, df, dt, s)) != hipSuccess) return e;
+    const void* Si = w0;
+    const int last = state_out ? N : nstates;          // writes that matter
+    for (int i = 0; i < last; ++i) {
+      const long c0 = (long)i * C;
+      const int ncol = (int)std::min<long>(C, w.Tpad - c0);   // the short last chunk to Tpad
+      GemmArgs g{};
+      // M_i = S_i W_proj
+      g.A = Si; g.lda = f; g.B = w.wpt; g.ldb = f; g.C = w.m; g.ldc = f;
+      g.M = d; g.N = f; g.K = f; g.in_dt = dt; g.out_dt = dt; g.epi = EPI_STORE; g.batch = 1;
+      if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+      // R~^T_i = (M_i dbar_i^T) * s_i   -> columns c0.. of rst
+      char* rst = (char*)w.rst + ((size_t)b * d * w.Tpad + c0) * es;
+      g = GemmArgs{};
+      g.A = w.m; g.lda = f; g.B = (const char*)w.dbar + ((size_t)b * w.Tpad + c0) * f * es;
+      g.ldb = f; g.C = rst; g.ldc = w.Tpad; g.M = d; g.N = ncol; g.K = f; g.in_dt = dt;
+      g.out_dt = dt; g.epi = EPI_STORE; g.colscale = w.sc + (size_t)b * w.Tpad + c0; g.batch = 1;
+      if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+      // dW_i = R~^T_i Zbar_S,i^T  (fp32)
+      g = GemmArgs{};
+      g.A = rst; g.lda = w.Tpad; g.B = (const char*)w.zbt + ((size_t)b * f * w.Tpad + c0) * es;
+      g.ldb = w.Tpad; g.C = w.dw; g.ldc = f; g.M = d; g.N = f; g.K = ncol; g.in_dt = dt;
+      g.out_dt = F32; g.epi = EPI_STORE; g.batch = 1;
+      if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+      // S_{i+1} = S_i + dW_i; its element-type copy is states[i]
+      void* s16 = i < nstates ? (char*)w.states + ((size_t)b * nstates + i) * df * es : nullptr;
+      if ((e = launch_state_step(w.dw, s32, s16, df, dt, s)) != hipSuccess) return e;
+      if (s16) Si = s16;
+    }
+  }
+  // apply: out = Z_main S_{t/C}^T
+  GemmArgs g{};
+  g.A = zmain; g.lda = f; g.B = w0; g.ldb = f; g.C = out; g.ldc = d;
+  g.M = T; g.N = d; g.K = f; g.in_dt = dt; g.out_dt = out_dt; g.epi = EPI_STORE;
+  g.batch = B; g.sA = (long)T * f; g.sB = 0; g.sC = (long)T * d;
+  g.chunk = C; g.Bchunks = w.states; g.sBchunk = df; g.sBchunksBatch = (long)nstates * df;
+  return launch_gemm(g, s);
+}
+
+size_t ttcd_fastweight_scan_on_policy_workspace_size(const ttcd_fw_desc* d) {
+  if (check_fw(d) != TTCD_OK) return 0;
+  Plan p(nullptr);
+  FwBufs w;
+  plan_fw(d->batch, d->seq, d->d_model, d->d_ff, d->chunk, d->in_dtype, p, w);
+  p.take((size_t)d->d_model * d->d_ff * sizeof(float));
+  return p.off;
+}
+
+ttcd_status ttcd_fastweight_scan_on_policy(const ttcd_fw_desc* d, const void* zt,
+                                           const void* zs, const void* zmain,
+                                           const void* conv_t, const void* conv_s,
+                                           const void* w_down0, const void* w_proj,
+                                           const float* beta, void* y, float* state_out,
+                                           void* ws, size_t ws_bytes, void* stream) {
+  ttcd_status st = check_fw(d);
+  if (st != TTCD_OK) return st;
+  REQ_PTR(zt); REQ_PTR(zs); REQ_PTR(zmain); REQ_PTR(conv_t); REQ_PTR(conv_s);
+  REQ_PTR(w_down0); REQ_PTR(w_proj); REQ_PTR(y); OPT_PTR(state_out);
+  if (!beta) return fail(TTCD_ERR_NULL_POINTER, "beta is NULL");
+  OPT_PTR4(beta);
+  const size_t need = ttcd_fastweight_scan_on_policy_workspace_size(d);
+  if (ws_bytes < need)
+    return fail(TTCD_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (!ws) return fail(TTCD_ERR_NULL_POINTER, "workspace is NULL");
+  OPT_PTR(ws);
+  Plan p(ws);
+  FwBufs w;
+  plan_fw(d->batch, d->seq, d->d_model, d->d_ff, d->chunk, d->in_dtype, p, w);
+  float* s32 = (float*)p.take((size_t)d->d_model * d->d_ff * sizeof(float));
+  const float eps = d->l2_eps > 0.f ? d->l2_eps : 1e-12f;
+  HIPCHK(run_fw_on_policy(d->batch, d->seq, d->d_model, d->d_ff, d->chunk, d->conv_k, eps,
+                          d->in_dtype, zt, zs, zmain, conv_t, conv_s, w_down0, w_proj, beta, y,
+                          d->out_dtype, state_out, w, s32, (hipStream_t)stream));
   return ok();
 }
 

@@ -130,6 +130,10 @@ struct DecodeAppendArgs {
   int in_dt;
 };
 hipError_t launch_fw_decode_append(const DecodeAppendArgs& a, hipStream_t s);
+// on-policy recurrence: s32 = float(w0); per chunk s32 += dw, s16 = s32 (dt)
+hipError_t launch_state_init(const void* w0, float* s32, long n, int dt, hipStream_t s);
+hipError_t launch_state_step(const float* dw, float* s32, void* s16, long n, int dt,
+                             hipStream_t s);
 size_t fw_stream_part_bytes(int B, int T, int f);
 
 // out [cols, rows] = in [rows, cols]^T (per batch), 2- or 4-byte elements

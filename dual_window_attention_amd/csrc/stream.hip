@@ -293,6 +293,28 @@ fw_decode_append_kernel(const T* __restrict__ zt, const T* __restrict__ zs, T* h
   }
 }
 
+// ------------------------------------------------- on-policy state update
+// The running fast weight of the on-policy recurrence, one chunk at a time:
+// s32 = float(w0) to start, then s32 += dw and s16 = s32 in the element type
+// (the operand of the next chunk's residual projection and of the apply).
+template <typename T>
+__global__ void __launch_bounds__(256)
+state_init_kernel(const T* __restrict__ w0, float* __restrict__ s32, long n) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) s32[i] = ldf(w0 + i);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+state_step_kernel(const float* __restrict__ dw, float* __restrict__ s32, T* __restrict__ s16,
+                  long n) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const float v = s32[i] + dw[i];
+  s32[i] = v;
+  if (s16) elem<T>::st(s16 + i, v);
+}
+
 // --------------------------------------------------------------- state prefix
 // Each thread owns 4 consecutive weight entries and walks the chunk writes in
 // order, 8 loads in flight at a time; the running sum never leaves fp32.
@@ -489,6 +511,25 @@ hipError_t launch_fw_decode_append(const DecodeAppendArgs& a, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
 #undef TTCD_APPEND_KC
+  return hipGetLastError();
+}
+
+hipError_t launch_state_init(const void* w0, float* s32, long n, int dt, hipStream_t s) {
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (dt == BF16)
+    hipLaunchKernelGGL((state_init_kernel<bf16_t>), grid, dim3(256), 0, s, (const bf16_t*)w0, s32, n);
+  else
+    hipLaunchKernelGGL((state_init_kernel<float>), grid, dim3(256), 0, s, (const float*)w0, s32, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_step(const float* dw, float* s32, void* s16, long n, int dt,
+                             hipStream_t s) {
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (dt == BF16)
+    hipLaunchKernelGGL((state_step_kernel<bf16_t>), grid, dim3(256), 0, s, dw, s32, (bf16_t*)s16, n);
+  else
+    hipLaunchKernelGGL((state_step_kernel<float>), grid, dim3(256), 0, s, dw, s32, (float*)s16, n);
   return hipGetLastError();
 }
 

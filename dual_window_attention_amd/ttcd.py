@@ -35,6 +35,7 @@ EXPORTS = (
     "ttcd_dual_window_attn_workspace_size", "ttcd_dual_window_attn",
     "ttcd_dual_window_attn_lse_split_workspace_size", "ttcd_dual_window_attn_lse_split",
     "ttcd_fastweight_scan_workspace_size", "ttcd_fastweight_scan",
+    "ttcd_fastweight_scan_on_policy_workspace_size", "ttcd_fastweight_scan_on_policy",
     "ttcd_fastweight_stream_workspace_size", "ttcd_fastweight_stream",
     "ttcd_layer_forward_workspace_size", "ttcd_layer_forward",
     "ttcd_fastweight_fold_workspace_size", "ttcd_fastweight_fold",
@@ -93,6 +94,9 @@ _sig = {
     "ttcd_fastweight_scan_workspace_size": (_sz, [C.POINTER(FwDesc)]),
     "ttcd_fastweight_scan": (C.c_int, [C.POINTER(FwDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _vp, _vp, _vp, _sz, _vp]),
+    "ttcd_fastweight_scan_on_policy_workspace_size": (_sz, [C.POINTER(FwDesc)]),
+    "ttcd_fastweight_scan_on_policy": (C.c_int, [C.POINTER(FwDesc), _vp, _vp, _vp, _vp, _vp, _vp,
+                                                 _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "ttcd_fastweight_stream_workspace_size": (_sz, [C.POINTER(FwDesc)]),
     "ttcd_fastweight_stream": (C.c_int, [C.POINTER(FwDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                          _vp, _vp, _sz, _vp]),
@@ -284,6 +288,28 @@ def fastweight_scan(z_teacher, z_student, z_main, conv_t, conv_s, w_down0, w_pro
                                      _ptr(conv_t), _ptr(conv_s), _ptr(w_down0), _ptr(w_proj),
                                      _ptr(beta), _ptr(y), _ptr(st), _ptr(ws), ws.numel(),
                                      _stream(stream)), "ttcd_fastweight_scan")
+    return y, st
+
+
+def fastweight_scan_on_policy(z_teacher, z_student, z_main, conv_t, conv_s, w_down0, w_proj,
+                              beta, chunk: int, *, out_dtype=torch.float32,
+                              want_state: bool = False, l2_eps: float = 0.0,
+                              workspace=None, stream=None):
+    """fastweight_scan with the on-policy recurrence: the residual of chunk i
+    is projected by the fast weight in force for chunk i, not by W_down^(0).
+    Returns (y, state) as fastweight_scan does."""
+    dm = w_down0.shape[0]
+    kc = conv_t.shape[1]
+    d = fw_desc(z_teacher, dm, chunk, kc, l2_eps, out_dtype)
+    B, T, f = z_teacher.shape
+    y = torch.empty((B, T, dm), dtype=out_dtype, device=z_teacher.device)
+    st = torch.empty((B, dm, f), dtype=torch.float32, device=z_teacher.device) if want_state else None
+    need = _lib.ttcd_fastweight_scan_on_policy_workspace_size(C.byref(d))
+    ws = _workspace(need, z_teacher.device, workspace)
+    _check(_lib.ttcd_fastweight_scan_on_policy(
+        C.byref(d), _ptr(z_teacher), _ptr(z_student), _ptr(z_main), _ptr(conv_t), _ptr(conv_s),
+        _ptr(w_down0), _ptr(w_proj), _ptr(beta), _ptr(y), _ptr(st), _ptr(ws), ws.numel(),
+        _stream(stream)), "ttcd_fastweight_scan_on_policy")
     return y, st
 
 

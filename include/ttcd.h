@@ -173,6 +173,27 @@ ttcd_status ttcd_fastweight_scan(const ttcd_fw_desc* desc,
                                  void* workspace, size_t workspace_bytes,
                                  void* stream);
 
+/* The same chunk-wise update with the on-policy recurrence, a variant of
+ * the update rule (papernotes.org notes, key design 2, and the podcast
+ * transcript's Eq. 12 state the practical rule with the residual taken at
+ * W_down^(0); here it is taken at the fast weight in force for the chunk):
+ *   r_t  = S_{floor(t/chunk)} W_proj (Zbar_T[t] - Zbar_S[t])
+ * with everything else as above (keys, beta, prefix, apply).  The chunks
+ * are processed one after another.  Arguments, layouts and errors are those
+ * of ttcd_fastweight_scan; state_out, when given, also serves as the fp32
+ * running state.  Its workspace adds d_model * d_ff fp32 values. */
+size_t ttcd_fastweight_scan_on_policy_workspace_size(const ttcd_fw_desc* desc);
+
+ttcd_status ttcd_fastweight_scan_on_policy(const ttcd_fw_desc* desc,
+                                           const void* z_teacher, const void* z_student,
+                                           const void* z_main,
+                                           const void* conv_t, const void* conv_s,
+                                           const void* w_down0, const void* w_proj,
+                                           const float* beta,
+                                           void* y, float* state_out,
+                                           void* workspace, size_t workspace_bytes,
+                                           void* stream);
+
 /* ------------------------------------------------------------------------
  * The fast-weight stream alone: the first, memory-bound step of
  * ttcd_fastweight_scan (papernotes.org notes, key design 3: the short

@@ -1,0 +1,118 @@
+"""ttcd_fastweight_scan_on_policy on the GPU against the fp64 oracle's
+sequential recurrence (residual projected by the weight in force for each
+chunk)."""
+import numpy as np
+import pytest
+
+from dual_window_attention_amd import inputs as I
+from oracle import ttcd_oracle as O
+from tests.gpu_helpers import assert_close, assert_close_stored, say, to_np, tol_for
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+BASE = I.CONFIGS[3]
+
+
+def run_on_policy(cfg, out_dtype="f32", beta_scale=1.0):
+    from dual_window_attention_amd import ttcd
+    say(f"on-policy {cfg.dtype} B={cfg.batch} T={cfg.seq} f={cfg.d_ff} d={cfg.d_model} "
+        f"C={cfg.chunk} kc={cfg.conv_k} y={out_dtype} beta*{beta_scale}")
+    z = I.hidden_activations(cfg)
+    w = I.layer_weights(cfg)
+    beta = (I.beta_for(cfg) * np.float32(beta_scale)).astype(np.float32)
+    zt, zs = I.to_torch(z["z_t"]), I.to_torch(z["z_s"])
+    dev = {n: I.to_torch(w[n]) for n in ("conv_t", "conv_s", "w_down0", "w_proj")}
+    odt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    y, st = ttcd.fastweight_scan_on_policy(zt, zs, zt, dev["conv_t"], dev["conv_s"],
+                                           dev["w_down0"], dev["w_proj"], I.f32_to_torch(beta),
+                                           cfg.chunk, out_dtype=odt, want_state=True)
+    torch.cuda.synchronize()
+    args = (z["z_t"].f64(), z["z_s"].f64(), z["z_t"].f64(), w["conv_t"].f64(),
+            w["conv_s"].f64(), w["w_down0"].f64(), w["w_proj"].f64(),
+            beta.astype(np.float64), cfg.chunk)
+    return to_np(y), to_np(st), O.fastweight_scan_on_policy(*args), O.fastweight_scan(*args), \
+        z["z_t"].f64() @ w["w_down0"].f64().T
+
+
+def check_on_policy(cfg, out_dtype="f32", beta_scale=1.0):
+    y, st, on, off, base = run_on_policy(cfg, out_dtype, beta_scale)
+    tol = tol_for(cfg.dtype)
+    if out_dtype == "f32":
+        assert_close(y, on["y"], tol, "y")
+    else:
+        assert_close_stored(y, on["y"], tol, "y (bf16 out)", "bf16")
+    assert_close(st, on["state"], tol, "state after all writes")
+    # the correction y - W0 z against the on-policy one, and closer to it
+    # than the off-policy correction is, so the test tells the rules apart
+    corr_on, corr_off, corr = on["y"] - base, off["y"] - base, y - base
+    n_on = np.linalg.norm(corr_on)
+    rel = np.linalg.norm(corr - corr_on) / max(n_on, 1e-30)
+    gap = np.linalg.norm(corr_off - corr_on) / max(n_on, 1e-30)
+    say(f"  correction relL2={rel:.3e}  (on vs off policy: {gap:.3e})")
+    if n_on > 0:
+        bound = 1e-4
+        if cfg.dtype == "bf16":
+            # each chunk's weight S_i is kept in bf16 for its GEMMs: one
+            # rounding, rms 2^-9/sqrt(3) of |S_i z|, lands on y of the later
+            # chunks; where the correction is a small part of y this floor
+            # (taken twice) exceeds the 5% bound
+            later = on["y"][:, cfg.chunk:]
+            floor = 2 * 2.0 ** -9 / np.sqrt(3.0) * np.linalg.norm(later) / n_on
+            bound = max(5e-2, floor)
+        assert rel <= bound, (rel, bound)
+    return rel, gap
+
+
+@pytest.mark.parametrize("case", [
+    dict(dtype="f32", batch=1, seq=300, d_model=64, d_ff=96, chunk=64, conv_k=4, seed=41),
+    dict(dtype="bf16", batch=2, seq=517, d_model=128, d_ff=256, chunk=128, conv_k=1, seed=42),
+    dict(dtype="bf16", batch=2, seq=700, d_model=96, d_ff=160, chunk=48, conv_k=8, seed=43),
+    dict(dtype="f32", batch=2, seq=333, d_model=64, d_ff=128, chunk=32, conv_k=7, seed=44),
+], ids=["f32-kc4", "bf16-kc1-B2-ragged", "bf16-kc8-chunk48", "f32-kc7-chunk32"])
+def test_on_policy_small(case):
+    check_on_policy(BASE.scaled(**case))
+
+
+def test_on_policy_tells_the_rules_apart():
+    """Here the two rules' corrections differ by about 13% (fp64): the GPU
+    result must follow the on-policy one far more closely than that."""
+    cfg = BASE.scaled(dtype="f32", batch=1, seq=512, d_model=64, d_ff=128, chunk=64, seed=45)
+    rel, gap = check_on_policy(cfg)
+    assert gap > 100 * rel
+
+
+def test_on_policy_bf16_output_and_single_chunk():
+    check_on_policy(BASE.scaled(batch=1, seq=640, d_model=128, d_ff=256, chunk=128, seed=46),
+                    out_dtype="bf16")
+    # T <= C: no write reaches any token, y = W0 z
+    y, st, on, _, base = run_on_policy(BASE.scaled(batch=2, seq=100, d_model=64, d_ff=128,
+                                                   chunk=128, seed=47))
+    assert_close(y, base, tol_for("bf16"), "single chunk y")
+    assert_close(st, on["state"], tol_for("bf16"), "single chunk state")
+
+
+def test_on_policy_first_two_chunks_equal_off_policy_call():
+    """Both rules give the same weight to chunks 0 and 1; the two entry
+    points compute those rows from the same bf16 operands."""
+    from dual_window_attention_amd import ttcd
+    cfg = BASE.scaled(batch=1, seq=1024, d_model=128, d_ff=256, chunk=256, seed=48)
+    z = I.hidden_activations(cfg)
+    w = I.layer_weights(cfg)
+    args = [I.to_torch(z["z_t"]), I.to_torch(z["z_s"])]
+    args.append(args[0])
+    args += [I.to_torch(w[n]) for n in ("conv_t", "conv_s", "w_down0", "w_proj")]
+    args.append(I.f32_to_torch(I.beta_for(cfg)))
+    y_on, _ = ttcd.fastweight_scan_on_policy(*args, cfg.chunk)
+    y_off, _ = ttcd.fastweight_scan(*args, cfg.chunk)
+    torch.cuda.synchronize()
+    a, b = to_np(y_on)[0, :512], to_np(y_off)[0, :512]
+    assert np.abs(a - b).max() <= 2e-2 * max(np.abs(b).max(), 1.0)
+
+
+def test_on_policy_qwen3_dims_ragged():
+    """d_model 1024, d_ff 3072, chunk 1024 (the 64K layer's fast-weight
+    shapes) over 4.5 chunks."""
+    check_on_policy(BASE.scaled(batch=1, seq=4500, d_model=1024, d_ff=3072, chunk=1024,
+                                conv_k=4, seed=49))
