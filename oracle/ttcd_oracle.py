@@ -382,6 +382,36 @@ def fastweight_scan_on_policy(z_t, z_s, z_main, conv_t, conv_s, w_down0, w_proj,
     return {"y": y, "state": st}
 
 
+def fastweight_scan_eq6(z_t, z_s, z_main, w_down0, beta, C: int):
+    """The unprojected write of the distillation gradient ([PODCAST] Eq. 4
+    and Eq. 6 cues), off-policy at W_down^(0), with no convs, no W_proj and
+    no key normalisation.  Chunk i's loss is half the squared gap between the
+    student's MLP output W z_S and the detached teacher's W0 z_T; its
+    gradient in W at W0 is  sum_t (W0 z_S,t - W0 z_T,t) z_S,t^T, and the
+    write is beta_i times its negative:
+
+        dW_i    = beta_i sum_{t in chunk i} W0 (z_T,t - z_S,t) z_S,t^T
+        S_{i+1} = S_i + dW_i,   S_0 = W0,   y_t = S_{floor(t/C)} z_main[t]
+
+    Returns dict with y [B,T,d], state [B,d,f] (= S_N) and dw [B,N,d,f]."""
+    z_t, z_s, z_main = _f64(z_t), _f64(z_s), _f64(z_main)
+    w0 = _f64(w_down0)
+    B, T, f = z_t.shape
+    bounds = chunk_bounds(T, C)
+    y = np.zeros((B, T, w0.shape[0]), F64)
+    st = np.zeros((B,) + w0.shape, F64)
+    dws = np.zeros((B, len(bounds)) + w0.shape, F64)
+    for b in range(B):
+        S = w0.copy()
+        for i, (a, e) in enumerate(bounds):
+            y[b, a:e] = z_main[b, a:e] @ S.T
+            gap = (z_t[b, a:e] - z_s[b, a:e]) @ w0.T         # teacher - student outputs
+            dws[b, i] = float(beta[b, i]) * (gap.T @ z_s[b, a:e])
+            S = S + dws[b, i]
+        st[b] = S
+    return {"y": y, "state": st, "dw": dws}
+
+
 # ==========================================================================
 # full layer (prefill) and one decode step
 # ==========================================================================

@@ -543,3 +543,40 @@ def test_on_policy_equals_pure_loop_per_token_recurrence():
     out = O.fastweight_scan_on_policy(*_on_policy_args(s))
     np.testing.assert_allclose(out["y"][0], y, atol=1e-12, rtol=0)
     np.testing.assert_allclose(out["state"][0], np.array(S), atol=1e-12, rtol=0)
+
+
+def test_eq6_write_is_minus_beta_times_autograd_gradient_of_the_loss():
+    """Each chunk's write equals -beta_i times torch.autograd's gradient of
+    0.5 sum_t ||W z_S,t - stopgrad(W z_T,t)||^2 at W = W0 (fp64), and the
+    prefix/apply use those writes."""
+    rng = np.random.default_rng(34)
+    s = _scan_inputs(rng, T=29, C=8)
+    out = O.fastweight_scan_eq6(s["z_t"][None], s["z_s"][None], s["z_t"][None], s["w0"],
+                                s["beta"][None], s["C"])
+    S = s["w0"].copy()
+    for i, (a, b) in enumerate(O.chunk_bounds(29, s["C"])):
+        W = torch.tensor(s["w0"], dtype=torch.float64, requires_grad=True)
+        zs = torch.tensor(s["z_s"][a:b])
+        zt = torch.tensor(s["z_t"][a:b])
+        loss = 0.5 * ((zs @ W.T - (zt @ W.T).detach()) ** 2).sum()
+        loss.backward()
+        dw = -s["beta"][i] * W.grad.numpy()
+        np.testing.assert_allclose(out["dw"][0, i], dw, atol=1e-13, rtol=0)
+        np.testing.assert_allclose(out["y"][0, a:b], s["z_t"][a:b] @ S.T, atol=1e-12, rtol=0)
+        S = S + dw
+    np.testing.assert_allclose(out["state"][0], S, atol=1e-12, rtol=0)
+
+
+def test_eq6_small_step_lowers_the_chunk_loss():
+    """A gradient step: with a small enough beta the student's chunk loss
+    at W0 + dW_i is below its value at W0; equal paths write nothing."""
+    rng = np.random.default_rng(35)
+    s = _scan_inputs(rng, T=16, C=16)
+    beta = np.array([1e-3])
+    out = O.fastweight_scan_eq6(s["z_t"][None], s["z_s"][None], s["z_t"][None], s["w0"],
+                                beta[None], 16)
+    loss = lambda W: 0.5 * np.sum((s["z_s"] @ W.T - s["z_t"] @ s["w0"].T) ** 2)
+    assert loss(s["w0"] + out["dw"][0, 0]) < loss(s["w0"])
+    same = O.fastweight_scan_eq6(s["z_t"][None], s["z_t"][None], s["z_t"][None], s["w0"],
+                                 beta[None], 16)
+    assert np.all(same["dw"] == 0)
