@@ -129,8 +129,9 @@ def scan_roofline(cfg, dev, n):
 def update_rules_bench(cfg, dev, n):
     """The fast-weight path (stream, residual projection, writes, prefix,
     apply) under the off-policy rule (all residuals at W_down^(0), parallel
-    over chunks) and under the on-policy recurrence (chunk after chunk),
-    same inputs, output y in fp32."""
+    over chunks), under the on-policy recurrence (chunk after chunk), and
+    the unprojected write (no convs, no W_proj, raw keys), same inputs,
+    output y in fp32."""
     import torch
     from dual_window_attention_amd import inputs as I
     from dual_window_attention_amd import ttcd
@@ -144,16 +145,21 @@ def update_rules_bench(cfg, dev, n):
     d = ttcd.fw_desc(zt, cfg.d_model, cfg.chunk, cfg.conv_k, 0.0, torch.float32)
     lib = ttcd.lib()
     ws = torch.empty(max(lib.ttcd_fastweight_scan_workspace_size(d),
-                         lib.ttcd_fastweight_scan_on_policy_workspace_size(d)),
+                         lib.ttcd_fastweight_scan_on_policy_workspace_size(d),
+                         lib.ttcd_fastweight_scan_eq6_workspace_size(d)),
                      dtype=torch.uint8, device=dev)
     st = torch.cuda.current_stream()
     off_ms = time_events(lambda: ttcd.fastweight_scan(*a, cfg.chunk, workspace=ws), n, st, 3)
     on_ms = time_events(lambda: ttcd.fastweight_scan_on_policy(*a, cfg.chunk, workspace=ws),
                         n, st, 3)
-    del a, ws
-    return {"kernel": "fast-weight path, off-policy (ttcd_fastweight_scan) vs on-policy "
-                      "recurrence (ttcd_fastweight_scan_on_policy)",
+    e6 = [a[0], a[1], a[2], a[5], a[7]]
+    eq6_ms = time_events(lambda: ttcd.fastweight_scan_eq6(*e6, cfg.chunk, workspace=ws), n, st, 3)
+    del a, e6, ws
+    return {"kernel": "fast-weight path: off-policy (ttcd_fastweight_scan), on-policy "
+                      "recurrence (ttcd_fastweight_scan_on_policy), unprojected write "
+                      "(ttcd_fastweight_scan_eq6)",
             "off_policy_ms": off_ms, "on_policy_ms": on_ms, "on_over_off": on_ms / off_ms,
+            "eq6_unprojected_ms": eq6_ms,
             "tokens": cfg.batch * cfg.seq, "chunks": cfg.n_chunks}
 
 

@@ -179,7 +179,9 @@ hipError_t run_fw(int B, int T, int d, int f, int C, int kc, float eps, int dt,
                   const void* zt, const void* zs, const void* zmain, const void* conv_t,
                   const void* conv_s, const void* w0, const void* wp, const float* beta,
                   const float* res, void* out, int out_dt, float* state_out, const FwBufs& w,
-                  hipStream_t s) {
+                  hipStream_t s, bool eq6 = false) {
+  // eq6: the unprojected write (residual W0 (z_T - z_S), raw student keys);
+  // the caller passes unit identity taps with kc = 1 and wp = NULL
   hipError_t e;
   const int N = w.N;
   // (1) conv, difference, key norms
@@ -187,18 +189,20 @@ hipError_t run_fw(int B, int T, int d, int f, int C, int kc, float eps, int dt,
   sa.zt = zt; sa.zs = zs; sa.conv_t = conv_t; sa.conv_s = conv_s; sa.beta = beta;
   sa.dbar = w.dbar; sa.zbt = w.zbt; sa.sc = w.sc; sa.part = w.part;
   sa.B = B; sa.T = T; sa.f = f; sa.kc = kc; sa.chunk = C; sa.nchunks = N; sa.eps = eps;
-  sa.in_dt = dt;
+  sa.in_dt = dt; sa.raw_keys = eq6 ? 1 : 0;
   if ((e = launch_fw_stream(sa, s)) != hipSuccess) return e;
-  // (2) M = W0 W_proj  (as NT: B operand = W_proj^T)
-  if ((e = launch_transpose(wp, w.wpt, f, f, f, f, 1, 0, 0, (int)dsize(dt), s)) != hipSuccess)
-    return e;
   GemmArgs g{};
-  g.A = w0; g.lda = f; g.B = w.wpt; g.ldb = f; g.C = w.m; g.ldc = f;
-  g.M = d; g.N = f; g.K = f; g.in_dt = dt; g.out_dt = dt; g.epi = EPI_STORE; g.batch = 1;
-  if ((e = launch_gemm(g, s)) != hipSuccess) return e;
-  // (3) Rs^T[b] = (M dbar_b^T) * sc_b   -> [d, Tpad]
+  if (!eq6) {
+    // (2) M = W0 W_proj  (as NT: B operand = W_proj^T)
+    if ((e = launch_transpose(wp, w.wpt, f, f, f, f, 1, 0, 0, (int)dsize(dt), s)) != hipSuccess)
+      return e;
+    g.A = w0; g.lda = f; g.B = w.wpt; g.ldb = f; g.C = w.m; g.ldc = f;
+    g.M = d; g.N = f; g.K = f; g.in_dt = dt; g.out_dt = dt; g.epi = EPI_STORE; g.batch = 1;
+    if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+  }
+  // (3) Rs^T[b] = (M dbar_b^T) * sc_b   -> [d, Tpad]   (M = W0 for eq6)
   g = GemmArgs{};
-  g.A = w.m; g.lda = f; g.B = w.dbar; g.ldb = f; g.C = w.rst; g.ldc = w.Tpad;
+  g.A = eq6 ? w0 : w.m; g.lda = f; g.B = w.dbar; g.ldb = f; g.C = w.rst; g.ldc = w.Tpad;
   g.M = d; g.N = w.Tpad; g.K = f; g.in_dt = dt; g.out_dt = dt; g.epi = EPI_STORE;
   g.colscale = w.sc; g.batch = B; g.sA = 0; g.sB = (long)w.Tpad * f;
   g.sC = (long)d * w.Tpad; g.sScale = w.Tpad;
@@ -546,6 +550,41 @@ ttcd_status ttcd_fastweight_scan_on_policy(const ttcd_fw_desc* d, const void* zt
   HIPCHK(run_fw_on_policy(d->batch, d->seq, d->d_model, d->d_ff, d->chunk, d->conv_k, eps,
                           d->in_dtype, zt, zs, zmain, conv_t, conv_s, w_down0, w_proj, beta, y,
                           d->out_dtype, state_out, w, s32, (hipStream_t)stream));
+  return ok();
+}
+
+size_t ttcd_fastweight_scan_eq6_workspace_size(const ttcd_fw_desc* d) {
+  if (check_fw(d) != TTCD_OK) return 0;
+  Plan p(nullptr);
+  FwBufs w;
+  plan_fw(d->batch, d->seq, d->d_model, d->d_ff, d->chunk, d->in_dtype, p, w);
+  p.take((size_t)d->d_ff * dsize(d->in_dtype));
+  return p.off;
+}
+
+ttcd_status ttcd_fastweight_scan_eq6(const ttcd_fw_desc* d, const void* zt, const void* zs,
+                                     const void* zmain, const void* w_down0, const float* beta,
+                                     void* y, float* state_out, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  ttcd_status st = check_fw(d);
+  if (st != TTCD_OK) return st;
+  REQ_PTR(zt); REQ_PTR(zs); REQ_PTR(zmain); REQ_PTR(w_down0); REQ_PTR(y); OPT_PTR(state_out);
+  if (!beta) return fail(TTCD_ERR_NULL_POINTER, "beta is NULL");
+  OPT_PTR4(beta);
+  const size_t need = ttcd_fastweight_scan_eq6_workspace_size(d);
+  if (ws_bytes < need)
+    return fail(TTCD_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (!ws) return fail(TTCD_ERR_NULL_POINTER, "workspace is NULL");
+  OPT_PTR(ws);
+  Plan p(ws);
+  FwBufs w;
+  plan_fw(d->batch, d->seq, d->d_model, d->d_ff, d->chunk, d->in_dtype, p, w);
+  void* taps = p.take((size_t)d->d_ff * dsize(d->in_dtype));
+  hipStream_t s = (hipStream_t)stream;
+  HIPCHK(launch_fill(taps, d->d_ff, 1.f, d->in_dtype, s));
+  HIPCHK(run_fw(d->batch, d->seq, d->d_model, d->d_ff, d->chunk, 1, 1e-12f, d->in_dtype, zt, zs,
+                zmain, taps, taps, w_down0, nullptr, beta, nullptr, y, d->out_dtype, state_out,
+                w, s, true));
   return ok();
 }
 

@@ -208,18 +208,21 @@ fw_stream2_kernel(const T* __restrict__ zt, const T* __restrict__ zs,
   }
 }
 
-// sc[b, t] = beta[b, t / chunk] / max(sqrt(sum of the partial norms), eps).
+// sc[b, t] = beta[b, t / chunk] / max(sqrt(sum of the partial norms), eps),
+// or beta[b, t / chunk] alone for raw (unnormalised) keys.
 // One token per lane; the partials are loaded eight at a time (all in
 // flight together) and added in feature-tile order.
 __global__ void __launch_bounds__(64)
 fw_key_scale_kernel(const float* __restrict__ part, const float* __restrict__ beta,
                     float* __restrict__ sc, int nft, int T_, int Tpad, int chunk, int nchunks,
-                    float eps) {
+                    float eps, int raw) {
   const int b = blockIdx.y;
   const int t = blockIdx.x * 64 + threadIdx.x;
   if (t >= Tpad) return;
   float v = 0.f;
-  if (t < T_) {
+  if (t < T_ && raw) {
+    v = beta[(size_t)b * nchunks + min(t / chunk, nchunks - 1)];
+  } else if (t < T_) {
     float ss = 0.f;
     const float* pp = part + (size_t)b * nft * Tpad + t;
     for (int y0 = 0; y0 < nft; y0 += 8) {
@@ -302,6 +305,12 @@ __global__ void __launch_bounds__(256)
 state_init_kernel(const T* __restrict__ w0, float* __restrict__ s32, long n) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i < n) s32[i] = ldf(w0 + i);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) fill_kernel(T* __restrict__ p, long n, float v) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) elem<T>::st(p + i, v);
 }
 
 template <typename T>
@@ -487,7 +496,7 @@ hipError_t launch_fw_stream(const StreamArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fw_key_scale_kernel, dim3(Tpad / 64, a.B), dim3(64), 0, s, a.part,
-                     a.beta, a.sc, nft, a.T, Tpad, a.chunk, a.nchunks, a.eps);
+                     a.beta, a.sc, nft, a.T, Tpad, a.chunk, a.nchunks, a.eps, a.raw_keys);
   return hipGetLastError();
 }
 
@@ -520,6 +529,15 @@ hipError_t launch_state_init(const void* w0, float* s32, long n, int dt, hipStre
     hipLaunchKernelGGL((state_init_kernel<bf16_t>), grid, dim3(256), 0, s, (const bf16_t*)w0, s32, n);
   else
     hipLaunchKernelGGL((state_init_kernel<float>), grid, dim3(256), 0, s, (const float*)w0, s32, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill(void* p, long n, float v, int dt, hipStream_t s) {
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (dt == BF16)
+    hipLaunchKernelGGL((fill_kernel<bf16_t>), grid, dim3(256), 0, s, (bf16_t*)p, n, v);
+  else
+    hipLaunchKernelGGL((fill_kernel<float>), grid, dim3(256), 0, s, (float*)p, n, v);
   return hipGetLastError();
 }
 

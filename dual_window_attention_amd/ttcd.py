@@ -36,6 +36,7 @@ EXPORTS = (
     "ttcd_dual_window_attn_lse_split_workspace_size", "ttcd_dual_window_attn_lse_split",
     "ttcd_fastweight_scan_workspace_size", "ttcd_fastweight_scan",
     "ttcd_fastweight_scan_on_policy_workspace_size", "ttcd_fastweight_scan_on_policy",
+    "ttcd_fastweight_scan_eq6_workspace_size", "ttcd_fastweight_scan_eq6",
     "ttcd_fastweight_stream_workspace_size", "ttcd_fastweight_stream",
     "ttcd_layer_forward_workspace_size", "ttcd_layer_forward",
     "ttcd_fastweight_fold_workspace_size", "ttcd_fastweight_fold",
@@ -97,6 +98,9 @@ _sig = {
     "ttcd_fastweight_scan_on_policy_workspace_size": (_sz, [C.POINTER(FwDesc)]),
     "ttcd_fastweight_scan_on_policy": (C.c_int, [C.POINTER(FwDesc), _vp, _vp, _vp, _vp, _vp, _vp,
                                                  _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "ttcd_fastweight_scan_eq6_workspace_size": (_sz, [C.POINTER(FwDesc)]),
+    "ttcd_fastweight_scan_eq6": (C.c_int, [C.POINTER(FwDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                           _vp, _sz, _vp]),
     "ttcd_fastweight_stream_workspace_size": (_sz, [C.POINTER(FwDesc)]),
     "ttcd_fastweight_stream": (C.c_int, [C.POINTER(FwDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                          _vp, _vp, _sz, _vp]),
@@ -310,6 +314,25 @@ def fastweight_scan_on_policy(z_teacher, z_student, z_main, conv_t, conv_s, w_do
         C.byref(d), _ptr(z_teacher), _ptr(z_student), _ptr(z_main), _ptr(conv_t), _ptr(conv_s),
         _ptr(w_down0), _ptr(w_proj), _ptr(beta), _ptr(y), _ptr(st), _ptr(ws), ws.numel(),
         _stream(stream)), "ttcd_fastweight_scan_on_policy")
+    return y, st
+
+
+def fastweight_scan_eq6(z_teacher, z_student, z_main, w_down0, beta, chunk: int, *,
+                        out_dtype=torch.float32, want_state: bool = False, workspace=None,
+                        stream=None):
+    """The unprojected write: r_t = W0 (z_T - z_S), raw keys z_S, no convs or
+    W_proj; chunk prefix and apply as in fastweight_scan.  Returns (y, state)."""
+    dm = w_down0.shape[0]
+    d = fw_desc(z_teacher, dm, chunk, 1, 0.0, out_dtype)
+    B, T, f = z_teacher.shape
+    y = torch.empty((B, T, dm), dtype=out_dtype, device=z_teacher.device)
+    st = torch.empty((B, dm, f), dtype=torch.float32, device=z_teacher.device) if want_state else None
+    need = _lib.ttcd_fastweight_scan_eq6_workspace_size(C.byref(d))
+    ws = _workspace(need, z_teacher.device, workspace)
+    _check(_lib.ttcd_fastweight_scan_eq6(C.byref(d), _ptr(z_teacher), _ptr(z_student),
+                                         _ptr(z_main), _ptr(w_down0), _ptr(beta), _ptr(y),
+                                         _ptr(st), _ptr(ws), ws.numel(), _stream(stream)),
+           "ttcd_fastweight_scan_eq6")
     return y, st
 
 

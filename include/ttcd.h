@@ -194,6 +194,28 @@ ttcd_status ttcd_fastweight_scan_on_policy(const ttcd_fw_desc* desc,
                                            void* workspace, size_t workspace_bytes,
                                            void* stream);
 
+/* The unprojected write of the distillation gradient, a variant of the
+ * update rule (the podcast transcript's Eq. 4 and Eq. 6 cues: half the
+ * squared gap between the student's and the detached teacher's MLP outputs;
+ * its negative gradient in W_down is the output gap times the student's
+ * activation).  Evaluated off-policy at W_down^(0), with no short convs, no
+ * W_proj and no key normalisation:
+ *   r_t     = W_down^(0) (Z_T[t] - Z_S[t])                            [d]
+ *   S_{i+1} = S_i + beta[b,i] * sum_{t in chunk i} r_t Z_S[t]^T,  S_0 = W_down^(0)
+ *   y[t]    = S_{floor(t/chunk)} z_main[t]
+ * beta carries the step size (and any 1/|chunk| of the loss).  desc's
+ * conv_k and l2_eps are ignored; everything else (layouts, state_out,
+ * workspace, errors) is as for ttcd_fastweight_scan. */
+size_t ttcd_fastweight_scan_eq6_workspace_size(const ttcd_fw_desc* desc);
+
+ttcd_status ttcd_fastweight_scan_eq6(const ttcd_fw_desc* desc,
+                                     const void* z_teacher, const void* z_student,
+                                     const void* z_main, const void* w_down0,
+                                     const float* beta,
+                                     void* y, float* state_out,
+                                     void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
 /* ------------------------------------------------------------------------
  * The fast-weight stream alone: the first, memory-bound step of
  * ttcd_fastweight_scan (papernotes.org notes, key design 3: the short
