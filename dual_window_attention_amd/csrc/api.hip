@@ -451,18 +451,47 @@ ttcd_status ttcd_fastweight_scan(const ttcd_fw_desc* d, const void* zt, const vo
 
 // ---- on-policy recurrence (a variant of the update rule)
 // R_i from the running fast weight S_i instead of W_down0:
-//   R~^T_i = ((S_i W_proj) dbar_i^T) * s_i,  dW_i = R~^T_i Zbar_S,i^T,
+//   R~^T_i = (S_i (W_proj dbar_i^T)) * s_i,  dW_i = R~^T_i Zbar_S,i^T,
 //   S_{i+1} = S_i + dW_i,  y_t = S_{t/C} z_main[t].
 // The chunks go one after another (each projection needs the state the
 // previous writes made); the stream, the operands and the apply are those
 // of the off-policy path.  The running state stays fp32 (in state_out when
 // given); its element-type copy is the next projection's and the apply's
 // operand.
+//
+// The split of the K = d_ff reduction in R~^T_i = S_i U_i^T: enough
+// workgroups to cover the GPU, each slice a multiple of 64.
+int on_policy_split(int d, int C, int f) {
+  const long tiles = (long)((d + 127) / 128) * ((C + 127) / 128);
+  int ns = 1;
+  while (ns < 8 && tiles * ns < 256 && f % (2 * ns * 64) == 0) ns *= 2;
+  return ns;
+}
+
+struct OnPolicyBufs {
+  float* s32;      // [d, f] running state (when the caller passes no state_out)
+  void* u;         // [B, Tpad, f] U = Dbar W_proj^T
+  float* part;     // [nsplit, d, C] split-K partials
+};
+
+void plan_on_policy(int B, int T, int d, int f, int C, int dt, Plan& p, FwBufs& w,
+                    OnPolicyBufs& o) {
+  plan_fw(B, T, d, f, C, dt, p, w);
+  o.s32 = (float*)p.take((size_t)d * f * sizeof(float));
+  o.u = p.take((size_t)B * w.Tpad * f * dsize(dt));
+  o.part = (float*)p.take((size_t)on_policy_split(d, C, f) * d * C * sizeof(float));
+}
+
+// The on-policy recurrence: chunk i's residual is projected by S_i.
+//   U = Dbar W_proj^T (all tokens, one GEMM; it does not depend on S)
+//   per chunk: R~^T_i = (S_i U_i^T) * s (split-K partials, then a reduce that
+//   applies the write scale), dW_i = R~^T_i Zbar_S,i^T (fp32), S_{i+1} = S_i + dW_i
 hipError_t run_fw_on_policy(int B, int T, int d, int f, int C, int kc, float eps, int dt,
                             const void* zt, const void* zs, const void* zmain,
                             const void* conv_t, const void* conv_s, const void* w0,
                             const void* wp, const float* beta, void* out, int out_dt,
-                            float* state_out, const FwBufs& w, float* s32_ws, hipStream_t s) {
+                            float* state_out, const FwBufs& w, const OnPolicyBufs& o,
+                            hipStream_t s) {
   hipError_t e;
   const int N = w.N;
   const size_t es = dsize(dt);
@@ -473,28 +502,34 @@ hipError_t run_fw_on_policy(int B, int T, int d, int f, int C, int kc, float eps
   sa.B = B; sa.T = T; sa.f = f; sa.kc = kc; sa.chunk = C; sa.nchunks = N; sa.eps = eps;
   sa.in_dt = dt;
   if ((e = launch_fw_stream(sa, s)) != hipSuccess) return e;
-  if ((e = launch_transpose(wp, w.wpt, f, f, f, f, 1, 0, 0, (int)es, s)) != hipSuccess) return e;
+  GemmArgs g{};
+  // U[t, a] = sum_c dbar[t, c] W_proj[a, c]: NT with W_proj as the B operand
+  g.A = w.dbar; g.lda = f; g.B = wp; g.ldb = f; g.C = o.u; g.ldc = f;
+  g.M = B * w.Tpad; g.N = f; g.K = f; g.in_dt = dt; g.out_dt = dt; g.epi = EPI_STORE;
+  g.batch = 1;
+  if ((e = launch_gemm(g, s)) != hipSuccess) return e;
   const int nstates = N - 1;
+  const int ns = on_policy_split(d, C, f);
+  const int ks = f / ns;
   for (int b = 0; b < B; ++b) {
-    float* s32 = state_out ? state_out + (size_t)b * df : s32_ws;
+    float* s32 = state_out ? state_out + (size_t)b * df : o.s32;
     if ((e = launch_state_init(w0, s32, df, dt, s)) != hipSuccess) return e;
     const void* Si = w0;
     const int last = state_out ? N : nstates;          // writes that matter
     for (int i = 0; i < last; ++i) {
       const long c0 = (long)i * C;
       const int ncol = (int)std::min<long>(C, w.Tpad - c0);   // the short last chunk to Tpad
-      GemmArgs g{};
-      // M_i = S_i W_proj
-      g.A = Si; g.lda = f; g.B = w.wpt; g.ldb = f; g.C = w.m; g.ldc = f;
-      g.M = d; g.N = f; g.K = f; g.in_dt = dt; g.out_dt = dt; g.epi = EPI_STORE; g.batch = 1;
-      if ((e = launch_gemm(g, s)) != hipSuccess) return e;
-      // R~^T_i = (M_i dbar_i^T) * s_i   -> columns c0.. of rst
       char* rst = (char*)w.rst + ((size_t)b * d * w.Tpad + c0) * es;
+      // partial[z] = S_i[:, z ks : (z+1) ks] U_i[:, z ks : (z+1) ks]^T
       g = GemmArgs{};
-      g.A = w.m; g.lda = f; g.B = (const char*)w.dbar + ((size_t)b * w.Tpad + c0) * f * es;
-      g.ldb = f; g.C = rst; g.ldc = w.Tpad; g.M = d; g.N = ncol; g.K = f; g.in_dt = dt;
-      g.out_dt = dt; g.epi = EPI_STORE; g.colscale = w.sc + (size_t)b * w.Tpad + c0; g.batch = 1;
+      g.A = Si; g.lda = f; g.B = (const char*)o.u + ((size_t)b * w.Tpad + c0) * f * es;
+      g.ldb = f; g.C = o.part; g.ldc = C; g.M = d; g.N = ncol; g.K = ks; g.in_dt = dt;
+      g.out_dt = F32; g.epi = EPI_STORE; g.batch = ns; g.sA = ks; g.sB = ks;
+      g.sC = (long)d * C;
       if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+      if ((e = launch_splitk_reduce(o.part, ns, (long)d * C, C, w.sc + (size_t)b * w.Tpad + c0,
+                                    rst, w.Tpad, d, ncol, dt, s)) != hipSuccess)
+        return e;
       // dW_i = R~^T_i Zbar_S,i^T  (fp32)
       g = GemmArgs{};
       g.A = rst; g.lda = w.Tpad; g.B = (const char*)w.zbt + ((size_t)b * f * w.Tpad + c0) * es;
@@ -508,7 +543,7 @@ hipError_t run_fw_on_policy(int B, int T, int d, int f, int C, int kc, float eps
     }
   }
   // apply: out = Z_main S_{t/C}^T
-  GemmArgs g{};
+  g = GemmArgs{};
   g.A = zmain; g.lda = f; g.B = w0; g.ldb = f; g.C = out; g.ldc = d;
   g.M = T; g.N = d; g.K = f; g.in_dt = dt; g.out_dt = out_dt; g.epi = EPI_STORE;
   g.batch = B; g.sA = (long)T * f; g.sB = 0; g.sC = (long)T * d;
@@ -520,8 +555,8 @@ size_t ttcd_fastweight_scan_on_policy_workspace_size(const ttcd_fw_desc* d) {
   if (check_fw(d) != TTCD_OK) return 0;
   Plan p(nullptr);
   FwBufs w;
-  plan_fw(d->batch, d->seq, d->d_model, d->d_ff, d->chunk, d->in_dtype, p, w);
-  p.take((size_t)d->d_model * d->d_ff * sizeof(float));
+  OnPolicyBufs o;
+  plan_on_policy(d->batch, d->seq, d->d_model, d->d_ff, d->chunk, d->in_dtype, p, w, o);
   return p.off;
 }
 
@@ -544,12 +579,12 @@ ttcd_status ttcd_fastweight_scan_on_policy(const ttcd_fw_desc* d, const void* zt
   OPT_PTR(ws);
   Plan p(ws);
   FwBufs w;
-  plan_fw(d->batch, d->seq, d->d_model, d->d_ff, d->chunk, d->in_dtype, p, w);
-  float* s32 = (float*)p.take((size_t)d->d_model * d->d_ff * sizeof(float));
+  OnPolicyBufs o;
+  plan_on_policy(d->batch, d->seq, d->d_model, d->d_ff, d->chunk, d->in_dtype, p, w, o);
   const float eps = d->l2_eps > 0.f ? d->l2_eps : 1e-12f;
   HIPCHK(run_fw_on_policy(d->batch, d->seq, d->d_model, d->d_ff, d->chunk, d->conv_k, eps,
                           d->in_dtype, zt, zs, zmain, conv_t, conv_s, w_down0, w_proj, beta, y,
-                          d->out_dtype, state_out, w, s32, (hipStream_t)stream));
+                          d->out_dtype, state_out, w, o, (hipStream_t)stream));
   return ok();
 }
 

@@ -541,6 +541,35 @@ hipError_t launch_fill(void* p, long n, float v, int dt, hipStream_t s) {
   return hipGetLastError();
 }
 
+// out[m, n] = colscale[n] * sum_z part[z, m, n]  (split-K partials, fp32),
+// stored in the element type with row stride ldo.
+template <typename T>
+__global__ void __launch_bounds__(256)
+splitk_reduce_kernel(const float* __restrict__ part, int nsplit, long zstride, int ldp,
+                     const float* __restrict__ colscale, T* __restrict__ out, long ldo, int M,
+                     int N) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long)M * N) return;
+  const int m = (int)(i / N), n = (int)(i % N);
+  float acc = 0.f;
+  for (int z = 0; z < nsplit; ++z) acc += part[z * zstride + (long)m * ldp + n];
+  if (colscale) acc *= colscale[n];
+  elem<T>::st(out + m * ldo + n, acc);
+}
+
+hipError_t launch_splitk_reduce(const float* part, int nsplit, long zstride, int ldp,
+                                const float* colscale, void* out, long ldo, int M, int N, int dt,
+                                hipStream_t s) {
+  const dim3 grid((unsigned)(((long)M * N + 255) / 256));
+  if (dt == BF16)
+    hipLaunchKernelGGL((splitk_reduce_kernel<bf16_t>), grid, dim3(256), 0, s, part, nsplit,
+                       zstride, ldp, colscale, (bf16_t*)out, ldo, M, N);
+  else
+    hipLaunchKernelGGL((splitk_reduce_kernel<float>), grid, dim3(256), 0, s, part, nsplit,
+                       zstride, ldp, colscale, (float*)out, ldo, M, N);
+  return hipGetLastError();
+}
+
 hipError_t launch_state_step(const float* dw, float* s32, void* s16, long n, int dt,
                              hipStream_t s) {
   const dim3 grid((unsigned)((n + 255) / 256));
