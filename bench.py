@@ -154,12 +154,21 @@ def update_rules_bench(cfg, dev, n):
                         n, st, 3)
     e6 = [a[0], a[1], a[2], a[5], a[7]]
     eq6_ms = time_events(lambda: ttcd.fastweight_scan_eq6(*e6, cfg.chunk, workspace=ws), n, st, 3)
-    del a, e6, ws
+    # how far the off-policy approximation moves y: the gap between the two
+    # rules' outputs, against the on-policy correction y - W_down0 z
+    y_off, _ = ttcd.fastweight_scan(*a, cfg.chunk, workspace=ws)
+    y_on, _ = ttcd.fastweight_scan_on_policy(*a, cfg.chunk, workspace=ws)
+    base = torch.matmul(zt[0].float(), a[5].float().t())
+    gap = float(torch.linalg.vector_norm(y_off[0] - y_on[0]))
+    corr = float(torch.linalg.vector_norm(y_on[0] - base))
+    yn = float(torch.linalg.vector_norm(y_on[0]))
+    del a, e6, ws, y_off, y_on, base
     return {"kernel": "fast-weight path: off-policy (ttcd_fastweight_scan), on-policy "
                       "recurrence (ttcd_fastweight_scan_on_policy), unprojected write "
                       "(ttcd_fastweight_scan_eq6)",
             "off_policy_ms": off_ms, "on_policy_ms": on_ms, "on_over_off": on_ms / off_ms,
             "eq6_unprojected_ms": eq6_ms,
+            "off_vs_on_gap_rel_correction": gap / corr, "off_vs_on_gap_rel_y": gap / yn,
             "tokens": cfg.batch * cfg.seq, "chunks": cfg.n_chunks}
 
 
@@ -298,6 +307,9 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=20480,
                     help="tokens of the oracle CPU baseline sample (0 = skip)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step section")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the LSE-combination and update-rule sections (the counter passes "
+                         "then see only the fused attention call)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (a reference "
                          "kernel of known traffic for scaling memory counters)")
@@ -366,8 +378,9 @@ def main():
     # shifted far-band call, exact merge), for the fused-versus-split figure
     sws = torch.empty(max(256, ttcd.lib().ttcd_dual_window_attn_lse_split_workspace_size(
         ttcd.attn_desc(q, k, cfg.w_teacher, cfg.w_student))), dtype=torch.uint8, device=dev)
-    split_ms = time_events(lambda: ttcd.dual_window_attn_lse_split(
-        q, k, v, cfg.w_teacher, cfg.w_student, with_lse=False, out=(o_t, o_s), workspace=sws),
+    split_ms = None if args.no_variants else time_events(
+        lambda: ttcd.dual_window_attn_lse_split(q, k, v, cfg.w_teacher, cfg.w_student,
+                                                with_lse=False, out=(o_t, o_s), workspace=sws),
         n_att, stream)
 
     res = {
@@ -392,17 +405,19 @@ def main():
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic("attention"),
                      "ms_per_launch": att_ms, "algorithmic_tflop": flops / 1e12},
-        "lse_split": {"kernel": "LSE-combination path (ttcd_dual_window_attn_lse_split)",
-                      "ms_per_launch": split_ms, "achieved": flops / (split_ms * 1e-3) / 1e12,
-                      "unit": "TFLOP/s", "fused_ms_per_launch": att_ms,
-                      "fused_saving": 1.0 - att_ms / split_ms},
     }
+    if split_ms is not None:
+        res["lse_split"] = {"kernel": "LSE-combination path (ttcd_dual_window_attn_lse_split)",
+                            "ms_per_launch": split_ms,
+                            "achieved": flops / (split_ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+                            "fused_ms_per_launch": att_ms, "fused_saving": 1.0 - att_ms / split_ms}
     del q, k, v, wd, x, out, ws, o_t, o_s, aws, sws
     torch.cuda.empty_cache()
     res["scan"] = scan_roofline(cfg, dev, n_att)
     torch.cuda.empty_cache()
-    res["update_rules"] = update_rules_bench(cfg, dev, 5)
-    torch.cuda.empty_cache()
+    if not args.no_variants:
+        res["update_rules"] = update_rules_bench(cfg, dev, 5)
+        torch.cuda.empty_cache()
     if not args.no_decode:
         res["decode"] = decode_bench(dev, n_att)
         torch.cuda.empty_cache()
