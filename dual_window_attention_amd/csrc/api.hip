@@ -472,6 +472,7 @@ struct OnPolicyBufs {
   float* s32;      // [d, f] running state (when the caller passes no state_out)
   void* u;         // [B, Tpad, f] U = Dbar W_proj^T
   float* part;     // [nsplit, d, C] split-K partials
+  float* dw;       // [2, d, f] the chunk write, split in two over its tokens
 };
 
 void plan_on_policy(int B, int T, int d, int f, int C, int dt, Plan& p, FwBufs& w,
@@ -480,6 +481,7 @@ void plan_on_policy(int B, int T, int d, int f, int C, int dt, Plan& p, FwBufs& 
   o.s32 = (float*)p.take((size_t)d * f * sizeof(float));
   o.u = p.take((size_t)B * w.Tpad * f * dsize(dt));
   o.part = (float*)p.take((size_t)on_policy_split(d, C, f) * d * C * sizeof(float));
+  o.dw = (float*)p.take((size_t)2 * d * f * sizeof(float));
 }
 
 // The on-policy recurrence: chunk i's residual is projected by S_i.
@@ -530,15 +532,18 @@ hipError_t run_fw_on_policy(int B, int T, int d, int f, int C, int kc, float eps
       if ((e = launch_splitk_reduce(o.part, ns, (long)d * C, C, w.sc + (size_t)b * w.Tpad + c0,
                                     rst, w.Tpad, d, ncol, dt, s)) != hipSuccess)
         return e;
-      // dW_i = R~^T_i Zbar_S,i^T  (fp32)
+      // dW_i = R~^T_i Zbar_S,i^T  (fp32), its token sum cut in two halves when
+      // they stay multiples of 64 (twice the workgroups); the step adds both
+      const int ns2 = ncol % 128 == 0 ? 2 : 1;
       g = GemmArgs{};
       g.A = rst; g.lda = w.Tpad; g.B = (const char*)w.zbt + ((size_t)b * f * w.Tpad + c0) * es;
-      g.ldb = w.Tpad; g.C = w.dw; g.ldc = f; g.M = d; g.N = f; g.K = ncol; g.in_dt = dt;
-      g.out_dt = F32; g.epi = EPI_STORE; g.batch = 1;
+      g.ldb = w.Tpad; g.C = o.dw; g.ldc = f; g.M = d; g.N = f; g.K = ncol / ns2; g.in_dt = dt;
+      g.out_dt = F32; g.epi = EPI_STORE; g.batch = ns2; g.sA = ncol / ns2; g.sB = ncol / ns2;
+      g.sC = df;
       if ((e = launch_gemm(g, s)) != hipSuccess) return e;
       // S_{i+1} = S_i + dW_i; its element-type copy is states[i]
       void* s16 = i < nstates ? (char*)w.states + ((size_t)b * nstates + i) * df * es : nullptr;
-      if ((e = launch_state_step(w.dw, s32, s16, df, dt, s)) != hipSuccess) return e;
+      if ((e = launch_state_step(o.dw, ns2, s32, s16, df, dt, s)) != hipSuccess) return e;
       if (s16) Si = s16;
     }
   }

@@ -137,7 +137,7 @@ hipError_t launch_fill(void* p, long n, float v, int dt, hipStream_t s);
 hipError_t launch_splitk_reduce(const float* part, int nsplit, long zstride, int ldp,
                                 const float* colscale, void* out, long ldo, int M, int N, int dt,
                                 hipStream_t s);
-hipError_t launch_state_step(const float* dw, float* s32, void* s16, long n, int dt,
+hipError_t launch_state_step(const float* dw, int nsplit, float* s32, void* s16, long n, int dt,
                              hipStream_t s);
 size_t fw_stream_part_bytes(int B, int T, int f);
 

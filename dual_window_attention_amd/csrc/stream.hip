@@ -315,11 +315,12 @@ __global__ void __launch_bounds__(256) fill_kernel(T* __restrict__ p, long n, fl
 
 template <typename T>
 __global__ void __launch_bounds__(256)
-state_step_kernel(const float* __restrict__ dw, float* __restrict__ s32, T* __restrict__ s16,
-                  long n) {
+state_step_kernel(const float* __restrict__ dw, int nsplit, float* __restrict__ s32,
+                  T* __restrict__ s16, long n) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
-  const float v = s32[i] + dw[i];
+  float v = s32[i];
+  for (int z = 0; z < nsplit; ++z) v += dw[z * n + i];     // split-K partials of the write
   s32[i] = v;
   if (s16) elem<T>::st(s16 + i, v);
 }
@@ -570,13 +571,15 @@ hipError_t launch_splitk_reduce(const float* part, int nsplit, long zstride, int
   return hipGetLastError();
 }
 
-hipError_t launch_state_step(const float* dw, float* s32, void* s16, long n, int dt,
+hipError_t launch_state_step(const float* dw, int nsplit, float* s32, void* s16, long n, int dt,
                              hipStream_t s) {
   const dim3 grid((unsigned)((n + 255) / 256));
   if (dt == BF16)
-    hipLaunchKernelGGL((state_step_kernel<bf16_t>), grid, dim3(256), 0, s, dw, s32, (bf16_t*)s16, n);
+    hipLaunchKernelGGL((state_step_kernel<bf16_t>), grid, dim3(256), 0, s, dw, nsplit, s32, (bf16_t*)s16,
+                       n);
   else
-    hipLaunchKernelGGL((state_step_kernel<float>), grid, dim3(256), 0, s, dw, s32, (float*)s16, n);
+    hipLaunchKernelGGL((state_step_kernel<float>), grid, dim3(256), 0, s, dw, nsplit, s32, (float*)s16,
+                       n);
   return hipGetLastError();
 }
 
