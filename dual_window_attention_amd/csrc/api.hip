@@ -207,8 +207,9 @@ hipError_t run_fw(int B, int T, int d, int f, int C, int kc, float eps, int dt,
   g.colscale = w.sc; g.batch = B; g.sA = 0; g.sB = (long)w.Tpad * f;
   g.sC = (long)d * w.Tpad; g.sScale = w.Tpad;
   if ((e = launch_gemm(g, s)) != hipSuccess) return e;
-  // (4) chunk writes dW_j = Rs^T_j Zbar_S,j^T (fp32, all chunks at once), then the causal
-  //     prefix S_{j+1} = W0 + sum_{i<=j} dW_i: states S_1 .. S_{N-1} (and S_N when asked for)
+  // (4) chunk writes dW_j = Rs^T_j Zbar_S,j^T (fp32 accumulation, stored in the element
+  //     type, all chunks at once), then the causal prefix S_{j+1} = W0 + sum_{i<=j} dW_i
+  //     in fp32: states S_1 .. S_{N-1} (and S_N when asked for)
   const int nstates = N - 1;
   const int nwrites = state_out ? N : nstates;
   if (nwrites > 0) {
@@ -216,10 +217,10 @@ hipError_t run_fw(int B, int T, int d, int f, int C, int kc, float eps, int dt,
     for (int b = 0; b < B; ++b) {
       const char* ab = (const char*)w.rst + (size_t)b * d * w.Tpad * dsize(dt);
       const char* bb = (const char*)w.zbt + (size_t)b * f * w.Tpad * dsize(dt);
-      float* cb = w.dw + (size_t)b * N * d * f;
+      char* cb = (char*)w.dw + (size_t)b * N * d * f * dsize(dt);
       g = GemmArgs{};
       g.lda = w.Tpad; g.ldb = w.Tpad; g.ldc = f; g.M = d; g.N = f;
-      g.in_dt = dt; g.out_dt = F32; g.epi = EPI_STORE;
+      g.in_dt = dt; g.out_dt = dt; g.epi = EPI_STORE;
       if (nfull > 0) {
         g.A = ab; g.B = bb; g.C = cb; g.K = C;
         g.batch = nfull; g.sA = C; g.sB = C; g.sC = (long)d * f;
@@ -229,7 +230,7 @@ hipError_t run_fw(int B, int T, int d, int f, int C, int kc, float eps, int dt,
         // the short last chunk: its columns past T are zero up to Tpad
         const long j0 = (long)nfull * C;
         g.A = ab + j0 * dsize(dt); g.B = bb + j0 * dsize(dt);
-        g.C = cb + (size_t)nfull * d * f; g.K = (int)(w.Tpad - j0); g.batch = 1;
+        g.C = cb + (size_t)nfull * d * f * dsize(dt); g.K = (int)(w.Tpad - j0); g.batch = 1;
         if ((e = launch_gemm(g, s)) != hipSuccess) return e;
       }
     }

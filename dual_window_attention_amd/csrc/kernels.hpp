@@ -90,9 +90,9 @@ size_t gemm_skinny_ws_floats(int M, int N, int K, int epi);
 // Causal prefix of the chunk writes (papernotes.org notes, key design 2):
 //   S_{j+1} = W0 + sum_{i <= j} dW_i, kept in fp32 while walking j;
 //   states[b, j] = S_{j+1} (st_dt) for j < nstates, final_out[b] = S_{nwrites}.
-//   dw [B, dw_chunks, n] fp32 (the first nwrites chunks of each batch element
+//   dw [B, dw_chunks, n] in st_dt (the first nwrites chunks of each batch element
 //   are read), w0 [n] w0_dt, states [B, nstates, n], final_out [B, n], n = d * f.
-hipError_t launch_state_prefix(const float* dw, long dw_chunks, const void* w0, void* states,
+hipError_t launch_state_prefix(const void* dw, long dw_chunks, const void* w0, void* states,
                                float* final_out, long n, int nstates, int nwrites, int batch,
                                int w0_dt, int st_dt, hipStream_t s);
 

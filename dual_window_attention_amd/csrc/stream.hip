@@ -328,9 +328,9 @@ state_step_kernel(const float* __restrict__ dw, int nsplit, float* __restrict__ 
 // --------------------------------------------------------------- state prefix
 // Each thread owns 4 consecutive weight entries and walks the chunk writes in
 // order, 8 loads in flight at a time; the running sum never leaves fp32.
-template <typename W0T, typename StT>
+template <typename DwT, typename W0T, typename StT>
 __global__ void __launch_bounds__(256)
-state_prefix_kernel(const float* __restrict__ dw, long dw_chunks, const W0T* __restrict__ w0,
+state_prefix_kernel(const DwT* __restrict__ dw, long dw_chunks, const W0T* __restrict__ w0,
                     StT* __restrict__ states, float* __restrict__ final_out, long n,
                     int nstates, int nwrites) {
   const int b = blockIdx.y;
@@ -339,14 +339,25 @@ state_prefix_kernel(const float* __restrict__ dw, long dw_chunks, const W0T* __r
   float acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = ldf(w0 + e + i);
-  const float* src = dw + (size_t)b * dw_chunks * n + e;
+  const DwT* src = dw + (size_t)b * dw_chunks * n + e;
   StT* dst = states + (size_t)b * nstates * n + e;
   constexpr int U = 8;
   for (int j0 = 0; j0 < nwrites; j0 += U) {
     f32x4 v[U];
+    if constexpr (sizeof(DwT) == 2) {
+      uint2 raw[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (j0 + u < nwrites) v[u] = *reinterpret_cast<const f32x4*>(src + (size_t)(j0 + u) * n);
+      for (int u = 0; u < U; ++u)
+        if (j0 + u < nwrites) raw[u] = *reinterpret_cast<const uint2*>(src + (size_t)(j0 + u) * n);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        v[u] = f32x4{__uint_as_float(raw[u].x << 16), __uint_as_float(raw[u].x & 0xFFFF0000u),
+                     __uint_as_float(raw[u].y << 16), __uint_as_float(raw[u].y & 0xFFFF0000u)};
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (j0 + u < nwrites) v[u] = *reinterpret_cast<const f32x4*>(src + (size_t)(j0 + u) * n);
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = j0 + u;
@@ -583,19 +594,20 @@ hipError_t launch_state_step(const float* dw, int nsplit, float* s32, void* s16,
   return hipGetLastError();
 }
 
-hipError_t launch_state_prefix(const float* dw, long dw_chunks, const void* w0, void* states,
+hipError_t launch_state_prefix(const void* dw, long dw_chunks, const void* w0, void* states,
                                float* final_out, long n, int nstates, int nwrites, int batch,
                                int w0_dt, int st_dt, hipStream_t s) {
   if (nwrites <= 0 || n % 4) return nwrites <= 0 ? hipSuccess : hipErrorInvalidValue;
   dim3 grid((unsigned)((n / 4 + 255) / 256), batch);
+  // bf16 operands: the chunk writes arrive in bf16; fp32 operands: in fp32
   if (w0_dt == BF16 && st_dt == BF16)
-    hipLaunchKernelGGL((state_prefix_kernel<bf16_t, bf16_t>), grid, dim3(256), 0, s, dw,
-                       dw_chunks, (const bf16_t*)w0, (bf16_t*)states, final_out, n, nstates,
-                       nwrites);
+    hipLaunchKernelGGL((state_prefix_kernel<bf16_t, bf16_t, bf16_t>), grid, dim3(256), 0, s,
+                       (const bf16_t*)dw, dw_chunks, (const bf16_t*)w0, (bf16_t*)states,
+                       final_out, n, nstates, nwrites);
   else if (w0_dt == F32 && st_dt == F32)
-    hipLaunchKernelGGL((state_prefix_kernel<float, float>), grid, dim3(256), 0, s, dw,
-                       dw_chunks, (const float*)w0, (float*)states, final_out, n, nstates,
-                       nwrites);
+    hipLaunchKernelGGL((state_prefix_kernel<float, float, float>), grid, dim3(256), 0, s,
+                       (const float*)dw, dw_chunks, (const float*)w0, (float*)states, final_out,
+                       n, nstates, nwrites);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
