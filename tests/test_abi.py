@@ -128,3 +128,34 @@ def test_no_oracle_import_in_product_code():
                 text = open(os.path.join(dirpath, fn)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle", text, flags=re.M), fn
                 assert "ttcd_oracle" not in text, fn
+
+
+def test_update_rule_variants_validate_before_any_launch():
+    """The on-policy and unprojected-write entry points check shapes,
+    pointers and workspace size on the host and return an error code."""
+    from dual_window_attention_amd import ttcd
+    lib = ttcd.lib()
+    fake = C.c_void_p(1 << 20)
+    good = ttcd.FwDesc(1, 65536, 1024, 3072, 1024, 4, 0.0, 1, 0)
+    n_scan = lib.ttcd_fastweight_scan_workspace_size(C.byref(good))
+    n_on = lib.ttcd_fastweight_scan_on_policy_workspace_size(C.byref(good))
+    n_e6 = lib.ttcd_fastweight_scan_eq6_workspace_size(C.byref(good))
+    # on-policy adds the fp32 running state, U = Dbar W_proj^T and the split partials
+    assert n_on >= n_scan + (1024 * 3072 * 4 + 65536 * 3072 * 2)
+    # the unprojected write adds one row of unit taps
+    assert n_scan < n_e6 <= n_scan + 3072 * 2 + 256
+    bad = ttcd.FwDesc(1, 100, 1024, 3072, 24, 4, 0.0, 1, 0)     # chunk not a multiple of 16
+    assert lib.ttcd_fastweight_scan_on_policy_workspace_size(C.byref(bad)) == 0
+    assert lib.ttcd_fastweight_scan_eq6_workspace_size(C.byref(bad)) == 0
+    assert lib.ttcd_fastweight_scan_on_policy(C.byref(bad), *([fake] * 10), fake, 1 << 40,
+                                              None) == 2
+    assert lib.ttcd_fastweight_scan_eq6(C.byref(bad), *([fake] * 7), fake, 1 << 40, None) == 2
+    # a NULL input, then too small a workspace
+    args = [fake] * 10
+    args[0] = None
+    assert lib.ttcd_fastweight_scan_on_policy(C.byref(good), *args, fake, 1 << 40, None) == 1
+    assert lib.ttcd_fastweight_scan_eq6(C.byref(good), None, *([fake] * 6), fake, 1 << 40,
+                                        None) == 1
+    assert lib.ttcd_fastweight_scan_on_policy(C.byref(good), *([fake] * 10), fake, n_on - 1,
+                                              None) == 4
+    assert lib.ttcd_fastweight_scan_eq6(C.byref(good), *([fake] * 7), fake, n_e6 - 1, None) == 4
