@@ -116,3 +116,31 @@ def test_on_policy_qwen3_dims_ragged():
     shapes) over 4.5 chunks."""
     check_on_policy(BASE.scaled(batch=1, seq=4500, d_model=1024, d_ff=3072, chunk=1024,
                                 conv_k=4, seed=49))
+
+
+def test_on_policy_qwen3_64k_full():
+    """The 64K workload's fast-weight shapes at full length (64 chunks):
+    sampled rows of every chunk and the final state against the oracle's
+    recurrence, in the launch configuration the benchmark times."""
+    from dual_window_attention_amd import ttcd
+    cfg = BASE
+    say(f"on-policy full {cfg.name} T={cfg.seq} C={cfg.chunk}")
+    z = I.hidden_activations(cfg)
+    w = I.layer_weights(cfg)
+    beta = I.beta_for(cfg)
+    zt, zs = I.to_torch(z["z_t"]), I.to_torch(z["z_s"])
+    y, st = ttcd.fastweight_scan_on_policy(zt, zs, zt, I.to_torch(w["conv_t"]),
+                                           I.to_torch(w["conv_s"]), I.to_torch(w["w_down0"]),
+                                           I.to_torch(w["w_proj"]), I.f32_to_torch(beta),
+                                           cfg.chunk, want_state=True)
+    torch.cuda.synchronize()
+    rows = np.arange(5, cfg.seq, 331)
+    y = to_np(y)[0, rows]
+    st = to_np(st)[0]
+    del zt, zs
+    torch.cuda.empty_cache()
+    ref = O.fastweight_scan_on_policy(z["z_t"].f64(), z["z_s"].f64(), z["z_t"].f64(),
+                                      w["conv_t"].f64(), w["conv_s"].f64(), w["w_down0"].f64(),
+                                      w["w_proj"].f64(), beta.astype(np.float64), cfg.chunk)
+    assert_close(y, ref["y"][0, rows], tol_for(cfg.dtype), f"y on {len(rows)} sampled rows")
+    assert_close(st, ref["state"][0], tol_for(cfg.dtype), "state after all 64 writes")
