@@ -81,3 +81,27 @@ def test_eq6_equal_paths_write_nothing():
                                      want_state=True)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(to_np(st)[0], w["w_down0"].f64())
+
+
+def test_eq6_qwen3_64k_full():
+    """The 64K workload's fast-weight shapes at full length: sampled rows of
+    every chunk and the final state against the oracle."""
+    from dual_window_attention_amd import ttcd
+    cfg = BASE
+    say(f"eq6 full {cfg.name} T={cfg.seq} C={cfg.chunk}")
+    z = I.hidden_activations(cfg)
+    w = I.layer_weights(cfg)
+    beta = eq6_beta(cfg, z["z_s"].f64())
+    zt, zs = I.to_torch(z["z_t"]), I.to_torch(z["z_s"])
+    y, st = ttcd.fastweight_scan_eq6(zt, zs, zt, I.to_torch(w["w_down0"]), I.f32_to_torch(beta),
+                                     cfg.chunk, want_state=True)
+    torch.cuda.synchronize()
+    rows = np.arange(7, cfg.seq, 331)
+    y = to_np(y)[0, rows]
+    st = to_np(st)[0]
+    del zt, zs
+    torch.cuda.empty_cache()
+    ref = O.fastweight_scan_eq6(z["z_t"].f64(), z["z_s"].f64(), z["z_t"].f64(),
+                                w["w_down0"].f64(), beta.astype(np.float64), cfg.chunk)
+    assert_close(y, ref["y"][0, rows], tol_for(cfg.dtype), f"y on {len(rows)} sampled rows")
+    assert_close(st, ref["state"][0], tol_for(cfg.dtype), "state after all 64 writes")
