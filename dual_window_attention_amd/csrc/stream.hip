@@ -388,21 +388,47 @@ rmsnorm_kernel(const float* __restrict__ h, const GT* __restrict__ gamma, OutT* 
   const long row = (long)blockIdx.x * 4 + wave;
   if (row >= rows) return;
   const float* hr = h + row * d;
+  // rows of up to 1024 values stay in registers between the two passes
+  // (all loads in flight together); longer rows are read twice
+  const bool held = d <= 1024;
+  f32x4 v[4];
   float ss = 0.f;
-  for (int i = lane * 4; i < d; i += 256) {
-    f32x4 v = *reinterpret_cast<const f32x4*>(hr + i);
-    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  if (held) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = lane * 4 + 256 * k;
+      v[k] = i < d ? *reinterpret_cast<const f32x4*>(hr + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      ss += v[k][0] * v[k][0] + v[k][1] * v[k][1] + v[k][2] * v[k][2] + v[k][3] * v[k][3];
+  } else {
+    for (int i = lane * 4; i < d; i += 256) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(hr + i);
+      ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+    }
   }
   ss = wave_sum(ss);
   const float rs = 1.f / sqrtf(ss / d + eps);
   OutT* ur = u + row * d;
-  for (int i = lane * 4; i < d; i += 256) {
-    f32x4 v = *reinterpret_cast<const f32x4*>(hr + i);
+  // four outputs per lane leave in one store
+  auto emit = [&](int i, f32x4 x) __attribute__((always_inline)) {
+    float o[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float gm = gamma ? ldf(gamma + i + e) : 1.f;
-      stf(ur + i + e, v[e] * rs * gm);
+    for (int e = 0; e < 4; ++e) o[e] = x[e] * rs * (gamma ? ldf(gamma + i + e) : 1.f);
+    if constexpr (sizeof(OutT) == 2)
+      *reinterpret_cast<uint2*>(ur + i) = uint2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    else
+      *reinterpret_cast<f32x4*>(ur + i) = f32x4{o[0], o[1], o[2], o[3]};
+  };
+  if (held) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = lane * 4 + 256 * k;
+      if (i < d) emit(i, v[k]);
     }
+  } else {
+    for (int i = lane * 4; i < d; i += 256) emit(i, *reinterpret_cast<const f32x4*>(hr + i));
   }
 }
 
