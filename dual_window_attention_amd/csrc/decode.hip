@@ -89,8 +89,12 @@ decode_attn_split(const T* __restrict__ q, const T* __restrict__ k, const T* __r
       for (int e = 0; e < 8; ++e) o[e] = __uint_as_float(r[e / 4][e % 4]);
     }
   };
+  // Rows are fetched only from [ks, ke), which lies inside [0, pos] <
+  // kv_rows; a split with no key (ks >= ke) fetches nothing and leaves the
+  // empty states (m = -inf, l = 0, acc = 0), which merge exactly.  The host
+  // launches no such split, but the kernel does not rely on it.
   Raw nk, nv;
-  {
+  if (ks < ke) {
     const int j = ks + wave * KPW + kg;
     fetch(j < ke ? j : ks, nk, nv);
   }
@@ -102,7 +106,7 @@ decode_attn_split(const T* __restrict__ q, const T* __restrict__ k, const T* __r
     unpack(nv, vv);
     {
       const int jn = j + 4 * KPW;
-      fetch(jn < ke ? jn : ks, nk, nv);       // (a valid row either way)
+      fetch(jn < ke ? jn : ks, nk, nv);       // ks < ke inside the loop
     }
     if (!ok) {
 #pragma unroll
@@ -443,6 +447,13 @@ void decode_attn_plan(int wT, int* nsplit, int* split_len) {
   *nsplit = (wT + sl - 1) / sl;
 }
 
+// Splits that hold at least one key of query position pos: the window
+// [max(0, pos - wT + 1), pos] has min(wT, pos + 1) keys.
+int decode_attn_splits_used(int wT, int pos, int split_len) {
+  const int keys = wT < pos + 1 ? wT : pos + 1;
+  return (keys + split_len - 1) / split_len;
+}
+
 size_t decode_attn_part_bytes(int B, int Hq, int D, int nsplit) {
   return (size_t)B * Hq * nsplit * 2 * (D + 2) * sizeof(float);
 }
@@ -451,35 +462,38 @@ hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   if (G > GMAX) return hipErrorInvalidValue;
   const float c = a.scale * 1.4426950408889634f;
-  dim3 grid(a.nsplit, a.Hkv, a.B);
+  // only the splits that hold keys (at most a.nsplit, the planned count)
+  const int ns = decode_attn_splits_used(a.wT, a.pos, a.split_len);
+  if (ns < 1 || ns > a.nsplit) return hipErrorInvalidValue;
+  dim3 grid(ns, a.Hkv, a.B);
   if (a.in_dt == BF16) {
     if (a.D == 64)
       hipLaunchKernelGGL((decode_attn_split<bf16_t, 64>), grid, dim3(256), 0, s,
                          (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, a.part,
-                         a.pos, a.kv_rows, a.Hq, a.Hkv, a.wT, a.wS, c, a.nsplit, a.split_len);
+                         a.pos, a.kv_rows, a.Hq, a.Hkv, a.wT, a.wS, c, ns, a.split_len);
     else
       hipLaunchKernelGGL((decode_attn_split<bf16_t, 128>), grid, dim3(256), 0, s,
                          (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, a.part,
-                         a.pos, a.kv_rows, a.Hq, a.Hkv, a.wT, a.wS, c, a.nsplit, a.split_len);
+                         a.pos, a.kv_rows, a.Hq, a.Hkv, a.wT, a.wS, c, ns, a.split_len);
   } else {
     if (a.D == 64)
       hipLaunchKernelGGL((decode_attn_split<float, 64>), grid, dim3(256), 0, s,
                          (const float*)a.q, (const float*)a.k, (const float*)a.v, a.part,
-                         a.pos, a.kv_rows, a.Hq, a.Hkv, a.wT, a.wS, c, a.nsplit, a.split_len);
+                         a.pos, a.kv_rows, a.Hq, a.Hkv, a.wT, a.wS, c, ns, a.split_len);
     else
       hipLaunchKernelGGL((decode_attn_split<float, 128>), grid, dim3(256), 0, s,
                          (const float*)a.q, (const float*)a.k, (const float*)a.v, a.part,
-                         a.pos, a.kv_rows, a.Hq, a.Hkv, a.wT, a.wS, c, a.nsplit, a.split_len);
+                         a.pos, a.kv_rows, a.Hq, a.Hkv, a.wT, a.wS, c, ns, a.split_len);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2(a.B * a.Hq);
   if (a.out_dt == BF16)
     hipLaunchKernelGGL(decode_attn_combine<bf16_t>, g2, dim3(128), 0, s, a.part,
-                       (bf16_t*)a.o_t, (bf16_t*)a.o_s, a.lse_t, a.lse_s, a.Hq, a.D, a.nsplit);
+                       (bf16_t*)a.o_t, (bf16_t*)a.o_s, a.lse_t, a.lse_s, a.Hq, a.D, ns);
   else
     hipLaunchKernelGGL(decode_attn_combine<float>, g2, dim3(128), 0, s, a.part, (float*)a.o_t,
-                       (float*)a.o_s, a.lse_t, a.lse_s, a.Hq, a.D, a.nsplit);
+                       (float*)a.o_s, a.lse_t, a.lse_s, a.Hq, a.D, ns);
   return hipGetLastError();
 }
 
