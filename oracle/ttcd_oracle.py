@@ -321,21 +321,28 @@ def fastweight_scan(z_t, z_s, z_main, conv_t, conv_s, w_down0, w_proj, beta,
     """Fast-weight stream + prefix + apply for a batch.
 
     z_* [B,T,f], beta [B, n_chunks].  Returns dict with y [B,T,d],
-    state [B,d,f] (= S_N, the weight after every chunk's write), r [B,T,d],
-    k [B,T,f] (unit keys), dbar [B,T,f].
+    state [B,d,f] (= S_N, the weight after every chunk's write),
+    state_complete [B,d,f] (= S_n, n = T // C: the weight after the writes
+    of the chunks that hold all C tokens -- a short last chunk is still
+    pending, its writes take effect once it completes, the decode position
+    convention), r [B,T,d], k [B,T,f] (unit keys), dbar [B,T,f].
     """
     z_t, z_s, z_main = _f64(z_t), _f64(z_s), _f64(z_main)
     B, T, f = z_t.shape
     d = w_down0.shape[0]
     y = np.zeros((B, T, d), F64)
     st = np.zeros((B, d, f), F64)
+    st_done = np.zeros((B, d, f), F64)
     rr = np.zeros((B, T, d), F64)
     kk = np.zeros((B, T, f), F64)
     dd = np.zeros((B, T, f), F64)
+    n_done = T // C
     for b in range(B):
         r, k, dbar, _ = fastweight_terms(z_t[b], z_s[b], conv_t, conv_s, w_down0, w_proj, eps)
         if form == "prefix":
-            yb, S = fastweight_apply_prefix(r, k, beta[b], z_main[b], w_down0, C)
+            yb, S, states = fastweight_apply_prefix(r, k, beta[b], z_main[b], w_down0, C,
+                                                    return_states=True)
+            st_done[b] = S if n_done == len(states) else states[n_done]
         elif form == "explicit":
             yb = fastweight_apply_explicit(r, k, beta[b], z_main[b], w_down0, C)
             S = None
@@ -348,7 +355,7 @@ def fastweight_scan(z_t, z_s, z_main, conv_t, conv_s, w_down0, w_proj, beta,
         if S is not None:
             st[b] = S
         rr[b], kk[b], dd[b] = r, k, dbar
-    return {"y": y, "state": st, "r": rr, "k": kk, "dbar": dd}
+    return {"y": y, "state": st, "state_complete": st_done, "r": rr, "k": kk, "dbar": dd}
 
 
 def fastweight_scan_on_policy(z_t, z_s, z_main, conv_t, conv_s, w_down0, w_proj, beta,
@@ -363,23 +370,28 @@ def fastweight_scan_on_policy(z_t, z_s, z_main, conv_t, conv_s, w_down0, w_proj,
         S_{i+1} = S_i + beta_i R_i^T K_i,            S_0 = W_down^(0)
 
     dbar and the unit keys are those of ``fastweight_terms`` (they do not
-    depend on the weight).  Returns dict with y [B,T,d] and state [B,d,f]
-    (= S_N)."""
+    depend on the weight).  Returns dict with y [B,T,d], state [B,d,f]
+    (= S_N) and state_complete (the weight after the complete chunks, as in
+    ``fastweight_scan``)."""
     z_t, z_s, z_main = _f64(z_t), _f64(z_s), _f64(z_main)
     B, T, f = z_t.shape
     d = w_down0.shape[0]
     wp = _f64(w_proj)
     y = np.zeros((B, T, d), F64)
     st = np.zeros((B, d, f), F64)
+    st_done = np.zeros((B, d, f), F64)
     for b in range(B):
         _, k, dbar, _ = fastweight_terms(z_t[b], z_s[b], conv_t, conv_s, w_down0, w_proj, eps)
         S = _f64(w_down0).copy()
+        st_done[b] = S
         for i, (a, e) in enumerate(chunk_bounds(T, C)):
             y[b, a:e] = z_main[b, a:e] @ S.T
             r = (dbar[a:e] @ wp.T) @ S.T
             S = S + float(beta[b, i]) * (r.T @ k[a:e])
+            if e - a == C:
+                st_done[b] = S
         st[b] = S
-    return {"y": y, "state": st}
+    return {"y": y, "state": st, "state_complete": st_done}
 
 
 def fastweight_scan_eq6(z_t, z_s, z_main, w_down0, beta, C: int):
@@ -393,23 +405,28 @@ def fastweight_scan_eq6(z_t, z_s, z_main, w_down0, beta, C: int):
         dW_i    = beta_i sum_{t in chunk i} W0 (z_T,t - z_S,t) z_S,t^T
         S_{i+1} = S_i + dW_i,   S_0 = W0,   y_t = S_{floor(t/C)} z_main[t]
 
-    Returns dict with y [B,T,d], state [B,d,f] (= S_N) and dw [B,N,d,f]."""
+    Returns dict with y [B,T,d], state [B,d,f] (= S_N), state_complete
+    (the weight after the complete chunks) and dw [B,N,d,f]."""
     z_t, z_s, z_main = _f64(z_t), _f64(z_s), _f64(z_main)
     w0 = _f64(w_down0)
     B, T, f = z_t.shape
     bounds = chunk_bounds(T, C)
     y = np.zeros((B, T, w0.shape[0]), F64)
     st = np.zeros((B,) + w0.shape, F64)
+    st_done = np.zeros((B,) + w0.shape, F64)
     dws = np.zeros((B, len(bounds)) + w0.shape, F64)
     for b in range(B):
         S = w0.copy()
+        st_done[b] = S
         for i, (a, e) in enumerate(bounds):
             y[b, a:e] = z_main[b, a:e] @ S.T
             gap = (z_t[b, a:e] - z_s[b, a:e]) @ w0.T         # teacher - student outputs
             dws[b, i] = float(beta[b, i]) * (gap.T @ z_s[b, a:e])
             S = S + dws[b, i]
+            if e - a == C:
+                st_done[b] = S
         st[b] = S
-    return {"y": y, "state": st, "dw": dws}
+    return {"y": y, "state": st, "state_complete": st_done, "dw": dws}
 
 
 # ==========================================================================
@@ -436,7 +453,8 @@ def layer_forward(q, k, v, x, w, w_teacher: int, w_student: int, C: int,
     out = h_main + fw["y"]
     return {"out": out, "o_t": o_t, "o_s": o_s, "lse_t": lse_t, "lse_s": lse_s,
             "h_t": h_t, "h_s": h_s, "z_t": z_t, "z_s": z_s, "y": fw["y"],
-            "r": fw["r"], "k": fw["k"], "dbar": fw["dbar"], "state": fw["state"]}
+            "r": fw["r"], "k": fw["k"], "dbar": fw["dbar"], "state": fw["state"],
+            "state_complete": fw["state_complete"]}
 
 
 def decode_step(q, k_cache, v_cache, x, w, pos: int, w_teacher: int, w_student: int,

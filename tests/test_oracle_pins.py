@@ -318,6 +318,35 @@ def test_writes_act_only_on_strictly_later_chunks():
     assert np.abs(y1[24:] - y0[24:]).max() > 1e-3
 
 
+def test_state_after_complete_chunks_is_the_state_of_the_truncated_sequence():
+    """The weight after the complete chunks of a ragged sequence is the final
+    weight of the same sequence cut after its last complete chunk (the
+    writes are causal: later tokens cannot change them); when T % C == 0 it
+    is the final weight, and T < C leaves W0.  Holds for all three update
+    rules.  A short chunk's write counted in, or one chunk too few, breaks
+    this."""
+    rng = np.random.default_rng(23)
+    s = _scan_inputs(rng, T=30, C=8)
+    fns = [
+        lambda zt, zs, b: O.fastweight_scan(zt[None], zs[None], zt[None], s["conv_t"],
+                                            s["conv_s"], s["w0"], s["wp"], b[None], s["C"]),
+        lambda zt, zs, b: O.fastweight_scan_on_policy(zt[None], zs[None], zt[None], s["conv_t"],
+                                                      s["conv_s"], s["w0"], s["wp"], b[None],
+                                                      s["C"]),
+        lambda zt, zs, b: O.fastweight_scan_eq6(zt[None], zs[None], zt[None], s["w0"], b[None],
+                                                s["C"]),
+    ]
+    for fn in fns:
+        ragged = fn(s["z_t"], s["z_s"], s["beta"])
+        cut = fn(s["z_t"][:24], s["z_s"][:24], s["beta"][:3])
+        np.testing.assert_allclose(ragged["state_complete"], cut["state"],
+                                   atol=1e-12 * np.abs(cut["state"]).max(), rtol=0)
+        np.testing.assert_array_equal(cut["state_complete"], cut["state"])
+        assert np.abs(ragged["state"] - ragged["state_complete"]).max() > 1e-6
+        short = fn(s["z_t"][:5], s["z_s"][:5], s["beta"][:1])
+        np.testing.assert_array_equal(short["state_complete"][0], s["w0"])
+
+
 def test_equal_paths_give_no_update():
     """Equal convs and equal activations: dbar = 0, R = 0, y = W0 z."""
     rng = np.random.default_rng(19)
