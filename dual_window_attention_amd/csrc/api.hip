@@ -154,7 +154,7 @@ ttcd_status check_fw(const ttcd_fw_desc* d) {
 
 struct FwBufs {
   void *dbar, *zbt, *wpt, *m, *rst, *states;
-  float *sc, *part, *dw;
+  float *sc, *inv, *part, *dw;
   int Tpad, N;
 };
 
@@ -165,6 +165,7 @@ void plan_fw(int B, int T, int d, int f, int C, int dt, Plan& p, FwBufs& w) {
   w.dbar = p.take((size_t)B * w.Tpad * f * es);
   w.zbt = p.take((size_t)B * f * w.Tpad * es);
   w.sc = (float*)p.take((size_t)B * w.Tpad * sizeof(float));
+  w.inv = (float*)p.take((size_t)B * w.Tpad * sizeof(float));
   w.part = (float*)p.take(fw_stream_part_bytes(B, T, f));
   w.wpt = p.take((size_t)f * f * es);
   w.m = p.take((size_t)d * f * es);
@@ -175,11 +176,14 @@ void plan_fw(int B, int T, int d, int f, int C, int dt, Plan& p, FwBufs& w) {
 
 // Runs the fast-weight stream, residual projection, prefix states and the
 // apply.  res (fp32 [B*T, d]) non-NULL: out = res + y; else out = y (out_dt).
+// state_out (fp32 [B, d, f]) receives S_n after the n = T / C complete
+// chunks; r_out [B, T, d] and k_out [B, T, f] (element type) the residual
+// terms and unit keys of every token (the low-rank chunk lists).
 hipError_t run_fw(int B, int T, int d, int f, int C, int kc, float eps, int dt,
                   const void* zt, const void* zs, const void* zmain, const void* conv_t,
                   const void* conv_s, const void* w0, const void* wp, const float* beta,
-                  const float* res, void* out, int out_dt, float* state_out, const FwBufs& w,
-                  hipStream_t s, bool eq6 = false) {
+                  const float* res, void* out, int out_dt, float* state_out, void* r_out,
+                  void* k_out, const FwBufs& w, hipStream_t s, bool eq6 = false) {
   // eq6: the unprojected write (residual W0 (z_T - z_S), raw student keys);
   // the caller passes unit identity taps with kc = 1 and wp = NULL
   hipError_t e;
@@ -187,10 +191,12 @@ hipError_t run_fw(int B, int T, int d, int f, int C, int kc, float eps, int dt,
   // (1) conv, difference, key norms
   StreamArgs sa{};
   sa.zt = zt; sa.zs = zs; sa.conv_t = conv_t; sa.conv_s = conv_s; sa.beta = beta;
-  sa.dbar = w.dbar; sa.zbt = w.zbt; sa.sc = w.sc; sa.part = w.part;
+  sa.dbar = w.dbar; sa.zbt = w.zbt; sa.sc = w.sc; sa.inv = k_out ? w.inv : nullptr;
+  sa.part = w.part;
   sa.B = B; sa.T = T; sa.f = f; sa.kc = kc; sa.chunk = C; sa.nchunks = N; sa.eps = eps;
   sa.in_dt = dt; sa.raw_keys = eq6 ? 1 : 0;
   if ((e = launch_fw_stream(sa, s)) != hipSuccess) return e;
+  if (k_out && (e = launch_unit_keys(w.zbt, w.inv, k_out, B, T, f, dt, s)) != hipSuccess) return e;
   GemmArgs g{};
   if (!eq6) {
     // (2) M = W0 W_proj  (as NT: B operand = W_proj^T)
@@ -198,6 +204,14 @@ hipError_t run_fw(int B, int T, int d, int f, int C, int kc, float eps, int dt,
       return e;
     g.A = w0; g.lda = f; g.B = w.wpt; g.ldb = f; g.C = w.m; g.ldc = f;
     g.M = d; g.N = f; g.K = f; g.in_dt = dt; g.out_dt = dt; g.epi = EPI_STORE; g.batch = 1;
+    if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+  }
+  if (r_out) {
+    // r_t = M dbar_t, token-major [B, T, d]
+    g = GemmArgs{};
+    g.A = w.dbar; g.lda = f; g.B = eq6 ? w0 : w.m; g.ldb = f; g.C = r_out; g.ldc = d;
+    g.M = T; g.N = d; g.K = f; g.in_dt = dt; g.out_dt = dt; g.epi = EPI_STORE;
+    g.batch = B; g.sA = (long)w.Tpad * f; g.sB = 0; g.sC = (long)T * d;
     if ((e = launch_gemm(g, s)) != hipSuccess) return e;
   }
   // (3) Rs^T[b] = (M dbar_b^T) * sc_b   -> [d, Tpad]   (M = W0 for eq6)
@@ -209,34 +223,28 @@ hipError_t run_fw(int B, int T, int d, int f, int C, int kc, float eps, int dt,
   if ((e = launch_gemm(g, s)) != hipSuccess) return e;
   // (4) chunk writes dW_j = Rs^T_j Zbar_S,j^T (fp32 accumulation, stored in the element
   //     type, all chunks at once), then the causal prefix S_{j+1} = W0 + sum_{i<=j} dW_i
-  //     in fp32: states S_1 .. S_{N-1} (and S_N when asked for)
+  //     in fp32: states S_1 .. S_{N-1} that the apply reads, and S_n (n = T / C, the
+  //     complete chunks) when asked for.  Every write used is a complete chunk: a short
+  //     last chunk acts on no token here, and its writes are still pending for a decode.
   const int nstates = N - 1;
-  const int nwrites = state_out ? N : nstates;
+  const int nwrites = state_out ? T / C : nstates;   // T / C >= N - 1
   if (nwrites > 0) {
-    const int nfull = std::min(nwrites, T / C);     // chunks holding all C tokens
     for (int b = 0; b < B; ++b) {
-      const char* ab = (const char*)w.rst + (size_t)b * d * w.Tpad * dsize(dt);
-      const char* bb = (const char*)w.zbt + (size_t)b * f * w.Tpad * dsize(dt);
-      char* cb = (char*)w.dw + (size_t)b * N * d * f * dsize(dt);
       g = GemmArgs{};
-      g.lda = w.Tpad; g.ldb = w.Tpad; g.ldc = f; g.M = d; g.N = f;
+      g.A = (const char*)w.rst + (size_t)b * d * w.Tpad * dsize(dt);
+      g.B = (const char*)w.zbt + (size_t)b * f * w.Tpad * dsize(dt);
+      g.C = (char*)w.dw + (size_t)b * N * d * f * dsize(dt);
+      g.lda = w.Tpad; g.ldb = w.Tpad; g.ldc = f; g.M = d; g.N = f; g.K = C;
       g.in_dt = dt; g.out_dt = dt; g.epi = EPI_STORE;
-      if (nfull > 0) {
-        g.A = ab; g.B = bb; g.C = cb; g.K = C;
-        g.batch = nfull; g.sA = C; g.sB = C; g.sC = (long)d * f;
-        if ((e = launch_gemm(g, s)) != hipSuccess) return e;
-      }
-      if (nwrites > nfull) {
-        // the short last chunk: its columns past T are zero up to Tpad
-        const long j0 = (long)nfull * C;
-        g.A = ab + j0 * dsize(dt); g.B = bb + j0 * dsize(dt);
-        g.C = cb + (size_t)nfull * d * f * dsize(dt); g.K = (int)(w.Tpad - j0); g.batch = 1;
-        if ((e = launch_gemm(g, s)) != hipSuccess) return e;
-      }
+      g.batch = nwrites; g.sA = C; g.sB = C; g.sC = (long)d * f;
+      if ((e = launch_gemm(g, s)) != hipSuccess) return e;
     }
     if ((e = launch_state_prefix(w.dw, (long)N, w0, w.states, state_out, (long)d * f, nstates,
                                  nwrites, B, dt, dt, s)) != hipSuccess)
       return e;
+  } else if (state_out) {
+    // no complete chunk: S_0 = W0
+    if ((e = launch_widen_repeat(w0, state_out, (long)d * f, B, dt, s)) != hipSuccess) return e;
   }
   // (5) apply: out = [res +] Z_main S_{t/C}^T
   g = GemmArgs{};
@@ -427,12 +435,13 @@ size_t ttcd_fastweight_scan_workspace_size(const ttcd_fw_desc* d) {
 ttcd_status ttcd_fastweight_scan(const ttcd_fw_desc* d, const void* zt, const void* zs,
                                  const void* zmain, const void* conv_t, const void* conv_s,
                                  const void* w_down0, const void* w_proj, const float* beta,
-                                 void* y, float* state_out, void* ws, size_t ws_bytes,
-                                 void* stream) {
+                                 void* y, float* state_out, void* r_out, void* k_out, void* ws,
+                                 size_t ws_bytes, void* stream) {
   ttcd_status st = check_fw(d);
   if (st != TTCD_OK) return st;
   REQ_PTR(zt); REQ_PTR(zs); REQ_PTR(zmain); REQ_PTR(conv_t); REQ_PTR(conv_s);
   REQ_PTR(w_down0); REQ_PTR(w_proj); REQ_PTR(y); OPT_PTR(state_out);
+  OPT_PTR(r_out); OPT_PTR(k_out);
   if (!beta) return fail(TTCD_ERR_NULL_POINTER, "beta is NULL");
   OPT_PTR4(beta);
   const size_t need = ttcd_fastweight_scan_workspace_size(d);
@@ -446,7 +455,7 @@ ttcd_status ttcd_fastweight_scan(const ttcd_fw_desc* d, const void* zt, const vo
   const float eps = d->l2_eps > 0.f ? d->l2_eps : 1e-12f;
   HIPCHK(run_fw(d->batch, d->seq, d->d_model, d->d_ff, d->chunk, d->conv_k, eps, d->in_dtype, zt,
                 zs, zmain, conv_t, conv_s, w_down0, w_proj, beta, nullptr, y, d->out_dtype,
-                state_out, w, (hipStream_t)stream));
+                state_out, r_out, k_out, w, (hipStream_t)stream));
   return ok();
 }
 
@@ -518,7 +527,9 @@ hipError_t run_fw_on_policy(int B, int T, int d, int f, int C, int kc, float eps
     float* s32 = state_out ? state_out + (size_t)b * df : o.s32;
     if ((e = launch_state_init(w0, s32, df, dt, s)) != hipSuccess) return e;
     const void* Si = w0;
-    const int last = state_out ? N : nstates;          // writes that matter
+    // writes that matter: those the apply reads (chunks 0..N-2) and, for
+    // state_out, every complete chunk (T / C >= N - 1)
+    const int last = state_out ? T / C : nstates;
     for (int i = 0; i < last; ++i) {
       const long c0 = (long)i * C;
       const int ncol = (int)std::min<long>(C, w.Tpad - c0);   // the short last chunk to Tpad
@@ -625,7 +636,7 @@ ttcd_status ttcd_fastweight_scan_eq6(const ttcd_fw_desc* d, const void* zt, cons
   HIPCHK(launch_fill(taps, d->d_ff, 1.f, d->in_dtype, s));
   HIPCHK(run_fw(d->batch, d->seq, d->d_model, d->d_ff, d->chunk, 1, 1e-12f, d->in_dtype, zt, zs,
                 zmain, taps, taps, w_down0, nullptr, beta, nullptr, y, d->out_dtype, state_out,
-                w, s, true));
+                nullptr, nullptr, w, s, true));
   return ok();
 }
 
@@ -774,8 +785,9 @@ ttcd_status ttcd_layer_forward(const ttcd_layer_desc* d, const ttcd_layer_weight
   if (!aux) aux = &no_aux;
   OPT_PTR(aux->o_teacher); OPT_PTR(aux->o_student); OPT_PTR4(aux->lse_teacher);
   OPT_PTR4(aux->lse_student); OPT_PTR(aux->z_teacher); OPT_PTR(aux->z_student);
-  OPT_PTR(aux->y); OPT_PTR(aux->state_out);
-  if (dec && aux->state_out) return fail(TTCD_ERR_BAD_SHAPE, "state_out is a prefill-only output");
+  OPT_PTR(aux->y); OPT_PTR(aux->state_out); OPT_PTR(aux->r); OPT_PTR(aux->k);
+  if (dec && (aux->state_out || aux->r || aux->k))
+    return fail(TTCD_ERR_BAD_SHAPE, "state_out, r and k are prefill-only outputs");
   const size_t need = ttcd_layer_forward_workspace_size(d, dec);
   if (ws_bytes < need)
     return fail(TTCD_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
@@ -828,12 +840,12 @@ ttcd_status ttcd_layer_forward(const ttcd_layer_desc* d, const ttcd_layer_weight
     if (y) {
       HIPCHK(run_fw(B, T, dm, f, d->chunk, d->conv_k, l2_eps, dt, z[0], z[1], z[main],
                     wt->conv_t, wt->conv_s, wt->w_down0, wt->w_proj, wt->beta, nullptr, y, F32,
-                    aux->state_out, b.fw, s));
+                    aux->state_out, aux->r, aux->k, b.fw, s));
       HIPCHK(launch_add(b.h[main], y, out, BT * dm, s));
     } else {
       HIPCHK(run_fw(B, T, dm, f, d->chunk, d->conv_k, l2_eps, dt, z[0], z[1], z[main],
                     wt->conv_t, wt->conv_s, wt->w_down0, wt->w_proj, wt->beta, b.h[main], out,
-                    F32, aux->state_out, b.fw, s));
+                    F32, aux->state_out, aux->r, aux->k, b.fw, s));
     }
     return ok();
   }

@@ -110,6 +110,7 @@ struct StreamArgs {
   const void* conv_t; const void* conv_s;
   const float* beta;
   void* dbar; void* zbt; float* sc;
+  float* inv;                     // [B, Tpad] 1 / max(key norm, eps), or NULL
   float* part;                    // workspace: partial key norms (fw_stream_part_bytes)
   int B, T, f, kc, chunk, nchunks;
   float eps;
@@ -117,6 +118,9 @@ struct StreamArgs {
   int raw_keys;                   // 1: sc = beta (keys not normalised)
 };
 hipError_t launch_fw_stream(const StreamArgs& a, hipStream_t s);
+// k_out [B, T, f] = zbt [B, f, Tpad]^T scaled per token by inv [B, Tpad]
+hipError_t launch_unit_keys(const void* zbt, const float* inv, void* k_out, int B, int T, int f,
+                            int dt, hipStream_t s);
 
 // One generated token: convs over the history and the token, dbar, the unit
 // key (to k_out + b * k_stride), and the history advanced by one row.

@@ -209,19 +209,21 @@ fw_stream2_kernel(const T* __restrict__ zt, const T* __restrict__ zs,
 }
 
 // sc[b, t] = beta[b, t / chunk] / max(sqrt(sum of the partial norms), eps),
-// or beta[b, t / chunk] alone for raw (unnormalised) keys.
+// or beta[b, t / chunk] alone for raw (unnormalised) keys; inv (when given)
+// receives the key normalisation alone, 1 / max(norm, eps) (1 for raw keys).
 // One token per lane; the partials are loaded eight at a time (all in
 // flight together) and added in feature-tile order.
 __global__ void __launch_bounds__(64)
 fw_key_scale_kernel(const float* __restrict__ part, const float* __restrict__ beta,
-                    float* __restrict__ sc, int nft, int T_, int Tpad, int chunk, int nchunks,
-                    float eps, int raw) {
+                    float* __restrict__ sc, float* __restrict__ inv, int nft, int T_, int Tpad,
+                    int chunk, int nchunks, float eps, int raw) {
   const int b = blockIdx.y;
   const int t = blockIdx.x * 64 + threadIdx.x;
   if (t >= Tpad) return;
-  float v = 0.f;
+  float v = 0.f, iv = 0.f;
   if (t < T_ && raw) {
     v = beta[(size_t)b * nchunks + min(t / chunk, nchunks - 1)];
+    iv = 1.f;
   } else if (t < T_) {
     float ss = 0.f;
     const float* pp = part + (size_t)b * nft * Tpad + t;
@@ -234,9 +236,37 @@ fw_key_scale_kernel(const float* __restrict__ part, const float* __restrict__ be
         if (y0 + j < nft) ss += x[j];
     }
     const int ci = min(t / chunk, nchunks - 1);
-    v = beta[(size_t)b * nchunks + ci] / fmaxf(sqrtf(ss), eps);
+    const float nrm = fmaxf(sqrtf(ss), eps);
+    v = beta[(size_t)b * nchunks + ci] / nrm;
+    iv = 1.f / nrm;
   }
   sc[(size_t)b * Tpad + t] = v;
+  if (inv) inv[(size_t)b * Tpad + t] = iv;
+}
+
+// The unit keys token-major, for the low-rank chunk lists:
+//   k_out[b, t, c] = zbt[b, c, t] * inv[b, t]   (t < T)
+// 32 x 32 tiles through LDS (the feature-major rows are read along t and
+// the token-major rows written along c).
+template <typename T>
+__global__ void __launch_bounds__(256)
+unit_keys_kernel(const T* __restrict__ zbt, const float* __restrict__ inv, T* __restrict__ k_out,
+                 int T_, int Tpad, int f) {
+  __shared__ float tile[32][33];
+  const int b = blockIdx.z;
+  const int t0 = blockIdx.x * 32, c0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const T* zp = zbt + (size_t)b * f * Tpad;
+  for (int i = ty; i < 32; i += 8) {
+    const int c = c0 + i, t = t0 + tx;
+    tile[i][tx] = (c < f && t < T_) ? ldf(zp + (size_t)c * Tpad + t) : 0.f;
+  }
+  __syncthreads();
+  for (int i = ty; i < 32; i += 8) {
+    const int t = t0 + i, c = c0 + tx;
+    if (t < T_ && c < f)
+      stf(k_out + ((size_t)b * T_ + t) * f + c, tile[tx][i] * inv[(size_t)b * Tpad + t]);
+  }
 }
 
 // ------------------------------------------------------- decode-time append
@@ -534,7 +564,20 @@ hipError_t launch_fw_stream(const StreamArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fw_key_scale_kernel, dim3(Tpad / 64, a.B), dim3(64), 0, s, a.part,
-                     a.beta, a.sc, nft, a.T, Tpad, a.chunk, a.nchunks, a.eps, a.raw_keys);
+                     a.beta, a.sc, a.inv, nft, a.T, Tpad, a.chunk, a.nchunks, a.eps, a.raw_keys);
+  return hipGetLastError();
+}
+
+hipError_t launch_unit_keys(const void* zbt, const float* inv, void* k_out, int B, int T, int f,
+                            int dt, hipStream_t s) {
+  const int Tpad = (T + 63) / 64 * 64;
+  dim3 grid((T + 31) / 32, (f + 31) / 32, B);
+  if (dt == BF16)
+    hipLaunchKernelGGL(unit_keys_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)zbt, inv,
+                       (bf16_t*)k_out, T, Tpad, f);
+  else
+    hipLaunchKernelGGL(unit_keys_kernel<float>, grid, dim3(256), 0, s, (const float*)zbt, inv,
+                       (float*)k_out, T, Tpad, f);
   return hipGetLastError();
 }
 

@@ -81,7 +81,7 @@ class LayerAux(C.Structure):
     _fields_ = [("o_teacher", C.c_void_p), ("o_student", C.c_void_p),
                 ("lse_teacher", C.c_void_p), ("lse_student", C.c_void_p),
                 ("z_teacher", C.c_void_p), ("z_student", C.c_void_p), ("y", C.c_void_p),
-                ("state_out", C.c_void_p)]
+                ("state_out", C.c_void_p), ("r", C.c_void_p), ("k", C.c_void_p)]
 
 
 _vp, _sz = C.c_void_p, C.c_size_t
@@ -94,7 +94,7 @@ _sig = {
                                                   _vp, _vp, _vp, _sz, _vp]),
     "ttcd_fastweight_scan_workspace_size": (_sz, [C.POINTER(FwDesc)]),
     "ttcd_fastweight_scan": (C.c_int, [C.POINTER(FwDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                       _vp, _vp, _vp, _sz, _vp]),
+                                       _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "ttcd_fastweight_scan_on_policy_workspace_size": (_sz, [C.POINTER(FwDesc)]),
     "ttcd_fastweight_scan_on_policy": (C.c_int, [C.POINTER(FwDesc), _vp, _vp, _vp, _vp, _vp, _vp,
                                                  _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -275,11 +275,14 @@ def fw_desc(z: torch.Tensor, d_model: int, chunk: int, conv_k: int, l2_eps: floa
 
 def fastweight_scan(z_teacher, z_student, z_main, conv_t, conv_s, w_down0, w_proj, beta,
                     chunk: int, *, out_dtype=torch.float32, want_state: bool = False,
+                    r_out: Optional[torch.Tensor] = None, k_out: Optional[torch.Tensor] = None,
                     l2_eps: float = 0.0, workspace=None, stream=None):
     """y [B,T,d] = S_{t//chunk} z_main[t] with the chunk-wise prefix fast weight.
 
-    Returns (y, state) where state is the fp32 weight after every chunk's
-    write (or None)."""
+    Returns (y, state) where state is the fp32 weight after the writes of
+    the T // chunk complete chunks (or None).  r_out [B,T,d] and k_out
+    [B,T,f] (the inputs' dtype, caller-allocated) receive the residual terms
+    and unit keys of the low-rank chunk lists when given."""
     dm = w_down0.shape[0]
     kc = conv_t.shape[1]
     d = fw_desc(z_teacher, dm, chunk, kc, l2_eps, out_dtype)
@@ -290,8 +293,8 @@ def fastweight_scan(z_teacher, z_student, z_main, conv_t, conv_s, w_down0, w_pro
     ws = _workspace(need, z_teacher.device, workspace)
     _check(_lib.ttcd_fastweight_scan(C.byref(d), _ptr(z_teacher), _ptr(z_student), _ptr(z_main),
                                      _ptr(conv_t), _ptr(conv_s), _ptr(w_down0), _ptr(w_proj),
-                                     _ptr(beta), _ptr(y), _ptr(st), _ptr(ws), ws.numel(),
-                                     _stream(stream)), "ttcd_fastweight_scan")
+                                     _ptr(beta), _ptr(y), _ptr(st), _ptr(r_out), _ptr(k_out),
+                                     _ptr(ws), ws.numel(), _stream(stream)), "ttcd_fastweight_scan")
     return y, st
 
 
@@ -480,6 +483,8 @@ def layer_forward(q, k, v, x, w: Dict[str, torch.Tensor], w_teacher: int, w_stud
         aux_t["z_student"] = torch.empty((B, Tq, f), dtype=q.dtype, device=dev)
         if decode is None:
             aux_t["state_out"] = torch.empty((B, dm, f), dtype=torch.float32, device=dev)
+            aux_t["r"] = torch.empty((B, Tq, dm), dtype=q.dtype, device=dev)
+            aux_t["k"] = torch.empty((B, Tq, f), dtype=q.dtype, device=dev)
         aux_s = LayerAux(*[_ptr(aux_t.get(n)) for n, _ in LayerAux._fields_])
     need = _lib.ttcd_layer_forward_workspace_size(C.byref(desc), dec_p)
     ws = _workspace(need, dev, workspace)

@@ -145,8 +145,17 @@ ttcd_status ttcd_dual_window_attn_lse_split(const ttcd_attn_desc* desc,
  *   w_down0 [d_model, d_ff], w_proj [d_ff, d_ff]     in_dtype
  *   beta    [batch, ceil(seq/chunk)] fp32 (the exact coefficient of R_i K_i^T)
  *   y       [batch, seq, d_model]  out_dtype
- *   state_out [batch, d_model, d_ff] fp32 or NULL: S after every chunk's
- *            write (the weight a decode step continues from).
+ *   state_out [batch, d_model, d_ff] fp32 or NULL: S_n, the weight after
+ *            the writes of the n = floor(seq/chunk) chunks that hold all
+ *            `chunk` tokens.  A short last chunk is still pending: its
+ *            writes take effect once it completes, so a decode step that
+ *            continues the sequence starts from S_n and appends the pending
+ *            chunk's tokens to its lists (ttcd_fastweight_decode_append).
+ *   r_out   [batch, seq, d_model] in_dtype or NULL: r_t, the residual terms
+ *   k_out   [batch, seq, d_ff]    in_dtype or NULL: k_t, the unit keys
+ *            (without beta): the low-rank chunk lists of ttcd_fw_state, rows
+ *            [j*chunk, (j+1)*chunk) holding chunk j, so that a decode loop
+ *            continues from this prefill in list form.
  * Requires chunk % 16 == 0, d_model % 8 == 0, d_ff % 8 == 0, conv_k in [1,8].
  * ---------------------------------------------------------------------- */
 typedef struct {
@@ -170,6 +179,7 @@ ttcd_status ttcd_fastweight_scan(const ttcd_fw_desc* desc,
                                  const void* w_down0, const void* w_proj,
                                  const float* beta,
                                  void* y, float* state_out,
+                                 void* r_out, void* k_out,
                                  void* workspace, size_t workspace_bytes,
                                  void* stream);
 
@@ -180,7 +190,8 @@ ttcd_status ttcd_fastweight_scan(const ttcd_fw_desc* desc,
  *   r_t  = S_{floor(t/chunk)} W_proj (Zbar_T[t] - Zbar_S[t])
  * with everything else as above (keys, beta, prefix, apply).  The chunks
  * are processed one after another.  Arguments, layouts and errors are those
- * of ttcd_fastweight_scan; state_out, when given, also serves as the fp32
+ * of ttcd_fastweight_scan (state_out is S_n after the complete chunks; this
+ * call has no list outputs); state_out, when given, also serves as the fp32
  * running state.  Its workspace adds d_model * d_ff fp32 values. */
 size_t ttcd_fastweight_scan_on_policy_workspace_size(const ttcd_fw_desc* desc);
 
@@ -204,8 +215,9 @@ ttcd_status ttcd_fastweight_scan_on_policy(const ttcd_fw_desc* desc,
  *   S_{i+1} = S_i + beta[b,i] * sum_{t in chunk i} r_t Z_S[t]^T,  S_0 = W_down^(0)
  *   y[t]    = S_{floor(t/chunk)} z_main[t]
  * beta carries the step size (and any 1/|chunk| of the loss).  desc's
- * conv_k and l2_eps are ignored; everything else (layouts, state_out,
- * workspace, errors) is as for ttcd_fastweight_scan. */
+ * conv_k and l2_eps are ignored; everything else (layouts, state_out after
+ * the complete chunks, workspace, errors) is as for ttcd_fastweight_scan,
+ * which alone has the list outputs. */
 size_t ttcd_fastweight_scan_eq6_workspace_size(const ttcd_fw_desc* desc);
 
 ttcd_status ttcd_fastweight_scan_eq6(const ttcd_fw_desc* desc,
@@ -309,7 +321,13 @@ typedef struct {
                            its Z is asked for here (the append below needs
                            both) */
   float* y;             /* [batch, seq_q, d_model] fast-weight MLP output */
-  float* state_out;     /* prefill only: [batch, d_model, d_ff] */
+  float* state_out;     /* prefill only: [batch, d_model, d_ff], the weight
+                           after the complete chunks (as in
+                           ttcd_fastweight_scan) */
+  void* r;              /* prefill only: [batch, seq_q, d_model] attn.in_dtype,
+                           the residual terms r_t of the chunk lists */
+  void* k;              /* prefill only: [batch, seq_q, d_ff] attn.in_dtype,
+                           the unit keys k_t of the chunk lists */
 } ttcd_layer_aux;
 
 size_t ttcd_layer_forward_workspace_size(const ttcd_layer_desc* desc,

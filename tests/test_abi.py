@@ -102,9 +102,16 @@ def test_fastweight_and_layer_reject_bad_shapes():
     lib = ttcd.lib()
     fake = C.c_void_p(1 << 20)
     fw = ttcd.FwDesc(1, 100, 1024, 3072, 24, 4, 0.0, 1, 0)     # chunk not a multiple of 16
-    assert lib.ttcd_fastweight_scan(C.byref(fw), *([fake] * 10), fake, 1 << 40, None) == 2
+    assert lib.ttcd_fastweight_scan(C.byref(fw), *([fake] * 12), fake, 1 << 40, None) == 2
     fw = ttcd.FwDesc(1, 100, 1024, 3072, 64, 9, 0.0, 1, 0)      # conv_k > 8
-    assert lib.ttcd_fastweight_scan(C.byref(fw), *([fake] * 10), fake, 1 << 40, None) == 2
+    assert lib.ttcd_fastweight_scan(C.byref(fw), *([fake] * 12), fake, 1 << 40, None) == 2
+    # the list outputs are optional but must be aligned when given
+    fw = ttcd.FwDesc(1, 100, 1024, 3072, 64, 4, 0.0, 1, 0)
+    odd = C.c_void_p((1 << 20) + 2)
+    assert lib.ttcd_fastweight_scan(C.byref(fw), *([fake] * 10), odd, None, fake, 1 << 40,
+                                    None) == 5
+    assert lib.ttcd_fastweight_scan(C.byref(fw), *([fake] * 10), None, odd, fake, 1 << 40,
+                                    None) == 5
     a = _attn(seq_q=128, seq_k=128)
     ld = ttcd.LayerDesc(a, 1004, 3072, 1024, 4, 0.0, 0.0, 0)   # d_model not a multiple of 8
     w = ttcd.LayerWeights(*([1 << 20] * 8), 1 << 20)
@@ -117,6 +124,12 @@ def test_fastweight_and_layer_reject_bad_shapes():
     dec = ttcd.FwState(None, None, None, None, 3)
     assert lib.ttcd_layer_forward(C.byref(ld), C.byref(w), fake, fake, fake, fake, fake,
                                   C.byref(dec), None, fake, 1 << 40, None) == 1
+    # the list outputs of a prefill are not outputs of a decode step
+    dec = ttcd.FwState(fake, None, None, None, 0)
+    aux = ttcd.LayerAux(*([None] * 8), fake, None)
+    assert lib.ttcd_layer_forward(C.byref(ld), C.byref(w), fake, fake, fake, fake, fake,
+                                  C.byref(dec), C.byref(aux), fake, 1 << 40, None) == 2
+    assert b"prefill-only" in lib.ttcd_last_error()
 
 
 def test_no_oracle_import_in_product_code():
