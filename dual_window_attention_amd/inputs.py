@@ -188,9 +188,7 @@ def attention_inputs(cfg: LayerConfig, seed: Optional[int] = None,
 def layer_weights(cfg: LayerConfig, seed: Optional[int] = None) -> Dict[str, Tensor]:
     """Fan-in scaled Gaussian weights, unit RMSNorm gain.
 
-    beta: the write coefficient of each chunk, drawn as u_i / |C_i| with
-    u_i ~ U(0,1) (the learned gate in (0,1) times the chunk-mean factor of
-    the distillation loss); see ``beta_for`` for the exact rule.
+    The write coefficients beta are drawn separately by ``beta_for``.
     """
     s = cfg.seed if seed is None else seed
     d, f, HD, kc = cfg.d_model, cfg.d_ff, cfg.n_q_heads * cfg.head_dim, cfg.conv_k
@@ -208,18 +206,20 @@ def layer_weights(cfg: LayerConfig, seed: Optional[int] = None) -> Dict[str, Ten
 
 
 def beta_for(cfg: LayerConfig, seed: Optional[int] = None, seq: Optional[int] = None,
-             gate_only: bool = False) -> np.ndarray:
+             chunk_mean: bool = False) -> np.ndarray:
     """Write coefficients [B, n_chunks] (float32).
 
-    u ~ U(0,1) per (batch, chunk); returned as u / |C_i| where |C_i| is the
-    number of tokens in chunk i (the last chunk may be short).  With
-    ``gate_only`` the raw u is returned.
+    beta_i ~ U(0,1) per (batch, chunk), the workloads' distribution: the
+    exact coefficient of R_i K_i^T.  With ``chunk_mean`` the draw is divided
+    by |C_i|, the number of tokens in chunk i (the last chunk may be short):
+    a second, small-write regime in which the fast-weight correction is a
+    few percent of the MLP output.
     """
     s = cfg.seed if seed is None else seed
     T = cfg.seq if seq is None else seq
     n = -(-T // cfg.chunk)
     u = _rng(s, "beta").random(size=(cfg.batch, n)).astype(np.float32)
-    if gate_only:
+    if not chunk_mean:
         return u
     sizes = np.full((n,), cfg.chunk, dtype=np.float32)
     sizes[-1] = T - cfg.chunk * (n - 1)

@@ -52,59 +52,87 @@ def test_decode_append_matches_oracle(kc):
         assert torch.equal(dh_s[:, :-1], h_s0[:, 1:]) and torch.equal(dh_s[:, -1], dz_s)
 
 
-def test_multi_step_generation_across_chunk_boundaries():
-    """Prefill state at L0 (completed chunks and the partial chunk's rows),
-    then one decode step per token: each output equals the prefill oracle's
-    row, each appended (r, k) equals its write terms, and the lists gain a
-    chunk at every boundary."""
+def test_hip_prefill_then_generation_across_chunk_boundaries():
+    """A ragged HIP prefill (L0 % C != 0) hands over to HIP decode steps:
+    the prefill's list outputs (r, k), its Z rows (conv histories) and its
+    weight after the complete chunks are the decode's starting state, with
+    nothing taken from the oracle.  Each generated token's output and its
+    appended (r, k) must equal the rows of one oracle prefill over the whole
+    sequence, in both state forms (the lists, and a dense weight refolded
+    whenever a chunk completes)."""
     from dual_window_attention_amd import ttcd
     cfg = I.CONFIGS[3].scaled(batch=2, seq=106, n_q_heads=4, n_kv_heads=2, d_model=128,
                               d_ff=256, w_teacher=48, w_student=12, chunk=32, seed=46)
     T, C, kc = cfg.seq, cfg.chunk, cfg.conv_k
-    L0 = 2 * C - 6
+    L0 = 2 * C - 6                                   # the prefill ends inside chunk 1
     att = I.attention_inputs(cfg)
     w = I.layer_weights(cfg)
     beta = I.beta_for(cfg)
     x = I.residual_input(cfg)
     wo = {k_: t.f64() for k_, t in w.items()}
     wo["beta"] = beta.astype(np.float64)
-    say("  oracle prefill")
+    say("  oracle prefill over the whole sequence")
     ref = O.layer_forward(att["q"].f64(), att["k"].f64(), att["v"].f64(), x.f64(), wo,
                           cfg.w_teacher, cfg.w_student, C)
     q, k, v = (I.to_torch(att[n_]) for n_ in ("q", "k", "v"))
     xd = I.to_torch(x)
     wd = {n_: I.to_torch(t) for n_, t in w.items()}
-    B, d, f = cfg.batch, cfg.d_model, cfg.d_ff
-    nmax = (T + C - 1) // C
-    # list buffers: rows before L0 from the prefill, the rest appended here
-    r_buf = torch.zeros((B, nmax * C, d), dtype=torch.bfloat16, device="cuda")
-    k_buf = torch.zeros((B, nmax * C, f), dtype=torch.bfloat16, device="cuda")
-    r_buf[:, :L0] = _bf16(ref["r"][:, :L0])
-    k_buf[:, :L0] = _bf16(ref["k"][:, :L0])
-    h_t = _bf16(ref["z_t"][:, L0 - (kc - 1):L0])
-    h_s = _bf16(ref["z_s"][:, L0 - (kc - 1):L0])
-    m = ttcd.fastweight_residual_proj(wd["w_down0"], wd["w_proj"])
     beta_dev = I.f32_to_torch(beta)
     tol = tol_for(cfg.dtype)
+    B, d, f = cfg.batch, cfg.d_model, cfg.d_ff
+
+    say(f"  HIP prefill of {L0} tokens (chunk {C})")
+    wp = dict(wd)
+    wp["beta"] = beta_dev[:, :-(-L0 // C)].contiguous()
+    out0, aux0 = ttcd.layer_forward(q[:, :L0].contiguous(), k[:, :L0].contiguous(),
+                                    v[:, :L0].contiguous(), xd[:, :L0].contiguous(), wp,
+                                    cfg.w_teacher, cfg.w_student, C, aux=True)
+    torch.cuda.synchronize()
+    assert_close(to_np(out0), ref["out"][:, :L0], tol, "prefill out")
+    assert_close(to_np(aux0["r"]), ref["r"][:, :L0], tol, "prefill r")
+    assert_close(to_np(aux0["k"]), ref["k"][:, :L0], tol, "prefill k")
+    n0 = L0 // C
+    want0 = O.fold_lists(wo["w_down0"], ref["r"][:, :n0 * C], ref["k"][:, :n0 * C],
+                         beta[:, :n0].astype(np.float64), C)
+    assert_close(to_np(aux0["state_out"]), want0, tol, f"prefill weight after {n0} chunk(s)")
+
+    nmax = (T + C - 1) // C
+    r_buf = torch.zeros((B, nmax * C, d), dtype=torch.bfloat16, device="cuda")
+    k_buf = torch.zeros((B, nmax * C, f), dtype=torch.bfloat16, device="cuda")
+    r_buf[:, :L0] = aux0["r"]
+    k_buf[:, :L0] = aux0["k"]
+    h_t = aux0["z_teacher"][:, L0 - (kc - 1):L0].contiguous()
+    h_s = aux0["z_student"][:, L0 - (kc - 1):L0].contiguous()
+    dense = aux0["state_out"].clone()
+    dense_n = n0
+    m = ttcd.fastweight_residual_proj(wd["w_down0"], wd["w_proj"])
     for t in range(L0, T):
         n = t // C                                   # chunks complete before t
+        if n > dense_n:                              # a chunk completed: refold
+            dense = ttcd.fastweight_fold(wd["w_down0"], r_buf[:, :n * C].contiguous(),
+                                         k_buf[:, :n * C].contiguous(),
+                                         beta_dev[:, :n].contiguous(), C)
+            dense_n = n
         dec = {"pos": t, "beta_list": beta_dev[:, :n].contiguous()}
         if n > 0:
             dec["r_list"] = r_buf[:, :n * C].contiguous()
             dec["k_list"] = k_buf[:, :n * C].contiguous()
-        out, aux = ttcd.layer_forward(q[:, t:t + 1].contiguous(), k, v,
-                                      xd[:, t:t + 1].contiguous(), wd, cfg.w_teacher,
-                                      cfg.w_student, C, aux=True, decode=dec)
+        qt, xt = q[:, t:t + 1].contiguous(), xd[:, t:t + 1].contiguous()
+        out_d = ttcd.layer_forward(qt, k, v, xt, wd, cfg.w_teacher, cfg.w_student, C,
+                                   decode={"pos": t, "state_dense": dense,
+                                           "beta_list": beta_dev[:, :n].contiguous()})
+        out, aux = ttcd.layer_forward(qt, k, v, xt, wd, cfg.w_teacher, cfg.w_student, C,
+                                      aux=True, decode=dec)
         ttcd.fastweight_decode_append(aux["z_teacher"][:, 0], aux["z_student"][:, 0], h_t, h_s,
                                       wd["conv_t"], wd["conv_s"], m, r_buf[:, t], k_buf[:, t])
         torch.cuda.synchronize()
-        assert_close(to_np(out)[:, 0], ref["out"][:, t], tol, f"step {t}: out")
+        assert_close(to_np(out)[:, 0], ref["out"][:, t], tol, f"step {t}: out (lists)")
+        assert_close(to_np(out_d)[:, 0], ref["out"][:, t], tol, f"step {t}: out (dense)")
         assert_close(to_np(r_buf[:, t]), ref["r"][:, t], tol, f"step {t}: r")
         assert_close(to_np(k_buf[:, t]), ref["k"][:, t], tol, f"step {t}: k")
-    # the folded lists give the prefill's state after the last complete chunk
+    # the lists folded once give the oracle's weight after the complete chunks
     n = T // C
     folded = ttcd.fastweight_fold(wd["w_down0"], r_buf[:, :n * C].contiguous(),
                                   k_buf[:, :n * C].contiguous(), beta_dev[:, :n].contiguous(), C)
     torch.cuda.synchronize()
-    want = O.fold_lists(wo["w_down0"], ref["r"][:, :n * C], ref["k"][:, :n * C], beta[:, :n], C)
-    assert_close(to_np(folded), want, tol, "folded state")
+    assert_close(to_np(folded), ref["state_complete"], tol, "folded state")

@@ -6,13 +6,20 @@ import pytest
 
 from dual_window_attention_amd import inputs as I
 from oracle import ttcd_oracle as O
-from tests.gpu_helpers import assert_close, assert_close_stored, say, to_np, tol_for
+from tests.gpu_helpers import assert_close, assert_correction, say, to_np, tol_for
 
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
 BASE = I.CONFIGS[3]
+
+# The on-policy recurrence multiplies the weight by (I + beta_i W_proj
+# Dbar_i^T K_i) at every chunk; with the workloads' beta ~ U(0,1) that factor
+# grows the weight geometrically (|S| ~ 1e4 after four chunks at the 64K
+# layer's shapes), so these tests take the chunk-mean betas u_i / |C_i|,
+# under which the recurrence stays near W_down0.
+CHUNK_MEAN = True
 
 
 def run_on_policy(cfg, out_dtype="f32", beta_scale=1.0):
@@ -21,7 +28,7 @@ def run_on_policy(cfg, out_dtype="f32", beta_scale=1.0):
         f"C={cfg.chunk} kc={cfg.conv_k} y={out_dtype} beta*{beta_scale}")
     z = I.hidden_activations(cfg)
     w = I.layer_weights(cfg)
-    beta = (I.beta_for(cfg) * np.float32(beta_scale)).astype(np.float32)
+    beta = (I.beta_for(cfg, chunk_mean=CHUNK_MEAN) * np.float32(beta_scale)).astype(np.float32)
     zt, zs = I.to_torch(z["z_t"]), I.to_torch(z["z_s"])
     dev = {n: I.to_torch(w[n]) for n in ("conv_t", "conv_s", "w_down0", "w_proj")}
     odt = torch.float32 if out_dtype == "f32" else torch.bfloat16
@@ -39,29 +46,16 @@ def run_on_policy(cfg, out_dtype="f32", beta_scale=1.0):
 def check_on_policy(cfg, out_dtype="f32", beta_scale=1.0):
     y, st, on, off, base = run_on_policy(cfg, out_dtype, beta_scale)
     tol = tol_for(cfg.dtype)
-    if out_dtype == "f32":
-        assert_close(y, on["y"], tol, "y")
-    else:
-        assert_close_stored(y, on["y"], tol, "y (bf16 out)", "bf16")
-    assert_close(st, on["state"], tol, "state after all writes")
+    assert_close(y, on["y"], tol, f"y ({out_dtype} out)")
+    assert_close(st, on["state_complete"], tol, f"state after the {cfg.seq // cfg.chunk} complete chunks")
     # the correction y - W0 z against the on-policy one, and closer to it
     # than the off-policy correction is, so the test tells the rules apart
     corr_on, corr_off, corr = on["y"] - base, off["y"] - base, y - base
     n_on = np.linalg.norm(corr_on)
     rel = np.linalg.norm(corr - corr_on) / max(n_on, 1e-30)
     gap = np.linalg.norm(corr_off - corr_on) / max(n_on, 1e-30)
-    say(f"  correction relL2={rel:.3e}  (on vs off policy: {gap:.3e})")
-    if n_on > 0:
-        bound = 1e-4
-        if cfg.dtype == "bf16":
-            # each chunk's weight S_i is kept in bf16 for its GEMMs: one
-            # rounding, rms 2^-9/sqrt(3) of |S_i z|, lands on y of the later
-            # chunks; where the correction is a small part of y this floor
-            # (taken twice) exceeds the 5% bound
-            later = on["y"][:, cfg.chunk:]
-            floor = 2 * 2.0 ** -9 / np.sqrt(3.0) * np.linalg.norm(later) / n_on
-            bound = max(5e-2, floor)
-        assert rel <= bound, (rel, bound)
+    say(f"  on vs off policy correction gap: {gap:.3e}")
+    assert_correction(corr, corr_on, on["y"], cfg.chunk, cfg.dtype)
     return rel, gap
 
 
@@ -90,7 +84,7 @@ def test_on_policy_bf16_output_and_single_chunk():
     y, st, on, _, base = run_on_policy(BASE.scaled(batch=2, seq=100, d_model=64, d_ff=128,
                                                    chunk=128, seed=47))
     assert_close(y, base, tol_for("bf16"), "single chunk y")
-    assert_close(st, on["state"], tol_for("bf16"), "single chunk state")
+    assert_close(st, on["state_complete"], tol_for("bf16"), "single chunk state (W0)")
 
 
 def test_on_policy_first_two_chunks_equal_off_policy_call():
@@ -103,7 +97,7 @@ def test_on_policy_first_two_chunks_equal_off_policy_call():
     args = [I.to_torch(z["z_t"]), I.to_torch(z["z_s"])]
     args.append(args[0])
     args += [I.to_torch(w[n]) for n in ("conv_t", "conv_s", "w_down0", "w_proj")]
-    args.append(I.f32_to_torch(I.beta_for(cfg)))
+    args.append(I.f32_to_torch(I.beta_for(cfg, chunk_mean=CHUNK_MEAN)))
     y_on, _ = ttcd.fastweight_scan_on_policy(*args, cfg.chunk)
     y_off, _ = ttcd.fastweight_scan(*args, cfg.chunk)
     torch.cuda.synchronize()
@@ -127,7 +121,7 @@ def test_on_policy_qwen3_64k_full():
     say(f"on-policy full {cfg.name} T={cfg.seq} C={cfg.chunk}")
     z = I.hidden_activations(cfg)
     w = I.layer_weights(cfg)
-    beta = I.beta_for(cfg)
+    beta = I.beta_for(cfg, chunk_mean=CHUNK_MEAN)
     zt, zs = I.to_torch(z["z_t"]), I.to_torch(z["z_s"])
     y, st = ttcd.fastweight_scan_on_policy(zt, zs, zt, I.to_torch(w["conv_t"]),
                                            I.to_torch(w["conv_s"]), I.to_torch(w["w_down0"]),

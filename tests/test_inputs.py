@@ -25,7 +25,11 @@ def test_generators_are_seeded_per_tensor():
     w1 = I.layer_weights(cfg)
     assert w1["w_down0"].shape == (cfg.d_model, cfg.d_ff)
     beta = I.beta_for(cfg)
-    assert beta.shape == (1, 1) and 0 < beta[0, 0] * 64 < 1
+    assert beta.shape == (1, 1) and 0 <= beta[0, 0] < 1
+    cm = I.beta_for(cfg, chunk_mean=True)
+    assert cm[0, 0] == np.float32(beta[0, 0] / 64)
+    ragged = I.beta_for(cfg, seq=100, chunk_mean=True) * np.array([64, 36], np.float32)
+    np.testing.assert_allclose(ragged, I.beta_for(cfg, seq=100), rtol=1e-6)
 
 
 def test_outlier_keys_fraction():
