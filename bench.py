@@ -141,7 +141,9 @@ def update_rules_bench(cfg, dev, n):
     zt, zs = I.to_torch(z["z_t"], dev), I.to_torch(z["z_s"], dev)
     del z
     a = [zt, zs, zt] + [I.to_torch(w[k], dev) for k in ("conv_t", "conv_s", "w_down0", "w_proj")]
-    a.append(I.f32_to_torch(I.beta_for(cfg), dev))
+    # chunk-mean write coefficients: under beta ~ U(0,1) the on-policy
+    # recurrence grows the weight geometrically and the gap below is moot
+    a.append(I.f32_to_torch(I.beta_for(cfg, chunk_mean=True), dev))
     d = ttcd.fw_desc(zt, cfg.d_model, cfg.chunk, cfg.conv_k, 0.0, torch.float32)
     lib = ttcd.lib()
     ws = torch.empty(max(lib.ttcd_fastweight_scan_workspace_size(d),
@@ -167,7 +169,7 @@ def update_rules_bench(cfg, dev, n):
                       "recurrence (ttcd_fastweight_scan_on_policy), unprojected write "
                       "(ttcd_fastweight_scan_eq6)",
             "off_policy_ms": off_ms, "on_policy_ms": on_ms, "on_over_off": on_ms / off_ms,
-            "eq6_unprojected_ms": eq6_ms,
+            "eq6_unprojected_ms": eq6_ms, "beta": "u_i / |C_i|, u_i ~ U(0,1)",
             "off_vs_on_gap_rel_correction": gap / corr, "off_vs_on_gap_rel_y": gap / yn,
             "tokens": cfg.batch * cfg.seq, "chunks": cfg.n_chunks}
 
@@ -273,29 +275,160 @@ def decode_bench(dev, n):
 
 
 def cpu_baseline(cfg, sample_tokens):
-    """The fp64 oracle, as it stands, on the first ``sample_tokens`` tokens
-    of the same inputs (same shapes, weights and windows)."""
+    """The fp64 oracle, as it stands, on two prefixes of the same inputs
+    (same shapes, weights and windows): the first ``sample_tokens`` tokens
+    and the first ``sample_tokens - w_T`` tokens.  Both prefixes are past the
+    window ramp by then, so the difference of their wall times is the
+    oracle's steady-state cost of ``w_T`` tokens with full windows; that
+    rate is the value, the whole-sample rate is reported beside it."""
     from dual_window_attention_amd import inputs as I
     from oracle import ttcd_oracle as O
 
-    sc = cfg.scaled(seq=sample_tokens)
-    att = I.attention_inputs(sc)
-    w = {n: t.f64() for n, t in I.layer_weights(sc).items()}
-    w["beta"] = I.beta_for(sc).astype(np.float64)
-    x = I.residual_input(sc).f64()
-    q, k, v = att["q"].f64(), att["k"].f64(), att["v"].f64()
-    t0 = time.perf_counter()
-    O.layer_forward(q, k, v, x, w, sc.w_teacher, sc.w_student, sc.chunk)
-    wall = time.perf_counter() - t0
+    def run(tokens):
+        sc = cfg.scaled(seq=tokens)
+        att = I.attention_inputs(sc)
+        w = {n: t.f64() for n, t in I.layer_weights(sc).items()}
+        w["beta"] = I.beta_for(sc).astype(np.float64)
+        x = I.residual_input(sc).f64()
+        q, k, v = att["q"].f64(), att["k"].f64(), att["v"].f64()
+        t0 = time.perf_counter()
+        O.layer_forward(q, k, v, x, w, sc.w_teacher, sc.w_student, sc.chunk)
+        return time.perf_counter() - t0
+
+    short = sample_tokens - cfg.w_teacher
+    if short < cfg.w_teacher:
+        raise ValueError("the CPU sample must cover at least two teacher windows")
+    wall_long = run(sample_tokens)
+    wall_short = run(short)
+    steady = cfg.w_teacher * cfg.batch / max(wall_long - wall_short, 1e-9)
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
-    return {"value": sample_tokens * sc.batch / wall, "unit": "tokens/s", "cores": cores,
-            "kind": "oracle",
+    return {"value": steady, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "whole_sample_tokens_per_s": sample_tokens * cfg.batch / wall_long,
             "sample": f"fp64 NumPy oracle, full layer forward over the first {sample_tokens} "
-                      f"tokens of the same config (windows fill up over the first "
-                      f"{sc.w_teacher} tokens), wall {wall:.1f} s"}
+                      f"and the first {short} tokens of the same config (wall {wall_long:.1f} s "
+                      f"and {wall_short:.1f} s); value = the {cfg.w_teacher} tokens between "
+                      f"them, all with full {cfg.w_teacher}-key windows, over the wall-time "
+                      f"difference"}
+
+
+def layer_inputs(cfg, dev):
+    """Device inputs, weights, workspace and output of one layer step of ``cfg``."""
+    import torch
+    from dual_window_attention_amd import inputs as I
+    from dual_window_attention_amd import ttcd
+
+    att = I.attention_inputs(cfg)
+    q, k, v = (I.to_torch(att[n], dev) for n in ("q", "k", "v"))
+    del att
+    wd = {n: I.to_torch(t, dev) for n, t in I.layer_weights(cfg).items()}
+    wd["beta"] = I.f32_to_torch(I.beta_for(cfg), dev)
+    x = I.to_torch(I.residual_input(cfg), dev)
+    ws = torch.empty(ttcd.layer_workspace_bytes(q, k, cfg.d_model, cfg.d_ff, cfg.w_teacher,
+                                                cfg.w_student, cfg.chunk, cfg.conv_k),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((cfg.batch, cfg.seq, cfg.d_model), dtype=torch.float32, device=dev)
+    return q, k, v, x, wd, ws, out
+
+
+def attention_call(cfg, dev, q, k, v, w_t, w_s, n):
+    """Mean time of the fused dual-window attention call (V^T prologue and
+    kernel, bf16 outputs, no LSE) and its fraction of the bf16 MFMA peak."""
+    import torch
+    from dual_window_attention_amd import ttcd
+
+    o_t = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    o_s = torch.empty_like(o_t)
+    aws = torch.empty(max(256, ttcd.lib().ttcd_dual_window_attn_workspace_size(
+        ttcd.attn_desc(q, k, w_t, w_s))), dtype=torch.uint8, device=dev)
+    ms = time_events(lambda: ttcd.dual_window_attn(q, k, v, w_t, w_s, with_lse=False,
+                                                   out=(o_t, o_s), workspace=aws),
+                     n, torch.cuda.current_stream())
+    flops = attention_flops(cfg, w_t)
+    achieved = flops / (ms * 1e-3) / 1e12
+    return {"w_teacher": w_t, "w_student": w_s, "ms_per_launch": ms,
+            "algorithmic_tflop": flops / 1e12, "achieved_tflops": achieved,
+            "mfma_frac": achieved / PEAK_BF16_TFLOPS}
+
+
+def smollm2_bench(dev, steps, n):
+    """The SmolLM2-360M-shaped layer at 16K (batch 1, 15/5 heads x 64, d_model
+    960, d_ff 2560, w_T 4096, w_S 256, chunk 512): layer tokens/s, the
+    attention call's fraction of the MFMA peak and the stream's of HBM."""
+    import torch
+    from dual_window_attention_amd import inputs as I
+    from dual_window_attention_amd import ttcd
+
+    cfg = I.CONFIGS[2]
+    q, k, v, x, wd, ws, out = layer_inputs(cfg, dev)
+
+    def step():
+        ttcd.layer_forward(q, k, v, x, wd, cfg.w_teacher, cfg.w_student, cfg.chunk, out=out,
+                           workspace=ws)
+
+    ms = time_events(step, steps, torch.cuda.current_stream(), warmup=3)
+    assert torch.isfinite(out).all().item()
+    res = {"workload": f"{cfg.name}: IP-TTCD layer forward, batch {cfg.batch}, seq {cfg.seq}, "
+                       f"{cfg.n_q_heads}/{cfg.n_kv_heads} heads x {cfg.head_dim}, d_model "
+                       f"{cfg.d_model}, d_ff {cfg.d_ff}, w_T {cfg.w_teacher}, w_S "
+                       f"{cfg.w_student}, chunk {cfg.chunk}",
+           "ms_per_step": ms, "tokens_per_s": cfg.batch * cfg.seq / (ms * 1e-3)}
+    res["attention"] = attention_call(cfg, dev, q, k, v, cfg.w_teacher, cfg.w_student, n)
+    del q, k, v, x, wd, ws, out
+    torch.cuda.empty_cache()
+    res["scan"] = scan_roofline(cfg, dev, n)
+    return res
+
+
+def attention_sweep_bench(dev, n):
+    """The attention-only workload (batch 8, 32K, 16/8 heads x 128, 5 % of
+    key rows x8) at its three (w_T, w_S) pairs: fraction of the MFMA peak."""
+    import torch
+    from dual_window_attention_amd import inputs as I
+
+    cfg = I.CONFIGS[4]
+    att = I.attention_inputs(cfg)
+    q, k, v = (I.to_torch(att[nm], dev) for nm in ("q", "k", "v"))
+    del att
+    pairs = [attention_call(cfg, dev, q, k, v, w_t, w_s, n) for w_t, w_s in cfg.windows]
+    del q, k, v
+    torch.cuda.empty_cache()
+    return {"workload": f"{cfg.name}: dual-window attention, batch {cfg.batch}, seq {cfg.seq}, "
+                        f"{cfg.n_q_heads}/{cfg.n_kv_heads} heads x {cfg.head_dim}, 5% of key "
+                        f"rows x8", "pairs": pairs}
+
+
+def summarize_trace(path):
+    """Per-shape table of a rocprofv3 CSV: a kernel trace (duration of each
+    dispatch) or a counter collection (value of each counter per dispatch),
+    grouped by kernel name and grid size, so that launches of one kernel at
+    different shapes are not averaged together."""
+    import csv
+    from collections import OrderedDict
+
+    groups = OrderedDict()
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            name = row.get("Kernel_Name", "?")
+            if "Grid_Size" in row:
+                grid = row["Grid_Size"]
+            else:
+                grid = "x".join(row.get(f"Grid_Size_{a}", "?") for a in "XYZ")
+            if "Counter_Name" in row:
+                key = (name, grid, row["Counter_Name"])
+                val = float(row["Counter_Value"])
+            else:
+                key = (name, grid, "duration_us")
+                val = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+            groups.setdefault(key, []).append(val)
+    print(f"{'kernel':<58} {'grid':>22} {'quantity':>26} {'n':>5} {'mean':>12} {'min':>12} "
+          f"{'max':>12}")
+    for (name, grid, qty), vals in groups.items():
+        short = name if len(name) <= 58 else name[:55] + "..."
+        print(f"{short:<58} {grid:>22} {qty:>26} {len(vals):>5} {np.mean(vals):>12.4g} "
+              f"{np.min(vals):>12.4g} {np.max(vals):>12.4g}")
 
 
 def main():
@@ -310,10 +443,18 @@ def main():
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the LSE-combination and update-rule sections (the counter passes "
                          "then see only the fused attention call)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the 16K SmolLM2-shaped layer and the batch-8 attention sweep")
+    ap.add_argument("--summarize-trace", metavar="CSV",
+                    help="print a per-shape table of a rocprofv3 kernel-trace or counter CSV "
+                         "and exit (no GPU work)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (a reference "
                          "kernel of known traffic for scaling memory counters)")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only (no collectives); "
               "run it with --gpus 1", file=sys.stderr)
@@ -420,6 +561,11 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_decode:
         res["decode"] = decode_bench(dev, n_att)
+        torch.cuda.empty_cache()
+    if not args.no_extra:
+        res["config2"] = smollm2_bench(dev, max(5, args.steps), n_att)
+        torch.cuda.empty_cache()
+        res["config4"] = attention_sweep_bench(dev, 5)
         torch.cuda.empty_cache()
     if args.cpu_sample > 0:
         res["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_sample, cfg.seq))
