@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/ttcd.h"
 #include "kernels.hpp"
@@ -761,10 +762,14 @@ size_t ttcd_layer_forward_workspace_size(const ttcd_layer_desc* d, const ttcd_fw
   return p.off;
 }
 
-ttcd_status ttcd_layer_forward(const ttcd_layer_desc* d, const ttcd_layer_weights* wt,
-                               const void* q, const void* k, const void* v, const void* x,
-                               float* out, const ttcd_fw_state* dec, const ttcd_layer_aux* aux,
-                               void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation of a layer call's arguments other than the workspace.
+ttcd_status check_layer_args(const ttcd_layer_desc* d, const ttcd_layer_weights* wt,
+                             const void* q, const void* k, const void* v, const void* x,
+                             float* out, const ttcd_fw_state* dec, const ttcd_layer_aux* aux) {
   ttcd_status st = check_layer(d, dec);
   if (st != TTCD_OK) return st;
   if (!wt) return fail(TTCD_ERR_NULL_POINTER, "weights is NULL");
@@ -781,19 +786,24 @@ ttcd_status ttcd_layer_forward(const ttcd_layer_desc* d, const ttcd_layer_weight
     if (!dec->state_dense && dec->n_chunks > 0 && (!dec->r_list || !dec->k_list || !dec->beta_list))
       return fail(TTCD_ERR_NULL_POINTER, "decode state: lists or state_dense required");
   }
+  if (aux) {
+    OPT_PTR(aux->o_teacher); OPT_PTR(aux->o_student); OPT_PTR4(aux->lse_teacher);
+    OPT_PTR4(aux->lse_student); OPT_PTR(aux->z_teacher); OPT_PTR(aux->z_student);
+    OPT_PTR(aux->y); OPT_PTR(aux->state_out); OPT_PTR(aux->r); OPT_PTR(aux->k);
+    if (dec && (aux->state_out || aux->r || aux->k))
+      return fail(TTCD_ERR_BAD_SHAPE, "state_out, r and k are prefill-only outputs");
+  }
+  return TTCD_OK;
+}
+
+// The layer forward on a workspace that holds at least
+// ttcd_layer_forward_workspace_size(d, dec) bytes (arguments validated).
+ttcd_status layer_forward_run(const ttcd_layer_desc* d, const ttcd_layer_weights* wt,
+                              const void* q, const void* k, const void* v, const void* x,
+                              float* out, const ttcd_fw_state* dec, const ttcd_layer_aux* aux,
+                              void* ws, void* stream) {
   const ttcd_layer_aux no_aux{};
   if (!aux) aux = &no_aux;
-  OPT_PTR(aux->o_teacher); OPT_PTR(aux->o_student); OPT_PTR4(aux->lse_teacher);
-  OPT_PTR4(aux->lse_student); OPT_PTR(aux->z_teacher); OPT_PTR(aux->z_student);
-  OPT_PTR(aux->y); OPT_PTR(aux->state_out); OPT_PTR(aux->r); OPT_PTR(aux->k);
-  if (dec && (aux->state_out || aux->r || aux->k))
-    return fail(TTCD_ERR_BAD_SHAPE, "state_out, r and k are prefill-only outputs");
-  const size_t need = ttcd_layer_forward_workspace_size(d, dec);
-  if (ws_bytes < need)
-    return fail(TTCD_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
-  if (!ws) return fail(TTCD_ERR_NULL_POINTER, "workspace is NULL");
-  OPT_PTR(ws);
-
   hipStream_t s = (hipStream_t)stream;
   const ttcd_attn_desc& a = d->attn;
   const int dt = a.in_dtype;
@@ -870,6 +880,73 @@ ttcd_status ttcd_layer_forward(const ttcd_layer_desc* d, const ttcd_layer_weight
   }
   HIPCHK(launch_add(b.h[main], y, out, (long)B * dm, s));
   return ok();
+}
+
+// ---- the layer forward without allocation: its scratch lives in a
+// file-scope device array, one per GPU, for callers that cannot allocate
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)TTCD_NOALLOC_SCRATCH_MIB << 20;
+__device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+// The device address of `scratch` on the current GPU, looked up once per
+// device with that device current (each GPU holds its own copy).  The name
+// `scratch` itself is a host-side stand-in and is never passed to a kernel.
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+ttcd_status scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TTCD_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(TTCD_ERR_UNSUPPORTED, "device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(TTCD_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TTCD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ttcd_status ttcd_layer_forward(const ttcd_layer_desc* d, const ttcd_layer_weights* wt,
+                               const void* q, const void* k, const void* v, const void* x,
+                               float* out, const ttcd_fw_state* dec, const ttcd_layer_aux* aux,
+                               void* ws, size_t ws_bytes, void* stream) {
+  ttcd_status st = check_layer_args(d, wt, q, k, v, x, out, dec, aux);
+  if (st != TTCD_OK) return st;
+  const size_t need = ttcd_layer_forward_workspace_size(d, dec);
+  if (ws_bytes < need)
+    return fail(TTCD_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (!ws) return fail(TTCD_ERR_NULL_POINTER, "workspace is NULL");
+  OPT_PTR(ws);
+  return layer_forward_run(d, wt, q, k, v, x, out, dec, aux, ws, stream);
+}
+
+size_t ttcd_layer_forward_noalloc_max_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
+
+ttcd_status ttcd_layer_forward_noalloc(const ttcd_layer_desc* d, const ttcd_layer_weights* wt,
+                                       const void* q, const void* k, const void* v,
+                                       const void* x, float* out, const ttcd_fw_state* dec,
+                                       const ttcd_layer_aux* aux, void* stream) {
+  ttcd_status st = check_layer_args(d, wt, q, k, v, x, out, dec, aux);
+  if (st != TTCD_OK) return st;
+  const size_t need = ttcd_layer_forward_workspace_size(d, dec);
+  if (need > NOALLOC_SCRATCH_BYTES)
+    return fail(TTCD_ERR_WORKSPACE_TOO_SMALL,
+                "this call needs %zu bytes of scratch; the no-allocation entry point holds "
+                "%zu (call ttcd_layer_forward with a workspace instead)",
+                need, NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = scratch_ptr(&ws);
+  if (st != TTCD_OK) return st;
+  return layer_forward_run(d, wt, q, k, v, x, out, dec, aux, ws, stream);
 }
 
 size_t ttcd_fastweight_fold_workspace_size(const ttcd_fw_desc* d, int32_t n_chunks) {

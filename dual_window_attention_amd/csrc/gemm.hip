@@ -9,7 +9,6 @@
 
 #include <mutex>
 #include <type_traits>
-#include <vector>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -672,15 +671,17 @@ const void* big_kernel(bool out_bf16, int epi) {
   return out_bf16 ? big_kernel_epi<bf16_t>(epi) : big_kernel_epi<float>(epi);
 }
 // the dynamic LDS limit of each kernel is raised once, on its first launch
+// (a fixed table: launching allocates no host memory)
 hipError_t big_attr(const void* kern) {
   static std::mutex mu;
-  static std::vector<const void*> done;
+  static const void* done[16];
+  static int ndone = 0;
   std::lock_guard<std::mutex> lock(mu);
-  for (const void* k : done)
-    if (k == kern) return hipSuccess;
+  for (int i = 0; i < ndone; ++i)
+    if (done[i] == kern) return hipSuccess;
   const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)big::lds_bytes(big::NST));
-  if (e == hipSuccess) done.push_back(kern);
+  if (e == hipSuccess && ndone < 16) done[ndone++] = kern;
   return e;
 }
 }  // namespace

@@ -39,6 +39,7 @@ EXPORTS = (
     "ttcd_fastweight_scan_eq6_workspace_size", "ttcd_fastweight_scan_eq6",
     "ttcd_fastweight_stream_workspace_size", "ttcd_fastweight_stream",
     "ttcd_layer_forward_workspace_size", "ttcd_layer_forward",
+    "ttcd_layer_forward_noalloc_max_bytes", "ttcd_layer_forward_noalloc",
     "ttcd_fastweight_fold_workspace_size", "ttcd_fastweight_fold",
     "ttcd_fastweight_residual_proj_workspace_size", "ttcd_fastweight_residual_proj",
     "ttcd_fastweight_decode_append_workspace_size", "ttcd_fastweight_decode_append",
@@ -108,6 +109,10 @@ _sig = {
     "ttcd_layer_forward": (C.c_int, [C.POINTER(LayerDesc), C.POINTER(LayerWeights), _vp, _vp,
                                      _vp, _vp, _vp, C.POINTER(FwState), C.POINTER(LayerAux),
                                      _vp, _sz, _vp]),
+    "ttcd_layer_forward_noalloc_max_bytes": (_sz, []),
+    "ttcd_layer_forward_noalloc": (C.c_int, [C.POINTER(LayerDesc), C.POINTER(LayerWeights), _vp,
+                                             _vp, _vp, _vp, _vp, C.POINTER(FwState),
+                                             C.POINTER(LayerAux), _vp]),
     "ttcd_fastweight_residual_proj_workspace_size": (_sz, [C.POINTER(FwDesc)]),
     "ttcd_fastweight_residual_proj": (C.c_int, [C.POINTER(FwDesc), _vp, _vp, _vp, _vp, _sz, _vp]),
     "ttcd_fastweight_decode_append_workspace_size": (_sz, [C.POINTER(FwDesc)]),
@@ -437,13 +442,16 @@ def layer_forward(q, k, v, x, w: Dict[str, torch.Tensor], w_teacher: int, w_stud
                   chunk: int, *, rms_eps: float = 1e-6, l2_eps: float = 1e-12,
                   main_path: str = "teacher", aux: bool = False,
                   decode: Optional[Dict[str, object]] = None, out: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None, stream=None):
+                  workspace: Optional[torch.Tensor] = None, stream=None,
+                  no_alloc: bool = False):
     """IP-TTCD layer forward.  Returns out [B,Tq,d] fp32, or (out, aux dict).
 
     w: w_o, w_gate, w_up, w_down0, w_proj, conv_t, conv_s, beta, optional
     gamma.  decode: dict(pos=L, state_dense=..., r_list=, k_list=,
     beta_list=) for one generated token (q is [B,1,Hq,D], k/v hold the
-    cache with the new token at row L).
+    cache with the new token at row L).  no_alloc: run through
+    ttcd_layer_forward_noalloc (the library's own scratch; no workspace is
+    allocated here).
     """
     dm, f = w["w_down0"].shape
     kc = w["conv_t"].shape[1] if w.get("conv_t") is not None else 4
@@ -486,11 +494,17 @@ def layer_forward(q, k, v, x, w: Dict[str, torch.Tensor], w_teacher: int, w_stud
             aux_t["r"] = torch.empty((B, Tq, dm), dtype=q.dtype, device=dev)
             aux_t["k"] = torch.empty((B, Tq, f), dtype=q.dtype, device=dev)
         aux_s = LayerAux(*[_ptr(aux_t.get(n)) for n, _ in LayerAux._fields_])
-    need = _lib.ttcd_layer_forward_workspace_size(C.byref(desc), dec_p)
-    ws = _workspace(need, dev, workspace)
-    _check(_lib.ttcd_layer_forward(C.byref(desc), C.byref(wt), _ptr(q), _ptr(k), _ptr(v), _ptr(x),
-                                   _ptr(out), dec_p, C.byref(aux_s) if aux_s is not None else None,
-                                   _ptr(ws), ws.numel(), _stream(stream)), "ttcd_layer_forward")
+    aux_p = C.byref(aux_s) if aux_s is not None else None
+    if no_alloc:
+        _check(_lib.ttcd_layer_forward_noalloc(C.byref(desc), C.byref(wt), _ptr(q), _ptr(k),
+                                               _ptr(v), _ptr(x), _ptr(out), dec_p, aux_p,
+                                               _stream(stream)), "ttcd_layer_forward_noalloc")
+    else:
+        need = _lib.ttcd_layer_forward_workspace_size(C.byref(desc), dec_p)
+        ws = _workspace(need, dev, workspace)
+        _check(_lib.ttcd_layer_forward(C.byref(desc), C.byref(wt), _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(x), _ptr(out), dec_p, aux_p, _ptr(ws), ws.numel(),
+                                       _stream(stream)), "ttcd_layer_forward")
     if aux:
         return out, aux_t
     return out

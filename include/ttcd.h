@@ -343,6 +343,40 @@ ttcd_status ttcd_layer_forward(const ttcd_layer_desc* desc,
                                void* stream);
 
 /* ------------------------------------------------------------------------
+ * The layer forward without allocation, for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight
+ * serving loops (one decode step per token), harnesses that forbid
+ * hipMalloc.  Same arguments, semantics and errors as ttcd_layer_forward,
+ * except that the scratch is a device array of TTCD_NOALLOC_SCRATCH_MIB MiB
+ * inside the library (one per GPU, held until the process ends) rather than
+ * a workspace argument.  The call allocates nothing (no hipMalloc, no host
+ * allocation); its first call on a device looks the array's address up
+ * once (hipGetSymbolAddress), so make that first call outside graph capture.
+ *
+ * A call whose ttcd_layer_forward_workspace_size() exceeds
+ * ttcd_layer_forward_noalloc_max_bytes() is rejected with
+ * TTCD_ERR_WORKSPACE_TOO_SMALL before anything is enqueued: decode steps
+ * (batch 32, a 64K cache, 64 chunk lists: about 52 MB) and short prefills
+ * fit; a 64K prefill does not.
+ *
+ * Every call on one GPU shares that GPU's array and leaves its last
+ * contents there (no call relies on them).  Calls that overlap in time on
+ * one GPU -- on different streams, or from different threads -- race on the
+ * array: serialise them.
+ * ---------------------------------------------------------------------- */
+#define TTCD_NOALLOC_SCRATCH_MIB 64
+
+size_t ttcd_layer_forward_noalloc_max_bytes(void);
+
+ttcd_status ttcd_layer_forward_noalloc(const ttcd_layer_desc* desc,
+                                       const ttcd_layer_weights* weights,
+                                       const void* q, const void* k, const void* v,
+                                       const void* x, float* out,
+                                       const ttcd_fw_state* dec,
+                                       const ttcd_layer_aux* aux,
+                                       void* stream);
+
+/* ------------------------------------------------------------------------
  * Decode-time fast-weight stream: the per-token part of the chunk writes
  * (papernotes.org notes, key design 3; the paper's Eq. 12 in the podcast
  * transcript) for a generated token, so that a decode loop can grow the

@@ -172,3 +172,22 @@ def test_update_rule_variants_validate_before_any_launch():
     assert lib.ttcd_fastweight_scan_on_policy(C.byref(good), *([fake] * 10), fake, n_on - 1,
                                               None) == 4
     assert lib.ttcd_fastweight_scan_eq6(C.byref(good), *([fake] * 7), fake, n_e6 - 1, None) == 4
+
+
+def test_noalloc_layer_entry_rejects_calls_beyond_its_scratch():
+    """The no-allocation layer entry point states its scratch size and
+    rejects, on the host, a call whose workspace would not fit (a 64K
+    prefill) and a call with a NULL input."""
+    from dual_window_attention_amd import ttcd
+    lib = ttcd.lib()
+    assert lib.ttcd_layer_forward_noalloc_max_bytes() == 64 << 20
+    fake = C.c_void_p(1 << 20)
+    a = _attn(seq_q=65536, seq_k=65536)
+    ld = ttcd.LayerDesc(a, 1024, 3072, 1024, 4, 0.0, 0.0, 0)
+    w = ttcd.LayerWeights(*([1 << 20] * 8), 1 << 20)
+    assert lib.ttcd_layer_forward_workspace_size(C.byref(ld), None) > 64 << 20
+    assert lib.ttcd_layer_forward_noalloc(C.byref(ld), C.byref(w), fake, fake, fake, fake, fake,
+                                          None, None, None) == 4
+    assert b"no-allocation" in lib.ttcd_last_error()
+    assert lib.ttcd_layer_forward_noalloc(C.byref(ld), C.byref(w), None, fake, fake, fake, fake,
+                                          None, None, None) == 1
