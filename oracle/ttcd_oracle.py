@@ -524,3 +524,163 @@ def decode_append(z_t, z_s, hist_t, hist_s, conv_t, conv_s, w_down0, w_proj,
     r = (dbar @ _f64(w_proj).T) @ _f64(w_down0).T
     k = l2_normalize(zb_s, eps)
     return r, k, dbar, win_t[:, 1:, :], win_s[:, 1:, :]
+
+
+# ==========================================================================
+# Backward pass (the gradient of the forward above; the pages give only its
+# cost, 1.1-1.2x of a standard layer in training: [NOTES] 局限与展望,
+# [PODCAST] the cue on training overhead).  Each function is the vector-
+# Jacobian product of the matching forward, written step by step with the
+# chain rule in the forward's own notation.
+# ==========================================================================
+
+
+def causal_depthwise_conv_backward(z, taps, dzbar):
+    """Gradients of zbar = causal_depthwise_conv(z, taps) given dzbar.
+
+    zbar[t, c] = sum_i taps[c, i] z[t - (kc-1) + i, c]  gives
+        dz[tau, c]    = sum_i taps[c, i] dzbar[tau + (kc-1) - i, c]   (t < T)
+        dtaps[c, i]   = sum_t dzbar[t, c] z[t - (kc-1) + i, c]        (tau >= 0)
+    z, dzbar [T, f]; taps [f, kc].  Returns (dz [T, f], dtaps [f, kc])."""
+    z, taps, dzbar = _f64(z), _f64(taps), _f64(dzbar)
+    T = z.shape[0]
+    kc = taps.shape[1]
+    dz = np.zeros_like(z)
+    dtaps = np.zeros_like(taps)
+    for i in range(kc):
+        shift = kc - 1 - i
+        if shift >= T:
+            continue
+        # zbar[t] takes z[t - shift] through tap i, for t >= shift
+        dz[:T - shift] += dzbar[shift:] * taps[:, i]
+        dtaps[:, i] = np.sum(dzbar[shift:] * z[:T - shift], axis=0)
+    return dz, dtaps
+
+
+def l2_normalize_backward(x, dk, eps: float = 1e-12):
+    """Gradient of k = x / max(||x||, eps) (per row) given dk:
+    (dk - k (k . dk)) / ||x|| where ||x|| > eps, else dk / eps."""
+    x, dk = _f64(x), _f64(dk)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    big = n > eps
+    k = x / np.maximum(n, eps)
+    proj = dk - k * np.sum(k * dk, axis=-1, keepdims=True)
+    return np.where(big, proj / np.maximum(n, eps), dk / eps)
+
+
+def fastweight_scan_backward(z_t, z_s, z_main, conv_t, conv_s, w_down0, w_proj, beta,
+                             C: int, dy, eps: float = 1e-12):
+    """Gradients of y = fastweight_scan(...)["y"] (off-policy rule) given dy.
+
+    With S_i the weight in force for chunk i (S_0 = W_down^(0)), the forward
+    is y_t = S_{c(t)} z_main[t], S_{i+1} = S_i + beta_i R_i^T K_i,
+    r_t = W_down^(0) q_t, q_t = W_proj dbar_t, dbar = zbar_T - zbar_S,
+    k_t = zbar_S[t] / max(||zbar_S[t]||, eps).  Backward, per sequence:
+        dS_i       = sum_{t in C_i} dy_t z_main[t]^T        (the apply)
+        dz_main[t] = S_{c(t)}^T dy_t
+        G_j        = sum_{i > j} dS_i                        (chunk j's write
+                                                              reaches every
+                                                              later chunk)
+        dbeta_j    = sum_{t in C_j} r_t . (G_j k_t)
+        dr_t       = beta_j G_j k_t,   dk_t = beta_j G_j^T r_t
+        dW_down0   = sum_i dS_i + sum_t dr_t q_t^T,   dq_t = W_down0^T dr_t
+        dW_proj    = sum_t dq_t dbar_t^T,             ddbar_t = W_proj^T dq_t
+        dzbar_S    = l2 backward of dk - ddbar,   dzbar_T = ddbar
+    and the conv backward of each path.  Returns dz_t, dz_s, dz_main [B,T,f],
+    dconv_t, dconv_s [f,kc], dw_down0 [d,f], dw_proj [f,f], dbeta [B,n]
+    (weights are shared by the batch: their gradients are summed over it)."""
+    z_t, z_s, z_main, dy = _f64(z_t), _f64(z_s), _f64(z_main), _f64(dy)
+    w0, wp = _f64(w_down0), _f64(w_proj)
+    B, T, f = z_t.shape
+    d = w0.shape[0]
+    bounds = chunk_bounds(T, C)
+    out = {"dz_t": np.zeros_like(z_t), "dz_s": np.zeros_like(z_s),
+           "dz_main": np.zeros_like(z_main), "dconv_t": np.zeros_like(_f64(conv_t)),
+           "dconv_s": np.zeros_like(_f64(conv_s)), "dw_down0": np.zeros_like(w0),
+           "dw_proj": np.zeros_like(wp), "dbeta": np.zeros((B, len(bounds)), F64)}
+    for b in range(B):
+        zb_t = causal_depthwise_conv(z_t[b], conv_t)
+        zb_s = causal_depthwise_conv(z_s[b], conv_s)
+        dbar = zb_t - zb_s
+        q = dbar @ wp.T
+        r = q @ w0.T
+        k = l2_normalize(zb_s, eps)
+        # forward states and the apply's backward
+        S = w0.copy()
+        dS = []
+        for i, (a, e) in enumerate(bounds):
+            out["dz_main"][b, a:e] = dy[b, a:e] @ S
+            dS.append(dy[b, a:e].T @ z_main[b, a:e])
+            S = S + float(beta[b, i]) * (r[a:e].T @ k[a:e])
+        # exclusive suffix sums of the chunk gradients
+        G = [None] * len(bounds)
+        acc = np.zeros((d, f), F64)
+        for j in range(len(bounds) - 1, -1, -1):
+            G[j] = acc.copy()
+            acc = acc + dS[j]
+        out["dw_down0"] += acc                       # sum_i dS_i
+        dr = np.zeros_like(r)
+        dk = np.zeros_like(k)
+        for j, (a, e) in enumerate(bounds):
+            gk = k[a:e] @ G[j].T                     # rows: G_j k_t
+            out["dbeta"][b, j] = float(np.sum(r[a:e] * gk))
+            dr[a:e] = float(beta[b, j]) * gk
+            dk[a:e] = float(beta[b, j]) * (r[a:e] @ G[j])
+        out["dw_down0"] += dr.T @ q
+        dq = dr @ w0
+        out["dw_proj"] += dq.T @ dbar
+        ddbar = dq @ wp
+        dzb_s = l2_normalize_backward(zb_s, dk, eps) - ddbar
+        dzb_t = ddbar
+        dz, dtap = causal_depthwise_conv_backward(z_t[b], conv_t, dzb_t)
+        out["dz_t"][b] = dz
+        out["dconv_t"] += dtap
+        dz, dtap = causal_depthwise_conv_backward(z_s[b], conv_s, dzb_s)
+        out["dz_s"][b] = dz
+        out["dconv_s"] += dtap
+    return out
+
+
+def window_attention_backward(q, k, v, o, lse, do, window: int, scale: Optional[float] = None):
+    """Gradients of o = window_attention(q, k, v, window)[0] given do, from
+    the forward's o and lse (the softmax weights are P = exp(s - lse) on the
+    visible keys):
+        dV_j  = sum_t P_tj dO_t
+        dP_tj = dO_t . v_j,   D_t = dO_t . o_t,   dS_tj = P_tj (dP_tj - D_t)
+        dQ_t  = scale sum_j dS_tj k_j,   dK_j = scale sum_t dS_tj q_t
+    q [B,T,Hq,D], k/v [B,T,Hkv,D]; a kv head's gradient sums its q heads.
+    Returns (dq, dk, dv)."""
+    q, k, v, o, do = _f64(q), _f64(k), _f64(v), _f64(o), _f64(do)
+    lse = _f64(lse)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    t = np.arange(T)
+    diff = t[:, None] - t[None, :]
+    mask = (diff >= 0) & (diff < window)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            s = (q[b, :, h] @ k[b, :, g].T) * scale
+            p = np.where(mask, np.exp(s - lse[b, h][:, None]), 0.0)
+            dp = do[b, :, h] @ v[b, :, g].T
+            dd = np.sum(do[b, :, h] * o[b, :, h], axis=-1, keepdims=True)
+            ds = p * (dp - dd)
+            dv[b, :, g] += p.T @ do[b, :, h]
+            dq[b, :, h] = scale * (ds @ k[b, :, g])
+            dk[b, :, g] += scale * (ds.T @ q[b, :, h])
+    return dq, dk, dv
+
+
+def dual_window_attention_backward(q, k, v, w_teacher: int, w_student: int, do_t, do_s,
+                                   scale: Optional[float] = None):
+    """Gradients of the teacher and student outputs of one shared Q/K/V given
+    dO_T and dO_S: the two windows' gradients add, since both read the same
+    q, k and v."""
+    o_t, o_s, lse_t, lse_s = dual_window_attention(q, k, v, w_teacher, w_student, scale)
+    gq_t, gk_t, gv_t = window_attention_backward(q, k, v, o_t, lse_t, do_t, w_teacher, scale)
+    gq_s, gk_s, gv_s = window_attention_backward(q, k, v, o_s, lse_s, do_s, w_student, scale)
+    return gq_t + gq_s, gk_t + gk_s, gv_t + gv_s
