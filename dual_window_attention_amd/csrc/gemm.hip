@@ -290,13 +290,22 @@ constexpr int ALD = BM * BK / 8 / (64 * NW);         // 16B loads per wave (A)
 constexpr int BLD = BN * BK / 8 / (64 * NW);         // 16B loads per wave (B)
 constexpr int LPW = ALD + BLD;
 constexpr int EPS = 72;                              // epilogue slab row stride (floats)
-static_assert(NW * 32 * EPS * 4 <= 2 * STAGE, "epilogue slabs fit in the operand ring");
+static_assert(NW * 32 * EPS * 4 <= 3 * STAGE, "epilogue slabs fit in the operand ring");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 
+// 16 bytes per lane, global -> LDS; lane i lands at lds_wave_base + 16 i.
+// Inline asm rather than the compiler builtin: the compiler counts a builtin
+// LDS DMA as an LDS operation of unknown order and then waits for every
+// outstanding LDS read (lgkmcnt 0) before any MFMA that needs one of them,
+// which serialises the fragment reads of the next k-step with the MFMAs of
+// this one.  The hardware counts the DMA in vmcnt alone and the loops order
+// it explicitly (a vmcnt wait before the barrier that publishes a stage).
+// M0 takes the LDS address; one wait state separates its write from the DMA.
 TTCD_DEV void g2l16(const void* src, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds_wave_base, 16, 0, 0);
+  const uint32_t m = (uint32_t)(size_t)(lds_void_t*)lds_wave_base;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(m) : "memory");
 }
 // barrier that leaves the in-flight stage fetches alone; every wave waits
 // for the stage it needs with wait_vm before it
@@ -323,19 +332,22 @@ TTCD_DEV void issue(char* dst, const RowPtr& row_ptr, long k0, int wave, int lan
   }
 }
 
-// stages still in flight after the one waited for (0 or 1)
+// stages still in flight after the one waited for (0, 1 or 2)
 TTCD_DEV void wait_pending(int pending) {
-  if (pending >= 1)
+  if (pending >= 2)
+    wait_vm<2 * LPW>();
+  else if (pending == 1)
     wait_vm<LPW>();
   else
     wait_vm<0>();
 }
 
-// 2-stage ring (48 KB): three workgroups share a CU.  (A 3-stage ring with
-// two workgroups per CU and register double buffering of the fragments
-// measured no faster.)
-constexpr int NST = 2;
-template <typename OutT, int EPI>
+// 3-stage ring (72 KB) fetched two stages ahead: two workgroups share a CU,
+// so one's epilogue and stage waits overlap the other's MFMAs.
+constexpr int NST = 3;
+// CHUNKED: the B operand of output row block m0 is chosen per chunk of rows
+// (the fast-weight apply: W_down0 for chunk 0, the state list after it)
+template <typename OutT, int EPI, bool CHUNKED>
 __global__ void __launch_bounds__(NTH, 2)
 gemm_nt_big(GemmArgs g) {
   extern __shared__ __align__(16) char lds[];
@@ -358,7 +370,7 @@ gemm_nt_big(GemmArgs g) {
   const bf16_t* A = (const bf16_t*)g.A + z * g.sA;
   const bf16_t* Bm = (const bf16_t*)g.B + z * g.sB;
   const bf16_t* B2 = g.B2 ? (const bf16_t*)g.B2 + z * g.sB : nullptr;
-  if (g.chunk > 0) {
+  if constexpr (CHUNKED) {
     const long c = m0 / g.chunk;
     if (c > 0) Bm = (const bf16_t*)g.Bchunks + z * g.sBchunksBatch + (c - 1) * g.sBchunk;
   }
@@ -395,40 +407,62 @@ gemm_nt_big(GemmArgs g) {
   wait_pending(npro - 1);
   barrier();
   // MFMA operand fragments of k-step ks (16 wide) of the stage at as
-  auto ldfrag = [&](const char* as, int ks, bf16x8* af, bf16x8* bfr) __attribute__((always_inline)) {
+  struct Frag {
+    bf16x8 a[4], b[2];
+  };
+  auto ldfrag = [&](const char* as, int ks, Frag& f) __attribute__((always_inline)) {
     const char* bs = as + AB;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 128 * wm + 32 * i + r;
-      af[i] = as_bf16x8(ld16(as + row * (BK * 2) + (((2 * ks + h) ^ swz(row)) << 4)));
+      f.a[i] = as_bf16x8(ld16(as + row * (BK * 2) + (((2 * ks + h) ^ swz(row)) << 4)));
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int row = 64 * wn + 32 * j + r;
-      bfr[j] = as_bf16x8(ld16(bs + row * (BK * 2) + (((2 * ks + h) ^ swz(row)) << 4)));
+      f.b[j] = as_bf16x8(ld16(bs + row * (BK * 2) + (((2 * ks + h) ^ swz(row)) << 4)));
     }
   };
-  auto mma = [&](const bf16x8* af, const bf16x8* bfr) __attribute__((always_inline)) {
+  auto mma = [&](const Frag& f) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(f.a[i], f.b[j], acc[i][j]);
   };
+  // Software pipeline: the second k-step's fragments are read while the
+  // first k-step's MFMAs run, the next stage's first fragments while the
+  // second k-step's run.
+  Frag f0, f1;
+  ldfrag(lds, 0, f0);
+  // drain the scalar loads of the set-up, so that inside the loop the LDS
+  // counter holds fragment reads alone and the compiler can wait for the
+  // older fragment set while the newer one is still in flight
+  __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0)
   for (int kt = 0; kt < nk; ++kt) {
-    // the buffer refilled here held stage kt-1, finished before the last barrier
+    // the slot refilled here held stage kt-1; every wave finished reading it
+    // before the barrier that ended the previous iteration
     if (kt + NST - 1 < nk) fetch(kt + NST - 1);
     const char* as = lds + (kt % NST) * STAGE;
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[4], bfr[2];
-      ldfrag(as, ks, af, bfr);
-      mma(af, bfr);
-    }
-    // stage kt+1 must have landed; later ones may still be in flight
+    ldfrag(as, 1, f1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f0);
+    __builtin_amdgcn_sched_barrier(0);
+    // stage kt+1 must have landed (later ones may still be in flight), and
+    // this wave's reads of stage kt are complete before the barrier
     const int last = kt + NST - 1 < nk ? kt + NST - 1 : nk - 1;
+    lds_wave_sync();
     wait_pending(last - (kt + 1));
     barrier();
+    // (after the last stage this reads a slot nobody uses; it stays in bounds)
+    ldfrag(lds + ((kt + 1) % NST) * STAGE, 0, f0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f1);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  // every wave's last MFMAs are done reading the ring before the epilogue
+  // reuses it as slabs
+  lds_wave_sync();
+  barrier();
 
   // Epilogue through a wave-private LDS slab (the operand ring is idle after
   // the last barrier): one 32-row block row of the wave's tile at a time is
@@ -541,6 +575,270 @@ gemm_nt_big(GemmArgs g) {
 }  // namespace big
 
 // --------------------------------------------------------------------------
+// Wide NT GEMM: 256 x 256 workgroup tile, 8 waves (two per SIMD) each
+// owning a 128 x 64 block, BK = 32, a 4-stage global->LDS ring (128 KB, one
+// workgroup per CU) fetched three stages ahead, so the direct-to-LDS loads
+// of a stage have three stages of MFMA work to land behind.  The MFMA
+// operand fragments of a stage's second k-step are read while the first
+// k-step's MFMAs run, and the next stage's first fragments while the
+// second k-step's run.  Per flop the tile moves 2/3 of the operand bytes of
+// the 256 x 128 tile.
+// --------------------------------------------------------------------------
+namespace wide {
+constexpr int BM = 256, BN = 256, BK = 32, NW = 8, NTH = 64 * NW, NST = 4;
+constexpr int AB = BM * BK * 2, BB = BN * BK * 2;    // operand bytes per stage
+constexpr int STAGE = AB + BB;                        // 32 KB
+constexpr size_t LDS_BYTES = (size_t)NST * STAGE;     // 128 KB
+constexpr int ALD = BM * BK / 8 / NTH;                // 16-byte loads per thread (A): 2
+constexpr int BLD = BN * BK / 8 / NTH;                // (B): 2
+constexpr int LPT = ALD + BLD;                        // loads per thread per stage
+constexpr int EPS = 72;                               // epilogue slab row stride (floats)
+static_assert(NW * 32 * EPS * 4 <= (int)LDS_BYTES, "epilogue slabs fit in the operand ring");
+
+using big::barrier;
+
+// 16 bytes per lane, global -> LDS; lane i lands at lds_wave_base + 16 i.
+// Inline asm rather than the compiler builtin: the compiler counts a builtin
+// LDS DMA as an LDS operation of unknown order and then waits for every
+// outstanding LDS read (lgkmcnt 0) before any MFMA that needs one of them,
+// which serialises the fragment reads of the next k-step with the MFMAs of
+// this one.  The hardware counts the DMA in vmcnt alone and the loop orders
+// it explicitly (wait_stages before the barrier that publishes a stage).
+// M0 takes the LDS address; one wait state separates its write from the DMA.
+TTCD_DEV void g2l16(const void* src, void* lds_wave_base) {
+  const uint32_t m = (uint32_t)(size_t)(big::lds_void_t*)lds_wave_base;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(m) : "memory");
+}
+using big::swz;
+using big::lds_wave_sync;
+
+template <int N>
+TTCD_DEV void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// stages still in flight after the one waited for: 0, 1 or 2
+TTCD_DEV void wait_stages(int pending) {
+  if (pending >= 2)
+    wait_vm<2 * LPT>();
+  else if (pending == 1)
+    wait_vm<LPT>();
+  else
+    wait_vm<0>();
+}
+
+template <int NLD, class RowPtr>
+TTCD_DEV void issue(char* dst, const RowPtr& row_ptr, long k0, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int p0 = (i * NW + wave) * 64;
+    const int p = p0 + lane;
+    const int row = p >> 2, cp = p & 3;
+    const int c = cp ^ swz(row);
+    g2l16(row_ptr(row) + k0 + 8 * c, dst + p0 * 16);
+  }
+}
+
+template <typename OutT, int EPI, bool CHUNKED>
+__global__ void __launch_bounds__(NTH, 1)
+gemm_nt_wide(GemmArgs g) {
+  extern __shared__ __align__(16) char lds[];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int h = lane >> 5, r = lane & 31;
+  const int z = blockIdx.z;
+  constexpr bool swiglu = EPI == EPI_SWIGLU;
+  const int ncols = swiglu ? BN / 2 : BN;                   // output columns per tile
+  const int ntn = (g.N + ncols - 1) / ncols;
+  const int ntm = (g.M + BM - 1) / BM;
+  const uint32_t lid = xcd_remap(blockIdx.x, (uint32_t)(ntm * ntn));
+  int tm, tn;
+  grouped_tile(lid, ntm, ntn, 4, tm, tn);
+  const long m0 = (long)tm * BM;
+  const long n0 = (long)tn * ncols;
+
+  const bf16_t* A = (const bf16_t*)g.A + z * g.sA;
+  const bf16_t* Bm = (const bf16_t*)g.B + z * g.sB;
+  const bf16_t* B2 = g.B2 ? (const bf16_t*)g.B2 + z * g.sB : nullptr;
+  if constexpr (CHUNKED) {
+    const long c = m0 / g.chunk;
+    if (c > 0) Bm = (const bf16_t*)g.Bchunks + z * g.sBchunksBatch + (c - 1) * g.sBchunk;
+  }
+  const long mmax = g.M - 1, nmax = g.N - 1;
+  const long lda = g.lda, ldb = g.ldb;
+  auto a_row = [=](int rr) { return A + min(m0 + rr, mmax) * lda; };
+  const long b2_off = swiglu ? (long)(B2 - Bm) : 0;
+  auto b_row = [=](int rr) {
+    if (swiglu) {
+      // LDS row blocks of 32 alternate gate / up for the same 32 columns
+      const int blk = rr >> 5;
+      const long col = min(n0 + 32 * (blk >> 1) + (rr & 31), nmax);
+      return Bm + ((blk & 1) ? b2_off : 0) + col * ldb;
+    }
+    return Bm + min(n0 + rr, nmax) * ldb;
+  };
+  auto fetch = [=](int kt) {
+    char* st = lds + (kt % NST) * STAGE;
+    issue<ALD>(st, a_row, (long)kt * BK, wave, lane);
+    issue<BLD>(st + AB, b_row, (long)kt * BK, wave, lane);
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
+
+  // MFMA operand fragments of k-step ks (16 wide) of the stage at `as`
+  struct Frag {
+    bf16x8 a[4], b[2];
+  };
+  auto ldfrag = [&](const char* as, int ks, Frag& f) __attribute__((always_inline)) {
+    const char* bs = as + AB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 128 * wm + 32 * i + r;
+      f.a[i] = as_bf16x8(ld16(as + row * (BK * 2) + (((2 * ks + h) ^ swz(row)) << 4)));
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = 64 * wn + 32 * j + r;
+      f.b[j] = as_bf16x8(ld16(bs + row * (BK * 2) + (((2 * ks + h) ^ swz(row)) << 4)));
+    }
+  };
+  auto mma = [&](const Frag& f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(f.a[i], f.b[j], acc[i][j]);
+  };
+
+  const int nk = g.K / BK;
+  const int npro = nk < NST - 1 ? nk : NST - 1;
+  for (int kt = 0; kt < npro; ++kt) fetch(kt);
+  wait_stages(npro - 1);
+  barrier();
+  Frag f0, f1;
+  ldfrag(lds, 0, f0);
+  // drain the scalar loads of the set-up before the loop, so that inside it
+  // the LDS counter holds fragment reads alone and the compiler can wait for
+  // the older fragment set while the newer one is still in flight
+  __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0)
+  for (int kt = 0; kt < nk; ++kt) {
+    // the slot refilled here held stage kt-1; every wave finished reading it
+    // before the barrier that ended the previous iteration
+    if (kt + NST - 1 < nk) fetch(kt + NST - 1);
+    const char* as = lds + (kt % NST) * STAGE;
+    ldfrag(as, 1, f1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f0);
+    __builtin_amdgcn_sched_barrier(0);
+    // stage kt+1 must have landed (later ones may still be in flight), and
+    // this wave's reads of stage kt are complete before the barrier
+    const int last = kt + NST - 1 < nk ? kt + NST - 1 : nk - 1;
+    lds_wave_sync();
+    wait_stages(last - (kt + 1));
+    barrier();
+    // (after the last stage this reads a slot nobody uses; it stays in bounds)
+    ldfrag(lds + ((kt + 1) % NST) * STAGE, 0, f0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // every wave's last MFMAs are done reading the ring before the epilogue
+  // reuses it as slabs
+  lds_wave_sync();
+  barrier();
+
+  // Epilogue through a wave-private LDS slab: one 32-row block row of the
+  // wave's tile at a time, written as the MFMA layout leaves it and read back
+  // row-major, so each lane stores 16 bytes of consecutive columns.
+  OutT* C = (OutT*)g.C + z * g.sC;
+  float* slab = reinterpret_cast<float*>(lds) + wave * (32 * EPS);
+  constexpr int ocols = swiglu ? 32 : 64;
+  constexpr int per_row = ocols / 4;
+  constexpr int npieces = 32 * per_row;
+  const long nw0 = swiglu ? n0 + 32 * wn : n0 + 64 * wn;
+  const bool full_tile = m0 + BM - 1 <= mmax && n0 + ncols - 1 <= nmax;
+  const float* res = (const float*)g.res;
+  const bf16_t* resb = (const bf16_t*)g.res;
+  const bool res_bf16 = g.res_dt == BF16;
+  const float* cscale = g.colscale ? g.colscale + z * g.sScale : nullptr;
+  auto finish = [&](long m, long n, f32x4 val) __attribute__((always_inline)) {
+    if constexpr (EPI == EPI_RESIDUAL) {
+      const long rm = (g.res_rows < g.M ? m % g.res_rows : m) * g.ldr + n + z * g.sRes;
+      if (res_bf16) {
+        const uint2 u = *reinterpret_cast<const uint2*>(resb + rm);
+        val[0] += __uint_as_float(u.x << 16);
+        val[1] += __uint_as_float(u.x & 0xFFFF0000u);
+        val[2] += __uint_as_float(u.y << 16);
+        val[3] += __uint_as_float(u.y & 0xFFFF0000u);
+      } else {
+        val += *reinterpret_cast<const f32x4*>(res + rm);
+      }
+    } else if constexpr (EPI == EPI_STORE) {
+      if (cscale) val *= *reinterpret_cast<const f32x4*>(cscale + n);
+    }
+    OutT* cp = C + m * g.ldc + n;
+    if constexpr (sizeof(OutT) == 4) {
+      *reinterpret_cast<f32x4*>(cp) = val;
+    } else {
+      *reinterpret_cast<uint2*>(cp) = uint2{pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = 8 * (v >> 2) + 4 * h + (v & 3);
+      if constexpr (swiglu) {
+        slab[row * EPS + r] = silu(acc[i][0][v]) * acc[i][1][v];
+      } else {
+        slab[row * EPS + r] = acc[i][0][v];
+        slab[row * EPS + 32 + r] = acc[i][1][v];
+      }
+    }
+    lds_wave_sync();
+    const long mb = m0 + 128 * wm + 32 * i;
+    if (full_tile) {
+#pragma unroll
+      for (int t = 0; t < npieces / 64; ++t) {
+        const int idx = lane + 64 * t;
+        const int rr = idx / per_row, c4 = 4 * (idx % per_row);
+        finish(mb + rr, nw0 + c4, *reinterpret_cast<const f32x4*>(slab + rr * EPS + c4));
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < npieces / 64; ++t) {
+        const int idx = lane + 64 * t;
+        const int rr = idx / per_row, c4 = 4 * (idx % per_row);
+        const long m = mb + rr, n = nw0 + c4;
+        if (m > mmax || n > nmax) continue;
+        f32x4 val = *reinterpret_cast<const f32x4*>(slab + rr * EPS + c4);
+        if (n + 3 <= nmax) {
+          finish(m, n, val);
+          continue;
+        }
+        for (int e = 0; e < 4; ++e) {
+          if (n + e > nmax) break;
+          float x = val[e];
+          if constexpr (EPI == EPI_RESIDUAL) {
+            const long rm = (g.res_rows < g.M ? m % g.res_rows : m) * g.ldr + n + e + z * g.sRes;
+            x += res_bf16 ? bf2f(resb[rm]) : res[rm];
+          } else if constexpr (EPI == EPI_STORE) {
+            if (cscale) x *= cscale[n + e];
+          }
+          stf(C + m * g.ldc + n + e, x);
+        }
+      }
+    }
+    lds_wave_sync();
+  }
+}
+}  // namespace wide
+
+// --------------------------------------------------------------------------
 // Few-row NT GEMM (a decode step: one row per sequence), M <= 32.  One wave
 // per 32-column tile and K slice: the MFMA operands come straight from
 // global memory (every A and B row is read once per slice), so enough waves
@@ -643,6 +941,19 @@ bool big_ok(const GemmArgs& g) {
   return tiles >= 256;
 }
 
+bool wide_ok(const GemmArgs& g) {
+  if (g.in_dt != BF16) return false;
+  if (g.K % wide::BK || g.lda % 8 || g.ldb % 8) return false;
+  if (g.ldc % 4 || g.sC % 4) return false;
+  if (g.epi == EPI_RESIDUAL && (g.ldr % 4 || g.sRes % 4)) return false;
+  if (g.chunk > 0 && g.chunk % wide::BM) return false;
+  // enough tiles to give every CU one
+  const long tiles = (long)((g.M + wide::BM - 1) / wide::BM) *
+                     ((g.N + wide::BN - 1) / (g.epi == EPI_SWIGLU ? wide::BN / 2 : wide::BN)) *
+                     (g.batch > 0 ? g.batch : 1);
+  return tiles >= 256;
+}
+
 bool mfma_ok(const GemmArgs& g) {
   if (g.in_dt != BF16) return false;
   if (g.K % 8 || g.lda % 8 || g.ldb % 8) return false;
@@ -658,30 +969,46 @@ size_t gemm_skinny_ws_floats(int M, int N, int K, int epi) {
 }
 
 namespace {
-template <typename OutT>
+template <typename OutT, bool CHUNKED>
 const void* big_kernel_epi(int epi) {
   switch (epi) {
-    case EPI_STORE: return (const void*)big::gemm_nt_big<OutT, EPI_STORE>;
-    case EPI_RESIDUAL: return (const void*)big::gemm_nt_big<OutT, EPI_RESIDUAL>;
-    case EPI_SWIGLU: return (const void*)big::gemm_nt_big<OutT, EPI_SWIGLU>;
+    case EPI_STORE: return (const void*)big::gemm_nt_big<OutT, EPI_STORE, CHUNKED>;
+    case EPI_RESIDUAL: return (const void*)big::gemm_nt_big<OutT, EPI_RESIDUAL, CHUNKED>;
+    case EPI_SWIGLU: return CHUNKED ? nullptr : (const void*)big::gemm_nt_big<OutT, EPI_SWIGLU, false>;
     default: return nullptr;
   }
 }
-const void* big_kernel(bool out_bf16, int epi) {
-  return out_bf16 ? big_kernel_epi<bf16_t>(epi) : big_kernel_epi<float>(epi);
+template <typename OutT, bool CHUNKED>
+const void* wide_kernel_epi(int epi) {
+  switch (epi) {
+    case EPI_STORE: return (const void*)wide::gemm_nt_wide<OutT, EPI_STORE, CHUNKED>;
+    case EPI_RESIDUAL: return (const void*)wide::gemm_nt_wide<OutT, EPI_RESIDUAL, CHUNKED>;
+    case EPI_SWIGLU: return CHUNKED ? nullptr : (const void*)wide::gemm_nt_wide<OutT, EPI_SWIGLU, false>;
+    default: return nullptr;
+  }
+}
+const void* wide_kernel(bool out_bf16, int epi, bool chunked) {
+  if (chunked)
+    return out_bf16 ? wide_kernel_epi<bf16_t, true>(epi) : wide_kernel_epi<float, true>(epi);
+  return out_bf16 ? wide_kernel_epi<bf16_t, false>(epi) : wide_kernel_epi<float, false>(epi);
+}
+const void* big_kernel(bool out_bf16, int epi, bool chunked) {
+  if (chunked)
+    return out_bf16 ? big_kernel_epi<bf16_t, true>(epi) : big_kernel_epi<float, true>(epi);
+  return out_bf16 ? big_kernel_epi<bf16_t, false>(epi) : big_kernel_epi<float, false>(epi);
 }
 // the dynamic LDS limit of each kernel is raised once, on its first launch
 // (a fixed table: launching allocates no host memory)
-hipError_t big_attr(const void* kern) {
+hipError_t lds_attr(const void* kern, size_t bytes) {
   static std::mutex mu;
-  static const void* done[16];
+  static const void* done[32];
   static int ndone = 0;
   std::lock_guard<std::mutex> lock(mu);
   for (int i = 0; i < ndone; ++i)
     if (done[i] == kern) return hipSuccess;
   const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)big::lds_bytes(big::NST));
-  if (e == hipSuccess && ndone < 16) done[ndone++] = kern;
+                                           (int)bytes);
+  if (e == hipSuccess && ndone < 32) done[ndone++] = kern;
   return e;
 }
 }  // namespace
@@ -707,11 +1034,23 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
                          nks_used, ncols);
     return hipGetLastError();
   }
+  if (wide_ok(g)) {
+    const void* kern = wide_kernel(g.out_dt == BF16, g.epi, g.chunk > 0);
+    if (!kern) return hipErrorInvalidValue;
+    const hipError_t e = lds_attr(kern, wide::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    const int ncols = g.epi == EPI_SWIGLU ? wide::BN / 2 : wide::BN;
+    const unsigned tiles =
+        (unsigned)(((g.M + wide::BM - 1) / wide::BM) * ((g.N + ncols - 1) / ncols));
+    dim3 grid(tiles, 1, nb);
+    void* args[] = {(void*)&g};
+    return hipLaunchKernel(kern, grid, dim3(wide::NTH), args, wide::LDS_BYTES, s);
+  }
   if (big_ok(g)) {
     const size_t lds = big::lds_bytes(big::NST);
-    const void* kern = big_kernel(g.out_dt == BF16, g.epi);
+    const void* kern = big_kernel(g.out_dt == BF16, g.epi, g.chunk > 0);
     if (!kern) return hipErrorInvalidValue;
-    const hipError_t e = big_attr(kern);
+    const hipError_t e = lds_attr(kern, lds);
     if (e != hipSuccess) return e;
     const int ncols = g.epi == EPI_SWIGLU ? big::BN / 2 : big::BN;
     const unsigned tiles = (unsigned)(((g.M + big::BM - 1) / big::BM) * ((g.N + ncols - 1) / ncols));

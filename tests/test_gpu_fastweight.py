@@ -91,6 +91,13 @@ def test_scan_qwen3_fast_weight_shapes():
     check_scan(BASE.scaled(batch=1, seq=4608))
 
 
+def test_scan_ragged_large_tiles():
+    """Shapes that take the 256 x 256 GEMM tiles (the residual projection,
+    the chunk writes and the apply) with ragged edges: T % 256 != 0, two
+    sequences."""
+    check_scan(BASE.scaled(batch=2, seq=20000, seed=18))
+
+
 def test_scan_single_chunk_is_base_mlp():
     """T <= C: no earlier chunk, y = W_down0 z exactly as the base MLP."""
     check_scan(BASE.scaled(batch=2, seq=100, d_model=64, d_ff=128, chunk=128, seed=27))

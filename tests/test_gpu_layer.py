@@ -89,6 +89,12 @@ def test_small_chunk_uses_generic_apply():
     check_layer(cfg)
 
 
+def test_smollm2_shapes_ragged_sequence():
+    """The SmolLM2-shaped layer over 12000 tokens: the SwiGLU and apply
+    GEMMs take 256 x 256 tiles with a ragged last row tile."""
+    check_layer(I.CONFIGS[2].scaled(seq=12000, seed=15))
+
+
 def test_smollm2_16k_layer_full():
     check_layer(I.CONFIGS[2])
 
