@@ -174,6 +174,44 @@ def update_rules_bench(cfg, dev, n):
             "tokens": cfg.batch * cfg.seq, "chunks": cfg.n_chunks}
 
 
+def backward_bench(cfg, dev, n):
+    """The fast-weight path's gradient (ttcd_fastweight_scan_backward) at the
+    workload's size, beside its forward (ttcd_fastweight_scan) on the same
+    inputs; gradients of the activations in bf16, of the weights in fp32."""
+    import torch
+    from dual_window_attention_amd import inputs as I
+    from dual_window_attention_amd import ttcd
+
+    z = I.hidden_activations(cfg)
+    w = I.layer_weights(cfg)
+    zt, zs = I.to_torch(z["z_t"], dev), I.to_torch(z["z_s"], dev)
+    del z
+    wt = [I.to_torch(w[k], dev) for k in ("conv_t", "conv_s", "w_down0", "w_proj")]
+    beta = I.f32_to_torch(I.beta_for(cfg), dev)
+    dy = torch.randn((cfg.batch, cfg.seq, cfg.d_model), generator=torch.Generator().manual_seed(5),
+                     dtype=torch.float32).to(dev, torch.bfloat16)
+    d = ttcd.fw_desc(zt, cfg.d_model, cfg.chunk, cfg.conv_k, 0.0, torch.bfloat16)
+    lib = ttcd.lib()
+    ws = torch.empty(max(lib.ttcd_fastweight_scan_backward_workspace_size(d),
+                         lib.ttcd_fastweight_scan_workspace_size(d)),
+                     dtype=torch.uint8, device=dev)
+    g = ttcd.fastweight_scan_backward(zt, zs, zt, *wt, beta, dy, cfg.chunk,
+                                      out_dtype=torch.bfloat16, workspace=ws)
+    st = torch.cuda.current_stream()
+    bwd_ms = time_events(lambda: ttcd.fastweight_scan_backward(
+        zt, zs, zt, *wt, beta, dy, cfg.chunk, out_dtype=torch.bfloat16, out=g, workspace=ws),
+        n, st, 3)
+    fwd_ms = time_events(lambda: ttcd.fastweight_scan(zt, zs, zt, *wt, beta, cfg.chunk,
+                                                      workspace=ws), n, st, 3)
+    finite = all(torch.isfinite(t).all().item() for t in g.values())
+    ws_gb = ws.numel() / 1e9
+    del zt, zs, wt, beta, dy, g, ws
+    return {"kernel": "fast-weight path backward (ttcd_fastweight_scan_backward): gradients of "
+                      "z_T, z_S, z_main, both convs, W_down0, W_proj and beta",
+            "ms_per_call": bwd_ms, "forward_ms_per_call": fwd_ms, "bwd_over_fwd": bwd_ms / fwd_ms,
+            "workspace_gb": ws_gb, "finite": finite, "tokens": cfg.batch * cfg.seq}
+
+
 def decode_bench(dev, n):
     """One decode token per sequence at the batch-32, 64K-cache workload:
     low-rank lists and folded dense state; the fold itself timed once."""
@@ -443,6 +481,7 @@ def main():
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the LSE-combination and update-rule sections (the counter passes "
                          "then see only the fused attention call)")
+    ap.add_argument("--no-backward", action="store_true", help="skip the gradient section")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the 16K SmolLM2-shaped layer and the batch-8 attention sweep")
     ap.add_argument("--summarize-trace", metavar="CSV",
@@ -558,6 +597,9 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_variants:
         res["update_rules"] = update_rules_bench(cfg, dev, 5)
+        torch.cuda.empty_cache()
+    if not args.no_backward:
+        res["backward"] = backward_bench(cfg, dev, 5)
         torch.cuda.empty_cache()
     if not args.no_decode:
         res["decode"] = decode_bench(dev, n_att)

@@ -673,6 +673,277 @@ ttcd_status ttcd_fastweight_stream(const ttcd_fw_desc* d, const void* zt, const 
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// ---- backward pass of the off-policy fast-weight scan
+// (buffers beyond the forward's; TC = chunks * chunk columns per sequence)
+struct BwdBufs {
+  FwBufs fw;
+  int TC;
+  void *w0t, *mt, *m_lo, *rtok, *dyt, *zmt, *g, *g_lo, *gt, *drt, *drtok, *khat, *dbart, *dmt_dt,
+      *dm_dt;
+  float *m32, *rtu, *ds, *total, *pt, *dbpart, *dk, *ddbar, *dmt, *dm, *kd, *sbpart;
+};
+
+void plan_bwd(int B, int T, int d, int f, int C, int kc, int dt, Plan& p, BwdBufs& w) {
+  plan_fw(B, T, d, f, C, dt, p, w.fw);
+  const size_t es = dsize(dt);
+  const int N = w.fw.N;
+  w.TC = N * C;
+  const size_t cols = (size_t)B * w.TC, BT = (size_t)B * T;
+  // bf16: M and G also keep their remainders (m_lo, g_lo), so that the
+  // residuals R and P = G K^T that meet in dbeta carry no bf16 rounding of M
+  // or G (dbeta is an inner product with cancellation)
+  const bool split = dt == BF16;
+  w.w0t = p.take((size_t)f * d * es);
+  w.mt = p.take((size_t)f * d * es);
+  w.m32 = split ? (float*)p.take((size_t)d * f * sizeof(float)) : nullptr;
+  w.m_lo = split ? p.take((size_t)d * f * es) : nullptr;
+  w.rtu = (float*)p.take((size_t)d * cols * sizeof(float));
+  w.rtok = p.take(BT * d * es);
+  w.dyt = p.take((size_t)d * cols * es);
+  w.zmt = p.take((size_t)f * cols * es);
+  w.ds = (float*)p.take((size_t)B * N * d * f * sizeof(float));
+  w.g = p.take((size_t)B * N * d * f * es);
+  w.g_lo = split ? p.take((size_t)B * N * d * f * es) : nullptr;
+  w.gt = p.take((size_t)B * N * d * f * es);
+  w.total = (float*)p.take((size_t)d * f * sizeof(float));
+  w.pt = (float*)p.take((size_t)d * cols * sizeof(float));
+  w.dbpart = (float*)p.take(dbeta_part_floats(B, N, d) * sizeof(float));
+  w.drt = p.take((size_t)d * cols * es);
+  w.drtok = p.take(BT * d * es);
+  w.khat = p.take(BT * f * es);
+  w.dk = (float*)p.take(BT * f * sizeof(float));
+  w.ddbar = (float*)p.take(BT * f * sizeof(float));
+  w.dbart = p.take((size_t)f * cols * es);
+  w.dmt = (float*)p.take((size_t)f * d * sizeof(float));
+  w.dm = (float*)p.take((size_t)d * f * sizeof(float));
+  w.dmt_dt = p.take((size_t)f * d * es);
+  w.dm_dt = p.take((size_t)d * f * es);
+  w.kd = (float*)p.take(BT * sizeof(float));
+  w.sbpart = (float*)p.take(stream_bwd_part_floats(B, T, f, kc) * sizeof(float));
+}
+
+// The gradient of y = fastweight_scan(...) given dy (see the header).  Every
+// contraction is the NT GEMM (both operands contiguous along the summed
+// index); the layout kernels put each operand that way.
+hipError_t run_fw_backward(int B, int T, int d, int f, int C, int kc, float eps, int dt,
+                           int out_dt, const void* zt, const void* zs, const void* zmain,
+                           const void* conv_t, const void* conv_s, const void* w0,
+                           const void* wp, const float* beta, const void* dy, void* dzt,
+                           void* dzs, void* dzmain, float* dconv_t, float* dconv_s,
+                           float* dw0, float* dwp, float* dbeta, const BwdBufs& w,
+                           hipStream_t s) {
+  hipError_t e;
+  const FwBufs& fw = w.fw;
+  const int N = fw.N, Tpad = fw.Tpad, TC = w.TC;
+  const size_t es = dsize(dt);
+  const long cols = (long)B * TC, BT = (long)B * T, df = (long)d * f;
+  // (1) the forward's stream and residual projection: dbar, Zbar_S^T, the
+  //     write scale and the inverse key norms
+  StreamArgs sa{};
+  sa.zt = zt; sa.zs = zs; sa.conv_t = conv_t; sa.conv_s = conv_s; sa.beta = beta;
+  sa.dbar = fw.dbar; sa.zbt = fw.zbt; sa.sc = fw.sc; sa.inv = fw.inv; sa.part = fw.part;
+  sa.B = B; sa.T = T; sa.f = f; sa.kc = kc; sa.chunk = C; sa.nchunks = N; sa.eps = eps;
+  sa.in_dt = dt;
+  if ((e = launch_fw_stream(sa, s)) != hipSuccess) return e;
+  if ((e = launch_unit_keys(fw.zbt, fw.inv, w.khat, B, T, f, dt, s)) != hipSuccess) return e;
+  // M = W0 W_proj and its transpose; W0^T
+  if ((e = launch_transpose(wp, fw.wpt, f, f, f, f, 1, 0, 0, (int)es, s)) != hipSuccess) return e;
+  GemmArgs g{};
+  g.A = w0; g.lda = f; g.B = fw.wpt; g.ldb = f; g.C = w.m32 ? (void*)w.m32 : fw.m; g.ldc = f;
+  g.M = d; g.N = f; g.K = f; g.in_dt = dt; g.out_dt = w.m32 ? F32 : dt; g.epi = EPI_STORE;
+  g.batch = 1;
+  if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+  if (w.m32 && (e = launch_split_bf16(w.m32, fw.m, w.m_lo, (long)d * f, s)) != hipSuccess)
+    return e;
+  if ((e = launch_transpose(fw.m, w.mt, d, f, f, d, 1, 0, 0, (int)es, s)) != hipSuccess) return e;
+  if ((e = launch_transpose(w0, w.w0t, d, f, f, d, 1, 0, 0, (int)es, s)) != hipSuccess) return e;
+  // R^T unscaled (fp32, [d, B*TC]), R token-major, and the forward's scaled R~^T
+  if ((e = launch_fill(w.rtu, (long)d * cols, 0.f, F32, s)) != hipSuccess) return e;
+  g = GemmArgs{};
+  g.A = fw.m; g.lda = f; g.B = fw.dbar; g.ldb = f; g.C = w.rtu; g.ldc = cols;
+  g.M = d; g.N = T; g.K = f; g.in_dt = dt; g.out_dt = F32; g.epi = EPI_STORE;
+  g.batch = B; g.sA = 0; g.sB = (long)Tpad * f; g.sC = TC;
+  if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+  if (w.m_lo) {   // += (M - bf16(M)) dbar, in place
+    g.A = w.m_lo; g.epi = EPI_RESIDUAL; g.res = w.rtu; g.ldr = cols; g.res_rows = d;
+    g.res_dt = F32; g.sRes = TC;
+    if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+  }
+  g = GemmArgs{};
+  g.A = fw.dbar; g.lda = f; g.B = fw.m; g.ldb = f; g.C = w.rtok; g.ldc = d;
+  g.M = T; g.N = d; g.K = f; g.in_dt = dt; g.out_dt = dt; g.epi = EPI_STORE;
+  g.batch = B; g.sA = (long)Tpad * f; g.sB = 0; g.sC = (long)T * d;
+  if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+  g = GemmArgs{};
+  g.A = fw.m; g.lda = f; g.B = fw.dbar; g.ldb = f; g.C = fw.rst; g.ldc = Tpad;
+  g.M = d; g.N = Tpad; g.K = f; g.in_dt = dt; g.out_dt = dt; g.epi = EPI_STORE;
+  g.colscale = fw.sc; g.batch = B; g.sA = 0; g.sB = (long)Tpad * f; g.sC = (long)d * Tpad;
+  g.sScale = Tpad;
+  if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+  // (2) the weights in force, transposed: S_i^T = W0^T + sum_{j<i} dW_j^T,
+  //     dW_j^T = Zbar_S,j R~_j^T (the forward's chunk writes, operands swapped)
+  const int nstates = N - 1;
+  if (nstates > 0) {
+    for (int b = 0; b < B; ++b) {
+      g = GemmArgs{};
+      g.A = (const char*)fw.zbt + (size_t)b * f * Tpad * es;
+      g.B = (const char*)fw.rst + (size_t)b * d * Tpad * es;
+      g.C = (char*)fw.dw + (size_t)b * N * df * es;
+      g.lda = Tpad; g.ldb = Tpad; g.ldc = d; g.M = f; g.N = d; g.K = C;
+      g.in_dt = dt; g.out_dt = dt; g.epi = EPI_STORE;
+      g.batch = nstates; g.sA = C; g.sB = C; g.sC = df;
+      if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+    }
+    if ((e = launch_state_prefix(fw.dw, (long)N, w.w0t, fw.states, nullptr, df, nstates, nstates,
+                                 B, dt, dt, s)) != hipSuccess)
+      return e;
+  }
+  // (3) dz_main[t] = S_{c(t)}^T dy_t (chunked B operand: W0^T, then S_i^T)
+  g = GemmArgs{};
+  g.A = dy; g.lda = d; g.B = w.w0t; g.ldb = d; g.C = dzmain; g.ldc = f;
+  g.M = T; g.N = f; g.K = d; g.in_dt = dt; g.out_dt = out_dt; g.epi = EPI_STORE;
+  g.batch = B; g.sA = (long)T * d; g.sB = 0; g.sC = (long)T * f;
+  g.chunk = C; g.Bchunks = fw.states; g.sBchunk = df; g.sBchunksBatch = (long)nstates * df;
+  if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+  // (4) dS_i = dY_i^T Z_main,i for every chunk; G_j = sum_{i > j} dS_i, their
+  //     transposes, and sum_i dS_i (the direct part of dW0)
+  if ((e = launch_to_feature_major(dy, w.dyt, B, T, T, TC, d, dt, s)) != hipSuccess) return e;
+  if ((e = launch_to_feature_major(zmain, w.zmt, B, T, T, TC, f, dt, s)) != hipSuccess) return e;
+  for (int b = 0; b < B; ++b) {
+    g = GemmArgs{};
+    g.A = (const char*)w.dyt + (size_t)b * TC * es; g.lda = cols;
+    g.B = (const char*)w.zmt + (size_t)b * TC * es; g.ldb = cols;
+    g.C = w.ds + (size_t)b * N * df; g.ldc = f;
+    g.M = d; g.N = f; g.K = C; g.in_dt = dt; g.out_dt = F32; g.epi = EPI_STORE;
+    g.batch = N; g.sA = C; g.sB = C; g.sC = df;
+    if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+  }
+  if ((e = launch_chunk_suffix(w.ds, w.g, w.g_lo, w.total, df, N, B, dt, s)) != hipSuccess)
+    return e;
+  if (nstates > 0 &&
+      (e = launch_transpose(w.g, w.gt, d, f, f, d, B * N, df, df, (int)es, s)) != hipSuccess)
+    return e;
+  // (5) P_j = G_j K_j^T (unscaled) for the chunks with a later chunk, stored
+  //     as P^T [d, B*TC]; dbeta_j = <R_j, P_j>, dR = beta P
+  if ((e = launch_fill(w.pt, (long)d * cols, 0.f, F32, s)) != hipSuccess) return e;
+  if (nstates > 0) {
+    for (int b = 0; b < B; ++b) {
+      g = GemmArgs{};
+      g.A = (const char*)w.g + (size_t)b * N * df * es; g.lda = f;
+      g.B = (const char*)w.khat + (size_t)b * T * f * es; g.ldb = f;
+      g.C = w.pt + (size_t)b * TC; g.ldc = cols;
+      g.M = d; g.N = C; g.K = f; g.in_dt = dt; g.out_dt = F32; g.epi = EPI_STORE;
+      g.batch = nstates; g.sA = df; g.sB = (long)C * f; g.sC = C;
+      if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+      if (w.g_lo) {   // += (G - bf16(G)) K^T, in place
+        g.A = (const char*)w.g_lo + (size_t)b * N * df * es; g.epi = EPI_RESIDUAL;
+        g.res = g.C; g.ldr = cols; g.res_rows = d; g.res_dt = F32; g.sRes = C;
+        if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+      }
+    }
+  }
+  if ((e = launch_dbeta(w.rtu, w.pt, beta, w.dbpart, dbeta, B, d, C, T, TC, N, s)) != hipSuccess)
+    return e;
+  if ((e = launch_to_token_major(w.pt, F32, w.drtok, dt, B, T, TC, d, nullptr, C, N, s)) !=
+      hipSuccess)
+    return e;
+  if ((e = launch_convert(w.pt, w.drt, (long)d * cols, dt, s)) != hipSuccess) return e;
+  // (6) dK_t = G_j^T r_t (unscaled; the last chunk's rows stay zero)
+  if ((e = launch_fill(w.dk, BT * f, 0.f, F32, s)) != hipSuccess) return e;
+  if (nstates > 0) {
+    for (int b = 0; b < B; ++b) {
+      g = GemmArgs{};
+      g.A = (const char*)w.rtok + (size_t)b * T * d * es; g.lda = d;
+      g.B = (const char*)w.gt + (size_t)b * N * df * es; g.ldb = d;
+      g.C = w.dk + (size_t)b * T * f; g.ldc = f;
+      g.M = C; g.N = f; g.K = d; g.in_dt = dt; g.out_dt = F32; g.epi = EPI_STORE;
+      g.batch = nstates; g.sA = (long)C * d; g.sB = df; g.sC = (long)C * f;
+      if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+    }
+  }
+  // (7) the residual projection: ddbar = dR M, dM = sum_t dr_t dbar_t^T,
+  //     dW_proj = W0^T dM, dW0 = sum_i dS_i + dM W_proj^T
+  g = GemmArgs{};
+  g.A = w.drtok; g.lda = d; g.B = w.mt; g.ldb = d; g.C = w.ddbar; g.ldc = f;
+  g.M = (int)BT; g.N = f; g.K = d; g.in_dt = dt; g.out_dt = F32; g.epi = EPI_STORE; g.batch = 1;
+  if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+  if ((e = launch_to_feature_major(fw.dbar, w.dbart, B, T, Tpad, TC, f, dt, s)) != hipSuccess)
+    return e;
+  g = GemmArgs{};
+  g.A = w.dbart; g.lda = cols; g.B = w.drt; g.ldb = cols; g.C = w.dmt; g.ldc = d;
+  g.M = f; g.N = d; g.K = (int)cols; g.in_dt = dt; g.out_dt = F32; g.epi = EPI_STORE; g.batch = 1;
+  if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+  if ((e = launch_transpose(w.dmt, w.dm, f, d, d, f, 1, 0, 0, 4, s)) != hipSuccess) return e;
+  if ((e = launch_convert(w.dmt, w.dmt_dt, (long)f * d, dt, s)) != hipSuccess) return e;
+  if ((e = launch_convert(w.dm, w.dm_dt, (long)d * f, dt, s)) != hipSuccess) return e;
+  g = GemmArgs{};
+  g.A = w.w0t; g.lda = d; g.B = w.dmt_dt; g.ldb = d; g.C = dwp; g.ldc = f;
+  g.M = f; g.N = f; g.K = d; g.in_dt = dt; g.out_dt = F32; g.epi = EPI_STORE; g.batch = 1;
+  if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+  g = GemmArgs{};
+  g.A = w.dm_dt; g.lda = f; g.B = wp; g.ldb = f; g.C = dw0; g.ldc = f;
+  g.M = d; g.N = f; g.K = f; g.in_dt = dt; g.out_dt = F32; g.epi = EPI_RESIDUAL;
+  g.res = w.total; g.ldr = f; g.res_rows = d; g.res_dt = F32; g.batch = 1;
+  if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+  // (8) the l2 and conv backward per token, and the taps' gradients
+  if ((e = launch_key_dot(w.khat, w.dk, beta, w.kd, B, T, f, C, N, dt, s)) != hipSuccess) return e;
+  StreamBwdArgs sb{};
+  sb.zt = zt; sb.zs = zs; sb.conv_t = conv_t; sb.conv_s = conv_s; sb.dk = w.dk;
+  sb.ddbar = w.ddbar; sb.kd = w.kd; sb.inv = fw.inv; sb.beta = beta; sb.dzt = dzt; sb.dzs = dzs;
+  sb.dconv_t = dconv_t; sb.dconv_s = dconv_s; sb.part = w.sbpart;
+  sb.B = B; sb.T = T; sb.f = f; sb.kc = kc; sb.chunk = C; sb.nch = N; sb.eps = eps;
+  sb.in_dt = dt; sb.out_dt = out_dt;
+  return launch_stream_bwd(sb, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ttcd_fastweight_scan_backward_workspace_size(const ttcd_fw_desc* d) {
+  if (check_fw(d) != TTCD_OK) return 0;
+  Plan p(nullptr);
+  BwdBufs w;
+  plan_bwd(d->batch, d->seq, d->d_model, d->d_ff, d->chunk, d->conv_k, d->in_dtype, p, w);
+  return p.off;
+}
+
+ttcd_status ttcd_fastweight_scan_backward(const ttcd_fw_desc* d, const void* zt, const void* zs,
+                                          const void* zmain, const void* conv_t,
+                                          const void* conv_s, const void* w_down0,
+                                          const void* w_proj, const float* beta, const void* dy,
+                                          void* dz_t, void* dz_s, void* dz_main, float* dconv_t,
+                                          float* dconv_s, float* dw_down0, float* dw_proj,
+                                          float* dbeta, void* ws, size_t ws_bytes, void* stream) {
+  ttcd_status st = check_fw(d);
+  if (st != TTCD_OK) return st;
+  REQ_PTR(zt); REQ_PTR(zs); REQ_PTR(zmain); REQ_PTR(conv_t); REQ_PTR(conv_s);
+  REQ_PTR(w_down0); REQ_PTR(w_proj); REQ_PTR(dy); REQ_PTR(dz_t); REQ_PTR(dz_s); REQ_PTR(dz_main);
+  if (!beta || !dconv_t || !dconv_s || !dw_down0 || !dw_proj || !dbeta)
+    return fail(TTCD_ERR_NULL_POINTER, "beta and every weight gradient are required");
+  OPT_PTR4(beta); OPT_PTR4(dconv_t); OPT_PTR4(dconv_s); OPT_PTR(dw_down0); OPT_PTR(dw_proj);
+  OPT_PTR4(dbeta);
+  if ((long)d->batch * d->seq > (1L << 30)) return fail(TTCD_ERR_BAD_SHAPE, "batch * seq too large");
+  const size_t need = ttcd_fastweight_scan_backward_workspace_size(d);
+  if (ws_bytes < need)
+    return fail(TTCD_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (!ws) return fail(TTCD_ERR_NULL_POINTER, "workspace is NULL");
+  OPT_PTR(ws);
+  Plan p(ws);
+  BwdBufs w;
+  plan_bwd(d->batch, d->seq, d->d_model, d->d_ff, d->chunk, d->conv_k, d->in_dtype, p, w);
+  const float eps = d->l2_eps > 0.f ? d->l2_eps : 1e-12f;
+  HIPCHK(run_fw_backward(d->batch, d->seq, d->d_model, d->d_ff, d->chunk, d->conv_k, eps,
+                         d->in_dtype, d->out_dtype, zt, zs, zmain, conv_t, conv_s, w_down0, w_proj,
+                         beta, dy, dz_t, dz_s, dz_main, dconv_t, dconv_s, dw_down0, dw_proj, dbeta,
+                         w, (hipStream_t)stream));
+  return ok();
+}
+
 // ---- decode-time fast-weight pieces
 size_t ttcd_fastweight_residual_proj_workspace_size(const ttcd_fw_desc* d) {
   if (check_fw(d) != TTCD_OK) return 0;

@@ -157,6 +157,50 @@ hipError_t launch_transpose_scale(const void* in, void* out, int rows, int cols,
 // V [B, kv_rows, Hkv, D] (bf16) -> vt [B, Hkv, D, vt_ld]: keys in [jlo, Tk), the
 // keys of each 16-group permuted for the attention kernel's MFMA operand reads
 
+// ---------------------------------------------------------------- backward
+// token-major [B, rows, F] (the first T rows of each sequence) ->
+// feature-major [F, B * TC], zero for T <= t < TC
+hipError_t launch_to_feature_major(const void* in, void* out, int B, int T, int rows, int TC,
+                                   int F, int dt, hipStream_t s);
+// feature-major [F, B * TC] -> token-major [B, T, F], each token scaled by
+// scale[b * n + t / chunk] when scale is given
+hipError_t launch_to_token_major(const void* in, int in_dt, void* out, int out_dt, int B, int T,
+                                 int TC, int F, const float* scale, int chunk, int n,
+                                 hipStream_t s);
+// x [rows, B * TC] *= s[b * Tpad + t] (zero for t >= T)
+hipError_t launch_scale_token_cols(void* x, const float* sc, int rows, int B, int T, int TC,
+                                   int Tpad, int dt, hipStream_t s);
+// G [B, nch, n] = exclusive suffix sums of ds (fp32) over the chunks, stored
+// in dt as g and, for bf16, the remainder g_lo = G - g (NULL: not wanted);
+// total [n] fp32 = sum over sequences and chunks of ds
+hipError_t launch_chunk_suffix(const float* ds, void* g, void* g_lo, float* total, long n,
+                               int nch, int B, int dt, hipStream_t s);
+// x fp32 [n] -> hi = bf16(x), lo = bf16(x - hi)
+hipError_t launch_split_bf16(const float* x, void* hi, void* lo, long n, hipStream_t s);
+// dbeta [B, nch] = per-chunk <R^T, P^T>; P^T *= beta (in place); rt, pt fp32 [d, B * TC]
+size_t dbeta_part_floats(int B, int nch, int d);
+hipError_t launch_dbeta(const float* rt, float* pt, const float* beta, float* part, float* dbeta,
+                        int B, int d, int chunk, int T, int TC, int nch, hipStream_t s);
+// kd [B * T] = beta_{c(t)} (khat_t . dk_t)
+hipError_t launch_key_dot(const void* khat, const float* dk, const float* beta, float* kd, int B,
+                          int T, int f, int chunk, int nch, int dt, hipStream_t s);
+struct StreamBwdArgs {
+  const void* zt; const void* zs; const void* conv_t; const void* conv_s;   // in_dt
+  const float* dk;       // [B*T, f] G_j^T r_t (beta not applied)
+  const float* ddbar;    // [B*T, f]
+  const float* kd;       // [B*T] beta (k . dK)
+  const float* inv;      // [B, Tpad] 1 / max(|zbar_S|, eps)
+  const float* beta;     // [B, nch]
+  void* dzt; void* dzs;  // [B, T, f] out_dt
+  float* dconv_t; float* dconv_s;   // [f, kc]
+  float* part;           // stream_bwd_part_floats
+  int B, T, f, kc, chunk, nch;
+  float eps;
+  int in_dt, out_dt;
+};
+size_t stream_bwd_part_floats(int B, int T, int f, int kc);
+hipError_t launch_stream_bwd(const StreamBwdArgs& a, hipStream_t s);
+
 // decode fast-weight apply from low-rank lists:
 //   c[b, t]  = k_list[b, t] . z[b]          (t < n*chunk)
 //   y[b]    += sum_j beta[b, j] sum_{t in j} c[b, t] r_list[b, t]

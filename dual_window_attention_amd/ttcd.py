@@ -37,6 +37,7 @@ EXPORTS = (
     "ttcd_fastweight_scan_workspace_size", "ttcd_fastweight_scan",
     "ttcd_fastweight_scan_on_policy_workspace_size", "ttcd_fastweight_scan_on_policy",
     "ttcd_fastweight_scan_eq6_workspace_size", "ttcd_fastweight_scan_eq6",
+    "ttcd_fastweight_scan_backward_workspace_size", "ttcd_fastweight_scan_backward",
     "ttcd_fastweight_stream_workspace_size", "ttcd_fastweight_stream",
     "ttcd_layer_forward_workspace_size", "ttcd_layer_forward",
     "ttcd_layer_forward_noalloc_max_bytes", "ttcd_layer_forward_noalloc",
@@ -102,6 +103,8 @@ _sig = {
     "ttcd_fastweight_scan_eq6_workspace_size": (_sz, [C.POINTER(FwDesc)]),
     "ttcd_fastweight_scan_eq6": (C.c_int, [C.POINTER(FwDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                            _vp, _sz, _vp]),
+    "ttcd_fastweight_scan_backward_workspace_size": (_sz, [C.POINTER(FwDesc)]),
+    "ttcd_fastweight_scan_backward": (C.c_int, [C.POINTER(FwDesc)] + [_vp] * 18 + [_sz, _vp]),
     "ttcd_fastweight_stream_workspace_size": (_sz, [C.POINTER(FwDesc)]),
     "ttcd_fastweight_stream": (C.c_int, [C.POINTER(FwDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                          _vp, _vp, _sz, _vp]),
@@ -342,6 +345,49 @@ def fastweight_scan_eq6(z_teacher, z_student, z_main, w_down0, beta, chunk: int,
                                          _ptr(st), _ptr(ws), ws.numel(), _stream(stream)),
            "ttcd_fastweight_scan_eq6")
     return y, st
+
+
+def fastweight_scan_backward(z_teacher, z_student, z_main, conv_t, conv_s, w_down0, w_proj,
+                             beta, dy, chunk: int, *, out_dtype=torch.float32,
+                             l2_eps: float = 0.0, out=None, workspace=None, stream=None):
+    """Gradients of fastweight_scan's y given dy [B,T,d] (the inputs' dtype).
+
+    Returns a dict: dz_t, dz_s, dz_main [B,T,f] (out_dtype), dconv_t,
+    dconv_s [f,kc], dw_down0 [d,f], dw_proj [f,f] (fp32, summed over the
+    batch) and dbeta [B, n_chunks] (fp32).  ``out``: such a dict to write
+    into (from an earlier call of the same shapes)."""
+    dm = w_down0.shape[0]
+    kc = conv_t.shape[1]
+    d = fw_desc(z_teacher, dm, chunk, kc, l2_eps, out_dtype)
+    B, T, f = z_teacher.shape
+    dev = z_teacher.device
+    if out is not None:
+        g = out
+    else:
+        g = {n: torch.empty((B, T, f), dtype=out_dtype, device=dev)
+             for n in ("dz_t", "dz_s", "dz_main")}
+        g["dconv_t"] = torch.empty((f, kc), dtype=torch.float32, device=dev)
+        g["dconv_s"] = torch.empty((f, kc), dtype=torch.float32, device=dev)
+        g["dw_down0"] = torch.empty((dm, f), dtype=torch.float32, device=dev)
+        g["dw_proj"] = torch.empty((f, f), dtype=torch.float32, device=dev)
+        g["dbeta"] = torch.empty((B, -(-T // chunk)), dtype=torch.float32, device=dev)
+    shapes = {"dz_t": (B, T, f), "dz_s": (B, T, f), "dz_main": (B, T, f), "dconv_t": (f, kc),
+              "dconv_s": (f, kc), "dw_down0": (dm, f), "dw_proj": (f, f),
+              "dbeta": (B, -(-T // chunk))}
+    for n, shp in shapes.items():
+        want = out_dtype if n.startswith("dz") else torch.float32
+        if tuple(g[n].shape) != shp or g[n].dtype != want or not g[n].is_contiguous():
+            raise ValueError(f"fastweight_scan_backward: out[{n!r}] must be a contiguous "
+                             f"{want} tensor of shape {shp}")
+    need = _lib.ttcd_fastweight_scan_backward_workspace_size(C.byref(d))
+    ws = _workspace(need, dev, workspace)
+    _check(_lib.ttcd_fastweight_scan_backward(
+        C.byref(d), _ptr(z_teacher), _ptr(z_student), _ptr(z_main), _ptr(conv_t), _ptr(conv_s),
+        _ptr(w_down0), _ptr(w_proj), _ptr(beta), _ptr(dy), _ptr(g["dz_t"]), _ptr(g["dz_s"]),
+        _ptr(g["dz_main"]), _ptr(g["dconv_t"]), _ptr(g["dconv_s"]), _ptr(g["dw_down0"]),
+        _ptr(g["dw_proj"]), _ptr(g["dbeta"]), _ptr(ws), ws.numel(), _stream(stream)),
+        "ttcd_fastweight_scan_backward")
+    return g
 
 
 def stream_pad(seq: int) -> int:

@@ -229,6 +229,47 @@ ttcd_status ttcd_fastweight_scan_eq6(const ttcd_fw_desc* desc,
                                      void* stream);
 
 /* ------------------------------------------------------------------------
+ * Backward pass of ttcd_fastweight_scan (the training cost of the method is
+ * 1.1-1.2x a standard layer on the papernotes.org notes, 局限与展望; the
+ * gradient itself is the chain rule of the update above).  Given dy, the
+ * gradient of a loss with respect to y, it returns the gradients of that
+ * loss with respect to every input of the scan:
+ *   dS_i       = sum_{t in chunk i} dy_t z_main[t]^T
+ *   dz_main[t] = S_{floor(t/chunk)}^T dy_t
+ *   G_j        = sum_{i > j} dS_i          (chunk j's write reaches later chunks)
+ *   dbeta[j]   = sum_{t in chunk j} r_t . (G_j k_t)
+ *   dr_t = beta_j G_j k_t,  dk_t = beta_j G_j^T r_t
+ *   dW_down0   = sum_i dS_i + sum_t dr_t (W_proj dbar_t)^T
+ *   dW_proj    = sum_t (W_down0^T dr_t) dbar_t^T
+ * then the l2 backward of the keys and the backward of both short convs.
+ *
+ *   inputs as for ttcd_fastweight_scan (desc->out_dtype is the type of the
+ *            activation gradients); dy [batch, seq, d_model] in_dtype
+ *   dz_teacher, dz_student, dz_main [batch, seq, d_ff] out_dtype: the
+ *            gradients through the conv paths and through the apply (when
+ *            z_main aliases an input, its gradient is the sum of the two)
+ *   dconv_t, dconv_s [d_ff, conv_k], dw_down0 [d_model, d_ff],
+ *   dw_proj [d_ff, d_ff] fp32: summed over the batch, overwritten
+ *   dbeta [batch, ceil(seq/chunk)] fp32 (the last chunk's entry is 0: its
+ *            write reaches no token)
+ * Requirements and errors as for ttcd_fastweight_scan; every output is
+ * required.
+ * ---------------------------------------------------------------------- */
+size_t ttcd_fastweight_scan_backward_workspace_size(const ttcd_fw_desc* desc);
+
+ttcd_status ttcd_fastweight_scan_backward(const ttcd_fw_desc* desc,
+                                          const void* z_teacher, const void* z_student,
+                                          const void* z_main,
+                                          const void* conv_t, const void* conv_s,
+                                          const void* w_down0, const void* w_proj,
+                                          const float* beta, const void* dy,
+                                          void* dz_teacher, void* dz_student, void* dz_main,
+                                          float* dconv_t, float* dconv_s,
+                                          float* dw_down0, float* dw_proj, float* dbeta,
+                                          void* workspace, size_t workspace_bytes,
+                                          void* stream);
+
+/* ------------------------------------------------------------------------
  * The fast-weight stream alone: the first, memory-bound step of
  * ttcd_fastweight_scan (papernotes.org notes, key design 3: the short
  * causal convs of both paths, their difference and the per-token l2 norm of
