@@ -684,8 +684,16 @@ struct BwdBufs {
   int TC;
   void *w0t, *mt, *m_lo, *rtok, *dyt, *zmt, *g, *g_lo, *gt, *drt, *drtok, *khat, *dbart, *dmt_dt,
       *dm_dt;
-  float *m32, *rtu, *ds, *total, *pt, *dbpart, *dk, *ddbar, *dmt, *dm, *kd, *sbpart;
+  float *m32, *rtu, *ds, *total, *pt, *dbpart, *dk, *ddbar, *dmt, *dm, *kd, *sbpart, *kparts;
+  int ksplit;   // K slices of dM^T = sum over all tokens (its K is B * TC)
 };
+
+// slices for a product whose K (= cols) is long and whose output is small
+int ksplit_for(long cols) {
+  for (int S = 8; S > 1; S /= 2)
+    if (cols % (64L * S) == 0 && cols / S >= 2048) return S;
+  return 1;
+}
 
 void plan_bwd(int B, int T, int d, int f, int C, int kc, int dt, Plan& p, BwdBufs& w) {
   plan_fw(B, T, d, f, C, dt, p, w.fw);
@@ -719,6 +727,8 @@ void plan_bwd(int B, int T, int d, int f, int C, int kc, int dt, Plan& p, BwdBuf
   w.ddbar = (float*)p.take(BT * f * sizeof(float));
   w.dbart = p.take((size_t)f * cols * es);
   w.dmt = (float*)p.take((size_t)f * d * sizeof(float));
+  w.ksplit = ksplit_for((long)cols);
+  w.kparts = w.ksplit > 1 ? (float*)p.take((size_t)w.ksplit * f * d * sizeof(float)) : nullptr;
   w.dm = (float*)p.take((size_t)d * f * sizeof(float));
   w.dmt_dt = p.take((size_t)f * d * es);
   w.dm_dt = p.take((size_t)d * f * es);
@@ -876,7 +886,15 @@ hipError_t run_fw_backward(int B, int T, int d, int f, int C, int kc, float eps,
   g = GemmArgs{};
   g.A = w.dbart; g.lda = cols; g.B = w.drt; g.ldb = cols; g.C = w.dmt; g.ldc = d;
   g.M = f; g.N = d; g.K = (int)cols; g.in_dt = dt; g.out_dt = F32; g.epi = EPI_STORE; g.batch = 1;
+  if (w.ksplit > 1) {   // K slices as a batch, then their sum
+    const long ks = cols / w.ksplit;
+    g.C = w.kparts; g.K = (int)ks; g.batch = w.ksplit; g.sA = ks; g.sB = ks;
+    g.sC = (long)f * d;
+  }
   if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+  if (w.ksplit > 1 &&
+      (e = launch_sum_slices(w.kparts, w.dmt, (long)f * d, w.ksplit, s)) != hipSuccess)
+    return e;
   if ((e = launch_transpose(w.dmt, w.dm, f, d, d, f, 1, 0, 0, 4, s)) != hipSuccess) return e;
   if ((e = launch_convert(w.dmt, w.dmt_dt, (long)f * d, dt, s)) != hipSuccess) return e;
   if ((e = launch_convert(w.dm, w.dm_dt, (long)d * f, dt, s)) != hipSuccess) return e;

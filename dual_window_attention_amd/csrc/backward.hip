@@ -16,55 +16,6 @@ namespace ttcd {
 
 namespace {
 
-// out[f_i][b * TC + t] = in[b][t][f_i] for t < T, 0 for T <= t < TC:
-// token-major [B, rows, F] (rows >= T per sequence) -> feature-major
-// [F, B * TC], zero padded.
-template <typename T>
-__global__ void __launch_bounds__(256)
-to_feature_major_kernel(const T* __restrict__ in, T* __restrict__ out, int Tn, int rows, int TC,
-                        int F) {
-  __shared__ float tile[32][33];
-  const int b = blockIdx.z;
-  const int t0 = blockIdx.x * 32, f0 = blockIdx.y * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  for (int i = ty; i < 32; i += 8) {
-    const int t = t0 + i, fi = f0 + tx;
-    tile[i][tx] = (t < Tn && fi < F) ? ldf(in + ((size_t)b * rows + t) * F + fi) : 0.f;
-  }
-  __syncthreads();
-  const size_t ld = (size_t)gridDim.z * TC;
-  for (int i = ty; i < 32; i += 8) {
-    const int fi = f0 + i, t = t0 + tx;
-    if (fi < F && t < TC) stf(out + (size_t)fi * ld + (size_t)b * TC + t, tile[tx][i]);
-  }
-}
-
-// out[b][t][f_i] = in[f_i][b * TC + t] * (scale ? scale[b * n + t / chunk] : 1)
-// for t < T: feature-major -> token-major, optionally scaled per token.
-template <typename TI, typename TO>
-__global__ void __launch_bounds__(256)
-to_token_major_kernel(const TI* __restrict__ in, TO* __restrict__ out, int Tn, int TC, int F,
-                      const float* __restrict__ scale, int chunk, int n) {
-  __shared__ float tile[32][33];
-  const int b = blockIdx.z;
-  const int t0 = blockIdx.x * 32, f0 = blockIdx.y * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  const size_t ld = (size_t)gridDim.z * TC;
-  for (int i = ty; i < 32; i += 8) {
-    const int fi = f0 + i, t = t0 + tx;
-    tile[i][tx] = (fi < F && t < Tn) ? ldf(in + (size_t)fi * ld + (size_t)b * TC + t) : 0.f;
-  }
-  __syncthreads();
-  for (int i = ty; i < 32; i += 8) {
-    const int t = t0 + i, fi = f0 + tx;
-    if (t < Tn && fi < F) {
-      float v = tile[tx][i];
-      if (scale) v *= scale[(size_t)b * n + t / chunk];
-      stf(out + ((size_t)b * Tn + t) * F + fi, v);
-    }
-  }
-}
-
 // x[a][b * TC + t] *= s[b * Tpad + t] for t < T (0 beyond): the write scale
 // beta / |Zbar_S| folded into the residual columns.
 template <typename T>
@@ -114,6 +65,16 @@ chunk_suffix_kernel(const float* __restrict__ ds, T* __restrict__ g, T* __restri
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) total[e + i] = tot[i];
+}
+
+// out[i] = sum_z parts[z][i], z in a fixed order (the K slices of a product)
+__global__ void __launch_bounds__(256)
+sum_slices_kernel(const float* __restrict__ parts, float* __restrict__ out, long n, int S) {
+  const long i = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(parts + i);
+  for (int z = 1; z < S; ++z) acc += *reinterpret_cast<const f32x4*>(parts + (size_t)z * n + i);
+  *reinterpret_cast<f32x4*>(out + i) = acc;
 }
 
 // x -> hi = bf16(x), lo = bf16(x - hi)
@@ -188,18 +149,58 @@ key_dot_kernel(const T* __restrict__ khat, const float* __restrict__ dk,
   if (lane == 0) kd[row] = beta[(size_t)b * nch + t / chunk] * s;
 }
 
-// The per-token end of the backward, one 64-token x 64-feature tile per
-// workgroup, one feature and 16 tokens per thread:
+// The per-token end of the backward.  Each wave walks 64 consecutive tokens
+// (plus the kc-1 after them) for V consecutive features per lane, keeping
+// the last kc rows of z_T, z_S and of dzbar_T, dzbar_S in registers:
 //   zbar_S[tau] = conv_S(z_s) (recomputed), k = zbar_S * inv,
 //   dzbar_S = (beta dK - k kd) inv - ddbar   (|zbar_S| > eps)
 //           = beta dK inv - ddbar             (otherwise; inv = 1/eps)
 //   dzbar_T = ddbar
 //   dz_p[t] = sum_i taps_p[i] dzbar_p[t + kc-1-i],  dtaps_p[i] += dzbar_p[t] z_p[t-(kc-1)+i]
-// kd already holds beta (k . dK).  The tile's dtaps partial sums go to
-// part[b][tile][2][f][kc] (teacher, student).
-constexpr int SB_TOK = 16, SB_GRP = 4, SB_TT = SB_TOK * SB_GRP, SB_FF = 64;
+// kd already holds beta (k . dK).  A workgroup is four waves over 256
+// consecutive tokens; its dtaps partial sums go to part[b][tile][2][f][kc]
+// (teacher, student).
+constexpr int SB_L = 64, SB_W = 4, SB_TT = SB_L * SB_W;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-template <typename T, typename OutT, int KC>
+template <int V, typename T>
+TTCD_DEV void ldv(const T* p, float* o) {
+  if constexpr (sizeof(T) == 2) {
+    if constexpr (V == 4) {
+      const u32x2 u = *reinterpret_cast<const u32x2*>(p);
+      o[0] = __uint_as_float(u[0] << 16); o[1] = __uint_as_float(u[0] & 0xffff0000u);
+      o[2] = __uint_as_float(u[1] << 16); o[3] = __uint_as_float(u[1] & 0xffff0000u);
+    } else {
+      const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+      o[0] = __uint_as_float(u << 16); o[1] = __uint_as_float(u & 0xffff0000u);
+    }
+  } else {
+    if constexpr (V == 4) {
+      const f32x4 u = *reinterpret_cast<const f32x4*>(p);
+      o[0] = u[0]; o[1] = u[1]; o[2] = u[2]; o[3] = u[3];
+    } else {
+      const f32x2 u = *reinterpret_cast<const f32x2*>(p);
+      o[0] = u[0]; o[1] = u[1];
+    }
+  }
+}
+
+template <int V, typename T>
+TTCD_DEV void stv(T* p, const float* v) {
+  if constexpr (sizeof(T) == 2) {
+    if constexpr (V == 4)
+      *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    else
+      *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(v[0], v[1]);
+  } else {
+    if constexpr (V == 4)
+      *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+    else
+      *reinterpret_cast<f32x2*>(p) = f32x2{v[0], v[1]};
+  }
+}
+
+template <typename T, typename OutT, int KC, int V>
 __global__ void __launch_bounds__(256)
 stream_bwd_kernel(const T* __restrict__ zt, const T* __restrict__ zs,
                   const T* __restrict__ conv_t, const T* __restrict__ conv_s,
@@ -209,138 +210,174 @@ stream_bwd_kernel(const T* __restrict__ zt, const T* __restrict__ zs,
                   float* __restrict__ part, int Tn, int Tpad, int f, int chunk, int nch,
                   float inv_eps) {
   constexpr int H = KC - 1;
+  constexpr int NSTEP = SB_L + H;
   const int b = blockIdx.z;
   const int tile = blockIdx.x;
-  const int fl = threadIdx.x % SB_FF, grp = threadIdx.x / SB_FF;
-  const int c = blockIdx.y * SB_FF + fl;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = (blockIdx.y * 64 + lane) * V;
   const bool fok = c < f;
-  const int t0 = tile * SB_TT + grp * SB_TOK;          // this thread's first token
+  const int t0 = tile * SB_TT + wv * SB_L;             // this wave's first token
   const size_t rowb = (size_t)b * Tn;
-  float wt[KC], ws[KC];
+  float wt[KC][V], ws[KC][V];
 #pragma unroll
-  for (int i = 0; i < KC; ++i) {
-    wt[i] = fok ? ldf(conv_t + (size_t)c * KC + i) : 0.f;
-    ws[i] = fok ? ldf(conv_s + (size_t)c * KC + i) : 0.f;
-  }
-  // inputs of rows t0 - H .. t0 + SB_TOK + H - 1 (zero outside [0, T))
-  constexpr int NR = SB_TOK + 2 * H;
-  float xt[NR], xs[NR];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    const int tau = t0 - H + r;
-    const bool in = fok && tau >= 0 && tau < Tn;
-    xt[r] = in ? ldf(zt + (rowb + tau) * f + c) : 0.f;
-    xs[r] = in ? ldf(zs + (rowb + tau) * f + c) : 0.f;
-  }
-  // dzbar of rows t0 .. t0 + SB_TOK + H - 1 (rows >= T are zero)
-  constexpr int ND = SB_TOK + H;
-  float gt[ND], gs[ND];
-#pragma unroll
-  for (int r = 0; r < ND; ++r) {
-    const int tau = t0 + r;
-    float a = 0.f, s_ = 0.f;
-    if (fok && tau < Tn) {
-      float zb = 0.f;
-#pragma unroll
-      for (int i = 0; i < KC; ++i) zb = __builtin_fmaf(ws[i], xs[r + i], zb);
-      const size_t ti = rowb + tau;
-      const float iv = inv[(size_t)b * Tpad + tau];
-      const float bj = beta[(size_t)b * nch + tau / chunk];
-      const float g = dk[ti * f + c];
-      const float dd = ddbar[ti * f + c];
-      const float kv = zb * iv;
-      float dz;
-      if (iv < inv_eps)
-        dz = (bj * g - kv * kd[ti]) * iv;       // (dk - k (k . dk)) / |zbar|, dk = beta dK
-      else
-        dz = bj * g * iv;                        // dk / eps
-      s_ = dz - dd;
-      a = dd;
-    }
-    gt[r] = a;
-    gs[r] = s_;
-  }
-  float dtap_t[KC], dtap_s[KC];
-#pragma unroll
-  for (int i = 0; i < KC; ++i) dtap_t[i] = dtap_s[i] = 0.f;
-#pragma unroll
-  for (int r = 0; r < SB_TOK; ++r) {
-    const int t = t0 + r;
-    float at = 0.f, as = 0.f;
+  for (int e = 0; e < V; ++e)
 #pragma unroll
     for (int i = 0; i < KC; ++i) {
-      // zbar[t + H - i] takes z[t] through tap i
-      at = __builtin_fmaf(wt[i], gt[r + H - i], at);
-      as = __builtin_fmaf(ws[i], gs[r + H - i], as);
-      // dtaps[i] += dzbar[t] z[t - H + i]
-      dtap_t[i] = __builtin_fmaf(gt[r], xt[r + i], dtap_t[i]);
-      dtap_s[i] = __builtin_fmaf(gs[r], xs[r + i], dtap_s[i]);
+      wt[i][e] = fok ? ldf(conv_t + (size_t)(c + e) * KC + i) : 0.f;
+      ws[i][e] = fok ? ldf(conv_s + (size_t)(c + e) * KC + i) : 0.f;
     }
-    if (fok && t < Tn) {
-      stf(dzt + (rowb + t) * f + c, at);
-      stf(dzs + (rowb + t) * f + c, as);
-    }
-  }
-  // reduce the tap partials over the token groups of the tile
-  __shared__ float red[SB_GRP][SB_FF][2 * KC];
+  // rings: slot j holds row tau - H + j (slot H the newest)
+  float xt[KC][V], xs[KC][V], gt[KC][V], gs[KC][V];
+  float dtt[KC][V], dts[KC][V];
 #pragma unroll
-  for (int i = 0; i < KC; ++i) {
-    red[grp][fl][i] = dtap_t[i];
-    red[grp][fl][KC + i] = dtap_s[i];
-  }
-  __syncthreads();
-  if (grp == 0 && fok) {
-    const int ntile = gridDim.x;
-    for (int i = 0; i < 2 * KC; ++i) {
-      float s = 0.f;
-      for (int g2 = 0; g2 < SB_GRP; ++g2) s += red[g2][fl][i];
-      const int p = i / KC, tap = i % KC;
-      part[((((size_t)b * ntile + tile) * 2 + p) * f + c) * KC + tap] = s;
+  for (int j = 0; j < KC; ++j)
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      xt[j][e] = xs[j][e] = gt[j][e] = gs[j][e] = 0.f;
+      dtt[j][e] = dts[j][e] = 0.f;
     }
+#pragma unroll
+  for (int j = 1; j < KC; ++j) {     // rows t0 - H .. t0 - 1 into slots 0 .. H-1 (after a shift)
+    const int tau = t0 - KC + j;
+    if (fok && tau >= 0 && tau < Tn) {
+      ldv<V>(zt + (rowb + tau) * f + c, xt[j]);
+      ldv<V>(zs + (rowb + tau) * f + c, xs[j]);
+    }
+  }
+  for (int s0 = 0; s0 < NSTEP; s0 += KC) {
+#pragma unroll
+    for (int u = 0; u < KC; ++u) {
+      const int st = s0 + u;
+      const int tau = t0 + st;
+      const bool row = st < NSTEP && tau < Tn;
+#pragma unroll
+      for (int j = 0; j < H; ++j)
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          xt[j][e] = xt[j + 1][e];
+          xs[j][e] = xs[j + 1][e];
+          gt[j][e] = gt[j + 1][e];
+          gs[j][e] = gs[j + 1][e];
+        }
+      float nt[V], ns[V], gk[V], dd[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) nt[e] = ns[e] = gk[e] = dd[e] = 0.f;
+      float iv = 0.f, bj = 0.f, kdv = 0.f;
+      if (row) {
+        const size_t ti = rowb + tau;
+        if (fok) {
+          ldv<V>(zt + ti * f + c, nt);
+          ldv<V>(zs + ti * f + c, ns);
+          ldv<V>(dk + ti * f + c, gk);
+          ldv<V>(ddbar + ti * f + c, dd);
+        }
+        iv = inv[(size_t)b * Tpad + tau];
+        bj = beta[(size_t)b * nch + tau / chunk];
+        kdv = kd[ti];
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        xt[H][e] = nt[e];
+        xs[H][e] = ns[e];
+        float zb = 0.f;
+#pragma unroll
+        for (int i = 0; i < KC; ++i) zb = __builtin_fmaf(ws[i][e], xs[i][e], zb);
+        float dz;
+        if (iv < inv_eps)
+          dz = (bj * gk[e] - zb * iv * kdv) * iv;   // (dk - k (k . dk)) / |zbar|, dk = beta dK
+        else
+          dz = bj * gk[e] * iv;                      // dk / eps
+        gt[H][e] = row ? dd[e] : 0.f;
+        gs[H][e] = row ? dz - dd[e] : 0.f;
+      }
+      if (row && st < SB_L) {
+#pragma unroll
+        for (int i = 0; i < KC; ++i)
+#pragma unroll
+          for (int e = 0; e < V; ++e) {
+            dtt[i][e] = __builtin_fmaf(gt[H][e], xt[i][e], dtt[i][e]);
+            dts[i][e] = __builtin_fmaf(gs[H][e], xs[i][e], dts[i][e]);
+          }
+      }
+      const int t = tau - H;
+      if (st >= H && st < NSTEP && t < Tn && fok) {
+        float at[V], as[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          at[e] = as[e] = 0.f;
+#pragma unroll
+          for (int i = 0; i < KC; ++i) {
+            at[e] = __builtin_fmaf(wt[i][e], gt[H - i][e], at[e]);
+            as[e] = __builtin_fmaf(ws[i][e], gs[H - i][e], as[e]);
+          }
+        }
+        stv<V>(dzt + (rowb + t) * f + c, at);
+        stv<V>(dzs + (rowb + t) * f + c, as);
+      }
+    }
+  }
+  // the workgroup's tap partials: sum over its four waves, one path at a time
+  __shared__ float red[SB_W][64][KC * V];
+  const int ntile = gridDim.x;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+#pragma unroll
+    for (int i = 0; i < KC; ++i)
+#pragma unroll
+      for (int e = 0; e < V; ++e) red[wv][lane][e * KC + i] = p == 0 ? dtt[i][e] : dts[i][e];
+    __syncthreads();
+    if (wv == 0 && fok) {
+      float* dst = part + (((size_t)b * ntile + tile) * 2 + p) * f * KC + (size_t)c * KC;
+#pragma unroll
+      for (int q = 0; q < KC * V; ++q) {
+        float s_ = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < SB_W; ++w2) s_ += red[w2][lane][q];
+        dst[q] = s_;
+      }
+    }
+    __syncthreads();
   }
 }
 
-// dconv_p[c][i] = sum over sequences and tiles of the partials
+// dconv_p[c][i] = sum over sequences and tiles of the partials: 64 outputs
+// per workgroup, each wave summing every fourth partial row, then the four
+// sums in a fixed order
 __global__ void __launch_bounds__(256)
 dtaps_sum_kernel(const float* __restrict__ part, float* __restrict__ dconv_t,
-                 float* __restrict__ dconv_s, int f, int kc, int ntile, int B) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
+                 float* __restrict__ dconv_s, int f, int kc, int nrows) {
   const int n = 2 * f * kc;
-  if (i >= n) return;
-  const int p = i / (f * kc), e = i % (f * kc);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int i = blockIdx.x * 64 + lane;
   float s = 0.f;
-  for (int b = 0; b < B; ++b)
-    for (int tl = 0; tl < ntile; ++tl) s += part[(((size_t)b * ntile + tl) * 2 + p) * f * kc + e];
-  (p == 0 ? dconv_t : dconv_s)[e] = s;
+  if (i < n)
+    for (int r = wv; r < nrows; r += 4) s += part[(size_t)r * n + i];
+  __shared__ float red[4][64];
+  red[wv][lane] = s;
+  __syncthreads();
+  if (wv == 0 && i < n) {
+    const float tot = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+    const int p = i / (f * kc), e = i % (f * kc);
+    (p == 0 ? dconv_t : dconv_s)[e] = tot;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_to_feature_major(const void* in, void* out, int B, int T, int rows, int TC,
                                    int F, int dt, hipStream_t s) {
-  dim3 grid((TC + 31) / 32, (F + 31) / 32, B);
-  if (dt == BF16)
-    hipLaunchKernelGGL(to_feature_major_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)in,
-                       (bf16_t*)out, T, rows, TC, F);
-  else
-    hipLaunchKernelGGL(to_feature_major_kernel<float>, grid, dim3(256), 0, s, (const float*)in,
-                       (float*)out, T, rows, TC, F);
-  return hipGetLastError();
+  // out[f][b * TC + t] = in[b][t][f] (t < T), zero for T <= t < TC
+  return launch_transpose64(in, dt, F, (long)rows * F, T, F, out, dt, (long)B * TC, TC, TC, B,
+                            nullptr, 0, 1, s);
 }
 
 hipError_t launch_to_token_major(const void* in, int in_dt, void* out, int out_dt, int B, int T,
                                  int TC, int F, const float* scale, int chunk, int n,
                                  hipStream_t s) {
-  dim3 grid((T + 31) / 32, (F + 31) / 32, B);
-#define TTCD_TTM(TI, TO)                                                                         \
-  hipLaunchKernelGGL((to_token_major_kernel<TI, TO>), grid, dim3(256), 0, s, (const TI*)in,    \
-                     (TO*)out, T, TC, F, scale, chunk, n)
-  if (in_dt == BF16 && out_dt == BF16) TTCD_TTM(bf16_t, bf16_t);
-  else if (in_dt == BF16) TTCD_TTM(bf16_t, float);
-  else if (out_dt == BF16) TTCD_TTM(float, bf16_t);
-  else TTCD_TTM(float, float);
-#undef TTCD_TTM
-  return hipGetLastError();
+  // out[b][t][f] = in[f][b * TC + t] * (scale ? scale[b * n + t / chunk] : 1)
+  return launch_transpose64(in, in_dt, (long)B * TC, TC, F, T, out, out_dt, F, (long)T * F, F, B,
+                            scale, n, scale ? chunk : 1, s);
 }
 
 hipError_t launch_scale_token_cols(void* x, const float* sc, int rows, int B, int T, int TC,
@@ -366,6 +403,13 @@ hipError_t launch_chunk_suffix(const float* ds, void* g, void* g_lo, float* tota
   else
     hipLaunchKernelGGL(chunk_suffix_kernel<float>, grid, dim3(256), 0, s, ds, (float*)g,
                        (float*)nullptr, total, n, nch, B);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_slices(const float* parts, float* out, long n, int S, hipStream_t s) {
+  if (n % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sum_slices_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s,
+                     parts, out, n, S);
   return hipGetLastError();
 }
 
@@ -410,22 +454,25 @@ size_t stream_bwd_part_floats(int B, int T, int f, int kc) {
 }
 
 hipError_t launch_stream_bwd(const StreamBwdArgs& a, hipStream_t s) {
+  if (a.f % 8) return hipErrorInvalidValue;
   const int ntile = (a.T + SB_TT - 1) / SB_TT;
-  dim3 grid(ntile, (a.f + SB_FF - 1) / SB_FF, a.B);
   const int Tpad = (a.T + 63) / 64 * 64;
   const float inv_eps = 1.f / a.eps;
-#define TTCD_SBW(T_, O_, K)                                                                      \
-  hipLaunchKernelGGL((stream_bwd_kernel<T_, O_, K>), grid, dim3(256), 0, s, (const T_*)a.zt,     \
+#define TTCD_SBW(T_, O_, K, V)                                                                   \
+  hipLaunchKernelGGL((stream_bwd_kernel<T_, O_, K, V>),                                          \
+                     dim3(ntile, (a.f / V + 63) / 64, a.B), dim3(256), 0, s, (const T_*)a.zt,    \
                      (const T_*)a.zs, (const T_*)a.conv_t, (const T_*)a.conv_s, a.dk, a.ddbar,    \
                      a.kd, a.inv, a.beta, (O_*)a.dzt, (O_*)a.dzs, a.part, a.T, Tpad, a.f,          \
                      a.chunk, a.nch, inv_eps)
 #define TTCD_SBW_KC(K)                                                                           \
-  case K:                                                                                        \
-    if (a.in_dt == BF16 && a.out_dt == BF16) TTCD_SBW(bf16_t, bf16_t, K);                        \
-    else if (a.in_dt == BF16) TTCD_SBW(bf16_t, float, K);                                        \
-    else if (a.out_dt == BF16) TTCD_SBW(float, bf16_t, K);                                       \
-    else TTCD_SBW(float, float, K);                                                              \
-    break;
+  case K: {                                                                                      \
+    constexpr int V = K <= 4 ? 4 : 2;                                                            \
+    if (a.in_dt == BF16 && a.out_dt == BF16) TTCD_SBW(bf16_t, bf16_t, K, V);                     \
+    else if (a.in_dt == BF16) TTCD_SBW(bf16_t, float, K, V);                                     \
+    else if (a.out_dt == BF16) TTCD_SBW(float, bf16_t, K, V);                                    \
+    else TTCD_SBW(float, float, K, V);                                                           \
+    break;                                                                                       \
+  }
   switch (a.kc) {
     TTCD_SBW_KC(1) TTCD_SBW_KC(2) TTCD_SBW_KC(3) TTCD_SBW_KC(4)
     TTCD_SBW_KC(5) TTCD_SBW_KC(6) TTCD_SBW_KC(7) TTCD_SBW_KC(8)
@@ -436,8 +483,8 @@ hipError_t launch_stream_bwd(const StreamBwdArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n = 2 * a.f * a.kc;
-  hipLaunchKernelGGL(dtaps_sum_kernel, dim3((n + 255) / 256), dim3(256), 0, s, a.part, a.dconv_t,
-                     a.dconv_s, a.f, a.kc, ntile, a.B);
+  hipLaunchKernelGGL(dtaps_sum_kernel, dim3((n + 63) / 64), dim3(256), 0, s, a.part, a.dconv_t,
+                     a.dconv_s, a.f, a.kc, a.B * ntile);
   return hipGetLastError();
 }
 

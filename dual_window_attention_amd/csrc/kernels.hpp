@@ -146,6 +146,13 @@ hipError_t launch_state_step(const float* dw, int nsplit, float* s32, void* s16,
 size_t fw_stream_part_bytes(int B, int T, int f);
 
 // out [cols, rows] = in [rows, cols]^T (per batch), 2- or 4-byte elements
+// out[z][c][r] = in[z][r][c] * (scale ? scale[z * s_scale + c / scale_div] : 1)
+// for r < in_rows, c < in_cols (dtypes in_dt -> out_dt); output columns
+// in_rows <= r < out_cols are written as zero
+hipError_t launch_transpose64(const void* in, int in_dt, long ld_in, long s_in, int in_rows,
+                              int in_cols, void* out, int out_dt, long ld_out, long s_out,
+                              int out_cols, int batch, const float* scale, long s_scale,
+                              int scale_div, hipStream_t s);
 hipError_t launch_transpose(const void* in, void* out, int rows, int cols, long ld_in,
                             long ld_out, int batch, long s_in, long s_out, int esize,
                             hipStream_t s);
@@ -175,6 +182,8 @@ hipError_t launch_scale_token_cols(void* x, const float* sc, int rows, int B, in
 // total [n] fp32 = sum over sequences and chunks of ds
 hipError_t launch_chunk_suffix(const float* ds, void* g, void* g_lo, float* total, long n,
                                int nch, int B, int dt, hipStream_t s);
+// out [n] = sum over z < S of parts [S, n] (n % 4 == 0)
+hipError_t launch_sum_slices(const float* parts, float* out, long n, int S, hipStream_t s);
 // x fp32 [n] -> hi = bf16(x), lo = bf16(x - hi)
 hipError_t launch_split_bf16(const float* x, void* hi, void* lo, long n, hipStream_t s);
 // dbeta [B, nch] = per-chunk <R^T, P^T>; P^T *= beta (in place); rt, pt fp32 [d, B * TC]

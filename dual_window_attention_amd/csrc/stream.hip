@@ -244,31 +244,6 @@ fw_key_scale_kernel(const float* __restrict__ part, const float* __restrict__ be
   if (inv) inv[(size_t)b * Tpad + t] = iv;
 }
 
-// The unit keys token-major, for the low-rank chunk lists:
-//   k_out[b, t, c] = zbt[b, c, t] * inv[b, t]   (t < T)
-// 32 x 32 tiles through LDS (the feature-major rows are read along t and
-// the token-major rows written along c).
-template <typename T>
-__global__ void __launch_bounds__(256)
-unit_keys_kernel(const T* __restrict__ zbt, const float* __restrict__ inv, T* __restrict__ k_out,
-                 int T_, int Tpad, int f) {
-  __shared__ float tile[32][33];
-  const int b = blockIdx.z;
-  const int t0 = blockIdx.x * 32, c0 = blockIdx.y * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  const T* zp = zbt + (size_t)b * f * Tpad;
-  for (int i = ty; i < 32; i += 8) {
-    const int c = c0 + i, t = t0 + tx;
-    tile[i][tx] = (c < f && t < T_) ? ldf(zp + (size_t)c * Tpad + t) : 0.f;
-  }
-  __syncthreads();
-  for (int i = ty; i < 32; i += 8) {
-    const int t = t0 + i, c = c0 + tx;
-    if (t < T_ && c < f)
-      stf(k_out + ((size_t)b * T_ + t) * f + c, tile[tx][i] * inv[(size_t)b * Tpad + t]);
-  }
-}
-
 // ------------------------------------------------------- decode-time append
 // One generated token per sequence (the fast-weight stream for one row):
 // the short causal convs of both paths over the last kc-1 inputs (the
@@ -463,24 +438,74 @@ rmsnorm_kernel(const float* __restrict__ h, const GT* __restrict__ gamma, OutT* 
 }
 
 // --------------------------------------------------------------- transposes
-template <typename E>
+// out[z][c][r] = in[z][r][c] * (scale ? scale[z * s_scale + c / scale_div] : 1)
+// for r < in_rows, c < in_cols; output columns in_rows <= r < out_cols are
+// written as zero.  One 64 x 64 tile per workgroup through LDS (fp32, padded
+// rows), eight consecutive elements per thread and access (16 bytes for bf16)
+// wherever the row is whole and aligned.
+template <typename TI, typename TO>
 __global__ void __launch_bounds__(256)
-transpose_kernel(const E* __restrict__ in, E* __restrict__ out, int rows, int cols, long ld_in,
-                 long ld_out, long s_in, long s_out) {
-  __shared__ E tile[32][33];
+transpose64_kernel(const TI* __restrict__ in, long ld_in, long s_in, int in_rows, int in_cols,
+                   TO* __restrict__ out, long ld_out, long s_out, int out_cols,
+                   const float* __restrict__ scale, long s_scale, int scale_div) {
+  __shared__ float tile[64][65];
   const int z = blockIdx.z;
-  const long r0 = (long)blockIdx.x * 32, c0 = (long)blockIdx.y * 32;
-  const E* ip = in + z * s_in;
-  E* op = out + z * s_out;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  for (int i = ty; i < 32; i += 8) {
-    const long r = r0 + i, c = c0 + tx;
-    tile[i][tx] = (r < rows && c < cols) ? ip[r * ld_in + c] : E(0);
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const TI* ip = in + z * s_in;
+  TO* op = out + z * s_out;
+  const int tr = threadIdx.x >> 3, tc = (threadIdx.x & 7) * 8;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int lr = h * 32 + tr, r = r0 + lr, c = c0 + tc;
+    float v[8];
+    const TI* src = ip + (long)r * ld_in + c;
+    if (r < in_rows && c + 8 <= in_cols && ((size_t)src % 16) == 0) {
+      if constexpr (sizeof(TI) == 2) {
+        const u32x4 u = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[2 * j] = __uint_as_float(u[j] << 16);
+          v[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
+        }
+      } else {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[j] = a[j];
+          v[4 + j] = b[j];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = (r < in_rows && c + j < in_cols) ? ldf(src + j) : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tile[lr][tc + j] = v[j];
   }
   __syncthreads();
-  for (int i = ty; i < 32; i += 8) {
-    const long c = c0 + i, r = r0 + tx;
-    if (c < cols && r < rows) op[c * ld_out + r] = tile[tx][i];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int lc = h * 32 + tr, c = c0 + lc, r = r0 + tc;
+    if (c >= in_cols) continue;
+    const float sc = scale ? scale[z * s_scale + c / scale_div] : 1.f;
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = tile[tc + j][lc] * sc;
+    TO* dst = op + (long)c * ld_out + r;
+    if (r + 8 <= out_cols && ((size_t)dst % 16) == 0) {
+      if constexpr (sizeof(TO) == 2) {
+        *reinterpret_cast<u32x4*>(dst) = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                               pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+      } else {
+        *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (r + j < out_cols) stf(dst + j, v[j]);
+    }
   }
 }
 
@@ -570,15 +595,10 @@ hipError_t launch_fw_stream(const StreamArgs& a, hipStream_t s) {
 
 hipError_t launch_unit_keys(const void* zbt, const float* inv, void* k_out, int B, int T, int f,
                             int dt, hipStream_t s) {
-  const int Tpad = (T + 63) / 64 * 64;
-  dim3 grid((T + 31) / 32, (f + 31) / 32, B);
-  if (dt == BF16)
-    hipLaunchKernelGGL(unit_keys_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)zbt, inv,
-                       (bf16_t*)k_out, T, Tpad, f);
-  else
-    hipLaunchKernelGGL(unit_keys_kernel<float>, grid, dim3(256), 0, s, (const float*)zbt, inv,
-                       (float*)k_out, T, Tpad, f);
-  return hipGetLastError();
+  // k[b][t][c] = zbar_S^T[b][c][t] * inv[b][t]
+  const long Tpad = (T + 63) / 64 * 64;
+  return launch_transpose64(zbt, dt, Tpad, (long)f * Tpad, f, T, k_out, dt, f, (long)T * f, f, B,
+                            inv, Tpad, 1, s);
 }
 
 hipError_t launch_fw_decode_append(const DecodeAppendArgs& a, hipStream_t s) {
@@ -703,17 +723,32 @@ hipError_t launch_rmsnorm(const float* h, const void* gamma, void* u, int rows, 
   return hipGetLastError();
 }
 
+hipError_t launch_transpose64(const void* in, int in_dt, long ld_in, long s_in, int in_rows,
+                              int in_cols, void* out, int out_dt, long ld_out, long s_out,
+                              int out_cols, int batch, const float* scale, long s_scale,
+                              int scale_div, hipStream_t s) {
+  if (in_rows <= 0 || in_cols <= 0 || batch <= 0) return hipSuccess;
+  if (out_cols < in_rows || scale_div < 1) return hipErrorInvalidValue;
+  dim3 grid((out_cols + 63) / 64, (in_cols + 63) / 64, batch);
+#define TTCD_T64(TI, TO)                                                                         \
+  hipLaunchKernelGGL((transpose64_kernel<TI, TO>), grid, dim3(256), 0, s, (const TI*)in, ld_in,  \
+                     s_in, in_rows, in_cols, (TO*)out, ld_out, s_out, out_cols, scale, s_scale,   \
+                     scale_div)
+  if (in_dt == BF16 && out_dt == BF16) TTCD_T64(bf16_t, bf16_t);
+  else if (in_dt == BF16) TTCD_T64(bf16_t, float);
+  else if (out_dt == BF16) TTCD_T64(float, bf16_t);
+  else TTCD_T64(float, float);
+#undef TTCD_T64
+  return hipGetLastError();
+}
+
 hipError_t launch_transpose(const void* in, void* out, int rows, int cols, long ld_in,
                             long ld_out, int batch, long s_in, long s_out, int esize,
                             hipStream_t s) {
-  dim3 grid((rows + 31) / 32, (cols + 31) / 32, batch > 0 ? batch : 1);
-  if (esize == 2)
-    hipLaunchKernelGGL(transpose_kernel<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)in,
-                       (uint16_t*)out, rows, cols, ld_in, ld_out, s_in, s_out);
-  else
-    hipLaunchKernelGGL(transpose_kernel<uint32_t>, grid, dim3(256), 0, s, (const uint32_t*)in,
-                       (uint32_t*)out, rows, cols, ld_in, ld_out, s_in, s_out);
-  return hipGetLastError();
+  // 2-byte elements move as bf16, 4-byte ones as fp32: both exact through fp32
+  const int dt = esize == 2 ? BF16 : F32;
+  return launch_transpose64(in, dt, ld_in, s_in, rows, cols, out, dt, ld_out, s_out, rows,
+                            batch > 0 ? batch : 1, nullptr, 0, 1, s);
 }
 
 hipError_t launch_transpose_scale(const void* in, void* out, int rows, int cols, int batch,
