@@ -212,6 +212,41 @@ def backward_bench(cfg, dev, n):
             "workspace_gb": ws_gb, "finite": finite, "tokens": cfg.batch * cfg.seq}
 
 
+def attn_backward_bench(cfg, dev, n):
+    """The dual-window attention's gradient (ttcd_dual_window_attn_backward)
+    at the workload's size.  Algorithmic flops: five products over the
+    teacher window's (query, key) pairs (S recomputed, dP, dV, dQ, dK:
+    2.5 x the forward's) plus two over the student window's (its dP and dV)."""
+    import torch
+    from dual_window_attention_amd import inputs as I
+    from dual_window_attention_amd import ttcd
+
+    att = I.attention_inputs(cfg)
+    q, k, v = (I.to_torch(att[n], dev) for n in ("q", "k", "v"))
+    del att
+    wT, wS = cfg.w_teacher, cfg.w_student
+    o_t, o_s, l_t, l_s = ttcd.dual_window_attn(q, k, v, wT, wS, out_dtype=torch.bfloat16)
+    gen = torch.Generator().manual_seed(6)
+    do_t = torch.randn(q.shape, generator=gen).to(dev, torch.bfloat16)
+    do_s = torch.randn(q.shape, generator=gen).to(dev, torch.bfloat16)
+    lib = ttcd.lib()
+    ws = torch.empty(lib.ttcd_dual_window_attn_backward_workspace_size(
+        ttcd.attn_desc(q, k, wT, wS)), dtype=torch.uint8, device=dev)
+    g = ttcd.dual_window_attn_backward(q, k, v, o_t, o_s, l_t, l_s, do_t, do_s, wT, wS,
+                                       workspace=ws)
+    st = torch.cuda.current_stream()
+    ms = time_events(lambda: ttcd.dual_window_attn_backward(
+        q, k, v, o_t, o_s, l_t, l_s, do_t, do_s, wT, wS, out=g, workspace=ws), n, st, 2)
+    flops = 2.5 * attention_flops(cfg, wT) + attention_flops(cfg, wS)
+    finite = all(torch.isfinite(t).all().item() for t in g)
+    del q, k, v, o_t, o_s, l_t, l_s, do_t, do_s, ws, g
+    achieved = flops / (ms * 1e-3) / 1e12
+    return {"kernel": "dual-window attention backward (ttcd_dual_window_attn_backward): dq, dk, "
+                      "dv in bf16",
+            "ms_per_call": ms, "algorithmic_tflop": flops / 1e12, "achieved": achieved,
+            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "finite": finite}
+
+
 def decode_bench(dev, n):
     """One decode token per sequence at the batch-32, 64K-cache workload:
     low-rank lists and folded dense state; the fold itself timed once."""
@@ -600,6 +635,8 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_backward:
         res["backward"] = backward_bench(cfg, dev, 5)
+        torch.cuda.empty_cache()
+        res["attention_backward"] = attn_backward_bench(cfg, dev, 3)
         torch.cuda.empty_cache()
     if not args.no_decode:
         res["decode"] = decode_bench(dev, n_att)

@@ -372,6 +372,63 @@ ttcd_status ttcd_dual_window_attn(const ttcd_attn_desc* d, const void* q, const 
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// ---- attention backward (prefill)
+ttcd_status check_attn_bwd(const ttcd_attn_desc* d) {
+  ttcd_status st = check_attn(d);
+  if (st != TTCD_OK) return st;
+  if (d->seq_q != d->seq_k || d->q_pos0 != 0 || (d->kv_rows && d->kv_rows != d->seq_k))
+    return fail(TTCD_ERR_UNSUPPORTED,
+                "the backward covers prefill: seq_q == seq_k == kv_rows, q_pos0 == 0");
+  return TTCD_OK;
+}
+
+AttnBwdArgs attn_bwd_args(const ttcd_attn_desc* d) {
+  AttnBwdArgs a{};
+  a.B = d->batch; a.T = d->seq_q; a.Hq = d->n_q_heads; a.Hkv = d->n_kv_heads;
+  a.D = d->head_dim; a.wT = d->w_teacher; a.wS = d->w_student; a.scale = attn_scale(d);
+  a.in_dt = d->in_dtype; a.out_dt = d->out_dtype;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ttcd_dual_window_attn_backward_workspace_size(const ttcd_attn_desc* d) {
+  if (check_attn_bwd(d) != TTCD_OK) return 0;
+  return attn_bwd_workspace_bytes(d->batch, d->seq_q, d->n_q_heads, d->n_kv_heads, d->head_dim,
+                                  d->in_dtype);
+}
+
+ttcd_status ttcd_dual_window_attn_backward(const ttcd_attn_desc* d, const void* q, const void* k,
+                                           const void* v, const void* o_t, const void* o_s,
+                                           const float* lse_t, const float* lse_s,
+                                           const void* do_t, const void* do_s, void* dq, void* dk,
+                                           void* dv, void* ws, size_t ws_bytes, void* stream) {
+  ttcd_status st = check_attn_bwd(d);
+  if (st != TTCD_OK) return st;
+  REQ_PTR(q); REQ_PTR(k); REQ_PTR(v); REQ_PTR(o_t); REQ_PTR(o_s); REQ_PTR(do_t); REQ_PTR(do_s);
+  REQ_PTR(dq); REQ_PTR(dk); REQ_PTR(dv);
+  if (!lse_t || !lse_s) return fail(TTCD_ERR_NULL_POINTER, "lse_teacher and lse_student are required");
+  OPT_PTR4(lse_t); OPT_PTR4(lse_s);
+  const size_t need = ttcd_dual_window_attn_backward_workspace_size(d);
+  if (ws_bytes < need)
+    return fail(TTCD_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (!ws) return fail(TTCD_ERR_NULL_POINTER, "workspace is NULL");
+  OPT_PTR(ws);
+  AttnBwdArgs a = attn_bwd_args(d);
+  a.q = q; a.k = k; a.v = v; a.o_t = o_t; a.o_s = o_s; a.lse_t = lse_t; a.lse_s = lse_s;
+  a.do_t = do_t; a.do_s = do_s; a.dq = dq; a.dk = dk; a.dv = dv;
+  AttnBwdBufs w;
+  attn_bwd_plan(a, (char*)ws, w);
+  HIPCHK(launch_dual_window_attn_backward(a, w, (hipStream_t)stream));
+  return ok();
+}
+
 // ---- LSE-combination path
 struct SplitBufs {
   void* vt = nullptr;

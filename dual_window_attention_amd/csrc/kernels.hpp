@@ -164,6 +164,29 @@ hipError_t launch_transpose_scale(const void* in, void* out, int rows, int cols,
 // V [B, kv_rows, Hkv, D] (bf16) -> vt [B, Hkv, D, vt_ld]: keys in [jlo, Tk), the
 // keys of each 16-group permuted for the attention kernel's MFMA operand reads
 
+// ------------------------------------------------------- attention backward
+struct AttnBwdArgs {
+  const void *q, *k, *v;            // [B,T,Hq,D], [B,T,Hkv,D] x2, in_dt
+  const void *o_t, *o_s;            // [B,T,Hq,D] in_dt (the forward's outputs)
+  const float *lse_t, *lse_s;       // [B,Hq,T] natural log
+  const void *do_t, *do_s;          // [B,T,Hq,D] in_dt
+  void *dq, *dk, *dv;               // out_dt
+  int B, T, Hq, Hkv, D, wT, wS;
+  float scale;
+  int in_dt, out_dt;
+};
+struct AttnBwdBufs {
+  float* meta;                      // per query row: LSE_T, LSE_S (log2), D_T, D_S
+  void *qT, *dotT, *dosT, *kT;      // transposed copies (bf16 MFMA path)
+};
+// 32-row blocks of the row data per (batch, kv group), one of them padding
+int attn_bwd_meta_blocks(int T, int G);
+long attn_bwd_key_ld(int T);
+size_t attn_bwd_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int in_dt);
+void attn_bwd_plan(const AttnBwdArgs& a, char* ws, AttnBwdBufs& w);
+hipError_t launch_dual_window_attn_backward(const AttnBwdArgs& a, const AttnBwdBufs& w,
+                                            hipStream_t s);
+
 // ---------------------------------------------------------------- backward
 // token-major [B, rows, F] (the first T rows of each sequence) ->
 // feature-major [F, B * TC], zero for T <= t < TC

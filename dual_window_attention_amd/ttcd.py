@@ -34,6 +34,7 @@ STATUS = {
 EXPORTS = (
     "ttcd_dual_window_attn_workspace_size", "ttcd_dual_window_attn",
     "ttcd_dual_window_attn_lse_split_workspace_size", "ttcd_dual_window_attn_lse_split",
+    "ttcd_dual_window_attn_backward_workspace_size", "ttcd_dual_window_attn_backward",
     "ttcd_fastweight_scan_workspace_size", "ttcd_fastweight_scan",
     "ttcd_fastweight_scan_on_policy_workspace_size", "ttcd_fastweight_scan_on_policy",
     "ttcd_fastweight_scan_eq6_workspace_size", "ttcd_fastweight_scan_eq6",
@@ -94,6 +95,8 @@ _sig = {
     "ttcd_dual_window_attn_lse_split_workspace_size": (_sz, [C.POINTER(AttnDesc)]),
     "ttcd_dual_window_attn_lse_split": (C.c_int, [C.POINTER(AttnDesc), _vp, _vp, _vp, _vp, _vp,
                                                   _vp, _vp, _vp, _sz, _vp]),
+    "ttcd_dual_window_attn_backward_workspace_size": (_sz, [C.POINTER(AttnDesc)]),
+    "ttcd_dual_window_attn_backward": (C.c_int, [C.POINTER(AttnDesc)] + [_vp] * 13 + [_sz, _vp]),
     "ttcd_fastweight_scan_workspace_size": (_sz, [C.POINTER(FwDesc)]),
     "ttcd_fastweight_scan": (C.c_int, [C.POINTER(FwDesc), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -240,6 +243,29 @@ def dual_window_attn(q, k, v, w_teacher: int, w_student: int, *, scale=None, q_p
                                       _ptr(lse_t), _ptr(lse_s), _ptr(ws), ws.numel(),
                                       _stream(stream)), "ttcd_dual_window_attn")
     return o_t, o_s, lse_t, lse_s
+
+
+def dual_window_attn_backward(q, k, v, o_teacher, o_student, lse_teacher, lse_student,
+                              do_teacher, do_student, w_teacher: int, w_student: int, *,
+                              scale=None, out_dtype=None, out=None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of the teacher and student outputs given
+    dO_T and dO_S (prefill: the forward's q, k, v, outputs and LSEs)."""
+    d = attn_desc(q, k, w_teacher, w_student, scale, 0, None, out_dtype)
+    odt = _tdt(d.out_dtype)
+    if out is None:
+        dq = torch.empty(q.shape, dtype=odt, device=q.device)
+        dk = torch.empty(k.shape, dtype=odt, device=q.device)
+        dv = torch.empty(v.shape, dtype=odt, device=q.device)
+    else:
+        dq, dk, dv = out
+    need = _lib.ttcd_dual_window_attn_backward_workspace_size(C.byref(d))
+    ws = _workspace(need, q.device, workspace)
+    _check(_lib.ttcd_dual_window_attn_backward(
+        C.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o_teacher), _ptr(o_student),
+        _ptr(lse_teacher), _ptr(lse_student), _ptr(do_teacher), _ptr(do_student), _ptr(dq),
+        _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream(stream)),
+        "ttcd_dual_window_attn_backward")
+    return dq, dk, dv
 
 
 def dual_window_attn_lse_split(q, k, v, w_teacher: int, w_student: int, *, scale=None,

@@ -125,6 +125,38 @@ ttcd_status ttcd_dual_window_attn_lse_split(const ttcd_attn_desc* desc,
                                             void* stream);
 
 /* ------------------------------------------------------------------------
+ * Backward of the dual-window attention (training; the papernotes.org notes
+ * price it in their limitations section).  Both windows read the same q, k
+ * and v, so their gradients add: with P_w = exp(s - LSE_w) on the keys of
+ * window w, D_w = rowsum(dO_w * O_w) and dS = sum_w P_w (dO_w v^T - D_w),
+ *   dq = scale dS k,   dk = scale dS^T q,   dv = sum_w P_w^T dO_w
+ * (a kv head's gradients sum over its q heads).
+ *
+ * Prefill only: seq_q == seq_k == kv_rows (or kv_rows 0), q_pos0 == 0.
+ *   q, k, v, o_teacher, o_student, do_teacher, do_student: layouts of
+ *            ttcd_dual_window_attn, all in in_dtype (o_* are that call's
+ *            outputs, produced with out_dtype == in_dtype)
+ *   lse_teacher, lse_student [batch, n_q_heads, seq_q] fp32 (required)
+ *   dq [batch, seq, n_q_heads, head_dim], dk, dv [batch, seq, n_kv_heads,
+ *            head_dim]: out_dtype, written in full.
+ * Deterministic: no atomics; the key and query sides each recompute the
+ * scores.  The workspace (size from
+ * ttcd_dual_window_attn_backward_workspace_size) holds the per-row LSE and
+ * D values and, for bf16, transposed copies of q, dO_T, dO_S and k.
+ * Outputs must not alias inputs.
+ * ---------------------------------------------------------------------- */
+size_t ttcd_dual_window_attn_backward_workspace_size(const ttcd_attn_desc* desc);
+
+ttcd_status ttcd_dual_window_attn_backward(const ttcd_attn_desc* desc,
+                                           const void* q, const void* k, const void* v,
+                                           const void* o_teacher, const void* o_student,
+                                           const float* lse_teacher, const float* lse_student,
+                                           const void* do_teacher, const void* do_student,
+                                           void* dq, void* dk, void* dv,
+                                           void* workspace, size_t workspace_bytes,
+                                           void* stream);
+
+/* ------------------------------------------------------------------------
  * Chunk-wise fast-weight update of W_down (IP-TTCD, off-policy).
  *
  * From the papernotes.org notes, key design 3 (the practical update, the

@@ -191,3 +191,26 @@ def test_noalloc_layer_entry_rejects_calls_beyond_its_scratch():
     assert b"no-allocation" in lib.ttcd_last_error()
     assert lib.ttcd_layer_forward_noalloc(C.byref(ld), C.byref(w), None, fake, fake, fake, fake,
                                           None, None, None) == 1
+
+
+def header_param_counts():
+    """Number of parameters of every function the header declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(ttcd_\w+)\s*\(([^;{]*?)\)\s*;", text, flags=re.S):
+        params = m.group(2).strip()
+        out[m.group(1)] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_binding_argument_counts_match_the_header():
+    """Every ctypes signature in the binding passes exactly the header's
+    parameters (an argument too few shifts the stream handle into a
+    variadic slot, where ctypes passes it as a 32-bit int)."""
+    from dual_window_attention_amd import ttcd
+    counts = header_param_counts()
+    assert set(counts) == set(ttcd.EXPORTS)
+    for name in ttcd.EXPORTS:
+        fn = getattr(ttcd.lib(), name)
+        assert len(fn.argtypes) == counts[name], (name, len(fn.argtypes), counts[name])
