@@ -270,6 +270,8 @@ ttcd_status check_layer(const ttcd_layer_desc* d, const ttcd_fw_state* dec) {
   if (d->conv_k < 1 || d->conv_k > 8) return fail(TTCD_ERR_BAD_SHAPE, "conv_k must be in [1, 8]");
   if (d->main_path != TTCD_MAIN_TEACHER && d->main_path != TTCD_MAIN_STUDENT)
     return fail(TTCD_ERR_BAD_SHAPE, "unknown main_path");
+  if ((long)d->attn.batch * d->attn.seq_q > (1L << 28))
+    return fail(TTCD_ERR_BAD_SHAPE, "batch * seq_q too large");
   if (dec) {
     if (d->attn.seq_q != 1) return fail(TTCD_ERR_BAD_SHAPE, "decode needs seq_q == 1");
     if (d->attn.q_pos0 != d->attn.seq_k - 1)
@@ -299,13 +301,18 @@ void plan_layer(const ttcd_layer_desc* d, const ttcd_fw_state* dec, Plan& p, Lay
   const long BT = (long)a.batch * a.seq_q;
   const long HD = (long)a.n_q_heads * a.head_dim;
   plan_attn(&a, p, b.at);
+  // both paths' O, h, u and Z each in one block, path 1 right after path 0,
+  // so that the per-path products can run as one launch over 2 BT rows
+  char* o = (char*)p.take(2 * BT * HD * es);
+  float* h = (float*)p.take(2 * BT * d->d_model * sizeof(float));
+  char* z = (char*)p.take(2 * BT * d->d_ff * es);
   for (int i = 0; i < 2; ++i) {
-    b.o[i] = p.take(BT * HD * es);
+    b.o[i] = o + i * BT * HD * es;
+    b.h[i] = h + i * BT * d->d_model;
+    b.z[i] = z + i * BT * d->d_ff * es;
     b.lse[i] = (float*)p.take((size_t)a.batch * a.n_q_heads * a.seq_q * sizeof(float));
-    b.h[i] = (float*)p.take(BT * d->d_model * sizeof(float));
-    b.z[i] = p.take(BT * d->d_ff * es);
   }
-  b.u = p.take(BT * d->d_model * es);
+  b.u = p.take(2 * BT * d->d_model * es);
   b.y = (float*)p.take(BT * d->d_model * sizeof(float));
   if (dec) {
     const long rows = (long)dec->n_chunks * d->chunk;
@@ -1174,7 +1181,24 @@ ttcd_status layer_forward_run(const ttcd_layer_desc* d, const ttcd_layer_weights
   // needs the main path, and the other one only when the caller asks for its
   // Z (both Z are the inputs of the fast-weight append of the token).
   const int main = (d->main_path == TTCD_MAIN_STUDENT) ? 1 : 0;
-  for (int path = 0; path < 2; ++path) {
+  // prefill with O and Z in the workspace: both paths as one launch of each
+  // product over 2 BT rows (the residual x serves both halves)
+  const bool joint = !dec && !aux->o_teacher && !aux->o_student && !aux->z_teacher &&
+                     !aux->z_student;
+  if (joint) {
+    GemmArgs g{};
+    g.A = b.o[0]; g.lda = HD; g.B = wt->w_o; g.ldb = HD; g.C = b.h[0]; g.ldc = dm;
+    g.M = (int)(2 * BT); g.N = dm; g.K = HD; g.in_dt = dt; g.out_dt = F32; g.epi = EPI_RESIDUAL;
+    g.res = x; g.ldr = dm; g.res_rows = (int)BT; g.res_dt = dt; g.batch = 1;
+    HIPCHK(launch_gemm(g, s));
+    HIPCHK(launch_rmsnorm(b.h[0], wt->rms_gamma, b.u, (int)(2 * BT), dm, rms_eps, dt, dt, s));
+    g = GemmArgs{};
+    g.A = b.u; g.lda = dm; g.B = wt->w_gate; g.B2 = wt->w_up; g.ldb = dm; g.C = b.z[0];
+    g.ldc = f; g.M = (int)(2 * BT); g.N = f; g.K = dm; g.in_dt = dt; g.out_dt = dt;
+    g.epi = EPI_SWIGLU; g.batch = 1;
+    HIPCHK(launch_gemm(g, s));
+  }
+  for (int path = 0; path < 2 && !joint; ++path) {
     if (dec && path != main && !(path == 0 ? aux->z_teacher : aux->z_student)) continue;
     GemmArgs g{};
     g.A = o[path]; g.lda = HD; g.B = wt->w_o; g.ldb = HD; g.C = b.h[path]; g.ldc = dm;
