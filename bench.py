@@ -473,15 +473,25 @@ def attention_sweep_bench(dev, n):
                         f"rows x8", "pairs": pairs}
 
 
-def summarize_trace(path):
+def summarize_trace(path, dispatch_regex=None):
     """Per-shape table of a rocprofv3 CSV: a kernel trace (duration of each
     dispatch) or a counter collection (value of each counter per dispatch),
     grouped by kernel name and grid size, so that launches of one kernel at
-    different shapes are not averaged together."""
+    different shapes are not averaged together.
+
+    For a counter collection holding SQ_VALU_MFMA_BUSY_CYCLES and
+    GRBM_GUI_ACTIVE it adds, per group, the matrix-core busy fraction
+    BUSY / 1024 SIMDs / (GRBM_GUI_ACTIVE / 8 XCDs) and the shader clock
+    GRBM_GUI_ACTIVE / 8 / duration.  With ``dispatch_regex`` it lists every
+    matching dispatch in issue order instead (index among the matches, grid,
+    duration or counter values), so that calls of one kernel at one grid but
+    different windows can be told apart by their place in the run."""
     import csv
+    import re
     from collections import OrderedDict
 
     groups = OrderedDict()
+    per_dispatch = OrderedDict()
     with open(path, newline="") as f:
         for row in csv.DictReader(f):
             name = row.get("Kernel_Name", "?")
@@ -489,19 +499,55 @@ def summarize_trace(path):
                 grid = row["Grid_Size"]
             else:
                 grid = "x".join(row.get(f"Grid_Size_{a}", "?") for a in "XYZ")
+            dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
             if "Counter_Name" in row:
                 key = (name, grid, row["Counter_Name"])
                 val = float(row["Counter_Value"])
+                d = per_dispatch.setdefault(row["Dispatch_Id"], {"name": name, "grid": grid,
+                                                                "duration_us": dur})
+                d[row["Counter_Name"]] = val
             else:
                 key = (name, grid, "duration_us")
-                val = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+                val = dur
+                per_dispatch[row.get("Dispatch_Id", str(len(per_dispatch)))] = {
+                    "name": name, "grid": grid, "duration_us": dur}
             groups.setdefault(key, []).append(val)
+    if dispatch_regex:
+        rx = re.compile(dispatch_regex)
+        qty = None
+        print(f"{'#':>4} {'dispatch':>9} {'grid':>22}  values")
+        i = 0
+        for did, d in per_dispatch.items():
+            if not rx.search(d["name"]):
+                continue
+            vals = {k: v for k, v in d.items() if k not in ("name", "grid")}
+            if qty is None:
+                qty = sorted(vals)
+            print(f"{i:>4} {did:>9} {d['grid']:>22}  " +
+                  "  ".join(f"{k}={vals[k]:.6g}" for k in qty if k in vals))
+            i += 1
+        return
     print(f"{'kernel':<58} {'grid':>22} {'quantity':>26} {'n':>5} {'mean':>12} {'min':>12} "
           f"{'max':>12}")
     for (name, grid, qty), vals in groups.items():
         short = name if len(name) <= 58 else name[:55] + "..."
         print(f"{short:<58} {grid:>22} {qty:>26} {len(vals):>5} {np.mean(vals):>12.4g} "
               f"{np.min(vals):>12.4g} {np.max(vals):>12.4g}")
+    # derived: matrix-core busy fraction and clock per (kernel, grid)
+    derived = OrderedDict()
+    for d in per_dispatch.values():
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in d and "GRBM_GUI_ACTIVE" in d:
+            derived.setdefault((d["name"], d["grid"]), []).append(d)
+    if derived:
+        print()
+        print(f"{'kernel':<58} {'grid':>22} {'n':>5} {'mfma_busy_frac':>15} {'clock_GHz':>10}")
+        for (name, grid), ds in derived.items():
+            busy = np.mean([x["SQ_VALU_MFMA_BUSY_CYCLES"] for x in ds])
+            act = np.mean([x["GRBM_GUI_ACTIVE"] for x in ds]) / 8.0
+            dur = np.mean([x["duration_us"] for x in ds])
+            short = name if len(name) <= 58 else name[:55] + "..."
+            print(f"{short:<58} {grid:>22} {len(ds):>5} {busy / 1024.0 / act:>15.3f} "
+                  f"{act / dur / 1e3:>10.2f}")
 
 
 def main():
@@ -522,12 +568,15 @@ def main():
     ap.add_argument("--summarize-trace", metavar="CSV",
                     help="print a per-shape table of a rocprofv3 kernel-trace or counter CSV "
                          "and exit (no GPU work)")
+    ap.add_argument("--dispatches", metavar="REGEX",
+                    help="with --summarize-trace: list the dispatches of the kernels matching "
+                         "REGEX in issue order")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (a reference "
                          "kernel of known traffic for scaling memory counters)")
     args = ap.parse_args()
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace)
+        summarize_trace(args.summarize_trace, args.dispatches)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only (no collectives); "
