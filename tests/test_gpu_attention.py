@@ -109,6 +109,7 @@ def _full_size_sampled(cfg, windows, nrows):
             assert_close(to_np(o_t[b, sel]), r_t[0, sel], tol_for("bf16"), f"b{b} O_teacher rows")
             assert_close(to_np(o_s[b, sel]), r_s[0, sel], tol_for("bf16"), f"b{b} O_student rows")
             assert_close(to_np(l_t[b][:, sel]), rl_t[0][:, sel], (1e-3, 1e-4), f"b{b} LSE_T rows")
+            assert_close(to_np(l_s[b][:, sel]), rl_s[0][:, sel], (1e-3, 1e-4), f"b{b} LSE_S rows")
 
 
 def test_smollm2_16k_sampled_rows():

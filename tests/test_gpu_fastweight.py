@@ -119,6 +119,26 @@ def test_scan_zero_student_conv_is_base_mlp():
     np.testing.assert_array_equal(to_np(st)[0], w["w_down0"].f64())
 
 
+def test_scan_equal_paths_write_nothing():
+    """Teacher and student identical (same activations, same conv): the
+    residual dbar is zero, so no chunk is written, y is the base MLP and the
+    weight after the complete chunks is W_down0 exactly (notes on "Learning
+    What to Remember", key design 3: the write is driven by the gap)."""
+    from dual_window_attention_amd import ttcd
+    cfg = BASE.scaled(batch=2, seq=700, d_model=128, d_ff=256, chunk=128, seed=29)
+    z, w, beta = scan_inputs(cfg)
+    zt = I.to_torch(z["z_t"])
+    ct = I.to_torch(w["conv_t"])
+    y, st = ttcd.fastweight_scan(zt, zt, zt, ct, ct, I.to_torch(w["w_down0"]),
+                                 I.to_torch(w["w_proj"]), I.f32_to_torch(beta), cfg.chunk,
+                                 want_state=True)
+    torch.cuda.synchronize()
+    ref = z["z_t"].f64() @ w["w_down0"].f64().T
+    assert_close(to_np(y), ref, tol_for(cfg.dtype), "y with equal paths")
+    for b in range(cfg.batch):
+        np.testing.assert_array_equal(to_np(st)[b], w["w_down0"].f64())
+
+
 def test_scan_deterministic():
     from dual_window_attention_amd import ttcd
     cfg = BASE.scaled(batch=1, seq=2048, d_model=256, d_ff=512, chunk=256, seed=29)
