@@ -517,6 +517,9 @@ def layer_forward(q, k, v, x, w: Dict[str, torch.Tensor], w_teacher: int, w_stud
                   workspace: Optional[torch.Tensor] = None, stream=None,
                   no_alloc: bool = False):
     """IP-TTCD layer forward.  Returns out [B,Tq,d] fp32, or (out, aux dict).
+    aux=True returns every intermediate; aux="fw" only the fast-weight ones
+    (y, and in a prefill the state and the chunk lists R, K), which keeps the
+    layer's O and Z internal (the launch configuration of a plain call).
 
     w: w_o, w_gate, w_up, w_down0, w_proj, conv_t, conv_s, beta, optional
     gamma.  decode: dict(pos=L, state_dense=..., r_list=, k_list=,
@@ -552,15 +555,16 @@ def layer_forward(q, k, v, x, w: Dict[str, torch.Tensor], w_teacher: int, w_stud
     aux_s = None
     if aux:
         Hq = q.shape[2]
-        aux_t["o_teacher"] = torch.empty(q.shape, dtype=q.dtype, device=dev)
-        aux_t["o_student"] = torch.empty(q.shape, dtype=q.dtype, device=dev)
-        aux_t["lse_teacher"] = torch.empty((B, Hq, Tq), dtype=torch.float32, device=dev)
-        aux_t["lse_student"] = torch.empty((B, Hq, Tq), dtype=torch.float32, device=dev)
-        aux_t["z_teacher"] = torch.empty((B, Tq, f), dtype=q.dtype, device=dev)
+        if aux != "fw":
+            aux_t["o_teacher"] = torch.empty(q.shape, dtype=q.dtype, device=dev)
+            aux_t["o_student"] = torch.empty(q.shape, dtype=q.dtype, device=dev)
+            aux_t["lse_teacher"] = torch.empty((B, Hq, Tq), dtype=torch.float32, device=dev)
+            aux_t["lse_student"] = torch.empty((B, Hq, Tq), dtype=torch.float32, device=dev)
+            aux_t["z_teacher"] = torch.empty((B, Tq, f), dtype=q.dtype, device=dev)
+            # in a decode step both Z are returned too: they feed the
+            # fast-weight append of the token (fastweight_decode_append)
+            aux_t["z_student"] = torch.empty((B, Tq, f), dtype=q.dtype, device=dev)
         aux_t["y"] = torch.empty((B, Tq, dm), dtype=torch.float32, device=dev)
-        # in a decode step both Z are returned too: they feed the
-        # fast-weight append of the token (fastweight_decode_append)
-        aux_t["z_student"] = torch.empty((B, Tq, f), dtype=q.dtype, device=dev)
         if decode is None:
             aux_t["state_out"] = torch.empty((B, dm, f), dtype=torch.float32, device=dev)
             aux_t["r"] = torch.empty((B, Tq, dm), dtype=q.dtype, device=dev)

@@ -57,6 +57,15 @@ def check_layer(cfg, main_path="teacher", chunk_mean=False):
     assert_close(to_np(aux["k"]), ref["k"], tol, "k (list unit keys)")
     st = to_np(aux["state_out"])
     assert_close(st, ref["state_complete"], tol, f"state after the {cfg.seq // cfg.chunk} complete chunks")
+    # the launch configuration of a plain call: O and Z stay in the
+    # workspace and both paths' products run as one launch each
+    say("  GPU, O and Z internal")
+    (out2, aux2), _ = run_layer(cfg, main_path, chunk_mean=chunk_mean, aux="fw")
+    assert_close(to_np(out2), ref["out"], tol, "out (O, Z internal)")
+    assert_close(to_np(aux2["y"]), ref["y"], tol, "y (O, Z internal)")
+    assert_close(to_np(aux2["r"]), ref["r"], tol, "r (O, Z internal)")
+    assert_close(to_np(aux2["k"]), ref["k"], tol, "k (O, Z internal)")
+    assert_close(to_np(aux2["state_out"]), ref["state_complete"], tol, "state (O, Z internal)")
 
 
 def test_tiny_fp32_layer():
@@ -93,6 +102,14 @@ def test_smollm2_shapes_ragged_sequence():
     """The SmolLM2-shaped layer over 12000 tokens: the SwiGLU and apply
     GEMMs take 256 x 256 tiles with a ragged last row tile."""
     check_layer(I.CONFIGS[2].scaled(seq=12000, seed=15))
+
+
+def test_qwen3_dims_8k_student_main_path():
+    """Qwen3 dims over 8192 tokens with the student as the main path: the
+    joint output projection and SwiGLU of both paths take the 256 x 256 tile
+    path, and the student half of h feeds the output."""
+    cfg = I.CONFIGS[3].scaled(seq=8192, w_teacher=1024, w_student=128, seed=17)
+    check_layer(cfg, main_path="student")
 
 
 def test_smollm2_16k_layer_full():
