@@ -626,18 +626,6 @@ TTCD_DEV void wait_stages(int pending) {
     wait_vm<0>();
 }
 
-template <int NLD, class RowPtr>
-TTCD_DEV void issue(char* dst, const RowPtr& row_ptr, long k0, int wave, int lane) {
-#pragma unroll
-  for (int i = 0; i < NLD; ++i) {
-    const int p0 = (i * NW + wave) * 64;
-    const int p = p0 + lane;
-    const int row = p >> 2, cp = p & 3;
-    const int c = cp ^ swz(row);
-    g2l16(row_ptr(row) + k0 + 8 * c, dst + p0 * 16);
-  }
-}
-
 template <typename OutT, int EPI, bool CHUNKED>
 __global__ void __launch_bounds__(NTH, 1)
 gemm_nt_wide(GemmArgs g) {
@@ -678,10 +666,19 @@ gemm_nt_wide(GemmArgs g) {
     }
     return Bm + min(n0 + rr, nmax) * ldb;
   };
-  auto fetch = [=](int kt) {
+  // one 16-byte direct-to-LDS load of stage kt: idx < ALD are the A
+  // tile's, the rest the B tile's; lane i of the wave lands at 16 i
+  auto dma = [&](int kt, int idx) __attribute__((always_inline)) {
     char* st = lds + (kt % NST) * STAGE;
-    issue<ALD>(st, a_row, (long)kt * BK, wave, lane);
-    issue<BLD>(st + AB, b_row, (long)kt * BK, wave, lane);
+    const long k0 = (long)kt * BK;
+    const bool is_a = idx < ALD;
+    const int p0 = ((is_a ? idx : idx - ALD) * NW + wave) * 64;
+    const int p = p0 + lane;
+    const int row = p >> 2, c = (p & 3) ^ swz(row);
+    if (is_a)
+      g2l16(a_row(row) + k0 + 8 * c, st + p0 * 16);
+    else
+      g2l16(b_row(row) + k0 + 8 * c, st + AB + p0 * 16);
   };
 
   f32x16 acc[4][2];
@@ -694,46 +691,52 @@ gemm_nt_wide(GemmArgs g) {
   struct Frag {
     bf16x8 a[4], b[2];
   };
-  auto ldfrag = [&](const char* as, int ks, Frag& f) __attribute__((always_inline)) {
-    const char* bs = as + AB;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 128 * wm + 32 * i + r;
-      f.a[i] = as_bf16x8(ld16(as + row * (BK * 2) + (((2 * ks + h) ^ swz(row)) << 4)));
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int row = 64 * wn + 32 * j + r;
-      f.b[j] = as_bf16x8(ld16(bs + row * (BK * 2) + (((2 * ks + h) ^ swz(row)) << 4)));
-    }
+  auto lfa = [&](const char* as, int ks, int i, Frag& f) __attribute__((always_inline)) {
+    const int row = 128 * wm + 32 * i + r;
+    f.a[i] = as_bf16x8(ld16(as + row * (BK * 2) + (((2 * ks + h) ^ swz(row)) << 4)));
   };
-  auto mma = [&](const Frag& f) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(f.a[i], f.b[j], acc[i][j]);
+  auto lfb = [&](const char* as, int ks, int j, Frag& f) __attribute__((always_inline)) {
+    const int row = 64 * wn + 32 * j + r;
+    f.b[j] = as_bf16x8(ld16(as + AB + row * (BK * 2) + (((2 * ks + h) ^ swz(row)) << 4)));
   };
 
   const int nk = g.K / BK;
   const int npro = nk < NST - 1 ? nk : NST - 1;
-  for (int kt = 0; kt < npro; ++kt) fetch(kt);
+  for (int kt = 0; kt < npro; ++kt)
+#pragma unroll
+    for (int idx = 0; idx < LPT; ++idx) dma(kt, idx);
   wait_stages(npro - 1);
   barrier();
   Frag f0, f1;
-  ldfrag(lds, 0, f0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lfa(lds, 0, i, f0);
+  lfb(lds, 0, 0, f0);
+  lfb(lds, 0, 1, f0);
   // drain the scalar loads of the set-up before the loop, so that inside it
   // the LDS counter holds fragment reads alone and the compiler can wait for
   // the older fragment set while the newer one is still in flight
   __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0)
+  // Each wave issues its loads one or two at a time between its own MFMAs
+  // (the scheduling barriers pin that order), so that they go out while
+  // the matrix core works instead of in one burst after each barrier,
+  // when every wave of the workgroup would stall on address issue at once.
+#define SB __builtin_amdgcn_sched_barrier(0)
+#define MM(F, I, J) acc[I][J] = mfma32(F.a[I], F.b[J], acc[I][J])
+  static_assert(LPT == 4, "one load after every second MFMA of the first k-step");
   for (int kt = 0; kt < nk; ++kt) {
     // the slot refilled here held stage kt-1; every wave finished reading it
     // before the barrier that ended the previous iteration
-    if (kt + NST - 1 < nk) fetch(kt + NST - 1);
+    const bool pf = kt + NST - 1 < nk;
+    const int kn = kt + NST - 1;
     const char* as = lds + (kt % NST) * STAGE;
-    ldfrag(as, 1, f1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(f0);
-    __builtin_amdgcn_sched_barrier(0);
+    MM(f0, 0, 0); SB; if (pf) dma(kn, 0); SB;
+    MM(f0, 0, 1); SB; lfa(as, 1, 0, f1); lfa(as, 1, 1, f1); SB;
+    MM(f0, 1, 0); SB; if (pf) dma(kn, 1); SB;
+    MM(f0, 1, 1); SB; lfa(as, 1, 2, f1); lfa(as, 1, 3, f1); SB;
+    MM(f0, 2, 0); SB; if (pf) dma(kn, 2); SB;
+    MM(f0, 2, 1); SB; lfb(as, 1, 0, f1); lfb(as, 1, 1, f1); SB;
+    MM(f0, 3, 0); SB; if (pf) dma(kn, 3); SB;
+    MM(f0, 3, 1); SB;
     // stage kt+1 must have landed (later ones may still be in flight), and
     // this wave's reads of stage kt are complete before the barrier
     const int last = kt + NST - 1 < nk ? kt + NST - 1 : nk - 1;
@@ -741,11 +744,18 @@ gemm_nt_wide(GemmArgs g) {
     wait_stages(last - (kt + 1));
     barrier();
     // (after the last stage this reads a slot nobody uses; it stays in bounds)
-    ldfrag(lds + ((kt + 1) % NST) * STAGE, 0, f0);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(f1);
-    __builtin_amdgcn_sched_barrier(0);
+    const char* an = lds + ((kt + 1) % NST) * STAGE;
+    MM(f1, 0, 0); SB; lfa(an, 0, 0, f0); SB;
+    MM(f1, 0, 1); SB; lfa(an, 0, 1, f0); SB;
+    MM(f1, 1, 0); SB; lfa(an, 0, 2, f0); SB;
+    MM(f1, 1, 1); SB; lfa(an, 0, 3, f0); SB;
+    MM(f1, 2, 0); SB; lfb(an, 0, 0, f0); SB;
+    MM(f1, 2, 1); SB; lfb(an, 0, 1, f0); SB;
+    MM(f1, 3, 0); SB;
+    MM(f1, 3, 1); SB;
   }
+#undef MM
+#undef SB
   // every wave's last MFMAs are done reading the ring before the epilogue
   // reuses it as slabs
   lds_wave_sync();
