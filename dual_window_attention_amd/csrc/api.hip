@@ -91,6 +91,9 @@ ttcd_status check_attn(const ttcd_attn_desc* d) {
     return fail(TTCD_ERR_BAD_SHAPE, "need 1 <= w_student <= w_teacher");
   if ((long)rows * d->n_kv_heads * d->head_dim * d->batch > (1L << 40))
     return fail(TTCD_ERR_BAD_SHAPE, "k/v too large");
+  // the kernels index (sequence, position, head) rows in 32-bit integers
+  if ((long)d->batch * (rows > d->seq_q ? rows : d->seq_q) * d->n_q_heads >= (1L << 31))
+    return fail(TTCD_ERR_BAD_SHAPE, "batch * max(seq_q, kv_rows) * n_q_heads must be below 2^31");
   if (d->seq_q == 1 && d->n_q_heads / d->n_kv_heads > 4)
     return fail(TTCD_ERR_UNSUPPORTED, "single-query path supports up to 4 q heads per kv head");
   return TTCD_OK;
@@ -145,6 +148,8 @@ ttcd_status check_fw(const ttcd_fw_desc* d) {
   if (!dt_ok(d->in_dtype) || !dt_ok(d->out_dtype))
     return fail(TTCD_ERR_UNSUPPORTED, "unknown dtype");
   if (d->batch < 1 || d->seq < 1) return fail(TTCD_ERR_BAD_SHAPE, "batch and seq must be >= 1");
+  if ((long)d->batch * d->seq > (1L << 28))
+    return fail(TTCD_ERR_BAD_SHAPE, "batch * seq must be at most 2^28");
   if (d->d_model < 8 || d->d_model % 8 || d->d_ff < 8 || d->d_ff % 8)
     return fail(TTCD_ERR_BAD_SHAPE, "d_model and d_ff must be positive multiples of 8");
   if (d->chunk < 16 || d->chunk % 16)

@@ -71,8 +71,10 @@ typedef enum { TTCD_MAIN_TEACHER = 0, TTCD_MAIN_STUDENT = 1 } ttcd_main_path;
  *   lse_teacher, lse_student [batch, n_q_heads, seq_q] fp32, natural-log
  *            log-sum-exp of each row's scaled scores; either may be NULL.
  * Query head h reads kv head h / (n_q_heads / n_kv_heads) (GQA).
- * Requires q_pos0 + seq_q <= seq_k <= kv_rows, 1 <= w_student <= w_teacher,
- * head_dim in {64, 128}.  Keys older than the teacher window of every query
+ * Requires batch, seq_q, seq_k >= 1 (an empty call is TTCD_ERR_BAD_SHAPE),
+ * q_pos0 + seq_q <= seq_k <= kv_rows, 1 <= w_student <= w_teacher,
+ * head_dim in {64, 128}, batch * max(seq_q, kv_rows) * n_q_heads < 2^31 and
+ * batch * kv_rows * n_kv_heads * head_dim <= 2^40.  Keys older than the teacher window of every query
  * are never read, so they may hold anything (NaN included).
  * ---------------------------------------------------------------------- */
 typedef struct {
@@ -188,7 +190,9 @@ ttcd_status ttcd_dual_window_attn_backward(const ttcd_attn_desc* desc,
  *            (without beta): the low-rank chunk lists of ttcd_fw_state, rows
  *            [j*chunk, (j+1)*chunk) holding chunk j, so that a decode loop
  *            continues from this prefill in list form.
- * Requires chunk % 16 == 0, d_model % 8 == 0, d_ff % 8 == 0, conv_k in [1,8].
+ * Requires batch, seq >= 1 (an empty call is TTCD_ERR_BAD_SHAPE),
+ * batch * seq <= 2^28, chunk % 16 == 0, d_model % 8 == 0, d_ff % 8 == 0,
+ * conv_k in [1,8].
  * ---------------------------------------------------------------------- */
 typedef struct {
   int32_t batch;
@@ -345,6 +349,8 @@ ttcd_status ttcd_fastweight_stream(const ttcd_fw_desc* desc,
  *   x   [batch, seq_q, d_model]  attn.in_dtype (residual stream)
  *   out [batch, seq_q, d_model]  fp32
  *
+ * Requirements of ttcd_dual_window_attn and of the fast-weight scan, and
+ * attn.batch * attn.seq_q <= 2^28.
  * Prefill: dec == NULL, attn.seq_q == attn.seq_k, attn.q_pos0 == 0.
  * Decode:  dec != NULL, attn.seq_q == 1, attn.q_pos0 = L, attn.seq_k = L+1
  *          (the new token's k/v already written at row L of the cache).

@@ -82,6 +82,63 @@ def test_attention_rejects_bad_descriptors(kw, status):
     assert lib.ttcd_last_error() != b""
 
 
+@pytest.mark.parametrize("kw", [dict(seq_q=0), dict(seq_q=0, seq_k=0), dict(batch=0),
+                                dict(seq_q=1, seq_k=0)])
+def test_empty_attention_is_an_error(kw):
+    """An empty call is TTCD_ERR_BAD_SHAPE (the header's stated behaviour),
+    before any device work, and sizes no workspace."""
+    from dual_window_attention_amd import ttcd
+    lib = ttcd.lib()
+    d = _attn(**kw)
+    fake = C.c_void_p(1 << 20)
+    assert lib.ttcd_dual_window_attn(C.byref(d), fake, fake, fake, fake, fake, None, None, fake,
+                                     1 << 40, None) == 2
+    assert b">= 1" in lib.ttcd_last_error()
+    assert lib.ttcd_dual_window_attn_workspace_size(C.byref(d)) == 0
+
+
+def test_empty_fastweight_and_layer_are_errors():
+    from dual_window_attention_amd import ttcd
+    lib = ttcd.lib()
+    fake = C.c_void_p(1 << 20)
+    for b, t in ((1, 0), (0, 64)):
+        fw = ttcd.FwDesc(b, t, 1024, 3072, 64, 4, 0.0, 1, 0)
+        assert lib.ttcd_fastweight_scan_workspace_size(C.byref(fw)) == 0
+        assert lib.ttcd_fastweight_scan(C.byref(fw), *([fake] * 12), fake, 1 << 40, None) == 2
+    ld = ttcd.LayerDesc(_attn(seq_q=0, seq_k=0), 1024, 3072, 1024, 4, 0.0, 0.0, 0)
+    w = ttcd.LayerWeights(*([1 << 20] * 8), 1 << 20)
+    assert lib.ttcd_layer_forward_workspace_size(C.byref(ld), None) == 0
+    assert lib.ttcd_layer_forward(C.byref(ld), C.byref(w), fake, fake, fake, fake, fake, None,
+                                  None, fake, 1 << 40, None) == 2
+
+
+def test_size_limits_at_and_past_the_maximum():
+    """The largest accepted sizes are sized (no overflow in the size
+    arithmetic), one row more is rejected: attention rows
+    batch * max(seq_q, kv_rows) * n_q_heads < 2^31 (32-bit row indices in
+    the kernels), fast-weight and layer tokens batch * seq <= 2^28."""
+    from dual_window_attention_amd import ttcd
+    lib = ttcd.lib()
+    top = (1 << 27) - 1                                       # x 16 q heads < 2^31
+    d = _attn(seq_q=top, seq_k=top)
+    assert lib.ttcd_dual_window_attn_workspace_size(C.byref(d)) == 8 * 128 * ((top + 63) // 64 * 64) * 2
+    d = _attn(seq_q=top + 1, seq_k=top + 1)
+    assert lib.ttcd_dual_window_attn_workspace_size(C.byref(d)) == 0
+    d = _attn(seq_q=1, q_pos0=100, seq_k=101, kv_rows=top + 1)    # a decode cache counts too
+    assert lib.ttcd_dual_window_attn_workspace_size(C.byref(d)) == 0
+    fw = ttcd.FwDesc(1, 1 << 28, 64, 64, 64, 4, 0.0, 1, 0)
+    assert lib.ttcd_fastweight_scan_workspace_size(C.byref(fw)) > (1 << 28) * 64 * 2 * 2
+    fw = ttcd.FwDesc(2, (1 << 27) + 1, 64, 64, 64, 4, 0.0, 1, 0)
+    assert lib.ttcd_fastweight_scan_workspace_size(C.byref(fw)) == 0
+    one = dict(n_q_heads=1, n_kv_heads=1, head_dim=64, w_teacher=64, w_student=16)
+    ld = ttcd.LayerDesc(_attn(batch=4, seq_q=1 << 26, seq_k=1 << 26, **one), 64, 64, 64, 4,
+                        0.0, 0.0, 0)
+    assert lib.ttcd_layer_forward_workspace_size(C.byref(ld), None) > 0
+    ld = ttcd.LayerDesc(_attn(batch=5, seq_q=1 << 26, seq_k=1 << 26, **one), 64, 64, 64, 4,
+                        0.0, 0.0, 0)
+    assert lib.ttcd_layer_forward_workspace_size(C.byref(ld), None) == 0
+
+
 def test_attention_rejects_null_misaligned_and_small_workspace():
     from dual_window_attention_amd import ttcd
     lib = ttcd.lib()
