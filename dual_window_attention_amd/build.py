@@ -36,13 +36,23 @@ CFLAGS = [
 ]
 
 
+# Per-file flags.  The attention backward keeps its dK/dV accumulators live
+# across a long loop at the edge of the register file; left to its own
+# heuristics the compiler parks them in AGPRs and copies them to and from
+# VGPRs around every MFMA (hundreds of extra VALU instructions per query
+# block).  The VGPR form of the MFMA removes most of those copies.
+FILE_FLAGS = {
+    "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def sources() -> List[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

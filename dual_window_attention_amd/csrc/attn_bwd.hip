@@ -211,7 +211,7 @@ struct DkdvCfg {
 // dV += P^T dO and dK += dS^T Q.  The LDS operands of each MFMA chain are
 // read four ahead of their MFMA (sched barriers keep that order), so that a
 // single wave per SIMD does not stall on every read.
-template <int D, bool STUD>
+template <int D, bool STUD, bool MASK>
 TTCD_DEV void dkdv_block(uint32_t st, int r32, int h, const bf16x8* kf, const bf16x8* vf,
                          f32x16* dka, f32x16* dva, int sb, int key, int G, int gshift, int wT,
                          int wS, float c2, bool tmask, bool smask) {
@@ -255,14 +255,14 @@ TTCD_DEV void dkdv_block(uint32_t st, int r32, int h, const bf16x8* kf, const bf
     for (int e = 0; e < 4; ++e) {
       const int vv = 4 * q4 + e;
       int dl = 0;
-      if (tmask || smask) dl = row_pos(sb * 32 + 4 * h + 8 * q4 + e, G, gshift) - key;
+      if (MASK) dl = row_pos(sb * 32 + 4 * h + 8 * q4 + e, G, gshift) - key;
       float pt = fast_exp2(__builtin_fmaf(sacc[0][vv], c2, -lt4[e]));
-      if (tmask && !(dl >= 0 && dl < wT)) pt = 0.f;
+      if (MASK && tmask && !(dl >= 0 && dl < wT)) pt = 0.f;
       float dsv = pt * (sacc[1][vv] - dt4[e]);
       pa[vv >> 3][vv & 7] = (__bf16)pt;
       if (STUD) {
         float ps = fast_exp2(__builtin_fmaf(sacc[0][vv], c2, -ls4[e]));
-        if (smask && !(dl >= 0 && dl < wS)) ps = 0.f;
+        if (MASK && smask && !(dl >= 0 && dl < wS)) ps = 0.f;
         dsv = __builtin_fmaf(ps, sacc[2][vv] - ds4[e], dsv);
         psa[vv >> 3][vv & 7] = (__bf16)ps;
       }
@@ -405,12 +405,16 @@ attn_bwd_dkdv_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const int tB = row_pos(min(sb * 32 + 31, R - 1), G, gshift);
     const BlockKind bk = block_kind(tA - (j0 + 31), tB - j0, wT, wS);
     if (bk.act && j0 < Tn) {
-      if (bk.stud)
-        dkdv_block<D, true>(st, r32, h, kf, vf, dka, dva, sb, j0 + r32, G, gshift, wT, wS, c2,
-                            bk.tmask, bk.smask);
-      else
-        dkdv_block<D, false>(st, r32, h, kf, vf, dka, dva, sb, j0 + r32, G, gshift, wT, wS, c2,
-                             bk.tmask, bk.smask);
+#define TTCD_DKDV(S, M) \
+  dkdv_block<D, S, M>(st, r32, h, kf, vf, dka, dva, sb, j0 + r32, G, gshift, wT, wS, c2, \
+                      bk.tmask, bk.smask)
+      const bool msk = bk.tmask || (bk.stud && bk.smask);
+      if (bk.stud) {
+        if (msk) TTCD_DKDV(true, true); else TTCD_DKDV(true, false);
+      } else {
+        if (msk) TTCD_DKDV(false, true); else TTCD_DKDV(false, false);
+      }
+#undef TTCD_DKDV
     }
     stage_barrier();
   }
@@ -450,7 +454,7 @@ struct DqCfg {
 // One 32-key tile of a wave in the dQ kernel: S^T = K Q^T, dP^T = V dO^T
 // (both windows), dS^T on the vector ALU, dQ^T += K^T dS^T; LDS operands
 // read four ahead of their MFMA, as in the dK/dV kernel.
-template <int D, bool STUD>
+template <int D, bool STUD, bool MASK>
 TTCD_DEV void dq_block(uint32_t st, int r32, int h, const bf16x8* qf, const bf16x8* dtf,
                        const bf16x8* dsf, f32x16* acc, int t, int jt, float lt, float ls,
                        float dt, float dsum, int wT, int wS, float c2, bool tmask, bool smask) {
@@ -482,11 +486,11 @@ TTCD_DEV void dq_block(uint32_t st, int r32, int h, const bf16x8* qf, const bf16
   for (int vv = 0; vv < 16; ++vv) {
     const int dl = t - (jt + 4 * h + 8 * (vv >> 2) + (vv & 3));
     float pt = fast_exp2(__builtin_fmaf(sacc[0][vv], c2, -lt));
-    if (tmask && !(dl >= 0 && dl < wT)) pt = 0.f;
+    if (MASK && tmask && !(dl >= 0 && dl < wT)) pt = 0.f;
     float dsv = pt * (sacc[1][vv] - dt);
     if (STUD) {
       float ps = fast_exp2(__builtin_fmaf(sacc[0][vv], c2, -ls));
-      if (smask && !(dl >= 0 && dl < wS)) ps = 0.f;
+      if (MASK && smask && !(dl >= 0 && dl < wS)) ps = 0.f;
       dsv = __builtin_fmaf(ps, sacc[2][vv] - dsum, dsv);
     }
     da[vv >> 3][vv & 7] = (__bf16)dsv;
@@ -602,12 +606,16 @@ attn_bwd_dq_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const uint32_t st = (uint32_t)((i & 1) * CF::STAGE);
     const BlockKind bk = block_kind(a_w - (jt + 31), b_w - jt, wT, wS);
     if (bk.act) {
-      if (bk.stud)
-        dq_block<D, true>(st, r32, h, qf, dtf, dsf, acc, t, jt, lt, ls, dt, dsum, wT, wS, c2,
-                          bk.tmask, bk.smask);
-      else
-        dq_block<D, false>(st, r32, h, qf, dtf, dsf, acc, t, jt, lt, ls, dt, dsum, wT, wS, c2,
-                           bk.tmask, bk.smask);
+#define TTCD_DQ(S, M) \
+  dq_block<D, S, M>(st, r32, h, qf, dtf, dsf, acc, t, jt, lt, ls, dt, dsum, wT, wS, c2, \
+                    bk.tmask, bk.smask)
+      const bool msk = bk.tmask || (bk.stud && bk.smask);
+      if (bk.stud) {
+        if (msk) TTCD_DQ(true, true); else TTCD_DQ(true, false);
+      } else {
+        if (msk) TTCD_DQ(false, true); else TTCD_DQ(false, false);
+      }
+#undef TTCD_DQ
     }
     stage_barrier();
   }
