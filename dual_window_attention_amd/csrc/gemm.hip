@@ -635,12 +635,18 @@ gemm_nt_wide(GemmArgs g) {
   const int lane = tid & 63;
   const int wm = wave >> 2, wn = wave & 3;
   const int h = lane >> 5, r = lane & 31;
-  const int z = blockIdx.z;
   constexpr bool swiglu = EPI == EPI_SWIGLU;
   const int ncols = swiglu ? BN / 2 : BN;                   // output columns per tile
   const int ntn = (g.N + ncols - 1) / ncols;
   const int ntm = (g.M + BM - 1) / BM;
-  const uint32_t lid = xcd_remap(blockIdx.x, (uint32_t)(ntm * ntn));
+  // The remap runs over (batch, tile) in dispatch order (tile fastest), so
+  // that each XCD takes whole batches of a batched call and the operands of
+  // a batch are fetched into one L2 (the 63 chunk writes of the 64K
+  // workload: 0.74 GB fetched instead of 1.83 GB).
+  const uint32_t per = (uint32_t)(ntm * ntn);
+  const uint32_t flat = xcd_remap(blockIdx.z * per + blockIdx.x, per * gridDim.z);
+  const int z = (int)(flat / per);
+  const uint32_t lid = flat % per;
   int tm, tn;
   grouped_tile(lid, ntm, ntn, 4, tm, tn);
   const long m0 = (long)tm * BM;
