@@ -161,8 +161,18 @@ ttcd_status check_fw(const ttcd_fw_desc* d) {
 struct FwBufs {
   void *dbar, *zbt, *wpt, *m, *rst, *states;
   float *sc, *inv, *part, *dw;
-  int Tpad, N;
+  float* mparts;      // K-slice partial sums of M = W0 W_proj (mks > 1)
+  int Tpad, N, mks;
 };
+
+// K slices for M = W0 W_proj [d, f] (K = f): a product of few output tiles
+// (under 256 of 128 x 128 at the 64K workload's 1024 x 3072) fills the GPU
+// only when its K range is split; the slices' fp32 sums are then added in
+// a fixed order.
+int m_kslices(int d, int f) {
+  const long tiles = (long)((d + 127) / 128) * ((f + 127) / 128);
+  return (tiles < 256 && f % (4 * 64) == 0 && f >= 1024) ? 4 : 1;
+}
 
 void plan_fw(int B, int T, int d, int f, int C, int dt, Plan& p, FwBufs& w) {
   const size_t es = dsize(dt);
@@ -175,6 +185,8 @@ void plan_fw(int B, int T, int d, int f, int C, int dt, Plan& p, FwBufs& w) {
   w.part = (float*)p.take(fw_stream_part_bytes(B, T, f));
   w.wpt = p.take((size_t)f * f * es);
   w.m = p.take((size_t)d * f * es);
+  w.mks = m_kslices(d, f);
+  w.mparts = w.mks > 1 ? (float*)p.take((size_t)w.mks * d * f * sizeof(float)) : nullptr;
   w.rst = p.take((size_t)B * d * w.Tpad * es);
   w.states = p.take((size_t)B * (w.N > 1 ? w.N - 1 : 0) * d * f * es);
   w.dw = (float*)p.take((size_t)B * w.N * d * f * sizeof(float));
@@ -210,7 +222,17 @@ hipError_t run_fw(int B, int T, int d, int f, int C, int kc, float eps, int dt,
       return e;
     g.A = w0; g.lda = f; g.B = w.wpt; g.ldb = f; g.C = w.m; g.ldc = f;
     g.M = d; g.N = f; g.K = f; g.in_dt = dt; g.out_dt = dt; g.epi = EPI_STORE; g.batch = 1;
-    if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+    if (w.mks > 1) {
+      // K slices as a batch into fp32 partials, then their fixed-order sum
+      const int ks = f / w.mks;
+      g.C = w.mparts; g.out_dt = F32; g.K = ks; g.batch = w.mks;
+      g.sA = ks; g.sB = ks; g.sC = (long)d * f;
+      if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+      if ((e = launch_sum_slices_to(w.mparts, w.m, (long)d * f, w.mks, dt, s)) != hipSuccess)
+        return e;
+    } else if ((e = launch_gemm(g, s)) != hipSuccess) {
+      return e;
+    }
   }
   if (r_out) {
     // r_t = M dbar_t, token-major [B, T, d]

@@ -77,6 +77,18 @@ sum_slices_kernel(const float* __restrict__ parts, float* __restrict__ out, long
   *reinterpret_cast<f32x4*>(out + i) = acc;
 }
 
+// out[i] = sum_z parts[z][i] in the element type of out (fixed slice order)
+template <typename OutT>
+__global__ void __launch_bounds__(256)
+sum_slices_to_kernel(const float* __restrict__ parts, OutT* __restrict__ out, long n, int S) {
+  const long i = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= n) return;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(parts + i);
+  for (int z = 1; z < S; ++z) acc += *reinterpret_cast<const f32x4*>(parts + (size_t)z * n + i);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) stf(out + i + e, acc[e]);
+}
+
 // x -> hi = bf16(x), lo = bf16(x - hi)
 __global__ void __launch_bounds__(256)
 split_bf16_kernel(const float* __restrict__ x, bf16_t* __restrict__ hi, bf16_t* __restrict__ lo,
@@ -410,6 +422,19 @@ hipError_t launch_sum_slices(const float* parts, float* out, long n, int S, hipS
   if (n % 4) return hipErrorInvalidValue;
   hipLaunchKernelGGL(sum_slices_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s,
                      parts, out, n, S);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_slices_to(const float* parts, void* out, long n, int S, int out_dt,
+                                hipStream_t s) {
+  if (n % 4) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((n / 4 + 255) / 256));
+  if (out_dt == BF16)
+    hipLaunchKernelGGL(sum_slices_to_kernel<bf16_t>, grid, dim3(256), 0, s, parts, (bf16_t*)out,
+                       n, S);
+  else
+    hipLaunchKernelGGL(sum_slices_to_kernel<float>, grid, dim3(256), 0, s, parts, (float*)out, n,
+                       S);
   return hipGetLastError();
 }
 

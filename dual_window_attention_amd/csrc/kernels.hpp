@@ -207,6 +207,9 @@ hipError_t launch_chunk_suffix(const float* ds, void* g, void* g_lo, float* tota
                                int nch, int B, int dt, hipStream_t s);
 // out [n] = sum over z < S of parts [S, n] (n % 4 == 0)
 hipError_t launch_sum_slices(const float* parts, float* out, long n, int S, hipStream_t s);
+// out[i] = sum over the S slices parts[z][i] (n % 4 == 0), stored as out_dt
+hipError_t launch_sum_slices_to(const float* parts, void* out, long n, int S, int out_dt,
+                                hipStream_t s);
 // x fp32 [n] -> hi = bf16(x), lo = bf16(x - hi)
 hipError_t launch_split_bf16(const float* x, void* hi, void* lo, long n, hipStream_t s);
 // dbeta [B, nch] = per-chunk <R^T, P^T>; P^T *= beta (in place); rt, pt fp32 [d, B * TC]
