@@ -109,3 +109,14 @@ def test_attention_backward_64k_prefix_rows_and_dv_sums():
     got = dv.double().sum(dim=1).cpu().numpy()                          # [1, Hkv, D]
     want = (dtt.double() + dst.double()).reshape(1, T, Hkv, G, D).sum(dim=(1, 3)).cpu().numpy()
     assert_close(got, want, tol_for("bf16"), "sum_j dv_j")
+
+
+def test_attention_backward_deterministic_run_to_run():
+    """No atomics: every gradient is a fixed-order sum, so two calls agree
+    bit for bit (GQA 2:1, both windows, a ragged tail)."""
+    say("attention backward determinism")
+    att, do_t, do_s = grads_case(2, 777, 4, 2, 128, 300, 40, "bf16", seed=9)
+    a = gpu_backward(att, 300, 40, do_t, do_s)
+    b = gpu_backward(att, 300, 40, do_t, do_s)
+    for n, x, y in zip(("dq", "dk", "dv"), a, b):
+        assert torch.equal(x, y), n

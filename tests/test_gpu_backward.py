@@ -125,3 +125,29 @@ def test_scan_backward_qwen3_fast_weight_shapes():
 def test_scan_backward_qwen3_16_chunks():
     """The 64K layer's fast-weight shapes over 16 chunks of 1024 tokens."""
     check_scan_backward(BASE.scaled(batch=1, seq=16384, seed=89))
+
+
+def test_scan_backward_deterministic_run_to_run():
+    """Every reduction of the gradient (chunk suffix, the K-sliced dM, the
+    tap partials, dbeta) runs in a fixed order: two calls on the same inputs
+    agree bit for bit."""
+    from dual_window_attention_amd import ttcd
+    cfg = BASE.scaled(batch=2, seq=1100, d_model=128, d_ff=256, chunk=128, conv_k=4, seed=90)
+    say(f"scan backward determinism B={cfg.batch} T={cfg.seq}")
+    z = I.hidden_activations(cfg)
+    w = I.layer_weights(cfg)
+    beta = I.f32_to_torch(I.beta_for(cfg))
+    dy = I.to_torch(I.normal(cfg.seed, "dy", (cfg.batch, cfg.seq, cfg.d_model), 1.0, cfg.dtype))
+    zt, zs = I.to_torch(z["z_t"]), I.to_torch(z["z_s"])
+    dev = {n: I.to_torch(w[n]) for n in ("conv_t", "conv_s", "w_down0", "w_proj")}
+
+    def run():
+        g = ttcd.fastweight_scan_backward(zt, zs, zt, dev["conv_t"], dev["conv_s"],
+                                          dev["w_down0"], dev["w_proj"], beta, dy, cfg.chunk,
+                                          out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        return g
+
+    a, b = run(), run()
+    for n in a:
+        assert torch.equal(a[n], b[n]), n

@@ -167,3 +167,25 @@ def test_qwen3_64k_layer_full_against_stored_oracle_rows():
     si = torch.from_numpy(ref["state_i"]).cuda()
     sj = torch.from_numpy(ref["state_j"]).cuda()
     assert_close(to_np(aux["state_out"][0, si, sj]), ref["state"], tol, "final state (sampled)")
+
+
+def test_layer_deterministic_run_to_run():
+    """The whole layer (both paths through the joint GEMMs, the stream, the
+    K-sliced M = W_down0 W_proj, the prefix) gives the same bits twice, at
+    Qwen3 widths over a ragged 2.5 chunks."""
+    from dual_window_attention_amd import ttcd
+    cfg = I.CONFIGS[3].scaled(seq=2560, w_teacher=1024, w_student=128, seed=93)
+    say(f"layer determinism T={cfg.seq} d={cfg.d_model} f={cfg.d_ff}")
+    att = I.attention_inputs(cfg)
+    w = I.layer_weights(cfg)
+    q, k, v = (I.to_torch(att[n]) for n in ("q", "k", "v"))
+    wd = {n: I.to_torch(t) for n, t in w.items()}
+    wd["beta"] = I.f32_to_torch(I.beta_for(cfg))
+    x = I.to_torch(I.residual_input(cfg))
+
+    def run():
+        out = ttcd.layer_forward(q, k, v, x, wd, cfg.w_teacher, cfg.w_student, cfg.chunk)
+        torch.cuda.synchronize()
+        return out.clone()
+
+    assert torch.equal(run(), run())
