@@ -803,53 +803,126 @@ gemm_nt_wide(GemmArgs g) {
       *reinterpret_cast<uint2*>(cp) = uint2{pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
     }
   };
+  // In a full tile a lane's pieces all sit in the same 4 columns (64 is a
+  // multiple of per_row): the column scale is read once, and the residual
+  // of block row i + 1 is read before block row i is stored, so that the
+  // reads are in flight together (a read issued after a store to C, which
+  // may alias the residual, would wait for it).
+  constexpr int NP = npieces / 64;
+  static_assert(64 % per_row == 0, "a lane's pieces share their columns");
+  const int c4l = 4 * (lane % per_row);
+  f32x4 csv = {1.f, 1.f, 1.f, 1.f};
+  if constexpr (EPI == EPI_STORE) {
+    if (cscale && full_tile) csv = *reinterpret_cast<const f32x4*>(cscale + nw0 + c4l);
+  }
+  // the residual's type is fixed per call: two copies of the epilogue, so
+  // that no branch sits between a residual read and its use
+  auto run_epilogue = [&](auto RBc, auto FTc) __attribute__((always_inline)) {
+    constexpr bool RB = decltype(RBc)::value;
+    constexpr bool FT = decltype(FTc)::value;
+    auto load_res = [&](int i, u32x4 (&rv)[NP]) __attribute__((always_inline)) {
+      const long mb = m0 + 128 * wm + 32 * i;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = 8 * (v >> 2) + 4 * h + (v & 3);
-      if constexpr (swiglu) {
-        slab[row * EPS + r] = silu(acc[i][0][v]) * acc[i][1][v];
-      } else {
-        slab[row * EPS + r] = acc[i][0][v];
-        slab[row * EPS + 32 + r] = acc[i][1][v];
-      }
-    }
-    lds_wave_sync();
-    const long mb = m0 + 128 * wm + 32 * i;
-    if (full_tile) {
-#pragma unroll
-      for (int t = 0; t < npieces / 64; ++t) {
-        const int idx = lane + 64 * t;
-        const int rr = idx / per_row, c4 = 4 * (idx % per_row);
-        finish(mb + rr, nw0 + c4, *reinterpret_cast<const f32x4*>(slab + rr * EPS + c4));
-      }
-    } else {
-#pragma unroll
-      for (int t = 0; t < npieces / 64; ++t) {
-        const int idx = lane + 64 * t;
-        const int rr = idx / per_row, c4 = 4 * (idx % per_row);
-        const long m = mb + rr, n = nw0 + c4;
-        if (m > mmax || n > nmax) continue;
-        f32x4 val = *reinterpret_cast<const f32x4*>(slab + rr * EPS + c4);
-        if (n + 3 <= nmax) {
-          finish(m, n, val);
-          continue;
+      for (int t = 0; t < NP; ++t) {
+        const long m = mb + (lane + 64 * t) / per_row;
+        const long rm = (g.res_rows < g.M ? m % g.res_rows : m) * g.ldr + nw0 + c4l + z * g.sRes;
+        if constexpr (RB) {
+          const uint2 u = *reinterpret_cast<const uint2*>(resb + rm);
+          rv[t] = u32x4{u.x, u.y, 0u, 0u};
+        } else {
+          rv[t] = *reinterpret_cast<const u32x4*>(res + rm);
         }
-        for (int e = 0; e < 4; ++e) {
-          if (n + e > nmax) break;
-          float x = val[e];
+      }
+    };
+    u32x4 rva[NP], rvb[NP];
+    if constexpr (EPI == EPI_RESIDUAL) {
+      if constexpr (FT) load_res(0, rva);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u32x4 (&rcur)[NP] = (i & 1) ? rvb : rva;
+      u32x4 (&rnext)[NP] = (i & 1) ? rva : rvb;
+      if constexpr (EPI == EPI_RESIDUAL) {
+        if (FT && i + 1 < 4) load_res(i + 1, rnext);
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = 8 * (v >> 2) + 4 * h + (v & 3);
+        if constexpr (swiglu) {
+          slab[row * EPS + r] = silu(acc[i][0][v]) * acc[i][1][v];
+        } else {
+          slab[row * EPS + r] = acc[i][0][v];
+          slab[row * EPS + 32 + r] = acc[i][1][v];
+        }
+      }
+      lds_wave_sync();
+      const long mb = m0 + 128 * wm + 32 * i;
+      if constexpr (FT) {
+#pragma unroll
+        for (int t = 0; t < NP; ++t) {
+          const int rr = (lane + 64 * t) / per_row;
+          f32x4 val = *reinterpret_cast<const f32x4*>(slab + rr * EPS + c4l);
           if constexpr (EPI == EPI_RESIDUAL) {
-            const long rm = (g.res_rows < g.M ? m % g.res_rows : m) * g.ldr + n + e + z * g.sRes;
-            x += res_bf16 ? bf2f(resb[rm]) : res[rm];
+            if constexpr (RB) {
+              val[0] += __uint_as_float(rcur[t][0] << 16);
+              val[1] += __uint_as_float(rcur[t][0] & 0xFFFF0000u);
+              val[2] += __uint_as_float(rcur[t][1] << 16);
+              val[3] += __uint_as_float(rcur[t][1] & 0xFFFF0000u);
+            } else {
+              val[0] += __uint_as_float(rcur[t][0]);
+              val[1] += __uint_as_float(rcur[t][1]);
+              val[2] += __uint_as_float(rcur[t][2]);
+              val[3] += __uint_as_float(rcur[t][3]);
+            }
           } else if constexpr (EPI == EPI_STORE) {
-            if (cscale) x *= cscale[n + e];
+            val *= csv;
           }
-          stf(C + m * g.ldc + n + e, x);
+          OutT* cp = C + (mb + rr) * g.ldc + nw0 + c4l;
+          if constexpr (sizeof(OutT) == 4) {
+            *reinterpret_cast<f32x4*>(cp) = val;
+          } else {
+            *reinterpret_cast<uint2*>(cp) =
+                uint2{pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
+          }
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < npieces / 64; ++t) {
+          const int idx = lane + 64 * t;
+          const int rr = idx / per_row, c4 = 4 * (idx % per_row);
+          const long m = mb + rr, n = nw0 + c4;
+          if (m > mmax || n > nmax) continue;
+          f32x4 val = *reinterpret_cast<const f32x4*>(slab + rr * EPS + c4);
+          if (n + 3 <= nmax) {
+            finish(m, n, val);
+            continue;
+          }
+          for (int e = 0; e < 4; ++e) {
+            if (n + e > nmax) break;
+            float x = val[e];
+            if constexpr (EPI == EPI_RESIDUAL) {
+              const long rm = (g.res_rows < g.M ? m % g.res_rows : m) * g.ldr + n + e + z * g.sRes;
+              x += res_bf16 ? bf2f(resb[rm]) : res[rm];
+            } else if constexpr (EPI == EPI_STORE) {
+              if (cscale) x *= cscale[n + e];
+            }
+            stf(C + m * g.ldc + n + e, x);
+          }
         }
       }
+      lds_wave_sync();
     }
-    lds_wave_sync();
+  };
+  if (EPI == EPI_RESIDUAL && res_bf16) {
+    if (full_tile)
+      run_epilogue(std::true_type{}, std::true_type{});
+    else
+      run_epilogue(std::true_type{}, std::false_type{});
+  } else {
+    if (full_tile)
+      run_epilogue(std::false_type{}, std::true_type{});
+    else
+      run_epilogue(std::false_type{}, std::false_type{});
   }
 }
 }  // namespace wide
