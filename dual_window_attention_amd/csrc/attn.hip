@@ -49,6 +49,13 @@ typedef __attribute__((address_space(3))) const u32x4 lds_u32x4_t;
 // 16-byte LDS read at a byte address.  The MFMA kernel has no static LDS, so
 // its dynamic LDS starts at address 0 and an offset into it is the address.
 TTCD_DEV u32x4 lds16(uint32_t addr) { return *reinterpret_cast<lds_u32x4_t*>((size_t)addr); }
+typedef __attribute__((address_space(3))) const char lds_char_t;
+// the same at a register address plus a constant byte offset, written as
+// pointer arithmetic so that the offset lands in the read's offset field
+TTCD_DEV u32x4 lds16(uint32_t base, uint32_t off) {
+  lds_char_t* p = reinterpret_cast<lds_char_t*>((size_t)base);
+  return *reinterpret_cast<lds_u32x4_t*>(p + off);
+}
 
 // 16 bytes per lane, global -> LDS; lane i lands at lds_wave_base + 16 i.
 // Written as inline asm rather than the compiler builtin: the compiler counts
@@ -162,6 +169,11 @@ TTCD_DEV void store_out(void* o, float* lse, int out_bf16, bool row_ok, size_t o
 // publishes it: group 0 at the end of X(2i-1), group 1 (one segment
 // behind) at the end of its M(2i-1).
 // --------------------------------------------------------------------------
+template <int V>
+struct Int {
+  static constexpr int value = V;
+};
+
 template <int D>
 struct MfmaCfg {
   static constexpr int NB = D / 32;
@@ -365,29 +377,36 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
 
   // LDS operand addresses.  The swizzled chunk of a K row or V^T row is
   // (logical chunk) ^ (per-lane swizzle); the k-step, key-half and sub-block
-  // parts of the logical chunk occupy address bits that no other part uses,
-  // so every fragment address is  uniform base + (lane part ^ constant).
+  // parts of the logical chunk occupy address bits that no other part uses:
   //   K, sub-block x, k-step i:  ring(x) + 32 sb(x) CPR 16 + (klane ^ 32 i)
   //   V^T, MFMA i of PV:         ring(x) + KPOS 16 + 4096 (i/2)
   //                              + (vlane ^ (64 sb(x) + 32 (i%2)))
-  // For K the bases are multiples of the 32-row block (KSB bytes, a power of
-  // two) and klane stays below it; for V^T the bases are multiples of 4 KB
-  // and vlane stays below that.  So the XOR can follow the add: one add per
-  // segment and one XOR per fragment.
+  // (klane stays below the 32-row block of KSB bytes, vlane below 4 KB).  The
+  // registers kl and vl hold ring(x) plus each lane part; the key half and
+  // the V^T region are immediate offsets of the LDS reads, so a fragment
+  // address costs no vector ALU work, and the registers move to the next
+  // ring slot once per tile.
   const uint32_t klane = (uint32_t)(r32 * (TL::CPR * 16) + ((h ^ TL::kswz(r32)) << 4));
   const uint32_t vlane = (uint32_t)(r32 * (BN * 2) + ((h ^ TL::vswz(r32)) << 4));
-  auto ring = [&](int x) { return (uint32_t)(((x >> 1) % NBUF) * TL::BYTES); };
-  auto sbit = [&](int x) { return (x & 1) ? 0 : 1; };
   constexpr int KSB = 32 * TL::CPR * 16;
   static_assert((KSB & (KSB - 1)) == 0 && TL::BYTES % KSB == 0 && 32 * KSTEP <= KSB &&
                 (TL::KPOS * 16) % 4096 == 0 && 32 * BN * 2 <= 4096, "fragment address layout");
-  auto kseg = [&](uint32_t kl, int x) { return kl + ring(x) + (uint32_t)(sbit(x) * KSB); };
-  auto vseg = [&](uint32_t vl, int x) { return vl + ring(x) + (uint32_t)(TL::KPOS * 16); };
-  auto load_k1 = [&](uint32_t kb, int i, bf16x8& dst) {
-    dst = as_bf16x8(lds16(kb ^ (uint32_t)(32 * i)));
+  static_assert(KSB < 65536 && TL::KPOS * 16 + 4096 * (NB - 1) < 65536, "16-bit read offsets");
+  uint32_t kl[KSTEP], vl[2][2];
+#pragma unroll
+  for (int i = 0; i < KSTEP; ++i) kl[i] = klane ^ (uint32_t)(32 * i);
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) vl[sb][e] = vlane ^ (uint32_t)(64 * sb + 32 * e);
+  }
+  // K fragment i of the current tile's sub-block half sb (1: the newer keys)
+  auto load_k1 = [&](int sb, int i, bf16x8& dst) __attribute__((always_inline)) {
+    dst = as_bf16x8(lds16(kl[i], (uint32_t)(sb * KSB)));
   };
-  auto load_v1 = [&](uint32_t vb, int x, int i, bf16x8& dst) {
-    dst = as_bf16x8(lds16((vb ^ (uint32_t)(64 * sbit(x) + 32 * (i & 1))) + 4096 * (i >> 1)));
+  // V^T fragment of MFMA i of the PV of the current tile's half sb
+  auto load_v1 = [&](int sb, int i, bf16x8& dst) __attribute__((always_inline)) {
+    dst = as_bf16x8(lds16(vl[sb][i & 1], (uint32_t)(TL::KPOS * 16 + 4096 * (i >> 1))));
   };
 
   // Tile fetch, 16 bytes per lane straight into LDS, by the four waves of a
@@ -448,17 +467,18 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   // reuses the registers of the fragment the MFMA before it read and has a
   // whole MFMA chain to land.  Sub-blocks the wave skips go through the
   // same code (their P is zero and their scores are not used).
-  auto seg_m = [&](int kk, f32x16& s, int fill) __attribute__((always_inline)) {
+  // SBc: the half of the current tile that sub-block kk is (1: the newer)
+  auto seg_m = [&](auto SBc, f32x16& s, int fill) __attribute__((always_inline)) {
+    constexpr int SB = decltype(SBc)::value;
     // while this wave feeds the matrix cores it takes the issue slots first;
     // the other wave of the SIMD runs its softmax in the gaps
     __builtin_amdgcn_s_setprio(2);
-    const uint32_t kb = kseg(klane, kk), vb = vseg(vlane, kk);
     bf16x8 kf[KSTEP];
 #pragma unroll
     for (int i = 0; i < KSTEP; ++i) {
       acc[i >> 1] = mfma32(vf[i >> 1][i & 1], (i & 1) ? p1 : p0, acc[i >> 1]);
       __builtin_amdgcn_sched_barrier(0);
-      load_k1(kb, i, kf[i]);
+      load_k1(SB, i, kf[i]);
       __builtin_amdgcn_sched_barrier(0);
     }
     // each group refills its part of a ring slot here, between the two
@@ -470,7 +490,7 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
     for (int i = 0; i < KSTEP; ++i) {
       s = mfma32(kf[i], qf[i], s);
       __builtin_amdgcn_sched_barrier(0);
-      load_v1(vb, kk, i, vf[i >> 1][i & 1]);
+      load_v1(SB, i, vf[i >> 1][i & 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
@@ -497,7 +517,7 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
     const int k0 = 2 * it, k1 = k0 + 1;
     const Item i0 = bd.item(j0_of(k0)), i1 = bd.item(j0_of(k1));
     f32x16 s;
-    seg_m(k0, s, -1);
+    seg_m(Int<1>{}, s, -1);
     ring_barrier();
     seg_x(k0, i0, s);
     lds_wait_all();
@@ -505,7 +525,19 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
     // every wave's reads of tile it - 1 completed before the last barrier:
     // each group refills its part of the slot with tile it - 1 + NBUF
     const int fill = it >= 1 && it - 1 + NBUF < NT ? it - 1 + NBUF : -1;
-    seg_m(k1, s, fill);
+    seg_m(Int<0>{}, s, fill);
+    // the operand registers move on to the next tile's ring slot
+    {
+      const uint32_t step = (it + 1) % NBUF == 0 ? (uint32_t)(-(NBUF - 1) * TL::BYTES)
+                                                 : (uint32_t)TL::BYTES;
+#pragma unroll
+      for (int i = 0; i < KSTEP; ++i) kl[i] += step;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        vl[sb][0] += step;
+        vl[sb][1] += step;
+      }
+    }
     // group 1 runs one segment behind, so the barrier after its M(k1) is the
     // one that publishes tile it + 1: its V^T part must have landed
     if (!issuer && it + 1 < NT) {
@@ -527,12 +559,11 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
     lds_wait_all();
     ring_barrier();
   }
-  {
-    // M(K): the PV of the last sub-block
-    f32x16 s;
-    seg_m(K, s, -1);
-    ring_barrier();
-  }
+  // M(K): the PV of the last sub-block
+#pragma unroll
+  for (int i = 0; i < KSTEP; ++i)
+    acc[i >> 1] = mfma32(vf[i >> 1][i & 1], (i & 1) ? p1 : p0, acc[i >> 1]);
+  ring_barrier();
   if (issuer) ring_barrier();                  // group 0's extra barrier
   if (kL == K - 1) {
     // the oldest walked sub-block was the last student one
