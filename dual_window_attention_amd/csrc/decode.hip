@@ -31,33 +31,40 @@ TTCD_DEV void merge_into(float& m, float& l, float* acc, float m2, float l2, con
   m = mn;
 }
 
-template <typename T, int D>
+// G: query heads per kv head (the per-head states are sized for it, so
+// fewer registers and more resident waves when G is small)
+template <typename T, int D, int G>
 __global__ void __launch_bounds__(256)
 decode_attn_split(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                   float* __restrict__ part, int pos, int kv_rows, int Hq, int Hkv, int wT,
                   int wS, float c, int nsplit, int split_len) {
+  static_assert(G >= 1 && G <= GMAX, "query heads per kv head");
   constexpr int LPK = D / 8;           // lanes per key
   constexpr int KPW = 64 / LPK;        // keys per wave step
   constexpr int PS = D + 2;            // floats per partial state
-  __shared__ float red[4][GMAX][2][PS];
-  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int G = Hq / Hkv;
+  __shared__ float red[4][G][2][PS];
+  // the kv heads of one split run next to each other in dispatch order:
+  // together they read whole cache rows (all heads of a token)
+  const uint32_t flat = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int g = (int)(flat % gridDim.y);
+  const int s = (int)((flat / gridDim.y) % gridDim.x);
+  const int b = (int)(flat / (gridDim.y * gridDim.x));
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int dc = lane % LPK, kg = lane / LPK;
   const int jlo = max(0, pos - wT + 1);
   const int ks = jlo + s * split_len;
   const int ke = min(ks + split_len, pos + 1);
 
-  float qv[GMAX][8];
+  float qv[G][8];
 #pragma unroll
-  for (int hh = 0; hh < GMAX; ++hh) {
-    if (hh >= G) break;
+  for (int hh = 0; hh < G; ++hh) {
     const T* qp = q + ((size_t)b * Hq + g * G + hh) * D + dc * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) qv[hh][e] = ldf(qp + e) * c;
   }
-  float mS[GMAX], lS[GMAX], aS[GMAX][8], mF[GMAX], lF[GMAX], aF[GMAX][8];
-  for (int hh = 0; hh < GMAX; ++hh) {
+  float mS[G], lS[G], aS[G][8], mF[G], lF[G], aF[G][8];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
     mS[hh] = mF[hh] = NEG_INF;
     lS[hh] = lF[hh] = 0.f;
 #pragma unroll
@@ -93,20 +100,24 @@ decode_attn_split(const T* __restrict__ q, const T* __restrict__ k, const T* __r
   // kv_rows; a split with no key (ks >= ke) fetches nothing and leaves the
   // empty states (m = -inf, l = 0, acc = 0), which merge exactly.  The host
   // launches no such split, but the kernel does not rely on it.
-  Raw nk, nv;
+  // two key steps in flight: buffer A holds step i, B step i+1; each step,
+  // once unpacked, refills its buffer with the step two ahead
+  Raw ak, av, bk, bv;
   if (ks < ke) {
     const int j = ks + wave * KPW + kg;
-    fetch(j < ke ? j : ks, nk, nv);
+    fetch(j < ke ? j : ks, ak, av);
+    const int j2 = j + 4 * KPW;
+    fetch(j2 < ke ? j2 : ks, bk, bv);
   }
-  for (int j0 = ks + wave * KPW; j0 < ke; j0 += 4 * KPW) {
+  auto step = [&](int j0, Raw& rk, Raw& rv) __attribute__((always_inline)) {
     const int j = j0 + kg;
     const bool ok = j < ke;
     float kv[8], vv[8];
-    unpack(nk, kv);
-    unpack(nv, vv);
+    unpack(rk, kv);
+    unpack(rv, vv);
     {
-      const int jn = j + 4 * KPW;
-      fetch(jn < ke ? jn : ks, nk, nv);       // ks < ke inside the loop
+      const int jn = j + 8 * KPW;
+      fetch(jn < ke ? jn : ks, rk, rv);       // ks < ke inside the loop
     }
     if (!ok) {
 #pragma unroll
@@ -123,8 +134,7 @@ decode_attn_split(const T* __restrict__ q, const T* __restrict__ k, const T* __r
       m = mn;
     };
 #pragma unroll
-    for (int hh = 0; hh < GMAX; ++hh) {
-      if (hh >= G) break;
+    for (int hh = 0; hh < G; ++hh) {
       float sc = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) sc = __builtin_fmaf(qv[hh][e], kv[e], sc);
@@ -136,12 +146,16 @@ decode_attn_split(const T* __restrict__ q, const T* __restrict__ k, const T* __r
       else
         upd(mF[hh], lF[hh], aF[hh], sc);
     }
+  };
+  for (int j0 = ks + wave * KPW; j0 < ke; j0 += 8 * KPW) {
+    step(j0, ak, av);
+    if (j0 + 4 * KPW >= ke) break;
+    step(j0 + 4 * KPW, bk, bv);
   }
   // merge the key groups inside the wave (lanes with equal dc)
   for (int o = LPK; o < 64; o <<= 1) {
 #pragma unroll
-    for (int hh = 0; hh < GMAX; ++hh) {
-      if (hh >= G) break;
+    for (int hh = 0; hh < G; ++hh) {
       float m2 = __shfl_xor(mS[hh], o, 64), l2 = __shfl_xor(lS[hh], o, 64), a2[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) a2[e] = __shfl_xor(aS[hh][e], o, 64);
@@ -155,8 +169,7 @@ decode_attn_split(const T* __restrict__ q, const T* __restrict__ k, const T* __r
   }
   if (kg == 0) {
 #pragma unroll
-    for (int hh = 0; hh < GMAX; ++hh) {
-      if (hh >= G) break;
+    for (int hh = 0; hh < G; ++hh) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         red[wave][hh][0][2 + dc * 8 + e] = aS[hh][e];
@@ -427,9 +440,19 @@ dense_apply(const float* __restrict__ S, const T* __restrict__ z, float* __restr
   if (a >= d) return;
   const float* sr = S + ((size_t)b * d + a) * f;
   float acc = 0.f;
-  for (int c = lane * 4; c < f; c += 256) {
-    f32x4 v = *reinterpret_cast<const f32x4*>(sr + c);
-    acc += v[0] * zs[c] + v[1] * zs[c + 1] + v[2] * zs[c + 2] + v[3] * zs[c + 3];
+  // four 16-byte reads of the row in flight per lane before they are used
+  for (int c0 = lane * 4; c0 < f; c0 += 1024) {
+    f32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + 256 * u;
+      v[u] = c < f ? *reinterpret_cast<const f32x4*>(sr + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + 256 * u;
+      if (c < f) acc += v[u][0] * zs[c] + v[u][1] * zs[c + 1] + v[u][2] * zs[c + 2] + v[u][3] * zs[c + 3];
+    }
   }
   acc = wave_sum(acc);
   if (lane == 0) {
@@ -458,6 +481,21 @@ size_t decode_attn_part_bytes(int B, int Hq, int D, int nsplit) {
   return (size_t)B * Hq * nsplit * 2 * (D + 2) * sizeof(float);
 }
 
+template <typename T, int D>
+void launch_split_g(const DecodeAttnArgs& a, int G, dim3 grid, float c, int ns, hipStream_t s) {
+#define TTCD_SPLIT(GG)                                                                          \
+  hipLaunchKernelGGL((decode_attn_split<T, D, GG>), grid, dim3(256), 0, s, (const T*)a.q,       \
+                     (const T*)a.k, (const T*)a.v, a.part, a.pos, a.kv_rows, a.Hq, a.Hkv, a.wT, \
+                     a.wS, c, ns, a.split_len)
+  switch (G) {
+    case 1: TTCD_SPLIT(1); break;
+    case 2: TTCD_SPLIT(2); break;
+    case 3: TTCD_SPLIT(3); break;
+    default: TTCD_SPLIT(4); break;
+  }
+#undef TTCD_SPLIT
+}
+
 hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   if (G > GMAX) return hipErrorInvalidValue;
@@ -468,22 +506,14 @@ hipError_t launch_decode_attn(const DecodeAttnArgs& a, hipStream_t s) {
   dim3 grid(ns, a.Hkv, a.B);
   if (a.in_dt == BF16) {
     if (a.D == 64)
-      hipLaunchKernelGGL((decode_attn_split<bf16_t, 64>), grid, dim3(256), 0, s,
-                         (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, a.part,
-                         a.pos, a.kv_rows, a.Hq, a.Hkv, a.wT, a.wS, c, ns, a.split_len);
+      launch_split_g<bf16_t, 64>(a, G, grid, c, ns, s);
     else
-      hipLaunchKernelGGL((decode_attn_split<bf16_t, 128>), grid, dim3(256), 0, s,
-                         (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, a.part,
-                         a.pos, a.kv_rows, a.Hq, a.Hkv, a.wT, a.wS, c, ns, a.split_len);
+      launch_split_g<bf16_t, 128>(a, G, grid, c, ns, s);
   } else {
     if (a.D == 64)
-      hipLaunchKernelGGL((decode_attn_split<float, 64>), grid, dim3(256), 0, s,
-                         (const float*)a.q, (const float*)a.k, (const float*)a.v, a.part,
-                         a.pos, a.kv_rows, a.Hq, a.Hkv, a.wT, a.wS, c, ns, a.split_len);
+      launch_split_g<float, 64>(a, G, grid, c, ns, s);
     else
-      hipLaunchKernelGGL((decode_attn_split<float, 128>), grid, dim3(256), 0, s,
-                         (const float*)a.q, (const float*)a.k, (const float*)a.v, a.part,
-                         a.pos, a.kv_rows, a.Hq, a.Hkv, a.wT, a.wS, c, ns, a.split_len);
+      launch_split_g<float, 128>(a, G, grid, c, ns, s);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
