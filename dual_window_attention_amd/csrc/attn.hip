@@ -46,12 +46,11 @@ constexpr float LN2 = 0.69314718055994530942f;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) const u32x4 lds_u32x4_t;
 
-// 16-byte LDS read at a byte address.  The MFMA kernel has no static LDS, so
-// its dynamic LDS starts at address 0 and an offset into it is the address.
-TTCD_DEV u32x4 lds16(uint32_t addr) { return *reinterpret_cast<lds_u32x4_t*>((size_t)addr); }
 typedef __attribute__((address_space(3))) const char lds_char_t;
-// the same at a register address plus a constant byte offset, written as
-// pointer arithmetic so that the offset lands in the read's offset field
+// 16-byte LDS read at a register byte address plus a constant byte offset,
+// written as pointer arithmetic so that the offset lands in the read's
+// offset field.  The MFMA kernel has no static LDS, so its dynamic LDS
+// starts at address 0 and an offset into it is the address.
 TTCD_DEV u32x4 lds16(uint32_t base, uint32_t off) {
   lds_char_t* p = reinterpret_cast<lds_char_t*>((size_t)base);
   return *reinterpret_cast<lds_u32x4_t*>(p + off);
