@@ -862,8 +862,11 @@ hipError_t run_fw_backward(int B, int T, int d, int f, int C, int kc, float eps,
     return e;
   if ((e = launch_transpose(fw.m, w.mt, d, f, f, d, 1, 0, 0, (int)es, s)) != hipSuccess) return e;
   if ((e = launch_transpose(w0, w.w0t, d, f, f, d, 1, 0, 0, (int)es, s)) != hipSuccess) return e;
-  // R^T unscaled (fp32, [d, B*TC]), R token-major, and the forward's scaled R~^T
-  if ((e = launch_fill(w.rtu, (long)d * cols, 0.f, F32, s)) != hipSuccess) return e;
+  // R^T unscaled (fp32, [d, B*TC]), R token-major, and the forward's scaled R~^T.
+  // The GEMM writes columns [0, T) of each sequence; its padding columns
+  // [T, TC) are zeroed so that the buffer holds no stale values.
+  if ((e = launch_fill2d(w.rtu + T, d, TC - T, cols, B, TC, 0.f, F32, s)) != hipSuccess)
+    return e;
   g = GemmArgs{};
   g.A = fw.m; g.lda = f; g.B = fw.dbar; g.ldb = f; g.C = w.rtu; g.ldc = cols;
   g.M = d; g.N = T; g.K = f; g.in_dt = dt; g.out_dt = F32; g.epi = EPI_STORE;
@@ -929,8 +932,12 @@ hipError_t run_fw_backward(int B, int T, int d, int f, int C, int kc, float eps,
       (e = launch_transpose(w.g, w.gt, d, f, f, d, B * N, df, df, (int)es, s)) != hipSuccess)
     return e;
   // (5) P_j = G_j K_j^T (unscaled) for the chunks with a later chunk, stored
-  //     as P^T [d, B*TC]; dbeta_j = <R_j, P_j>, dR = beta P
-  if ((e = launch_fill(w.pt, (long)d * cols, 0.f, F32, s)) != hipSuccess) return e;
+  //     as P^T [d, B*TC]; dbeta_j = <R_j, P_j>, dR = beta P.  The GEMMs write
+  //     the columns of the chunks with a later chunk; the last chunk's (P = 0)
+  //     and the padding are zeroed.
+  if ((e = launch_fill2d(w.pt + (long)nstates * C, d, TC - (long)nstates * C, cols, B, TC, 0.f,
+                         F32, s)) != hipSuccess)
+    return e;
   if (nstates > 0) {
     for (int b = 0; b < B; ++b) {
       g = GemmArgs{};
@@ -953,8 +960,11 @@ hipError_t run_fw_backward(int B, int T, int d, int f, int C, int kc, float eps,
       hipSuccess)
     return e;
   if ((e = launch_convert(w.pt, w.drt, (long)d * cols, dt, s)) != hipSuccess) return e;
-  // (6) dK_t = G_j^T r_t (unscaled; the last chunk's rows stay zero)
-  if ((e = launch_fill(w.dk, BT * f, 0.f, F32, s)) != hipSuccess) return e;
+  // (6) dK_t = G_j^T r_t (unscaled); the GEMMs write the rows of the chunks
+  //     with a later chunk, the last chunk's rows are zeroed
+  if ((e = launch_fill2d(w.dk + (long)nstates * C * f, T - (long)nstates * C, f, f, B, (long)T * f,
+                         0.f, F32, s)) != hipSuccess)
+    return e;
   if (nstates > 0) {
     for (int b = 0; b < B; ++b) {
       g = GemmArgs{};

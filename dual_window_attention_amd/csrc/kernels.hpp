@@ -138,6 +138,10 @@ hipError_t launch_fw_decode_append(const DecodeAppendArgs& a, hipStream_t s);
 // on-policy recurrence: s32 = float(w0); per chunk s32 += dw, s16 = s32 (dt)
 hipError_t launch_state_init(const void* w0, float* s32, long n, int dt, hipStream_t s);
 hipError_t launch_fill(void* p, long n, float v, int dt, hipStream_t s);
+// a strided 2-D region: p[b * bstride + r * ld + c] = v, r < rows, c < width,
+// b < nbatch (a no-op for an empty region)
+hipError_t launch_fill2d(void* p, long rows, long width, long ld, int nbatch, long bstride,
+                         float v, int dt, hipStream_t s);
 hipError_t launch_splitk_reduce(const float* part, int nsplit, long zstride, int ldp,
                                 const float* colscale, void* out, long ldo, int M, int N, int dt,
                                 hipStream_t s);

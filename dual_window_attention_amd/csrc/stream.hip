@@ -318,6 +318,16 @@ __global__ void __launch_bounds__(256) fill_kernel(T* __restrict__ p, long n, fl
   if (i < n) elem<T>::st(p + i, v);
 }
 
+// p[b * bstride + r * ld + c] = v for r < rows, c < width, b = blockIdx.y
+template <typename T>
+__global__ void __launch_bounds__(256)
+fill2d_kernel(T* __restrict__ p, long rows, long width, long ld, long bstride, float v) {
+  const long n = rows * width;
+  T* pb = p + (long)blockIdx.y * bstride;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256)
+    elem<T>::st(pb + (i / width) * ld + i % width, v);
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256)
 state_step_kernel(const float* __restrict__ dw, int nsplit, float* __restrict__ s32,
@@ -639,6 +649,21 @@ hipError_t launch_fill(void* p, long n, float v, int dt, hipStream_t s) {
     hipLaunchKernelGGL((fill_kernel<bf16_t>), grid, dim3(256), 0, s, (bf16_t*)p, n, v);
   else
     hipLaunchKernelGGL((fill_kernel<float>), grid, dim3(256), 0, s, (float*)p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill2d(void* p, long rows, long width, long ld, int nbatch, long bstride,
+                         float v, int dt, hipStream_t s) {
+  const long n = rows * width;
+  if (n <= 0 || nbatch <= 0) return hipSuccess;
+  const long nb = (n + 255) / 256;
+  const dim3 grid((unsigned)(nb < 4096 ? nb : 4096), (unsigned)nbatch);
+  if (dt == BF16)
+    hipLaunchKernelGGL((fill2d_kernel<bf16_t>), grid, dim3(256), 0, s, (bf16_t*)p, rows, width,
+                       ld, bstride, v);
+  else
+    hipLaunchKernelGGL((fill2d_kernel<float>), grid, dim3(256), 0, s, (float*)p, rows, width, ld,
+                       bstride, v);
   return hipGetLastError();
 }
 
