@@ -954,12 +954,17 @@ hipError_t run_fw_backward(int B, int T, int d, int f, int C, int kc, float eps,
       }
     }
   }
-  if ((e = launch_dbeta(w.rtu, w.pt, beta, w.dbpart, dbeta, B, d, C, T, TC, N, s)) != hipSuccess)
-    return e;
-  if ((e = launch_to_token_major(w.pt, F32, w.drtok, dt, B, T, TC, d, nullptr, C, N, s)) !=
+  // dbeta, and dR^T = beta P^T straight into the gradient's type (columns
+  // t < T; the padding columns are zeroed: they are summed over in dM)
+  if ((e = launch_dbeta(w.rtu, w.pt, beta, w.dbpart, dbeta, w.drt, dt, B, d, C, T, TC, N, s)) !=
       hipSuccess)
     return e;
-  if ((e = launch_convert(w.pt, w.drt, (long)d * cols, dt, s)) != hipSuccess) return e;
+  if ((e = launch_fill2d((char*)w.drt + (size_t)T * es, d, TC - T, cols, B, TC, 0.f, dt, s)) !=
+      hipSuccess)
+    return e;
+  if ((e = launch_to_token_major(w.drt, dt, w.drtok, dt, B, T, TC, d, nullptr, C, N, s)) !=
+      hipSuccess)
+    return e;
   // (6) dK_t = G_j^T r_t (unscaled); the GEMMs write the rows of the chunks
   //     with a later chunk, the last chunk's rows are zeroed
   if ((e = launch_fill2d(w.dk + (long)nstates * C * f, T - (long)nstates * C, f, f, B, (long)T * f,

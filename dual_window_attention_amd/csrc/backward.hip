@@ -104,11 +104,12 @@ split_bf16_kernel(const float* __restrict__ x, bf16_t* __restrict__ hi, bf16_t* 
 // dbeta partials and the scaled residual gradient: for sequence b, chunk j
 // and a group of 16 rows a of P^T [d, B * TC] (P_j = G_j K_j^T, unscaled):
 //   part[b][j][group] = sum_{a in group} sum_{t in C_j} R^T[a][t] P^T[a][t]
-//   dR^T[a][t] = beta_j P^T[a][t]   (in place)
+//   dR^T[a][t] = beta_j P^T[a][t], written in the gradient's type (OutT)
+template <typename OutT>
 __global__ void __launch_bounds__(256)
-dbeta_part_kernel(const float* __restrict__ rt, float* __restrict__ pt,
-                  const float* __restrict__ beta, float* __restrict__ part, int d, int chunk,
-                  int Tn, int TC, int nch) {
+dbeta_part_kernel(const float* __restrict__ rt, const float* __restrict__ pt,
+                  const float* __restrict__ beta, float* __restrict__ part,
+                  OutT* __restrict__ drt, int d, int chunk, int Tn, int TC, int nch) {
   const int grp = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const size_t ld = (size_t)gridDim.z * TC;
   const float bj = beta[(size_t)b * nch + j];
@@ -122,7 +123,7 @@ dbeta_part_kernel(const float* __restrict__ rt, float* __restrict__ pt,
       const size_t i = (size_t)a * ld + (size_t)b * TC + t;
       const float p = pt[i];
       s = __builtin_fmaf(rt[i], p, s);
-      pt[i] = bj * p;
+      stf(drt + i, bj * p);
     }
   }
   __shared__ float red[4];
@@ -447,11 +448,16 @@ hipError_t launch_split_bf16(const float* x, void* hi, void* lo, long n, hipStre
 
 size_t dbeta_part_floats(int B, int nch, int d) { return (size_t)B * nch * ((d + 15) / 16); }
 
-hipError_t launch_dbeta(const float* rt, float* pt, const float* beta, float* part, float* dbeta,
-                        int B, int d, int chunk, int T, int TC, int nch, hipStream_t s) {
+hipError_t launch_dbeta(const float* rt, const float* pt, const float* beta, float* part,
+                        float* dbeta, void* drt, int drt_dt, int B, int d, int chunk, int T,
+                        int TC, int nch, hipStream_t s) {
   const int ngrp = (d + 15) / 16;
-  hipLaunchKernelGGL(dbeta_part_kernel, dim3(ngrp, nch, B), dim3(256), 0, s, rt, pt, beta, part,
-                     d, chunk, T, TC, nch);
+  if (drt_dt == BF16)
+    hipLaunchKernelGGL(dbeta_part_kernel<bf16_t>, dim3(ngrp, nch, B), dim3(256), 0, s, rt, pt,
+                       beta, part, (bf16_t*)drt, d, chunk, T, TC, nch);
+  else
+    hipLaunchKernelGGL(dbeta_part_kernel<float>, dim3(ngrp, nch, B), dim3(256), 0, s, rt, pt,
+                       beta, part, (float*)drt, d, chunk, T, TC, nch);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int total = B * nch;

@@ -218,8 +218,9 @@ hipError_t launch_sum_slices_to(const float* parts, void* out, long n, int S, in
 hipError_t launch_split_bf16(const float* x, void* hi, void* lo, long n, hipStream_t s);
 // dbeta [B, nch] = per-chunk <R^T, P^T>; P^T *= beta (in place); rt, pt fp32 [d, B * TC]
 size_t dbeta_part_floats(int B, int nch, int d);
-hipError_t launch_dbeta(const float* rt, float* pt, const float* beta, float* part, float* dbeta,
-                        int B, int d, int chunk, int T, int TC, int nch, hipStream_t s);
+hipError_t launch_dbeta(const float* rt, const float* pt, const float* beta, float* part,
+                        float* dbeta, void* drt, int drt_dt, int B, int d, int chunk, int T,
+                        int TC, int nch, hipStream_t s);
 // kd [B * T] = beta_{c(t)} (khat_t . dk_t)
 hipError_t launch_key_dot(const void* khat, const float* dk, const float* beta, float* kd, int B,
                           int T, int f, int chunk, int nch, int dt, hipStream_t s);
