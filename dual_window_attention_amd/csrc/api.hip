@@ -877,17 +877,14 @@ hipError_t run_fw_backward(int B, int T, int d, int f, int C, int kc, float eps,
     g.res_dt = F32; g.sRes = TC;
     if ((e = launch_gemm(g, s)) != hipSuccess) return e;
   }
-  g = GemmArgs{};
-  g.A = fw.dbar; g.lda = f; g.B = fw.m; g.ldb = f; g.C = w.rtok; g.ldc = d;
-  g.M = T; g.N = d; g.K = f; g.in_dt = dt; g.out_dt = dt; g.epi = EPI_STORE;
-  g.batch = B; g.sA = (long)Tpad * f; g.sB = 0; g.sC = (long)T * d;
-  if ((e = launch_gemm(g, s)) != hipSuccess) return e;
-  g = GemmArgs{};
-  g.A = fw.m; g.lda = f; g.B = fw.dbar; g.ldb = f; g.C = fw.rst; g.ldc = Tpad;
-  g.M = d; g.N = Tpad; g.K = f; g.in_dt = dt; g.out_dt = dt; g.epi = EPI_STORE;
-  g.colscale = fw.sc; g.batch = B; g.sA = 0; g.sB = (long)Tpad * f; g.sC = (long)d * Tpad;
-  g.sScale = Tpad;
-  if ((e = launch_gemm(g, s)) != hipSuccess) return e;
+  // R token-major and the forward's write-scaled R~^T: the same product, so
+  // both come from R^T (fp32, with the remainder of M when it is split)
+  // rather than from two more GEMMs
+  if ((e = launch_to_token_major(w.rtu, F32, w.rtok, dt, B, T, TC, d, nullptr, C, N, s)) !=
+      hipSuccess)
+    return e;
+  if ((e = launch_scaled_rt(w.rtu, fw.sc, fw.rst, dt, d, T, TC, Tpad, B, s)) != hipSuccess)
+    return e;
   // (2) the weights in force, transposed: S_i^T = W0^T + sum_{j<i} dW_j^T,
   //     dW_j^T = Zbar_S,j R~_j^T (the forward's chunk writes, operands swapped)
   const int nstates = N - 1;

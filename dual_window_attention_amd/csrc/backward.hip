@@ -31,6 +31,20 @@ scale_token_cols_kernel(T* __restrict__ x, const float* __restrict__ s, int rows
   stf(x + i, v);
 }
 
+// out[b][a][t] = R^T[a][b * TC + t] * s[b * Tpad + t] for t < T, 0 for
+// T <= t < Tpad: the forward's write-scaled R~^T (one row of d per
+// workgroup column) from the unscaled fp32 R^T
+template <typename T>
+__global__ void __launch_bounds__(256)
+scaled_rt_kernel(const float* __restrict__ rt, const float* __restrict__ s, T* __restrict__ out,
+                 int Tn, int TC, int Tpad, int B) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= Tpad) return;
+  const int a = blockIdx.y, b = blockIdx.z;
+  const float v = t < Tn ? rt[((size_t)a * B + b) * TC + t] * s[(size_t)b * Tpad + t] : 0.f;
+  stf(out + ((size_t)b * gridDim.y + a) * Tpad + t, v);
+}
+
 // Exclusive suffix sums of the chunk gradients, per sequence:
 //   G_j = sum_{i > j} dS_i  (element type),  total += sum_i dS_i  (fp32,
 // summed over the batch).  Each thread owns 4 consecutive entries and walks
@@ -391,6 +405,19 @@ hipError_t launch_to_token_major(const void* in, int in_dt, void* out, int out_d
   // out[b][t][f] = in[f][b * TC + t] * (scale ? scale[b * n + t / chunk] : 1)
   return launch_transpose64(in, in_dt, (long)B * TC, TC, F, T, out, out_dt, F, (long)T * F, F, B,
                             scale, n, scale ? chunk : 1, s);
+}
+
+hipError_t launch_scaled_rt(const float* rt, const float* sc, void* out, int out_dt, int d, int T,
+                            int TC, int Tpad, int B, hipStream_t s) {
+  if (d <= 0 || B <= 0 || Tpad <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((Tpad + 255) / 256), (unsigned)d, (unsigned)B);
+  if (out_dt == BF16)
+    hipLaunchKernelGGL(scaled_rt_kernel<bf16_t>, grid, dim3(256), 0, s, rt, sc, (bf16_t*)out, T, TC,
+                       Tpad, B);
+  else
+    hipLaunchKernelGGL(scaled_rt_kernel<float>, grid, dim3(256), 0, s, rt, sc, (float*)out, T, TC,
+                       Tpad, B);
+  return hipGetLastError();
 }
 
 hipError_t launch_scale_token_cols(void* x, const float* sc, int rows, int B, int T, int TC,

@@ -201,6 +201,10 @@ hipError_t launch_to_feature_major(const void* in, void* out, int B, int T, int 
 hipError_t launch_to_token_major(const void* in, int in_dt, void* out, int out_dt, int B, int T,
                                  int TC, int F, const float* scale, int chunk, int n,
                                  hipStream_t s);
+// out [B, d, Tpad] = R^T [d, B * TC] (fp32) times s[b * Tpad + t], zero for
+// t >= T (the forward's write-scaled residual, from the unscaled fp32 one)
+hipError_t launch_scaled_rt(const float* rt, const float* sc, void* out, int out_dt, int d, int T,
+                            int TC, int Tpad, int B, hipStream_t s);
 // x [rows, B * TC] *= s[b * Tpad + t] (zero for t >= T)
 hipError_t launch_scale_token_cols(void* x, const float* sc, int rows, int B, int T, int TC,
                                    int Tpad, int dt, hipStream_t s);
