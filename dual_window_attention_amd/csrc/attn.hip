@@ -30,7 +30,10 @@
 //     Rows whose far band is empty finish with bit-identical teacher and
 //     student results.
 //   * Lazy rescaling: the running max only moves when a new score exceeds
-//     it by more than 2^8; the result is unchanged up to rounding.
+//     it by more than 2^8; the result is unchanged up to rounding.  The
+//     softmax segment does not sum its terms: the wave adds them to the
+//     denominator in fp32 between its next MFMAs, and the rescale test is
+//     one exponent bit of the packed bf16 terms.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -100,12 +103,15 @@ struct Tile {
   static TTCD_DEV int vswz(int d) { return (d >> 1) & 7; }
 };
 
+// The running max m is held TAU - 1 above the scaled row max it was last
+// raised to, so every term 2^(s c - m) starts at most 2^-(TAU-1); a term
+// that reaches 2 (its score exceeds the row max by TAU) raises m.
 struct SoftState {
-  float m;      // running max (log2 domain, scaled)
-  float l;      // this lane's partial denominator
-  float negm;   // -m, or 0 while m = -inf (the exponent offset)
-  float thr;    // 2^TAU, or -1 while m = -inf: a sub-block sum above it
-                // raises m (lazy rescale)
+  float m;          // running max plus TAU - 1 (log2 domain, scaled)
+  float l, l2;      // this lane's partial denominator, two interleaved sums
+  float negm;       // -m, or 0 while m = -inf (the exponent offset)
+  uint32_t force;   // the exponent bits of a packed bf16 term >= 2 while
+                    // m = -inf (forces the first raise), else 0
 };
 
 // O = acc / l and LSE = ln 2 (m + log2 l) of the lane's row; o or lse may be
@@ -114,7 +120,8 @@ struct SoftState {
 template <int NB>
 TTCD_DEV void store_out(void* o, float* lse, int out_bf16, bool row_ok, size_t obase, size_t li,
                         const SoftState& st, const f32x16* acc, int h) {
-  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.l), __float_as_uint(st.l),
+  const float lp = st.l + st.l2;
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lp), __float_as_uint(lp),
                                                    false, false);
   const float l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -224,51 +231,68 @@ TTCD_DEV void mask32(f32x16& s, int t, int j0, int h, int lo, int hi) {
   }
 }
 
-// 2^(s c + negm) of this lane's 16 scores, stage by stage (sixteen
-// independent fma -> exp chains), and their fp32 sum
-TTCD_DEV float exp_sum16(const f32x16& s, float c, float negm, f32x16& x) {
+// 2^(s c + negm) of this lane's 16 scores (sixteen independent fma -> exp
+// chains), and the terms packed to bf16 for the PV product
+TTCD_DEV void exp_pack16(const f32x16& s, float c, float negm, f32x16& x, bf16x8& p0,
+                         bf16x8& p1) {
 #pragma unroll
   for (int v = 0; v < 16; ++v) x[v] = __builtin_fmaf(s[v], c, negm);
 #pragma unroll
   for (int v = 0; v < 16; ++v) x[v] = fast_exp2(x[v]);
-  float la = x[0], lb = x[1];
-#pragma unroll
-  for (int v = 2; v < 16; v += 2) {
-    la += x[v];
-    lb += x[v + 1];
-  }
-  return la + lb;
-}
-
-// P = 2^(s c - m) in bf16 and its fp32 sum into the denominator, against the
-// running max m as it stands.  The rescale is lazy and needs no row max in
-// the common case: only when some lane's sum exceeds 2^TAU (then one of its
-// terms exceeds 2^TAU / 16, or overflowed), or the lane has no finite max
-// yet, does the wave raise m to the sub-block's row max, rescale its
-// accumulators and recompute the terms.  Every term used is therefore at
-// most 2^TAU.
-template <int NB>
-TTCD_DEV void softmax_p(const f32x16& s, float c, SoftState& st, f32x16* acc, bf16x8& p0,
-                        bf16x8& p1) {
-  f32x16 x;
-  float sum = exp_sum16(s, c, st.negm, x);
-  if (__builtin_expect(__any(sum > st.thr), 0)) {
-    const float mnew = fmaxf(st.m, row_max32(s) * c);
-    const float alpha = (st.m == NEG_INF) ? 0.f : fast_exp2(st.m - mnew);
-    st.l *= alpha;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] *= alpha;
-    st.m = mnew;
-    st.negm = mnew == NEG_INF ? 0.f : -mnew;
-    st.thr = mnew == NEG_INF ? -1.f : __builtin_exp2f(TAU);
-    sum = exp_sum16(s, c, st.negm, x);
-  }
 #pragma unroll
   for (int v = 0; v < 8; ++v) {
     p0[v] = (__bf16)x[v];
     p1[v] = (__bf16)x[v + 8];
   }
-  st.l += sum;
+}
+
+// Whether some packed bf16 term is >= 2 (or +inf/NaN): the terms are not
+// negative, so that is the top exponent bit of either half of some word.
+TTCD_DEV bool any_ge2(const bf16x8& p0, const bf16x8& p1, uint32_t force) {
+  const u32x4 a = __builtin_bit_cast(u32x4, p0), b = __builtin_bit_cast(u32x4, p1);
+  const uint32_t o = (a[0] | a[1] | a[2]) | (a[3] | b[0] | b[1]) | (b[2] | b[3] | force);
+  return (o & 0x40004000u) != 0u;
+}
+
+// P = 2^(s c - m) in bf16 for the PV product and in fp32 (x) for the
+// denominator, against the running max m as it stands; the denominator sum
+// is left to the matrix segment (den_add).  The rescale is lazy and needs no
+// row max in the common case: only when some term of the wave reaches 2
+// (a score more than 2^TAU above the max m was last raised for), or a lane
+// has no finite max yet, does the wave raise m to the sub-block's row max
+// plus TAU - 1, rescale its accumulators and recompute the terms.
+template <int NB>
+TTCD_DEV void softmax_p(const f32x16& s, float c, SoftState& st, f32x16* acc, f32x16& x,
+                        bf16x8& p0, bf16x8& p1) {
+  exp_pack16(s, c, st.negm, x, p0, p1);
+  if (__builtin_expect(__any(any_ge2(p0, p1, st.force)), 0)) {
+    const float mnew = fmaxf(st.m, row_max32(s) * c + (TAU - 1.f));
+    const float alpha = (st.m == NEG_INF) ? 0.f : fast_exp2(st.m - mnew);
+    st.l *= alpha;
+    st.l2 *= alpha;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] *= alpha;
+    st.m = mnew;
+    st.negm = mnew == NEG_INF ? 0.f : -mnew;
+    st.force = mnew == NEG_INF ? 0x4000u : 0u;
+    exp_pack16(s, c, st.negm, x, p0, p1);
+  }
+}
+
+// Terms v0 .. v0+N-1 of a sub-block's fp32 P into the two denominator sums.
+// The empty asm takes both sums as operands at this point, so the compiler
+// keeps the adds here (between the MFMAs of the matrix segment) instead of
+// sinking them towards their first use, in front of the next softmax.
+template <int N>
+TTCD_DEV void den_add(SoftState& st, const f32x16& x, int v0) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    if ((v0 + j) & 1)
+      st.l2 += x[v0 + j];
+    else
+      st.l += x[v0 + j];
+  }
+  asm volatile("" : "+v"(st.l), "+v"(st.l2));
 }
 
 // How this wave takes the sub-block of 32 keys starting at j0 in the walk:
@@ -359,7 +383,7 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
   f32x16 acc[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) acc[i] = zero16();
-  SoftState st = {NEG_INF, 0.f, 0.f, -1.f};
+  SoftState st = {NEG_INF, 0.f, 0.f, 0.f, 0x4000u};
 
   const bf16_t* kbase = k + ((size_t)b * kv_rows * Hkv + g) * D;
   const size_t kstride = (size_t)Hkv * D;
@@ -456,12 +480,14 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
 
   bf16x8 vf[NB][2];        // V^T fragments of the sub-block whose PV comes next
   bf16x8 p0, p1;           // its P (zero when the wave skips it)
+  f32x16 px = zero16();    // the same terms in fp32, for the denominator
 #pragma unroll
   for (int v = 0; v < 8; ++v) p0[v] = p1[v] = (__bf16)0.f;
 #pragma unroll
   for (int i = 0; i < NB; ++i) vf[i][0] = vf[i][1] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
 
-  // M(kk): PV(kk-1) with the K fragments of sub-block kk loaded behind it,
+  // M(kk): PV(kk-1) with the K fragments of sub-block kk loaded behind it
+  // and the terms of P(kk-1) added to the denominator between the MFMAs,
   // then QK(kk) with the V^T fragments of kk loaded behind it: each load
   // reuses the registers of the fragment the MFMA before it read and has a
   // whole MFMA chain to land.  Sub-blocks the wave skips go through the
@@ -478,12 +504,9 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
       acc[i >> 1] = mfma32(vf[i >> 1][i & 1], (i & 1) ? p1 : p0, acc[i >> 1]);
       __builtin_amdgcn_sched_barrier(0);
       load_k1(SB, i, kf[i]);
+      den_add<16 / KSTEP>(st, px, i * (16 / KSTEP));
       __builtin_amdgcn_sched_barrier(0);
     }
-    // each group refills its part of a ring slot here, between the two
-    // MFMA chains
-    if (fill >= 0) issue(fill);
-    __builtin_amdgcn_sched_barrier(0);
     s = zero16();
 #pragma unroll
     for (int i = 0; i < KSTEP; ++i) {
@@ -492,6 +515,10 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
       load_v1(SB, i, vf[i >> 1][i & 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // each group refills its part of a ring slot here, behind the MFMA
+    // chains (a branch before them would split the block and let the
+    // compiler move the second chain behind its loads)
+    if (fill >= 0) issue(fill);
     __builtin_amdgcn_s_setprio(0);
   };
   // X(kk): the student output right after PV(kL) (P(kL+1) is not in yet),
@@ -502,10 +529,11 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
       store_out<NB>(o_s, lse_s, out_bf16, row_ok, obase, li, st, acc, h);
     if (ic.act) {
       if (ic.masked) mask32(s, t, j0_of(kk), h, ic.lo, ic.hi);
-      softmax_p<NB>(s, c, st, acc, p0, p1);
+      softmax_p<NB>(s, c, st, acc, px, p0, p1);
     } else {
 #pragma unroll
       for (int v = 0; v < 8; ++v) p0[v] = p1[v] = (__bf16)0.f;
+      px = zero16();
     }
   };
 
@@ -562,6 +590,7 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
 #pragma unroll
   for (int i = 0; i < KSTEP; ++i)
     acc[i >> 1] = mfma32(vf[i >> 1][i & 1], (i & 1) ? p1 : p0, acc[i >> 1]);
+  den_add<16>(st, px, 0);
   ring_barrier();
   if (issuer) ring_barrier();                  // group 0's extra barrier
   if (kL == K - 1) {
@@ -593,7 +622,8 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
 #pragma unroll
       for (int i = 0; i < KSTEP; ++i) s = mfma32(kf[i], qf[i], s);
       mask32(s, t, j0, h, wS, wT);
-      softmax_p<NB>(s, c, st, acc, p0, p1);
+      softmax_p<NB>(s, c, st, acc, px, p0, p1);
+      den_add<16>(st, px, 0);
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb) {
         acc[bb] = mfma32(vf[bb][0], p0, acc[bb]);
