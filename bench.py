@@ -65,6 +65,92 @@ def measured_traffic(part):
         return None
 
 
+TRAFFIC_HEADER = """\
+# HBM traffic per launch on the 64K Qwen3 layer workload (rocprofv3 --pmc)
+#
+# Two counter passes, each its own run, from /tmp with TMPDIR=/tmp (R = repository root):
+#   rocprofv3 --pmc FETCH_SIZE --kernel-include-regex "ttcd|copyBuffer" --output-format csv -d <dir> -o FETCH_SIZE -- python3 R/bench.py --steps 1 --warmup 0 --no-decode --no-variants --no-extra --no-backward --cpu-sample 0 --calib-copy
+#   rocprofv3 --pmc WRITE_SIZE --kernel-include-regex "ttcd|copyBuffer" --output-format csv -d <dir> -o WRITE_SIZE -- python3 R/bench.py --steps 1 --warmup 0 --no-decode --no-variants --no-extra --no-backward --cpu-sample 0 --calib-copy
+# then: python3 R/bench.py --write-traffic <dir>/FETCH_SIZE_counter_collection.csv <dir>/WRITE_SIZE_counter_collection.csv
+#
+# Scaling: the same counters on the plain 1 GiB device-to-device copy that --calib-copy runs
+# (__amd_rocclr_copyBuffer, the largest grid of that kernel): FETCH_SIZE {cf:.0f} KiB, WRITE_SIZE {cw:.0f} KiB for
+# 1048576 KiB read and written, so bytes = FETCH_SIZE KiB x 1024 x {ff:.5f} and WRITE_SIZE KiB x 1024 x {fw:.5f}.
+# FETCH_SIZE counts what L2 requests from the memory side, so Infinity Cache hits are included.
+# bench.py reports bytes_per_launch as roofline.traffic while sources_sha256 matches the sources.
+"""
+
+# (section, comment, [(short name, kernel-name substring, grid)], algorithmic bytes)
+TRAFFIC_PARTS = [
+    ("attention",
+     "ttcd_dual_window_attn: V^T prologue + dual-window kernel (bf16 O, no LSE); "
+     "algorithmic = Q,K,V read + O_T,O_S written",
+     [("vt", "v_transpose_kernel", "4194304"), ("attn", "dual_window_attn_mfma", "2097152")],
+     2 * 65536 * (16 + 8 + 8 + 16 + 16) * 128),
+    ("scan",
+     "fw_stream2_kernel (the key-scale reduction adds 6 MB); algorithmic = 8 B T f",
+     [("stream", "fw_stream2_kernel", "6291456")],
+     8 * 65536 * 3072),
+]
+
+
+def write_traffic(fetch_csv, write_csv, out_path=TRAFFIC_FILE):
+    """Write the per-launch HBM traffic summary from the two counter passes
+    (FETCH_SIZE and WRITE_SIZE, KiB per dispatch), each scaled by what the
+    same counter reads for the 1 GiB copy of the calibration run."""
+    import csv
+
+    def per_dispatch(path, counter):
+        rows = []
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                grid = row["Grid_Size"] if "Grid_Size" in row else "x".join(
+                    row.get(f"Grid_Size_{a}", "?") for a in "XYZ")
+                rows.append((row["Kernel_Name"], grid, float(row["Counter_Value"])))
+        return rows
+
+    fetch = per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = per_dispatch(write_csv, "WRITE_SIZE")
+
+    def calib(rows):
+        copies = [(int(g), v) for n, g, v in rows if "copyBuffer" in n and g.isdigit()]
+        if not copies:
+            raise SystemExit("no copyBuffer dispatch in the counter file (run with --calib-copy)")
+        big = max(g for g, _ in copies)
+        return float(np.mean([v for g, v in copies if g == big]))
+
+    cf, cw = calib(fetch), calib(write)
+    ff, fw = 1048576.0 / cf, 1048576.0 / cw
+    out = [TRAFFIC_HEADER.format(cf=cf, cw=cw, ff=ff, fw=fw)]
+    for sec, comment, kernels, alg in TRAFFIC_PARTS:
+        lines = [f"[{sec}]", f"# {comment}", "kernels: " + ", ".join(k for k, _, _ in kernels)]
+        rd = wr = 0.0
+        counts = []
+        body = []
+        for short, sub, grid in kernels:
+            fv = [v for n, g, v in fetch if sub in n and g == grid]
+            wv = [v for n, g, v in write if sub in n and g == grid]
+            if not fv or not wv:
+                raise SystemExit(f"no {sub} dispatch at grid {grid} in the counter files")
+            counts.append(min(len(fv), len(wv)))
+            body.append(f"fetch_kib_per_dispatch_{short}: {np.mean(fv):.0f}")
+            body.append(f"write_kib_per_dispatch_{short}: {np.mean(wv):.0f}")
+            rd += np.mean(fv) * 1024 * ff
+            wr += np.mean(wv) * 1024 * fw
+        lines.append(f"dispatches: {min(counts)}")
+        lines += body
+        lines += [f"read_bytes_per_launch: {rd:.4e}", f"write_bytes_per_launch: {wr:.4e}",
+                  f"bytes_per_launch: {rd + wr:.4e}", f"algorithmic_bytes_per_launch: {alg:.4e}",
+                  f"traffic_over_algorithmic: {(rd + wr) / alg:.2f}",
+                  f"sources_sha256: {source_digest(TRAFFIC_SOURCES[sec])}", ""]
+        out.append("\n".join(lines))
+    with open(out_path, "w") as f:
+        f.write("\n".join(out))
+    print(f"wrote {out_path}")
+
+
 def attention_flops(cfg, wT):
     """Algorithmic flops: 4*D per (query, key) pair inside the teacher
     window (2D for QK^T, 2D for PV); the student band is a subset of it."""
@@ -584,12 +670,18 @@ def main():
     ap.add_argument("--dispatches", metavar="REGEX",
                     help="with --summarize-trace: list the dispatches of the kernels matching "
                          "REGEX in issue order")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM traffic summary under profiles/ from the FETCH_SIZE and "
+                         "WRITE_SIZE counter collections of the calibration run, and exit")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (a reference "
                          "kernel of known traffic for scaling memory counters)")
     args = ap.parse_args()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.dispatches)
+        return
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only (no collectives); "
