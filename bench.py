@@ -74,7 +74,7 @@ TRAFFIC_HEADER = """\
 # then: python3 R/bench.py --write-traffic <dir>/FETCH_SIZE_counter_collection.csv <dir>/WRITE_SIZE_counter_collection.csv
 #
 # Scaling: the same counters on the plain 1 GiB device-to-device copy that --calib-copy runs
-# (__amd_rocclr_copyBuffer, the largest grid of that kernel): FETCH_SIZE {cf:.0f} KiB, WRITE_SIZE {cw:.0f} KiB for
+# (__amd_rocclr_copyBuffer, the largest copy of the run): FETCH_SIZE {cf:.0f} KiB, WRITE_SIZE {cw:.0f} KiB for
 # 1048576 KiB read and written, so bytes = FETCH_SIZE KiB x 1024 x {ff:.5f} and WRITE_SIZE KiB x 1024 x {fw:.5f}.
 # FETCH_SIZE counts what L2 requests from the memory side, so Infinity Cache hits are included.
 # bench.py reports bytes_per_launch as roofline.traffic while sources_sha256 matches the sources.
@@ -115,11 +115,12 @@ def write_traffic(fetch_csv, write_csv, out_path=TRAFFIC_FILE):
     write = per_dispatch(write_csv, "WRITE_SIZE")
 
     def calib(rows):
-        copies = [(int(g), v) for n, g, v in rows if "copyBuffer" in n and g.isdigit()]
+        # the 1 GiB calibration copy is the largest copy of the run (the
+        # stream's copy ceiling runs smaller copies at the same grid)
+        copies = [v for n, g, v in rows if "copyBuffer" in n]
         if not copies:
             raise SystemExit("no copyBuffer dispatch in the counter file (run with --calib-copy)")
-        big = max(g for g, _ in copies)
-        return float(np.mean([v for g, v in copies if g == big]))
+        return float(max(copies))
 
     cf, cw = calib(fetch), calib(write)
     ff, fw = 1048576.0 / cf, 1048576.0 / cw
