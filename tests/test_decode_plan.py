@@ -2,10 +2,13 @@
 
 The decode kernel splits the teacher window of one query at position pos
 into pieces of split_len keys; each piece's four waves step through its keys
-KPW at a time, fetching one key step ahead.  This replays the host's choice
-of split count and every row index a lane fetches, and checks that each
-fetched row lies in the window [max(0, pos - w_T + 1), pos], so inside a
-cache of pos + 1 rows, and that every launched split holds a key.
+KPW at a time with two key steps in flight (the prologue fetches the first
+two steps, each step then refills its buffer with the step two ahead), and
+every fetch index is clamped to the split's first key when it would leave
+the split.  This replays the host's choice of split count and every row
+index a lane fetches, and checks that each fetched row lies in the window
+[max(0, pos - w_T + 1), pos], so inside a cache of pos + 1 rows, and that
+every launched split holds a key.
 """
 import pytest
 
@@ -30,6 +33,10 @@ def fetched_rows(w_t: int, pos: int, head_dim: int):
     kpw = 64 // lpk                   # keys per wave step
     jlo = max(0, pos - w_t + 1)
     rows = set()
+
+    def fetch(j, ks, ke):
+        rows.add(j if j < ke else ks)
+
     for s in range(ns):
         ks = jlo + s * sl
         ke = min(ks + sl, pos + 1)
@@ -37,12 +44,15 @@ def fetched_rows(w_t: int, pos: int, head_dim: int):
         for wave in range(4):
             for kg in range(kpw):
                 j = ks + wave * kpw + kg
-                rows.add(j if j < ke else ks)            # the prologue fetch
+                fetch(j, ks, ke)                         # prologue: step 0
+                fetch(j + 4 * kpw, ks, ke)               # and step 1
                 j0 = ks + wave * kpw
                 while j0 < ke:
-                    jn = j0 + kg + 4 * kpw               # one step ahead
-                    rows.add(jn if jn < ke else ks)
-                    j0 += 4 * kpw
+                    fetch(j0 + kg + 8 * kpw, ks, ke)     # step(j0) refills two ahead
+                    if j0 + 4 * kpw >= ke:
+                        break
+                    fetch(j0 + 4 * kpw + kg + 8 * kpw, ks, ke)
+                    j0 += 8 * kpw
     return rows, jlo
 
 
