@@ -1399,8 +1399,12 @@ ttcd_status ttcd_fastweight_fold(const ttcd_fw_desc* d, const void* w_down0, con
   void* rst = p.take((size_t)B * dm * rows * dsize(dt));
   void* kt = p.take((size_t)B * f * rows * dsize(dt));
   if (n_chunks > 0) {
-    HIPCHK(launch_transpose_scale(r_list, rst, (int)rows, dm, B, beta_list, C, n_chunks, dt, s));
-    HIPCHK(launch_transpose_scale(k_list, kt, (int)rows, f, B, nullptr, 1, 0, dt, s));
+    // Rs^T[b][c][r] = R[b][r][c] beta[b][r / C] and K^T[b][c][r] = K[b][r][c]
+    HIPCHK(launch_transpose64(r_list, dt, dm, (long)rows * dm, (int)rows, dm, rst, dt, rows,
+                              (long)dm * rows, (int)rows, B, nullptr, 0, 1, s, beta_list,
+                              n_chunks, C));
+    HIPCHK(launch_transpose64(k_list, dt, f, (long)rows * f, (int)rows, f, kt, dt, rows,
+                              (long)f * rows, (int)rows, B, nullptr, 0, 1, s));
   }
   if (n_chunks > 0) {
     // state_out[b] = W0 + Rs^T[b] K^T[b]^T: one GEMM over all list rows, W0 as residual

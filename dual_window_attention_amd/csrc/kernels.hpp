@@ -151,20 +151,17 @@ size_t fw_stream_part_bytes(int B, int T, int f);
 
 // out [cols, rows] = in [rows, cols]^T (per batch), 2- or 4-byte elements
 // out[z][c][r] = in[z][r][c] * (scale ? scale[z * s_scale + c / scale_div] : 1)
-// for r < in_rows, c < in_cols (dtypes in_dt -> out_dt); output columns
-// in_rows <= r < out_cols are written as zero
+//                            * (rscale ? rscale[z * s_rscale + r / rscale_div] : 1)
+// for r < in_rows, c < in_cols (dtypes in_dt -> out_dt), one rounding to the
+// output type; output columns in_rows <= r < out_cols are written as zero
 hipError_t launch_transpose64(const void* in, int in_dt, long ld_in, long s_in, int in_rows,
                               int in_cols, void* out, int out_dt, long ld_out, long s_out,
                               int out_cols, int batch, const float* scale, long s_scale,
-                              int scale_div, hipStream_t s);
+                              int scale_div, hipStream_t s, const float* rscale = nullptr,
+                              long s_rscale = 0, int rscale_div = 1);
 hipError_t launch_transpose(const void* in, void* out, int rows, int cols, long ld_in,
                             long ld_out, int batch, long s_in, long s_out, int esize,
                             hipStream_t s);
-// out[b] [cols, rows] = in[b] [rows, cols]^T, row r scaled by
-// scale[b * nscale + r / rows_per_scale] when scale is given
-hipError_t launch_transpose_scale(const void* in, void* out, int rows, int cols, int batch,
-                                  const float* scale, int rows_per_scale, int nscale, int dt,
-                                  hipStream_t s);
 // V [B, kv_rows, Hkv, D] (bf16) -> vt [B, Hkv, D, vt_ld]: keys in [jlo, Tk), the
 // keys of each 16-group permuted for the attention kernel's MFMA operand reads
 

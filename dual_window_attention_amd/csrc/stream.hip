@@ -449,6 +449,7 @@ rmsnorm_kernel(const float* __restrict__ h, const GT* __restrict__ gamma, OutT* 
 
 // --------------------------------------------------------------- transposes
 // out[z][c][r] = in[z][r][c] * (scale ? scale[z * s_scale + c / scale_div] : 1)
+//                            * (rscale ? rscale[z * s_rscale + r / rscale_div] : 1)
 // for r < in_rows, c < in_cols; output columns in_rows <= r < out_cols are
 // written as zero.  One 64 x 64 tile per workgroup through LDS (fp32, padded
 // rows), eight consecutive elements per thread and access (16 bytes for bf16)
@@ -457,7 +458,8 @@ template <typename TI, typename TO>
 __global__ void __launch_bounds__(256)
 transpose64_kernel(const TI* __restrict__ in, long ld_in, long s_in, int in_rows, int in_cols,
                    TO* __restrict__ out, long ld_out, long s_out, int out_cols,
-                   const float* __restrict__ scale, long s_scale, int scale_div) {
+                   const float* __restrict__ scale, long s_scale, int scale_div,
+                   const float* __restrict__ rscale, long s_rscale, int rscale_div) {
   __shared__ float tile[64][65];
   const int z = blockIdx.z;
   const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
@@ -490,6 +492,11 @@ transpose64_kernel(const TI* __restrict__ in, long ld_in, long s_in, int in_rows
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] = (r < in_rows && c + j < in_cols) ? ldf(src + j) : 0.f;
     }
+    if (rscale && r < in_rows) {
+      const float rs = rscale[z * s_rscale + r / rscale_div];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] *= rs;
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) tile[lr][tc + j] = v[j];
   }
@@ -516,33 +523,6 @@ transpose64_kernel(const TI* __restrict__ in, long ld_in, long s_in, int in_rows
       for (int j = 0; j < 8; ++j)
         if (r + j < out_cols) stf(dst + j, v[j]);
     }
-  }
-}
-
-// out[b][c][r] = in[b][r][c] * (scale ? scale[b * nscale + r / rows_per_scale] : 1)
-template <typename T>
-__global__ void __launch_bounds__(256)
-transpose_scale_kernel(const T* __restrict__ in, T* __restrict__ out, int rows, int cols,
-                       const float* __restrict__ scale, int rows_per_scale, int nscale) {
-  __shared__ float tile[32][33];
-  const int z = blockIdx.z;
-  const long r0 = (long)blockIdx.x * 32, c0 = (long)blockIdx.y * 32;
-  const T* ip = in + (size_t)z * rows * cols;
-  T* op = out + (size_t)z * rows * cols;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  for (int i = ty; i < 32; i += 8) {
-    const long r = r0 + i, c = c0 + tx;
-    float v = 0.f;
-    if (r < rows && c < cols) {
-      v = ldf(ip + r * cols + c);
-      if (scale) v *= scale[(size_t)z * nscale + r / rows_per_scale];
-    }
-    tile[i][tx] = v;
-  }
-  __syncthreads();
-  for (int i = ty; i < 32; i += 8) {
-    const long c = c0 + i, r = r0 + tx;
-    if (c < cols && r < rows) stf(op + c * rows + r, tile[tx][i]);
   }
 }
 
@@ -751,14 +731,15 @@ hipError_t launch_rmsnorm(const float* h, const void* gamma, void* u, int rows, 
 hipError_t launch_transpose64(const void* in, int in_dt, long ld_in, long s_in, int in_rows,
                               int in_cols, void* out, int out_dt, long ld_out, long s_out,
                               int out_cols, int batch, const float* scale, long s_scale,
-                              int scale_div, hipStream_t s) {
+                              int scale_div, hipStream_t s, const float* rscale, long s_rscale,
+                              int rscale_div) {
   if (in_rows <= 0 || in_cols <= 0 || batch <= 0) return hipSuccess;
-  if (out_cols < in_rows || scale_div < 1) return hipErrorInvalidValue;
+  if (out_cols < in_rows || scale_div < 1 || rscale_div < 1) return hipErrorInvalidValue;
   dim3 grid((out_cols + 63) / 64, (in_cols + 63) / 64, batch);
 #define TTCD_T64(TI, TO)                                                                         \
   hipLaunchKernelGGL((transpose64_kernel<TI, TO>), grid, dim3(256), 0, s, (const TI*)in, ld_in,  \
                      s_in, in_rows, in_cols, (TO*)out, ld_out, s_out, out_cols, scale, s_scale,   \
-                     scale_div)
+                     scale_div, rscale, s_rscale, rscale_div)
   if (in_dt == BF16 && out_dt == BF16) TTCD_T64(bf16_t, bf16_t);
   else if (in_dt == BF16) TTCD_T64(bf16_t, float);
   else if (out_dt == BF16) TTCD_T64(float, bf16_t);
@@ -774,19 +755,6 @@ hipError_t launch_transpose(const void* in, void* out, int rows, int cols, long 
   const int dt = esize == 2 ? BF16 : F32;
   return launch_transpose64(in, dt, ld_in, s_in, rows, cols, out, dt, ld_out, s_out, rows,
                             batch > 0 ? batch : 1, nullptr, 0, 1, s);
-}
-
-hipError_t launch_transpose_scale(const void* in, void* out, int rows, int cols, int batch,
-                                  const float* scale, int rows_per_scale, int nscale, int dt,
-                                  hipStream_t s) {
-  dim3 grid((rows + 31) / 32, (cols + 31) / 32, batch);
-  if (dt == BF16)
-    hipLaunchKernelGGL(transpose_scale_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)in,
-                       (bf16_t*)out, rows, cols, scale, rows_per_scale, nscale);
-  else
-    hipLaunchKernelGGL(transpose_scale_kernel<float>, grid, dim3(256), 0, s, (const float*)in,
-                       (float*)out, rows, cols, scale, rows_per_scale, nscale);
-  return hipGetLastError();
 }
 
 hipError_t launch_add(const float* a, const float* b, float* out, long n, hipStream_t s) {
