@@ -48,37 +48,55 @@ scaled_rt_kernel(const float* __restrict__ rt, const float* __restrict__ s, T* _
 // Exclusive suffix sums of the chunk gradients, per sequence:
 //   G_j = sum_{i > j} dS_i  (element type),  total += sum_i dS_i  (fp32,
 // summed over the batch).  Each thread owns 4 consecutive entries and walks
-// the chunks from the last, the running sum in fp32.  dS arrives in fp32;
-// G is stored as g (the operand dtype) and, for bf16, also as the remainder
-// g_lo = bf16(G - g), so that a product with g + g_lo carries G to about
-// fp32 accuracy.
+// the chunks from the last, 8 loads in flight at a time, the running sum in
+// fp32.  dS arrives in fp32; G is stored as g (the operand dtype) and, for
+// bf16, also as the remainder g_lo = bf16(G - g), so that a product with
+// g + g_lo carries G to about fp32 accuracy.  Each 4-entry group is written
+// with one access.
 template <typename T>
 __global__ void __launch_bounds__(256)
 chunk_suffix_kernel(const float* __restrict__ ds, T* __restrict__ g, T* __restrict__ g_lo,
                     float* __restrict__ total, long n, int nch, int B) {
+  typedef T T4 __attribute__((ext_vector_type(4)));
   const long e = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
   if (e >= n) return;
   float tot[4] = {0.f, 0.f, 0.f, 0.f};
   for (int b = 0; b < B; ++b) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int j = nch - 1; j >= 0; --j) {
-      const size_t off = ((size_t)b * nch + j) * n + e;
+    for (int j0 = nch - 1; j0 >= 0; j0 -= 8) {
+      f32x4 v[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        T hv;
-        stf(&hv, acc[i]);
-        g[off + i] = hv;
-        if (g_lo) stf(g_lo + off + i, acc[i] - ldf(&hv));
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 - u;
+        if (j >= 0) v[u] = *reinterpret_cast<const f32x4*>(ds + ((size_t)b * nch + j) * n + e);
       }
-      const f32x4 v = *reinterpret_cast<const f32x4*>(ds + off);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] += v[i];
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 - u;
+        if (j < 0) break;
+        const size_t off = ((size_t)b * nch + j) * n + e;
+        T4 hv, lo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          T h;
+          stf(&h, acc[i]);
+          hv[i] = h;
+          if (g_lo) {
+            T l;
+            stf(&l, acc[i] - ldf(&h));
+            lo[i] = l;
+          }
+        }
+        *reinterpret_cast<T4*>(g + off) = hv;
+        if (g_lo) *reinterpret_cast<T4*>(g_lo + off) = lo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += v[u][i];
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) tot[i] += acc[i];
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) total[e + i] = tot[i];
+  *reinterpret_cast<f32x4*>(total + e) = f32x4{tot[0], tot[1], tot[2], tot[3]};
 }
 
 // out[i] = sum_z parts[z][i], z in a fixed order (the K slices of a product)
