@@ -133,6 +133,59 @@ attn_bwd_meta_kernel(const T* __restrict__ o_t, const T* __restrict__ o_s,
   }
 }
 
+// The same row data for bf16 rows of D = 64 or 128: D / 8 lanes per row, one
+// 16-byte load of each of O_T, O_S, dO_T, dO_S per lane, the dot products
+// reduced over those lanes only; 64 / (D / 8) rows per wave.
+template <int D>
+__global__ void __launch_bounds__(256)
+attn_bwd_meta_vec_kernel(const bf16_t* __restrict__ o_t, const bf16_t* __restrict__ o_s,
+                         const bf16_t* __restrict__ do_t, const bf16_t* __restrict__ do_s,
+                         const float* __restrict__ lse_t, const float* __restrict__ lse_s,
+                         float* __restrict__ meta, int Tn, int Hq, int Hkv, int nblk,
+                         long nrows) {
+  constexpr int LPR = D / 8, RPW = 64 / LPR;
+  const int lane = threadIdx.x & 63;
+  const int sub = lane % LPR;
+  const long id = ((long)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / LPR;
+  if (id >= nrows) return;                 // whole row groups: the lanes of a row agree
+  const int G = Hq / Hkv;
+  const int R = Tn * G;
+  const long per = (long)nblk * 32;
+  const int x = (int)(id % per);
+  const int bg = (int)(id / per);
+  const int g = bg % Hkv, b = bg / Hkv;
+  float dt = 0.f, dsum = 0.f;
+  size_t li = 0;
+  if (x < R) {
+    const int t = x / G, hq = g * G + x % G;
+    const size_t off = ((size_t)(b * Tn + t) * Hq + hq) * D + 8 * sub;
+    const u32x4 a = ld16(do_t + off), c = ld16(o_t + off);
+    const u32x4 e = ld16(do_s + off), f = ld16(o_s + off);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      dt = __builtin_fmaf(__uint_as_float(a[j] << 16), __uint_as_float(c[j] << 16), dt);
+      dt = __builtin_fmaf(__uint_as_float(a[j] & 0xFFFF0000u),
+                          __uint_as_float(c[j] & 0xFFFF0000u), dt);
+      dsum = __builtin_fmaf(__uint_as_float(e[j] << 16), __uint_as_float(f[j] << 16), dsum);
+      dsum = __builtin_fmaf(__uint_as_float(e[j] & 0xFFFF0000u),
+                            __uint_as_float(f[j] & 0xFFFF0000u), dsum);
+    }
+    li = ((size_t)b * Hq + hq) * Tn + t;
+  }
+#pragma unroll
+  for (int o = LPR / 2; o >= 1; o >>= 1) {
+    dt += __shfl_xor(dt, o, 64);
+    dsum += __shfl_xor(dsum, o, 64);
+  }
+  if (sub == 0) {
+    float* m = meta + ((size_t)bg * nblk + x / 32) * 128 + x % 32;
+    m[0] = x < R ? lse_t[li] * LOG2E : POS_INF;
+    m[32] = x < R ? lse_s[li] * LOG2E : POS_INF;
+    m[64] = dt;
+    m[96] = dsum;
+  }
+}
+
 // Transposed copy of a [B, T, H, D] array, per kv group: out[b][g][d][c] =
 // in row perm16-stored (c) of the group, where row x = (position x / G, head
 // g G + x % G); rows >= rows_valid are zero.  For K (G = 1, H = Hkv) the rows
@@ -867,7 +920,20 @@ hipError_t launch_dual_window_attn_backward(const AttnBwdArgs& a, const AttnBwdB
   {
     const long nrows = (long)a.B * a.Hkv * nmeta * 32;
     dim3 grid((unsigned)((nrows + 3) / 4));
-    if (a.in_dt == BF16)
+    if (a.in_dt == BF16 && (a.D == 64 || a.D == 128)) {
+      const int rows_per_block = 4 * (64 / (a.D / 8));
+      const dim3 vgrid((unsigned)((nrows + rows_per_block - 1) / rows_per_block));
+      if (a.D == 64)
+        hipLaunchKernelGGL(attn_bwd_meta_vec_kernel<64>, vgrid, dim3(256), 0, s,
+                           (const bf16_t*)a.o_t, (const bf16_t*)a.o_s, (const bf16_t*)a.do_t,
+                           (const bf16_t*)a.do_s, a.lse_t, a.lse_s, w.meta, a.T, a.Hq, a.Hkv,
+                           nmeta, nrows);
+      else
+        hipLaunchKernelGGL(attn_bwd_meta_vec_kernel<128>, vgrid, dim3(256), 0, s,
+                           (const bf16_t*)a.o_t, (const bf16_t*)a.o_s, (const bf16_t*)a.do_t,
+                           (const bf16_t*)a.do_s, a.lse_t, a.lse_s, w.meta, a.T, a.Hq, a.Hkv,
+                           nmeta, nrows);
+    } else if (a.in_dt == BF16)
       hipLaunchKernelGGL(attn_bwd_meta_kernel<bf16_t>, grid, dim3(256), 0, s,
                          (const bf16_t*)a.o_t, (const bf16_t*)a.o_s, (const bf16_t*)a.do_t,
                          (const bf16_t*)a.do_s, a.lse_t, a.lse_s, w.meta, a.T, a.Hq, a.Hkv, a.D,
