@@ -591,11 +591,55 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
     lds_wait_all();
     ring_barrier();
   }
+  // The far part of the (at most two) sub-blocks at the w_S edge comes from
+  // global memory at the end (keys with w_S <= t - j < w_T that the walk
+  // left out).  Their operand loads are issued early: the first edge
+  // sub-block's right after the last PV product (before the closing
+  // barriers), the second's before the first one's products, so that their
+  // latency overlaps other work.
+  const bool edge0 = wT > wS && j0_lastS <= bd.b_w - wS;
+  const bool edge1 = wT > wS && j0_lastS + 32 <= bd.b_w - wS;
+  auto load_edge_k = [&](int j0, bf16x8* kf) __attribute__((always_inline)) {
+    const int j = min(max(j0 + r32, jlo), jhi);
+    const bf16_t* kp = kbase + (size_t)j * kstride + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < KSTEP; ++ks) kf[ks] = as_bf16x8(ld16(kp + 16 * ks));
+  };
+  auto load_edge_v = [&](int j0, bf16x8 (*ve)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      const bf16_t* vp = vbase + (size_t)(32 * bb + r32) * vt_ld + j0 + 8 * h;
+      ve[bb][0] = as_bf16x8(ld16(vp));
+      ve[bb][1] = as_bf16x8(ld16(vp + 16));
+    }
+  };
+  auto edge_qk = [&](const bf16x8* kf) __attribute__((always_inline)) {
+    f32x16 s = zero16();
+#pragma unroll
+    for (int i = 0; i < KSTEP; ++i) s = mfma32(kf[i], qf[i], s);
+    return s;
+  };
+  auto edge_pv = [&](int j0, f32x16& s, const bf16x8 (*ve)[2]) __attribute__((always_inline)) {
+    mask32(s, t, j0, h, wS, wT);
+    softmax_p<NB>(s, c, st, acc, px, p0, p1);
+    den_add<16>(st, px, 0);
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      acc[bb] = mfma32(ve[bb][0], p0, acc[bb]);
+      acc[bb] = mfma32(ve[bb][1], p1, acc[bb]);
+    }
+  };
+
   // M(K): the PV of the last sub-block
 #pragma unroll
   for (int i = 0; i < KSTEP; ++i)
     acc[i >> 1] = mfma32(vf[i >> 1][i & 1], (i & 1) ? p1 : p0, acc[i >> 1]);
   den_add<16>(st, px, 0);
+  bf16x8 kf0[KSTEP], ve0[NB][2];
+  if (edge0) {
+    load_edge_k(j0_lastS, kf0);
+    load_edge_v(j0_lastS, ve0);
+  }
   ring_barrier();
   if (issuer) ring_barrier();                  // group 0's extra barrier
   if (kL == K - 1) {
@@ -603,37 +647,18 @@ dual_window_attn_mfma(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k
     store_out<NB>(o_s, lse_s, out_bf16, row_ok, obase, li, st, acc, h);
   }
 
-  // ---- far part of the (at most two) sub-blocks at the w_S edge, from
-  // global memory: keys with w_S <= t - j < w_T that the walk left out
-  if (wT > wS) {
-#pragma unroll 1
-    for (int e = 0; e < 2; ++e) {
-      const int j0 = j0_lastS + 32 * e;
-      if (j0 > bd.b_w - wS) continue;
-      bf16x8 kf[KSTEP];
-      {
-        const int j = min(max(j0 + r32, jlo), jhi);
-        const bf16_t* kp = kbase + (size_t)j * kstride + 8 * h;
-#pragma unroll
-        for (int ks = 0; ks < KSTEP; ++ks) kf[ks] = as_bf16x8(ld16(kp + 16 * ks));
-#pragma unroll
-        for (int bb = 0; bb < NB; ++bb) {
-          const bf16_t* vp = vbase + (size_t)(32 * bb + r32) * vt_ld + j0 + 8 * h;
-          vf[bb][0] = as_bf16x8(ld16(vp));
-          vf[bb][1] = as_bf16x8(ld16(vp + 16));
-        }
-      }
-      f32x16 s = zero16();
-#pragma unroll
-      for (int i = 0; i < KSTEP; ++i) s = mfma32(kf[i], qf[i], s);
-      mask32(s, t, j0, h, wS, wT);
-      softmax_p<NB>(s, c, st, acc, px, p0, p1);
-      den_add<16>(st, px, 0);
-#pragma unroll
-      for (int bb = 0; bb < NB; ++bb) {
-        acc[bb] = mfma32(vf[bb][0], p0, acc[bb]);
-        acc[bb] = mfma32(vf[bb][1], p1, acc[bb]);
-      }
+  if (edge0) {
+    // the second edge sub-block's K fragments load behind the first one's
+    // QK product, its V^T fragments (into vf, free after the last PV)
+    // behind the first one's softmax and PV
+    f32x16 s = edge_qk(kf0);
+    bf16x8 kf1[KSTEP];
+    if (edge1) load_edge_k(j0_lastS + 32, kf1);
+    edge_pv(j0_lastS, s, ve0);
+    if (edge1) {
+      load_edge_v(j0_lastS + 32, vf);
+      s = edge_qk(kf1);
+      edge_pv(j0_lastS + 32, s, vf);
     }
   }
   store_out<NB>(o_t, lse_t, out_bf16, row_ok, obase, li, st, acc, h);
