@@ -408,6 +408,21 @@ def decode_bench(dev, n):
                      "algorithmic_gb": gb, "achieved_gbs": gb / (ms * 1e-3),
                      "hbm_frac": gb / (ms * 1e-3) / PEAK_HBM_GBS}
         assert torch.isfinite(out).all().item()
+        # the same step captured once in a HIP graph and replayed (the
+        # library's calls are kernel launches only, so they capture whole)
+        try:
+            ref = out.clone()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                step()
+            gms = time_events(graph.replay, n, stream, warmup=3)
+            torch.cuda.synchronize()
+            res[form].update({"graph_ms_per_step": gms, "graph_tokens_per_s": B / (gms * 1e-3),
+                              "graph_hbm_frac": gb / (gms * 1e-3) / PEAK_HBM_GBS,
+                              "graph_equals_eager": bool(torch.equal(out, ref))})
+            del graph
+        except RuntimeError as e:       # report, keep the rest of the run
+            res[form]["graph_error"] = str(e)[:200]
     # a generation step that also extends the fast weight: the dense-state
     # decode step returning both paths' Z, then the token's (r, k) appended
     # to the pending chunk (conv over a history of kc-1 rows per path)
