@@ -1229,13 +1229,33 @@ ttcd_status layer_forward_run(const ttcd_layer_desc* d, const ttcd_layer_weights
     g.A = b.o[0]; g.lda = HD; g.B = wt->w_o; g.ldb = HD; g.C = b.h[0]; g.ldc = dm;
     g.M = (int)(2 * BT); g.N = dm; g.K = HD; g.in_dt = dt; g.out_dt = F32; g.epi = EPI_RESIDUAL;
     g.res = x; g.ldr = dm; g.res_rows = (int)BT; g.res_dt = dt; g.batch = 1;
-    HIPCHK(launch_gemm(g, s));
-    HIPCHK(launch_rmsnorm(b.h[0], wt->rms_gamma, b.u, (int)(2 * BT), dm, rms_eps, dt, dt, s));
-    g = GemmArgs{};
-    g.A = b.u; g.lda = dm; g.B = wt->w_gate; g.B2 = wt->w_up; g.ldb = dm; g.C = b.z[0];
-    g.ldc = f; g.M = (int)(2 * BT); g.N = f; g.K = dm; g.in_dt = dt; g.out_dt = dt;
-    g.epi = EPI_SWIGLU; g.batch = 1;
-    HIPCHK(launch_gemm(g, s));
+    GemmArgs g2{};
+    g2.A = b.u; g2.lda = dm; g2.B = wt->w_gate; g2.B2 = wt->w_up; g2.ldb = dm; g2.C = b.z[0];
+    g2.ldc = f; g2.M = (int)(2 * BT); g2.N = f; g2.K = dm; g2.in_dt = dt; g2.out_dt = dt;
+    g2.epi = EPI_SWIGLU; g2.batch = 1;
+    // RMSNorm inside the two products where both run on full 256 x 256
+    // tiles: RMSNorm(h) W^T = rs_t (h * gamma) W^T with rs_t a per-row scale,
+    // so the output projection's epilogue writes h * gamma (bf16) and the
+    // row's partial sums of squares, and the SwiGLU epilogue scales both
+    // accumulators by rs_t.  The scale and the partials sit in b.y, which a
+    // prefill does not otherwise use.
+    GemmArgs gn = g;
+    gn.epi = EPI_RESNORM;
+    const bool fuse_norm = dt == BF16 && dm % 64 == 0 && gemm_wide_full(gn) &&
+                           gemm_wide_full(g2) && BT * dm >= 2 * BT * (dm / 64 + 1);
+    if (fuse_norm) {
+      float* rs = b.y;
+      float* rowss = b.y + 2 * BT;
+      gn.U = b.u; gn.gamma = wt->rms_gamma; gn.rowss = rowss;
+      HIPCHK(launch_gemm(gn, s));
+      HIPCHK(launch_rms_rowscale(rowss, (int)(2 * BT), dm, rms_eps, rs, s));
+      g2.rowscale = rs;
+      HIPCHK(launch_gemm(g2, s));
+    } else {
+      HIPCHK(launch_gemm(g, s));
+      HIPCHK(launch_rmsnorm(b.h[0], wt->rms_gamma, b.u, (int)(2 * BT), dm, rms_eps, dt, dt, s));
+      HIPCHK(launch_gemm(g2, s));
+    }
   }
   for (int path = 0; path < 2 && !joint; ++path) {
     if (dec && path != main && !(path == 0 ? aux->z_teacher : aux->z_student)) continue;

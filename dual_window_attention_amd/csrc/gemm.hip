@@ -635,7 +635,11 @@ gemm_nt_wide(GemmArgs g) {
   const int lane = tid & 63;
   const int wm = wave >> 2, wn = wave & 3;
   const int h = lane >> 5, r = lane & 31;
-  constexpr bool swiglu = EPI == EPI_SWIGLU;
+  // EPI_RESNORM is the residual epilogue plus the RMSNorm pieces
+  constexpr int E = EPI == EPI_RESNORM ? EPI_RESIDUAL : EPI == EPI_SWIGLU_RS ? EPI_SWIGLU : EPI;
+  constexpr bool NORM = EPI == EPI_RESNORM;
+  constexpr bool RS = EPI == EPI_SWIGLU_RS;
+  constexpr bool swiglu = E == EPI_SWIGLU;
   const int ncols = swiglu ? BN / 2 : BN;                   // output columns per tile
   const int ntn = (g.N + ncols - 1) / ncols;
   const int ntm = (g.M + BM - 1) / BM;
@@ -777,12 +781,24 @@ gemm_nt_wide(GemmArgs g) {
   constexpr int npieces = 32 * per_row;
   const long nw0 = swiglu ? n0 + 32 * wn : n0 + 64 * wn;
   const bool full_tile = m0 + BM - 1 <= mmax && n0 + ncols - 1 <= nmax;
+  const int c4l_n = 4 * (lane % per_row);
   const float* res = (const float*)g.res;
   const bf16_t* resb = (const bf16_t*)g.res;
   const bool res_bf16 = g.res_dt == BF16;
   const float* cscale = g.colscale ? g.colscale + z * g.sScale : nullptr;
+  const float* rsc = g.rowscale;   // read by the EPI_SWIGLU_RS copy only
+  // RMSNorm pieces: a lane's 4 columns are fixed over the epilogue, so is
+  // its gamma; the 16 lanes of a row piece hold its 64 columns
+  f32x4 gam = {1.f, 1.f, 1.f, 1.f};
+  if constexpr (NORM) {
+    if (g.gamma) {
+      const uint2 gu = *reinterpret_cast<const uint2*>((const bf16_t*)g.gamma + nw0 + c4l_n);
+      gam = f32x4{__uint_as_float(gu.x << 16), __uint_as_float(gu.x & 0xFFFF0000u),
+                  __uint_as_float(gu.y << 16), __uint_as_float(gu.y & 0xFFFF0000u)};
+    }
+  }
   auto finish = [&](long m, long n, f32x4 val) __attribute__((always_inline)) {
-    if constexpr (EPI == EPI_RESIDUAL) {
+    if constexpr (E == EPI_RESIDUAL) {
       const long rm = (g.res_rows < g.M ? m % g.res_rows : m) * g.ldr + n + z * g.sRes;
       if (res_bf16) {
         const uint2 u = *reinterpret_cast<const uint2*>(resb + rm);
@@ -793,7 +809,7 @@ gemm_nt_wide(GemmArgs g) {
       } else {
         val += *reinterpret_cast<const f32x4*>(res + rm);
       }
-    } else if constexpr (EPI == EPI_STORE) {
+    } else if constexpr (E == EPI_STORE) {
       if (cscale) val *= *reinterpret_cast<const f32x4*>(cscale + n);
     }
     OutT* cp = C + m * g.ldc + n;
@@ -812,7 +828,7 @@ gemm_nt_wide(GemmArgs g) {
   static_assert(64 % per_row == 0, "a lane's pieces share their columns");
   const int c4l = 4 * (lane % per_row);
   f32x4 csv = {1.f, 1.f, 1.f, 1.f};
-  if constexpr (EPI == EPI_STORE) {
+  if constexpr (E == EPI_STORE) {
     if (cscale && full_tile) csv = *reinterpret_cast<const f32x4*>(cscale + nw0 + c4l);
   }
   // the residual's type is fixed per call: two copies of the epilogue, so
@@ -835,21 +851,40 @@ gemm_nt_wide(GemmArgs g) {
       }
     };
     u32x4 rva[NP], rvb[NP];
-    if constexpr (EPI == EPI_RESIDUAL) {
+    if constexpr (E == EPI_RESIDUAL) {
       if constexpr (FT) load_res(0, rva);
     }
+    // SwiGLU row scale: a lane's 16 rows of block row i are 4 runs of 4
+    // (every tile is full); block row i + 1's are read before block row i
+    // is stored, since a read issued after the stores would wait for them
+    auto load_rs = [&](int i, f32x4 (&sv)[4]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        sv[q] = *reinterpret_cast<const f32x4*>(rsc + m0 + 128 * wm + 32 * i + 8 * q + 4 * h);
+    };
+    f32x4 rsa[4], rsb[4];
+    if constexpr (RS) load_rs(0, rsa);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       u32x4 (&rcur)[NP] = (i & 1) ? rvb : rva;
       u32x4 (&rnext)[NP] = (i & 1) ? rva : rvb;
-      if constexpr (EPI == EPI_RESIDUAL) {
+      if constexpr (E == EPI_RESIDUAL) {
         if (FT && i + 1 < 4) load_res(i + 1, rnext);
+      }
+      f32x4 (&scur)[4] = (i & 1) ? rsb : rsa;
+      if constexpr (RS) {
+        if (i + 1 < 4) load_rs(i + 1, (i & 1) ? rsa : rsb);
       }
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = 8 * (v >> 2) + 4 * h + (v & 3);
         if constexpr (swiglu) {
-          slab[row * EPS + r] = silu(acc[i][0][v]) * acc[i][1][v];
+          if constexpr (RS) {
+            const float sc = scur[v >> 2][v & 3];
+            slab[row * EPS + r] = silu(sc * acc[i][0][v]) * (sc * acc[i][1][v]);
+          } else {
+            slab[row * EPS + r] = silu(acc[i][0][v]) * acc[i][1][v];
+          }
         } else {
           slab[row * EPS + r] = acc[i][0][v];
           slab[row * EPS + 32 + r] = acc[i][1][v];
@@ -862,7 +897,7 @@ gemm_nt_wide(GemmArgs g) {
         for (int t = 0; t < NP; ++t) {
           const int rr = (lane + 64 * t) / per_row;
           f32x4 val = *reinterpret_cast<const f32x4*>(slab + rr * EPS + c4l);
-          if constexpr (EPI == EPI_RESIDUAL) {
+          if constexpr (E == EPI_RESIDUAL) {
             if constexpr (RB) {
               val[0] += __uint_as_float(rcur[t][0] << 16);
               val[1] += __uint_as_float(rcur[t][0] & 0xFFFF0000u);
@@ -874,8 +909,17 @@ gemm_nt_wide(GemmArgs g) {
               val[2] += __uint_as_float(rcur[t][2]);
               val[3] += __uint_as_float(rcur[t][3]);
             }
-          } else if constexpr (EPI == EPI_STORE) {
+          } else if constexpr (E == EPI_STORE) {
             val *= csv;
+          }
+          if constexpr (NORM) {
+            bf16_t* up = (bf16_t*)g.U + (mb + rr) * g.ldc + nw0 + c4l;
+            *reinterpret_cast<uint2*>(up) = uint2{pack_bf16x2(val[0] * gam[0], val[1] * gam[1]),
+                                                  pack_bf16x2(val[2] * gam[2], val[3] * gam[3])};
+            float ss = val[0] * val[0] + val[1] * val[1] + val[2] * val[2] + val[3] * val[3];
+#pragma unroll
+            for (int o = 8; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+            if ((lane & 15) == 0) g.rowss[(nw0 >> 6) * (long)g.M + mb + rr] = ss;
           }
           OutT* cp = C + (mb + rr) * g.ldc + nw0 + c4l;
           if constexpr (sizeof(OutT) == 4) {
@@ -900,10 +944,10 @@ gemm_nt_wide(GemmArgs g) {
           for (int e = 0; e < 4; ++e) {
             if (n + e > nmax) break;
             float x = val[e];
-            if constexpr (EPI == EPI_RESIDUAL) {
+            if constexpr (E == EPI_RESIDUAL) {
               const long rm = (g.res_rows < g.M ? m % g.res_rows : m) * g.ldr + n + e + z * g.sRes;
               x += res_bf16 ? bf2f(resb[rm]) : res[rm];
-            } else if constexpr (EPI == EPI_STORE) {
+            } else if constexpr (E == EPI_STORE) {
               if (cscale) x *= cscale[n + e];
             }
             stf(C + m * g.ldc + n + e, x);
@@ -913,7 +957,7 @@ gemm_nt_wide(GemmArgs g) {
       lds_wave_sync();
     }
   };
-  if (EPI == EPI_RESIDUAL && res_bf16) {
+  if (E == EPI_RESIDUAL && res_bf16) {
     if (full_tile)
       run_epilogue(std::true_type{}, std::true_type{});
     else
@@ -1034,7 +1078,7 @@ bool wide_ok(const GemmArgs& g) {
   if (g.in_dt != BF16) return false;
   if (g.K % wide::BK || g.lda % 8 || g.ldb % 8) return false;
   if (g.ldc % 4 || g.sC % 4) return false;
-  if (g.epi == EPI_RESIDUAL && (g.ldr % 4 || g.sRes % 4)) return false;
+  if ((g.epi == EPI_RESIDUAL || g.epi == EPI_RESNORM) && (g.ldr % 4 || g.sRes % 4)) return false;
   if (g.chunk > 0 && g.chunk % wide::BM) return false;
   // enough tiles to give every CU one
   const long tiles = (long)((g.M + wide::BM - 1) / wide::BM) *
@@ -1073,6 +1117,9 @@ const void* wide_kernel_epi(int epi) {
     case EPI_STORE: return (const void*)wide::gemm_nt_wide<OutT, EPI_STORE, CHUNKED>;
     case EPI_RESIDUAL: return (const void*)wide::gemm_nt_wide<OutT, EPI_RESIDUAL, CHUNKED>;
     case EPI_SWIGLU: return CHUNKED ? nullptr : (const void*)wide::gemm_nt_wide<OutT, EPI_SWIGLU, false>;
+    case EPI_RESNORM:
+      return CHUNKED || sizeof(OutT) != 4 ? nullptr
+                                          : (const void*)wide::gemm_nt_wide<float, EPI_RESNORM, false>;
     default: return nullptr;
   }
 }
@@ -1102,9 +1149,21 @@ hipError_t lds_attr(const void* kern, size_t bytes) {
 }
 }  // namespace
 
+bool gemm_wide_full(const GemmArgs& g) {
+  const int ncols = g.epi == EPI_SWIGLU ? wide::BN / 2 : wide::BN;
+  return g.M > 0 && !skinny_ok(g) && wide_ok(g) && g.batch <= 1 && g.chunk == 0 &&
+         g.M % wide::BM == 0 && g.N % ncols == 0;
+}
+
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   const int nb = g.batch > 0 ? g.batch : 1;
+  // the RMSNorm pieces exist in the full-tile 256 x 256 epilogue only
+  if (g.epi == EPI_RESNORM || g.rowscale) {
+    if (!gemm_wide_full(g) || g.in_dt != BF16 || (g.epi == EPI_RESNORM && (!g.U || !g.rowss ||
+                                                                           g.out_dt != F32)))
+      return hipErrorInvalidValue;
+  }
   if (skinny_ok(g)) {
     const int ncols = g.epi == EPI_SWIGLU ? 2 * g.N : g.N;
     const int nks = skinny::ksplit_for(g.N, g.K, g.epi);
@@ -1124,7 +1183,11 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
     return hipGetLastError();
   }
   if (wide_ok(g)) {
-    const void* kern = wide_kernel(g.out_dt == BF16, g.epi, g.chunk > 0);
+    const void* kern =
+        g.rowscale ? (g.out_dt == BF16 && g.epi == EPI_SWIGLU
+                          ? (const void*)wide::gemm_nt_wide<bf16_t, EPI_SWIGLU_RS, false>
+                          : nullptr)
+                   : wide_kernel(g.out_dt == BF16, g.epi, g.chunk > 0);
     if (!kern) return hipErrorInvalidValue;
     const hipError_t e = lds_attr(kern, wide::LDS_BYTES);
     if (e != hipSuccess) return e;

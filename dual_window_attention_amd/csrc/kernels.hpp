@@ -59,6 +59,12 @@ enum Epi {
   EPI_STORE = 0,        // C = acc (* colscale[n] if given)
   EPI_RESIDUAL = 1,     // C(f32) = acc + res[(m % res_rows) * ldr + n]
   EPI_SWIGLU = 2,       // C = silu(A Bg^T) * (A Bu^T); B2 = Bu, N = f
+                        //   (with rowscale: silu(s_m A Bg^T) * (s_m A Bu^T))
+  EPI_SWIGLU_RS = 4,    // (kernel selection only: EPI_SWIGLU with rowscale)
+  EPI_RESNORM = 3,      // EPI_RESIDUAL, and also U(bf16) = C * gamma[n] and the
+                        //   sum over each 64-column group of C^2 into
+                        //   rowss[(n / 64) * M + m]; the 256 x 256 tile only,
+                        //   full tiles only, batch 1, bf16 operands
 };
 struct GemmArgs {
   const void* A; long lda;
@@ -79,9 +85,20 @@ struct GemmArgs {
   // optional fp32 workspace for the few-row (M <= 32) split-K path; NULL
   // disables it (gemm_skinny_ws_floats gives the size it needs)
   float* ws; size_t ws_floats;
+  // EPI_RESNORM outputs (U [M, ldc] bf16; gamma [N] bf16 or NULL for ones;
+  // rowss [N / 64, M] fp32) and the EPI_SWIGLU row scale (NULL: none)
+  void* U; const void* gamma; float* rowss;
+  const float* rowscale;
 };
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
 size_t gemm_skinny_ws_floats(int M, int N, int K, int epi);
+// Whether launch_gemm runs g on the 256 x 256 tile with every tile full, the
+// condition for EPI_RESNORM and for a SwiGLU row scale.
+bool gemm_wide_full(const GemmArgs& g);
+// RMSNorm row scale from the EPI_RESNORM partials:
+//   rs[m] = 1 / sqrt(sum_j rowss[j * M + m] / N + eps), j < N / 64.
+hipError_t launch_rms_rowscale(const float* rowss, int M, int N, float eps, float* rs,
+                               hipStream_t s);
 
 // Fast-weight prefix states:
 //   acc = W0 (fp32); for i in [0, nstates): acc += A_i B_i^T over tokens of

@@ -546,6 +546,18 @@ __global__ void convert_kernel(const float* in, OutT* out, long n) {
   if (i < n) stf(out + i, in[i]);
 }
 
+// RMSNorm row scale from the 64-column partial sums of squares that the
+// output projection's epilogue leaves (the same scale as rmsnorm_kernel's,
+// the partials added in column order)
+__global__ void __launch_bounds__(256)
+rms_rowscale_kernel(const float* __restrict__ rowss, int M, int nparts, float inv_n, float eps,
+                    float* __restrict__ rs) {
+  const long m = (long)blockIdx.x * 256 + threadIdx.x;
+  if (m >= M) return;
+  float ss = 0.f;
+  for (int j = 0; j < nparts; ++j) ss += rowss[j * (long)M + m];
+  rs[m] = 1.f / sqrtf(ss * inv_n + eps);
+}
 }  // namespace
 
 size_t fw_stream_part_bytes(int B, int T, int f) {
@@ -704,6 +716,15 @@ hipError_t launch_state_prefix(const void* dw, long dw_chunks, const void* w0, v
                        n, nstates, nwrites);
   else
     return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_rms_rowscale(const float* rowss, int M, int N, float eps, float* rs,
+                               hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (N % 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rms_rowscale_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s,
+                     rowss, M, N / 64, 1.f / (float)N, eps, rs);
   return hipGetLastError();
 }
 
